@@ -28,9 +28,10 @@ from .codec import bf16_to_f64, fp8_decode
 
 
 def decode_kv(raw, kv_dtype, scale=1.0):
-    """Stored cache values -> exact float64 (fp8: decoded code times scale)."""
+    """Stored cache values -> exact float64: the decoded element times the
+    per-tensor scale (1 for a plain bf16 cache)."""
     if kv_dtype == "bf16":
-        return bf16_to_f64(raw)
+        return bf16_to_f64(raw) * np.float64(scale)
     if kv_dtype == "fp8":
         return fp8_decode(raw) * np.float64(scale)
     raise ValueError(kv_dtype)

@@ -5,7 +5,8 @@ precision" as a variable to control ([ES-lim]) and the deployment they report
 runs FP8; which fp8 variant is not stated.  Reading taken: OCP E4M3FN
 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
 infinities, the all-ones pattern S.1111.111 is NaN, largest finite 448),
-with a per-tensor fp32 scale: value = decode(code) * scale.
+with a per-tensor fp32 scale: value = decode(code) * scale.  The same
+per-tensor scale form is kept for a bf16 cache (scale 1 unless stated).
 """
 
 import numpy as np

@@ -17,7 +17,8 @@ Readings taken:
     two apart;
   * the new token sits at position pos = len_b - 1 (len_b counts it); its k
     (normalised and rotated) and v are stored into that cache slot, in the
-    cache format: fp8 codes of x / scale, or bf16 rounded to nearest-even;
+    cache format as x / scale (per-tensor scale, 1 for a plain bf16 cache):
+    fp8 codes, or bf16 rounded to nearest-even;
   * attention then uses the normalised, rotated q.
 """
 
@@ -93,8 +94,8 @@ def prologue_step(q, k_new, v_new, q_norm_w, k_norm_w, seq_lens, rms_eps,
         k_codes = fp8_encode(k_p / np.float64(k_scale))
         v_codes = fp8_encode(vf / np.float64(v_scale))
     elif kv_dtype == "bf16":
-        k_codes = bf16_encode(k_p)
-        v_codes = bf16_encode(vf)
+        k_codes = bf16_encode(k_p / np.float64(k_scale))
+        v_codes = bf16_encode(vf / np.float64(v_scale))
     else:
         raise ValueError(kv_dtype)
     return q_p, k_p, vf, k_codes, v_codes
