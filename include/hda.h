@@ -1,0 +1,205 @@
+/*
+ * hda.h -- dynamic split-KV paged decode attention on MI355X (gfx950).
+ *
+ * C ABI of libhda.so.  Plain C types and pointers only; no HIP or torch
+ * types appear here (a HIP stream is passed as an opaque void*).
+ *
+ * What the library computes (the method the pages describe as "Dynamic
+ * Attention"): one decode step of grouped-query attention for a batch of
+ * requests whose cached context lengths differ widely.  A host planner cuts
+ * every request's KV range into uniform tiles and spreads the tiles over a
+ * fixed set of persistent workgroups, rebuilt each step from the current
+ * lengths; the kernel computes per-item partial softmax results and merges
+ * partials of one request by log-sum-exp.  Sources: page "Tencent HPC llega
+ * a SGLang y desafía a los kernels de inferencia predeterminados"
+ * (remio.ai), section "Por qué Tencent HPC importa para el serving de
+ * modelos en línea" (uniform tiles assigned to thread blocks by the current
+ * workload, rebuilt as lengths change; a static split leaves units idle or
+ * launches empty chunks); page "腾讯混元三算子杀入 SGLang…" (arex-research.com),
+ * the Dynamic Attention paragraphs (a persistent kernel allocating tiles at
+ * every decode step by the actual KV length); page "vLLM × HPC-Ops:
+ * High-Performance Attention and MoE Backends from Tencent Hunyuan" (8sync
+ * summary): a per-step load-balanced scheduler replacing fixed split-KV,
+ * with a fused RoPE + QK-Norm + KV-write prologue.
+ *
+ * Conventions
+ *   - Every function that can fail returns an int status (HDA_OK = 0, errors
+ *     negative).  No C++ exception crosses this boundary.
+ *   - All memory is owned by the caller.  The library allocates no device
+ *     memory and never synchronises the stream.
+ *   - Host pointers are marked [host], device pointers [device].  Device
+ *     pointers must stay valid until the work enqueued on the stream ends.
+ *   - Functions are reentrant; there is no global mutable state.
+ */
+#ifndef HDA_H
+#define HDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HDA_VERSION 1
+#define HDA_PLAN_VERSION 1
+#define HDA_PLAN_HEADER_INTS 8
+
+/* status codes */
+#define HDA_OK 0
+#define HDA_ERR_INVALID_ARG (-1)   /* null pointer, non-positive size, bad length */
+#define HDA_ERR_CAPACITY (-2)      /* plan buffer too small; *plan_len = ints needed */
+#define HDA_ERR_UNSUPPORTED (-3)   /* shape or dtype this build has no kernel for */
+#define HDA_ERR_PLAN_MISMATCH (-4) /* plan built for another batch / other lengths */
+#define HDA_ERR_HIP (-5)           /* a HIP launch or runtime call failed */
+#define HDA_ERR_WORKSPACE (-6)     /* workspace missing or smaller than required */
+#define HDA_ERR_BAD_PLAN (-7)      /* plan array malformed (format, coverage, slots) */
+
+/* KV cache element types */
+#define HDA_KV_BF16 0      /* bfloat16 */
+#define HDA_KV_FP8_E4M3 1  /* OCP FP8 E4M3FN code, value = decode(code) * scale */
+
+/*
+ * Plan format (int32 array), produced by hda_plan / hda_plan_static:
+ *   [0..7]   header: VERSION, B, tile_len (0 for a static plan), W, T, N, P, 0
+ *            W workgroups, T tiles (chunks for a static plan), N items,
+ *            P partial slots
+ *   [8 ..]   wg_ptr[W+1]: items of workgroup w are wg_ptr[w] .. wg_ptr[w+1]-1
+ *   then     items[N][4] = (b, kv_begin, kv_end, slot); slot -1 means the item
+ *            covers its whole request and writes the output directly
+ *   then     req_part_ptr[B+1]: partial slots of request b are
+ *            req_part_ptr[b] .. req_part_ptr[b+1]-1
+ * Items of one request appear in token order and tile [0, len_b) exactly once.
+ * Total length: 8 + (W+1) + 4N + (B+1) ints.
+ */
+
+/*
+ * Upper bound on the plan length for `batch` requests over `n_workgroups`
+ * workgroups: 8 + (W+1) + 4(W+B-1) + (B+1).  Also bounds a static plan with
+ * n_workgroups = batch * n_splits.  Returns -1 for non-positive arguments.
+ */
+int64_t hda_plan_capacity(int32_t batch, int32_t n_workgroups);
+
+/*
+ * Per-step tile plan.  Tiles of `tile_len` tokens are taken request-major
+ * (tile j of request b covers [j*tile_len, min((j+1)*tile_len, len_b)));
+ * the T tiles are split contiguously over the W workgroups, the first
+ * (T mod W) taking one extra; consecutive tiles of one request within a
+ * workgroup form one item; requests with more than one item get partial
+ * slots numbered in item order.  Cost O(B + W + N), no allocation.
+ *
+ *   seq_lens   [host] int32[batch], every length >= 1 (the current KV length,
+ *              including a new token the prologue will write)
+ *   plan       [host] output array of `capacity` ints (may be NULL when
+ *              capacity is 0, to query the size)
+ *   plan_len   [host] receives the number of ints used (or needed)
+ * Errors: HDA_ERR_INVALID_ARG (null pointers, batch/tile_len/W < 1, a length
+ * < 1, T or W+B beyond int32), HDA_ERR_CAPACITY (buffer too small).
+ */
+int hda_plan(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
+             int32_t n_workgroups, int32_t* plan, int64_t capacity,
+             int64_t* plan_len);
+
+/*
+ * Static split baseline in the same format: request b is cut into n_splits
+ * chunks [floor(c*len_b/S), floor((c+1)*len_b/S)), chunk c handled by
+ * workgroup b*S + c (W = B*S); empty chunks leave their workgroup without an
+ * item.  This is the fixed split-KV schedule the dynamic plan is compared to.
+ * Errors as hda_plan.
+ */
+int hda_plan_static(const int32_t* seq_lens, int32_t batch, int32_t n_splits,
+                    int32_t* plan, int64_t capacity, int64_t* plan_len);
+
+/*
+ * Checks a plan against the lengths it will be used with: format and total
+ * length, wg_ptr monotone, items in range and covering each [0, len_b)
+ * exactly once in token order, slot numbering, and (for a dynamic plan) the
+ * tile count.  [host] pointers.  Returns HDA_OK, HDA_ERR_INVALID_ARG,
+ * HDA_ERR_PLAN_MISMATCH (batch or lengths differ) or HDA_ERR_BAD_PLAN.
+ */
+int hda_plan_validate(const int32_t* plan, int64_t plan_len,
+                      const int32_t* seq_lens, int32_t batch);
+
+/*
+ * Bytes of workspace hda_decode needs for this plan: partial outputs
+ * float32 [P][Hq][D], partial log-sum-exp float32 [P][Hq], and merge
+ * counters int32 [B][Hkv], each region aligned to 256 bytes.  Returns -1 for
+ * a malformed plan header or non-positive sizes.
+ */
+int64_t hda_workspace_bytes(const int32_t* plan, int64_t plan_len,
+                            int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim);
+
+typedef struct hda_params {
+  int32_t batch;              /* B, must equal the plan's batch */
+  int32_t n_q_heads;          /* Hq; Hq / Hkv (the group) in 1..16 */
+  int32_t n_kv_heads;         /* Hkv */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t page_size;          /* tokens per page: power of two, 16..1024 */
+  int32_t max_pages_per_req;  /* row length of block_table */
+  int64_t num_pages;          /* pages in each pool; ids outside are never read */
+  int32_t kv_dtype;           /* HDA_KV_BF16 or HDA_KV_FP8_E4M3 */
+  float sm_scale;             /* softmax scale, e.g. 1/sqrt(D) */
+  float k_scale;              /* per-tensor scale of K: value = stored * k_scale
+                                 (either dtype; 1 for a plain bf16 cache) */
+  float v_scale;              /* per-tensor scale of V, likewise */
+  /* fused new-token prologue (RMSNorm then rotate-half RoPE on q and k, then
+   * k and v stored into slot len_b - 1 of the cache, then attention) */
+  int32_t prologue;           /* 0 off, 1 on */
+  float rms_eps;
+  float rope_theta;
+  const void* q_norm_w;       /* [device] bf16 [D] */
+  const void* k_norm_w;       /* [device] bf16 [D] */
+  const void* k_new;          /* [device] bf16 [B][Hkv][D], pre-norm k of the new token */
+  const void* v_new;          /* [device] bf16 [B][Hkv][D] */
+  /* scratch: partials and merge counters, hda_workspace_bytes() bytes.
+   * Must be zero-filled before its first use; every completed hda_decode
+   * leaves the counters at zero again.  Calls that share a workspace must
+   * be ordered on one stream. */
+  void* workspace;            /* [device] */
+  int64_t workspace_bytes;
+} hda_params;
+
+/*
+ * One decode step: (optional prologue) + tile attention + log-sum-exp merge,
+ * enqueued as a single kernel launch on `stream`.  Asynchronous; no host
+ * synchronisation, no allocation.
+ *
+ *   q            [device] bf16 [B][Hq][D] (pre-norm when the prologue is on)
+ *   k_pages,
+ *   v_pages      [device] page pools [num_pages][Hkv][page_size][D] of bf16
+ *                or fp8 codes; written only by the prologue (slot len_b-1)
+ *   block_table  [device] int32 [B][max_pages_per_req]; token t of request b
+ *                is row t % page_size of page block_table[b][t / page_size]
+ *   seq_lens     [device] int32 [B], the same lengths the plan was built for
+ *   plan_host    [host] the plan (header read for the launch shape)
+ *   plan_dev     [device] an identical copy of the plan, plan_len ints
+ *   out          [device] float32 [B][Hq][D]
+ *   stream       hipStream_t, or NULL for the default stream
+ * q head h reads kv head floor(h * Hkv / Hq).  Rows past len_b are never
+ * used, whatever they hold.
+ * Errors (all detected on the host before any launch): HDA_ERR_INVALID_ARG,
+ * HDA_ERR_UNSUPPORTED, HDA_ERR_PLAN_MISMATCH, HDA_ERR_BAD_PLAN,
+ * HDA_ERR_WORKSPACE; HDA_ERR_HIP if the launch fails.  Device faults
+ * surface at the caller's next synchronisation.
+ */
+int hda_decode(const hda_params* p, const void* q, void* k_pages,
+               void* v_pages, const int32_t* block_table,
+               const int32_t* seq_lens, const int32_t* plan_host,
+               const int32_t* plan_dev, int64_t plan_len, float* out,
+               void* stream);
+
+/* Static description of a status code. */
+const char* hda_status_string(int status);
+
+/* HDA_VERSION of the built library. */
+int hda_version(void);
+
+/* sizeof(hda_params) in this build, for bindings that lay the struct out
+ * themselves. */
+int64_t hda_params_bytes(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HDA_H */

@@ -1,0 +1,636 @@
+// Dynamic split-KV paged decode attention for MI355X (gfx950 / CDNA4).
+//
+// One launch per decode step.  Workgroup (w, h) handles the work items that
+// the host plan gives workgroup w, for kv head h (grid = W * Hkv, kv head
+// fastest).  Each workgroup is 4 waves; the waves of a workgroup take the
+// 32-token chunks of an item round-robin, keep their own online-softmax
+// state, and combine through LDS when the item ends.  An item that covers a
+// whole request writes its output; the other items write a normalised
+// partial and its log-sum-exp, and the last workgroup to finish a request
+// (per kv head) merges that request's partials.
+//
+// Method: page "Tencent HPC llega a SGLang y desafía a los kernels de
+// inferencia predeterminados" (remio.ai), section "Por qué Tencent HPC
+// importa para el serving de modelos en línea" -- KV work cut into uniform
+// tiles and spread over thread blocks by the current lengths; arex-research
+// page, Dynamic Attention paragraphs -- a persistent kernel allocating tiles
+// per decode step by actual KV length; "vLLM × HPC-Ops" summary page -- the
+// load-balanced scheduler replaces fixed split-KV scheduling and a fused
+// RoPE + QK-Norm + KV-write prologue precedes attention.  The exact merge of
+// split partials by log-sum-exp and the online softmax are the standard
+// exact form of split-KV attention; the page layout, tile shapes and MFMA
+// mapping below are this library's own.
+//
+// Data path per chunk (32 tokens, one wave): K and V rows come straight from
+// HBM into VGPRs through buffer loads whose resource covers only the valid
+// rows of the page (rows past len read as zero, so poisoned or stale rows are
+// never seen).  QK^T and PV run on v_mfma_f32_16x16x32_bf16 with the group of
+// q heads padded to 16; V is transposed in registers (16-bit lane-local
+// shuffles) to give the PV product its token-contiguous operand.  The path is
+// HBM-bound (8 flop per KV byte for bf16), so MFMA only does the small dense
+// products.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "hda.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kWaves = 4;             // waves per workgroup
+constexpr int kChunk = 32;            // tokens per wave per step
+constexpr int kMaxGroup = 16;         // q heads per kv head (MFMA N)
+constexpr int kRsrcWord3 = 0x00020000;  // buffer resource dword 3 for gfx9 raw buffers
+
+struct Args {
+  const uint16_t* q;
+  uint8_t* k_pages;
+  uint8_t* v_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* plan;
+  float* out;
+  float* part_o;
+  float* part_lse;
+  int32_t* counters;
+  const uint16_t* q_norm_w;
+  const uint16_t* k_norm_w;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t page_stride;   // bytes per page (all kv heads)
+  int64_t num_pages;
+  int32_t head_stride;   // bytes per (page, kv head) slab
+  int32_t batch, n_q_heads, n_kv_heads, group;
+  int32_t page_size, log2_ps, max_pages;
+  int32_t n_wg, n_items, n_parts;
+  float qk_scale_log2;   // sm_scale * k_scale * log2(e)
+  float v_scale;
+  float k_scale, rms_eps, rope_theta;
+};
+
+template <int D, bool FP8>
+struct Geo {
+  static constexpr int ELEM = FP8 ? 1 : 2;
+  static constexpr int RB = D * ELEM;        // bytes per token row of one head
+  static constexpr int KL = D * ELEM / 64;   // 16-byte K loads per lane per 16-token half
+  static constexpr int VW = D * ELEM / 64;   // dwords of V per token per lane
+  static constexpr int DPL = D / 16;         // output d values per lane (PV N blocks)
+  static constexpr int STEPS = D / 32;       // QK k-steps of 32
+};
+
+// Registers of one in-flight chunk.
+template <int D, bool FP8>
+struct Chunk {
+  u32x4 k[2][Geo<D, FP8>::KL];
+  uint32_t v[8][Geo<D, FP8>::VW];
+};
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes,
+                                           kRsrcWord3);
+}
+
+__device__ inline float bf16_bits_to_float(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// Two fp32 values that are exact in bf16 -> one dword of two bf16 (lo first).
+__device__ inline uint32_t pack_bf16_exact(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// Four OCP E4M3FN codes -> four bf16 (exact: every code is a bf16 value).
+__device__ inline void fp8x4_to_bf16x4(uint32_t c, uint32_t& lo, uint32_t& hi) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
+  lo = pack_bf16_exact(a.x, a.y);
+  hi = pack_bf16_exact(b.x, b.y);
+}
+
+// fp32 -> OCP E4M3FN code: round to nearest, ties to even, saturating at
+// +-448, NaN -> 0x7F.  Written from the format: subnormals are multiples of
+// 2^-9 below 2^-6; a normal binade [2^e, 2^(e+1)) holds 8 steps of 2^(e-3).
+__device__ inline uint32_t fp8_encode(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a == a)) return 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
+  int e;
+  (void)frexpf(a, &e);                      // a = m * 2^e, m in [0.5, 1)
+  const float q = rintf(ldexpf(a, 4 - e));  // 1.mmm scaled to [8, 16]
+  uint32_t code = (uint32_t)((e + 6) << 3) + ((uint32_t)q - 8u);  // q == 16 carries
+  if (code > 0x7Eu) code = 0x7Eu;
+  return sign | code;
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// cos/sin of pos * theta^(-2l/D) for lane l < D/2, in double precision.
+__device__ inline void rope_angle(int pos, int lane, int D, float theta, float& c, float& s) {
+  const double inv = exp(-(2.0 * (double)lane / (double)D) * log((double)theta));
+  double sd, cd;
+  sincos((double)pos * inv, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// RMSNorm (over D, weight w) then rotate-half RoPE of one head vector held as
+// (x0 = x[lane], x1 = x[lane + D/2]) on lanes < D/2.
+__device__ inline void norm_rope(float& x0, float& x1, bool act, const uint16_t* w, int lane,
+                                 int D, float eps, float c, float s) {
+  const float ss = wave_sum(act ? x0 * x0 + x1 * x1 : 0.0f);
+  const float r = 1.0f / sqrtf(ss / (float)D + eps);
+  if (act) {
+    const float y0 = x0 * r * bf16_bits_to_float(w[lane]);
+    const float y1 = x1 * r * bf16_bits_to_float(w[lane + D / 2]);
+    x0 = y0 * c - y1 * s;
+    x1 = y1 * c + y0 * s;
+  }
+}
+
+// Start of the 8 contiguous head dims a lane feeds to QK step s.  Any
+// assignment works as long as K and q use the same one; this one makes each
+// lane's K load 16 contiguous bytes.
+template <bool FP8>
+__device__ inline int qk_dim(int s, int kg) {
+  return FP8 ? 64 * (s >> 1) + 16 * kg + 8 * (s & 1) : 32 * s + 8 * kg;
+}
+
+template <int D, bool FP8>
+__device__ inline bf16x8 k_operand(const Chunk<D, FP8>& ch, int hf, int s) {
+  if constexpr (!FP8) {
+    return __builtin_bit_cast(bf16x8, ch.k[hf][s]);
+  } else {
+    const u32x4 raw = ch.k[hf][s >> 1];
+    const uint32_t c0 = (s & 1) ? raw[2] : raw[0];
+    const uint32_t c1 = (s & 1) ? raw[3] : raw[1];
+    uint32_t o0, o1, o2, o3;
+    fp8x4_to_bf16x4(c0, o0, o1);
+    fp8x4_to_bf16x4(c1, o2, o3);
+    return __builtin_bit_cast(bf16x8, u32x4{o0, o1, o2, o3});
+  }
+}
+
+// Buffer resources for the two 16-token halves of chunk c of (request b,
+// kv head h).  A half with no valid rows (past len, outside the block table
+// or an out-of-range page id) gets an empty resource and reads zeros.
+template <int D, bool FP8>
+__device__ inline void chunk_rsrc(const Args& a, int b, int L, int h, int c, bool live,
+                                  __amdgpu_buffer_rsrc_t (&kr)[2],
+                                  __amdgpu_buffer_rsrc_t (&vr)[2]) {
+  using G = Geo<D, FP8>;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int t = c * kChunk + 16 * hf;
+    int rows = L - t;
+    rows = rows > 16 ? 16 : rows;
+    int64_t off = 0;
+    int bytes = 0;
+    if (live && rows > 0) {
+      const int pidx = t >> a.log2_ps;
+      if (pidx < a.max_pages) {
+        const int64_t page = a.block_table[(int64_t)b * a.max_pages + pidx];
+        if (page >= 0 && page < a.num_pages) {
+          off = page * a.page_stride + (int64_t)h * a.head_stride +
+                (int64_t)(t & (a.page_size - 1)) * G::RB;
+          bytes = rows * G::RB;
+        }
+      }
+    }
+    kr[hf] = make_rsrc(a.k_pages + off, bytes);
+    vr[hf] = make_rsrc(a.v_pages + off, bytes);
+  }
+}
+
+template <int D, bool FP8>
+__device__ inline void issue_chunk(Chunk<D, FP8>& ch, const __amdgpu_buffer_rsrc_t (&kr)[2],
+                                   const __amdgpu_buffer_rsrc_t (&vr)[2], int i, int kg) {
+  using G = Geo<D, FP8>;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int u = 0; u < G::KL; ++u)
+      ch.k[hf][u] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr[hf], i * G::RB + 64 * u + 16 * kg, 0, 0));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int hf = j >> 2;
+    const int off = (4 * kg + (j & 3)) * G::RB + i * G::VW * 4;
+    if constexpr (G::VW == 4) {
+      const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr[hf], off, 0, 0));
+      ch.v[j][0] = x[0]; ch.v[j][1] = x[1]; ch.v[j][2] = x[2]; ch.v[j][3] = x[3];
+    } else if constexpr (G::VW == 2) {
+      const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr[hf], off, 0, 0));
+      ch.v[j][0] = x[0]; ch.v[j][1] = x[1];
+    } else {
+      ch.v[j][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(vr[hf], off, 0, 0);
+    }
+  }
+}
+
+// One chunk: S^T = K Q^T on MFMA, online-softmax update, acc += P V on MFMA.
+// Lane (i = lane % 16, kg = lane / 16): score of q head i for tokens
+// 16*hf + 4*kg + r; PV accumulator for q head 4*kg + r, head dim DPL*i + nb.
+template <int D, bool FP8>
+__device__ inline void compute_chunk(const Chunk<D, FP8>& ch, const bf16x8 (&qop)[Geo<D, FP8>::STEPS],
+                                     int c, int k0, int k1, float qk_scale_log2, int kg,
+                                     float& m_run, float& l_run, f32x4 (&acc)[Geo<D, FP8>::DPL]) {
+  using G = Geo<D, FP8>;
+  f32x4 sacc[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    sacc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < G::STEPS; ++s)
+      sacc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<D, FP8>(ch, hf, s), qop[s],
+                                                         sacc[hf], 0, 0, 0);
+  }
+  float sc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sc[j] = sacc[j >> 2][j & 3] * qk_scale_log2;
+  const int t0 = c * kChunk;
+  if (t0 < k0 || t0 + kChunk > k1) {  // partial chunk: mask tokens outside [k0, k1)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = t0 + 16 * (j >> 2) + 4 * kg + (j & 3);
+      if (t < k0 || t >= k1) sc[j] = -INFINITY;
+    }
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  bf16x8 pop;
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 p = (__bf16)__builtin_amdgcn_exp2f(sc[j] - m_new);
+    pop[j] = p;
+    psum += (float)p;   // normalise with the same rounded weights PV uses
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  if (__ballot(alpha != 1.0f) != 0) {
+    float ar[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * kg + r);
+#pragma unroll
+    for (int nb = 0; nb < G::DPL; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[nb][r] *= ar[r];
+  }
+  // V rows as bf16 pairs: rows[j][a] holds head dims DPL*i + 2a, +1 of token j.
+  uint32_t rows[8][G::DPL / 2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int a2 = 0; a2 < G::DPL / 2; ++a2) rows[j][a2] = ch.v[j][a2];
+    } else {
+#pragma unroll
+      for (int u = 0; u < G::VW; ++u) fp8x4_to_bf16x4(ch.v[j][u], rows[j][2 * u], rows[j][2 * u + 1]);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < G::DPL; ++nb) {
+    const int a2 = nb >> 1;
+    u32x4 bv;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = rows[2 * q][a2], hi = rows[2 * q + 1][a2];
+      bv[q] = (nb & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop, __builtin_bit_cast(bf16x8, bv), acc[nb], 0, 0, 0);
+  }
+}
+
+template <int D, bool FP8, bool PRO>
+__global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(Args a) {
+  using G = Geo<D, FP8>;
+  __shared__ float sm_acc[kWaves][kMaxGroup][D];
+  __shared__ float sm_m[kWaves][kMaxGroup];
+  __shared__ float sm_l[kWaves][kMaxGroup];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_q[kMaxGroup][D];
+  __shared__ int sm_last;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, kg = lane >> 4;
+  const int h = blockIdx.x % a.n_kv_heads;
+  const int w = blockIdx.x / a.n_kv_heads;
+  const int g = a.group;
+  const int32_t* wg_ptr = a.plan + HDA_PLAN_HEADER_INTS;
+  const int32_t* items = wg_ptr + a.n_wg + 1;
+  const int32_t* rpp = items + 4 * a.n_items;
+  const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
+  if (it_begin >= it_end) return;
+
+  if constexpr (PRO) {
+    // New token of each request whose last item is ours: k' = RoPE(RMSNorm(k)),
+    // v as given, both stored into slot len-1 for this kv head.  Only this
+    // workgroup reads that row (it lies inside its item), so a fence and a
+    // barrier order the write before the chunk loads.
+    if (wave == 0) {
+      for (int it = it_begin; it < it_end; ++it) {
+        const int b = items[4 * it], k1 = items[4 * it + 2];
+        if ((unsigned)b >= (unsigned)a.batch) continue;
+        const int L = a.seq_lens[b];
+        if (k1 != L || L < 1) continue;
+        const int pos = L - 1, pidx = pos >> a.log2_ps;
+        if (pidx >= a.max_pages) continue;
+        const int64_t page = a.block_table[(int64_t)b * a.max_pages + pidx];
+        if (page < 0 || page >= a.num_pages) continue;
+        const bool act = lane < D / 2;
+        float c = 1.f, s = 0.f;
+        if (act) rope_angle(pos, lane, D, a.rope_theta, c, s);
+        const int64_t src = ((int64_t)b * a.n_kv_heads + h) * D;
+        float k0v = act ? bf16_bits_to_float(a.k_new[src + lane]) : 0.f;
+        float k1v = act ? bf16_bits_to_float(a.k_new[src + lane + D / 2]) : 0.f;
+        norm_rope(k0v, k1v, act, a.k_norm_w, lane, D, a.rms_eps, c, s);
+        if (act) {
+          const float v0 = bf16_bits_to_float(a.v_new[src + lane]);
+          const float v1 = bf16_bits_to_float(a.v_new[src + lane + D / 2]);
+          const int64_t row = page * a.page_stride + (int64_t)h * a.head_stride +
+                              (int64_t)(pos & (a.page_size - 1)) * G::RB;
+          if constexpr (FP8) {
+            a.k_pages[row + lane] = (uint8_t)fp8_encode(k0v / a.k_scale);
+            a.k_pages[row + lane + D / 2] = (uint8_t)fp8_encode(k1v / a.k_scale);
+            a.v_pages[row + lane] = (uint8_t)fp8_encode(v0 / a.v_scale);
+            a.v_pages[row + lane + D / 2] = (uint8_t)fp8_encode(v1 / a.v_scale);
+          } else {
+            uint16_t* kp = reinterpret_cast<uint16_t*>(a.k_pages + row);
+            uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pages + row);
+            kp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(k0v / a.k_scale));
+            kp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(k1v / a.k_scale));
+            vp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(v0 / a.v_scale));
+            vp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(v1 / a.v_scale));
+          }
+        }
+      }
+    }
+    __threadfence();
+    __syncthreads();
+  }
+
+  for (int it = it_begin; it < it_end; ++it) {
+    const int b = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
+              slot = items[4 * it + 3];
+    if ((unsigned)b >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
+    const int L = a.seq_lens[b];
+    const int64_t qrow0 = ((int64_t)b * a.n_q_heads + (int64_t)h * g) * D;
+
+    // q operand (MFMA B): lane (i, kg) holds q head i, dims qk_dim(s, kg) + 0..7.
+    bf16x8 qop[G::STEPS];
+    if constexpr (PRO) {
+      const bool act = lane < D / 2;
+      float c = 1.f, s = 0.f;
+      if (act) rope_angle(L - 1, lane, D, a.rope_theta, c, s);
+      for (int hh = wave; hh < g; hh += kWaves) {
+        float x0 = act ? bf16_bits_to_float(a.q[qrow0 + (int64_t)hh * D + lane]) : 0.f;
+        float x1 = act ? bf16_bits_to_float(a.q[qrow0 + (int64_t)hh * D + lane + D / 2]) : 0.f;
+        norm_rope(x0, x1, act, a.q_norm_w, lane, D, a.rms_eps, c, s);
+        if (act) {
+          sm_q[hh][lane] = __builtin_bit_cast(uint16_t, (__bf16)x0);
+          sm_q[hh][lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)x1);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s2 = 0; s2 < G::STEPS; ++s2) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (i < g) v = *reinterpret_cast<const u32x4*>(&sm_q[i][qk_dim<FP8>(s2, kg)]);
+        qop[s2] = __builtin_bit_cast(bf16x8, v);
+      }
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < G::STEPS; ++s2) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (i < g) v = *reinterpret_cast<const u32x4*>(a.q + qrow0 + (int64_t)i * D + qk_dim<FP8>(s2, kg));
+        qop[s2] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[G::DPL];
+#pragma unroll
+    for (int nb = 0; nb < G::DPL; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
+    const int c_last = (k1 - 1) / kChunk;
+    int c = k0 / kChunk + wave;
+    if (c <= c_last) {
+      Chunk<D, FP8> A, B;
+      __amdgpu_buffer_rsrc_t kr[2], vr[2];
+      chunk_rsrc<D, FP8>(a, b, L, h, c, true, kr, vr);
+      issue_chunk<D, FP8>(A, kr, vr, i, kg);
+      while (true) {
+        int cn = c + kWaves;
+        chunk_rsrc<D, FP8>(a, b, L, h, cn, cn <= c_last, kr, vr);
+        issue_chunk<D, FP8>(B, kr, vr, i, kg);
+        compute_chunk<D, FP8>(A, qop, c, k0, k1, a.qk_scale_log2, kg, m_run, l_run, acc);
+        c = cn;
+        if (c > c_last) break;
+        cn = c + kWaves;
+        chunk_rsrc<D, FP8>(a, b, L, h, cn, cn <= c_last, kr, vr);
+        issue_chunk<D, FP8>(A, kr, vr, i, kg);
+        compute_chunk<D, FP8>(B, qop, c, k0, k1, a.qk_scale_log2, kg, m_run, l_run, acc);
+        c = cn;
+        if (c > c_last) break;
+      }
+    }
+
+    // Combine the waves of this workgroup.
+    float l_tot = l_run;
+    l_tot += __shfl_xor(l_tot, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (kg == 0) {
+      sm_m[wave][i] = m_run;
+      sm_l[wave][i] = l_tot;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hh = 4 * kg + r;
+      if (hh < g) {
+#pragma unroll
+        for (int v4 = 0; v4 < G::DPL / 4; ++v4) {
+          f32x4 o = {acc[4 * v4][r], acc[4 * v4 + 1][r], acc[4 * v4 + 2][r], acc[4 * v4 + 3][r]};
+          *reinterpret_cast<f32x4*>(&sm_acc[wave][hh][G::DPL * i + 4 * v4]) = o;
+        }
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < g * D; idx += 64 * kWaves) {
+      const int hh = idx / D, d = idx - hh * D;
+      float M = sm_m[0][hh];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+      float lsum = 0.f, o = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float wt = __builtin_amdgcn_exp2f(sm_m[ww][hh] - M);
+        lsum += wt * sm_l[ww][hh];
+        o += wt * sm_acc[ww][hh][d];
+      }
+      o = o / lsum * a.v_scale;
+      const int64_t hq = (int64_t)h * g + hh;
+      if (slot < 0) {
+        a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = o;
+      } else {
+        a.part_o[((int64_t)slot * a.n_q_heads + hq) * D + d] = o;
+        if (d == 0)
+          a.part_lse[(int64_t)slot * a.n_q_heads + hq] = (M + log2f(lsum)) * 0.69314718055994531f;
+      }
+    }
+
+    if (slot >= 0) {
+      // Last workgroup to finish request b (for this kv head) merges its
+      // partials in slot order.
+      const int s0 = max(0, rpp[b]), s1 = min(a.n_parts, rpp[b + 1]);
+      __threadfence();
+      __syncthreads();
+      if (tid == 0) {
+        const int old = atomicAdd(&a.counters[(int64_t)b * a.n_kv_heads + h], 1);
+        sm_last = (old == s1 - s0 - 1);
+      }
+      __syncthreads();
+      if (sm_last) {
+        __threadfence();
+        for (int idx = tid; idx < g * D; idx += 64 * kWaves) {
+          const int hh = idx / D, d = idx - hh * D;
+          const int64_t hq = (int64_t)h * g + hh;
+          float M = -INFINITY;
+          for (int sl = s0; sl < s1; ++sl)
+            M = fmaxf(M, __hip_atomic_load(&a.part_lse[(int64_t)sl * a.n_q_heads + hq],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          float wsum = 0.f, o = 0.f;
+          for (int sl = s0; sl < s1; ++sl) {
+            const float lse = __hip_atomic_load(&a.part_lse[(int64_t)sl * a.n_q_heads + hq],
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float po = __hip_atomic_load(&a.part_o[((int64_t)sl * a.n_q_heads + hq) * D + d],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float wt = expf(lse - M);
+            wsum += wt;
+            o += wt * po;
+          }
+          a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = o / wsum;
+        }
+        if (tid == 0)
+          __hip_atomic_store(&a.counters[(int64_t)b * a.n_kv_heads + h], 0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();  // LDS is reused by the next item
+  }
+}
+
+template <int D, bool FP8, bool PRO>
+hipError_t launch(const Args& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, PRO>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const Args& a, bool fp8, bool pro, int grid, hipStream_t st) {
+  if (fp8) return pro ? launch<D, true, true>(a, grid, st) : launch<D, true, false>(a, grid, st);
+  return pro ? launch<D, false, true>(a, grid, st) : launch<D, false, false>(a, grid, st);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, void* v_pages,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          const int32_t* plan_host, const int32_t* plan_dev, int64_t plan_len,
+                          float* out, void* stream) {
+  if (!p || !q || !k_pages || !v_pages || !block_table || !seq_lens || !plan_host ||
+      !plan_dev || !out)
+    return HDA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1 || p->head_dim < 1 ||
+      p->page_size < 1 || p->max_pages_per_req < 1 || p->num_pages < 1)
+    return HDA_ERR_INVALID_ARG;
+  if (!(p->sm_scale > 0.f) || !(p->k_scale > 0.f) || !(p->v_scale > 0.f) ||
+      !isfinite(p->sm_scale) || !isfinite(p->k_scale) || !isfinite(p->v_scale))
+    return HDA_ERR_INVALID_ARG;
+  if (p->n_q_heads % p->n_kv_heads != 0) return HDA_ERR_INVALID_ARG;
+  const int g = p->n_q_heads / p->n_kv_heads;
+  if (g > kMaxGroup) return HDA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return HDA_ERR_UNSUPPORTED;
+  if (p->page_size < 16 || p->page_size > 1024 || (p->page_size & (p->page_size - 1)))
+    return HDA_ERR_UNSUPPORTED;
+  if (p->kv_dtype != HDA_KV_BF16 && p->kv_dtype != HDA_KV_FP8_E4M3) return HDA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages)) return HDA_ERR_INVALID_ARG;
+  if (p->prologue) {
+    if (!p->q_norm_w || !p->k_norm_w || !p->k_new || !p->v_new) return HDA_ERR_INVALID_ARG;
+    if (!(p->rms_eps >= 0.f) || !(p->rope_theta > 0.f)) return HDA_ERR_INVALID_ARG;
+  }
+  if (plan_len < HDA_PLAN_HEADER_INTS || plan_host[0] != HDA_PLAN_VERSION) return HDA_ERR_BAD_PLAN;
+  if (plan_host[1] != p->batch) return HDA_ERR_PLAN_MISMATCH;
+  const int64_t W = plan_host[3], N = plan_host[5], P = plan_host[6];
+  if (W < 1 || N < 1 || P < 0 || plan_len != HDA_PLAN_HEADER_INTS + (W + 1) + 4 * N + p->batch + 1)
+    return HDA_ERR_BAD_PLAN;
+  const int64_t grid = W * p->n_kv_heads;
+  if (grid > 0x7fffffffLL) return HDA_ERR_UNSUPPORTED;
+  const int64_t ws_need = hda_workspace_bytes(plan_host, plan_len, p->n_q_heads, p->n_kv_heads,
+                                              p->head_dim);
+  if (ws_need < 0) return HDA_ERR_BAD_PLAN;
+  if (P > 0 && (!p->workspace || p->workspace_bytes < ws_need)) return HDA_ERR_WORKSPACE;
+
+  const int D = p->head_dim;
+  const int elem = p->kv_dtype == HDA_KV_FP8_E4M3 ? 1 : 2;
+  Args a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pages = static_cast<uint8_t*>(k_pages);
+  a.v_pages = static_cast<uint8_t*>(v_pages);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.plan = plan_dev;
+  a.out = out;
+  uint8_t* ws = static_cast<uint8_t*>(p->workspace);
+  const int64_t o_bytes = (P * p->n_q_heads * D * 4 + 255) / 256 * 256;
+  const int64_t l_bytes = (P * p->n_q_heads * 4 + 255) / 256 * 256;
+  a.part_o = ws ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_lse = ws ? reinterpret_cast<float*>(ws + o_bytes) : nullptr;
+  a.counters = ws ? reinterpret_cast<int32_t*>(ws + o_bytes + l_bytes) : nullptr;
+  a.q_norm_w = static_cast<const uint16_t*>(p->q_norm_w);
+  a.k_norm_w = static_cast<const uint16_t*>(p->k_norm_w);
+  a.k_new = static_cast<const uint16_t*>(p->k_new);
+  a.v_new = static_cast<const uint16_t*>(p->v_new);
+  a.head_stride = p->page_size * D * elem;
+  a.page_stride = (int64_t)a.head_stride * p->n_kv_heads;
+  a.num_pages = p->num_pages;
+  a.batch = p->batch;
+  a.n_q_heads = p->n_q_heads;
+  a.n_kv_heads = p->n_kv_heads;
+  a.group = g;
+  a.page_size = p->page_size;
+  a.log2_ps = __builtin_ctz((unsigned)p->page_size);
+  a.max_pages = p->max_pages_per_req;
+  a.n_wg = (int32_t)W;
+  a.n_items = (int32_t)N;
+  a.n_parts = (int32_t)P;
+  a.qk_scale_log2 = (float)((double)p->sm_scale * (double)p->k_scale * 1.4426950408889634);
+  a.v_scale = p->v_scale;
+  a.k_scale = p->k_scale;
+  a.rms_eps = p->rms_eps;
+  a.rope_theta = p->rope_theta;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
+  hipError_t e = D == 64 ? launch_d<64>(a, fp8, p->prologue != 0, (int)grid, st)
+                         : launch_d<128>(a, fp8, p->prologue != 0, (int)grid, st);
+  return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
+}

@@ -1,0 +1,280 @@
+"""ctypes binding of libhda.so (include/hda.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+library.  PyTorch supplies device memory and streams.  Importing this module
+does not load the library; the first call does, and raises if libhda.so is
+missing -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhda.so")
+
+HDA_OK = 0
+HDA_ERR_INVALID_ARG = -1
+HDA_ERR_CAPACITY = -2
+HDA_ERR_UNSUPPORTED = -3
+HDA_ERR_PLAN_MISMATCH = -4
+HDA_ERR_HIP = -5
+HDA_ERR_WORKSPACE = -6
+HDA_ERR_BAD_PLAN = -7
+
+HDA_KV_BF16 = 0
+HDA_KV_FP8_E4M3 = 1
+PLAN_HEADER_INTS = 8
+
+# every symbol include/hda.h declares
+EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_plan_static", "hda_plan_validate",
+           "hda_workspace_bytes", "hda_decode", "hda_status_string", "hda_version",
+           "hda_params_bytes")
+
+
+class HdaError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: {hda_status_string(status)} ({status})")
+
+
+class hda_params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_req", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("kv_dtype", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
+        ("prologue", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float),
+        ("rope_theta", ctypes.c_float),
+        ("q_norm_w", ctypes.c_void_p),
+        ("k_norm_w", ctypes.c_void_p),
+        ("k_new", ctypes.c_void_p),
+        ("v_new", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libhda.so (once).  Raises OSError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise OSError(f"libhda.so not found at {path}; run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    pi64 = ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "hda_plan_capacity": (i64, [i32, i32]),
+        "hda_plan": (ctypes.c_int, [pi32, i32, i32, i32, pi32, i64, pi64]),
+        "hda_plan_static": (ctypes.c_int, [pi32, i32, i32, pi32, i64, pi64]),
+        "hda_plan_validate": (ctypes.c_int, [pi32, i64, pi32, i32]),
+        "hda_workspace_bytes": (i64, [pi32, i64, i32, i32, i32]),
+        "hda_decode": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp, pi32, vp,
+                                      i64, vp, vp]),
+        "hda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "hda_version": (ctypes.c_int, []),
+        "hda_params_bytes": (i64, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.hda_params_bytes() != ctypes.sizeof(hda_params):
+        raise OSError("hda_params layout differs between libhda.so and this binding")
+    _lib = lib
+    return lib
+
+
+def _i32p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _lens(seq_lens):
+    a = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if a.ndim != 1:
+        raise ValueError("seq_lens must be 1-D")
+    return a
+
+
+def hda_status_string(status: int) -> str:
+    return load_library().hda_status_string(int(status)).decode()
+
+
+def hda_version() -> int:
+    return load_library().hda_version()
+
+
+def hda_plan_capacity(batch: int, n_workgroups: int) -> int:
+    return load_library().hda_plan_capacity(int(batch), int(n_workgroups))
+
+
+def _plan_call(fn, lens, *args):
+    lib = load_library()
+    n = ctypes.c_int64(0)
+    st = fn(_i32p(lens), len(lens), *args, None, 0, ctypes.byref(n))
+    if st not in (HDA_OK, HDA_ERR_CAPACITY, HDA_ERR_INVALID_ARG):
+        raise HdaError(st, fn.__name__)
+    if st == HDA_ERR_INVALID_ARG and n.value == 0:
+        raise HdaError(st, fn.__name__)
+    plan = np.empty(n.value, dtype=np.int32)
+    st = fn(_i32p(lens), len(lens), *args, _i32p(plan), plan.size, ctypes.byref(n))
+    if st != HDA_OK:
+        raise HdaError(st, fn.__name__)
+    return plan
+
+
+def hda_plan(seq_lens, tile_len: int, n_workgroups: int) -> np.ndarray:
+    """Dynamic tile plan (int32 array) for the host lengths."""
+    lib = load_library()
+    return _plan_call(lib.hda_plan, _lens(seq_lens), int(tile_len), int(n_workgroups))
+
+
+def hda_plan_static(seq_lens, n_splits: int) -> np.ndarray:
+    """Static split baseline plan (int32 array)."""
+    lib = load_library()
+    return _plan_call(lib.hda_plan_static, _lens(seq_lens), int(n_splits))
+
+
+def hda_plan_validate(plan, seq_lens) -> int:
+    """Status code of hda_plan_validate (HDA_OK when the plan fits the lengths)."""
+    lib = load_library()
+    plan = np.ascontiguousarray(plan, dtype=np.int32)
+    lens = _lens(seq_lens)
+    return lib.hda_plan_validate(_i32p(plan), plan.size, _i32p(lens), len(lens))
+
+
+def hda_workspace_bytes(plan, n_q_heads: int, n_kv_heads: int, head_dim: int) -> int:
+    lib = load_library()
+    plan = np.ascontiguousarray(plan, dtype=np.int32)
+    return lib.hda_workspace_bytes(_i32p(plan), plan.size, int(n_q_heads), int(n_kv_heads),
+                                   int(head_dim))
+
+
+def hda_decode(params: hda_params, q, k_pages, v_pages, block_table, seq_lens, plan_host,
+               plan_dev, out, stream=None) -> None:
+    """Enqueue one decode step.  q, k_pages, ... are device pointers (ints) or
+    torch tensors; plan_host is the host int32 array; stream is a raw
+    hipStream_t (int) or a torch stream, default the current torch stream."""
+    lib = load_library()
+    plan_host = np.ascontiguousarray(plan_host, dtype=np.int32)
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    if hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = lib.hda_decode(ctypes.byref(params), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                        _ptr(block_table), _ptr(seq_lens), _i32p(plan_host), _ptr(plan_dev),
+                        plan_host.size, _ptr(out), ctypes.c_void_p(int(stream) if stream else 0))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_decode")
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return ctypes.c_void_p(x.data_ptr())
+    return ctypes.c_void_p(int(x))
+
+
+class DeviceBatch:
+    """Device-resident copy of one generated batch (torch tensors) plus the
+    hda_params that describe it.  Convenience for tests and the bench."""
+
+    def __init__(self, tensors, params_kw, device):
+        self.t = tensors
+        self.kw = params_kw
+        self.device = device
+        self._ws = None
+
+    @classmethod
+    def from_inputs(cls, inp, device="cuda:0"):
+        import torch
+        w = inp["workload"]
+        t = {
+            "q": torch.from_numpy(inp["q"].view(np.int16)).to(device),
+            "k_pages": torch.from_numpy(inp["k_pages"].view(np.uint8).reshape(-1)).to(device),
+            "v_pages": torch.from_numpy(inp["v_pages"].view(np.uint8).reshape(-1)).to(device),
+            "block_table": torch.from_numpy(inp["block_table"]).to(device),
+            "seq_lens": torch.from_numpy(inp["seq_lens"]).to(device),
+        }
+        kw = dict(batch=len(inp["seq_lens"]), n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                  head_dim=w.head_dim, page_size=w.page_size,
+                  max_pages_per_req=inp["block_table"].shape[1],
+                  num_pages=inp["k_pages"].shape[0],
+                  kv_dtype=HDA_KV_FP8_E4M3 if w.kv_dtype == "fp8" else HDA_KV_BF16,
+                  sm_scale=float(inp["sm_scale"]), k_scale=float(inp["k_scale"]),
+                  v_scale=float(inp["v_scale"]), prologue=0)
+        if w.prologue:
+            for k in ("q_norm_w", "k_norm_w", "k_new", "v_new"):
+                t[k] = torch.from_numpy(inp[k].view(np.int16)).to(device)
+            kw.update(prologue=1, rms_eps=float(inp["rms_eps"]), rope_theta=float(inp["rope_theta"]))
+        return cls(t, kw, device)
+
+    def workspace(self, nbytes):
+        import torch
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def params(self, plan, workspace=None):
+        p = hda_params(**self.kw)
+        t = self.t
+        if self.kw.get("prologue"):
+            p.q_norm_w = t["q_norm_w"].data_ptr()
+            p.k_norm_w = t["k_norm_w"].data_ptr()
+            p.k_new = t["k_new"].data_ptr()
+            p.v_new = t["v_new"].data_ptr()
+        need = hda_workspace_bytes(plan, self.kw["n_q_heads"], self.kw["n_kv_heads"],
+                                   self.kw["head_dim"])
+        ws = workspace if workspace is not None else self.workspace(need)
+        p.workspace = ws.data_ptr()
+        p.workspace_bytes = ws.numel()
+        return p
+
+    def decode(self, plan, out=None, plan_dev=None, stream=None, k_pages=None, v_pages=None,
+               block_table=None):
+        import torch
+        plan = np.ascontiguousarray(plan, dtype=np.int32)
+        t = self.t
+        if out is None:
+            out = torch.empty((self.kw["batch"], self.kw["n_q_heads"], self.kw["head_dim"]),
+                              dtype=torch.float32, device=self.device)
+        if plan_dev is None:
+            plan_dev = torch.from_numpy(plan).to(self.device)
+        p = self.params(plan)
+        hda_decode(p, t["q"], t["k_pages"] if k_pages is None else k_pages,
+                   t["v_pages"] if v_pages is None else v_pages,
+                   t["block_table"] if block_table is None else block_table,
+                   t["seq_lens"], plan, plan_dev, out, stream)
+        return out
+
+
+def launch_config(seq_lens, n_kv_heads: int, n_cu: int = 256, wg_per_cu: int = 2,
+                  tile_len: int = 128):
+    """Default (tile_len, n_workgroups) for a step: enough workgroups for
+    `wg_per_cu` resident 4-wave workgroups per compute unit across all kv
+    heads, never more than there are tiles."""
+    lens = _lens(seq_lens)
+    T = int(((lens.astype(np.int64) + tile_len - 1) // tile_len).sum())
+    W = max(1, min(T, (n_cu * wg_per_cu) // max(1, int(n_kv_heads))))
+    return tile_len, W

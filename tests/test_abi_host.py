@@ -1,0 +1,205 @@
+"""Host side of the C ABI (CPU only): the library loads and exports every
+symbol include/hda.h declares, the C planners match the oracle planners
+bit for bit, and argument errors come back as the documented status codes
+before anything reaches the GPU."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import load_balanced_split_step_amd.hda as hda
+from load_balanced_split_step_amd.workloads import CONFIGS, draw_lengths
+from oracle.planner import plan_dynamic, plan_static
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hda.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return hda.load_library()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "hda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hda_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_match_header(lib):
+    names = header_functions()
+    assert sorted(hda.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.hda_version() == 1
+
+
+@pytest.mark.parametrize("cfg", list(CONFIGS))
+@pytest.mark.parametrize("tile_len", [16, 64, 128, 256, 512])
+@pytest.mark.parametrize("W", [1, 7, 64, 256, 1024])
+def test_dynamic_plan_bit_exact(lib, cfg, tile_len, W):
+    w = CONFIGS[cfg]
+    lens = draw_lengths(w, w.seed)
+    got = hda.hda_plan(lens, tile_len, W)
+    want = np.array(plan_dynamic(lens.tolist(), tile_len, W).to_list(), dtype=np.int32)
+    assert np.array_equal(got, want)
+    assert got.size <= hda.hda_plan_capacity(len(lens), W)
+    assert hda.hda_plan_validate(got, lens) == hda.HDA_OK
+
+
+@pytest.mark.parametrize("cfg", list(CONFIGS))
+@pytest.mark.parametrize("S", [1, 2, 4, 8, 16, 32, 64])
+def test_static_plan_bit_exact(lib, cfg, S):
+    w = CONFIGS[cfg]
+    lens = draw_lengths(w, w.seed)
+    got = hda.hda_plan_static(lens, S)
+    want = np.array(plan_static(lens.tolist(), S).to_list(), dtype=np.int32)
+    assert np.array_equal(got, want)
+    assert got.size <= hda.hda_plan_capacity(len(lens), len(lens) * S)
+    assert hda.hda_plan_validate(got, lens) == hda.HDA_OK
+
+
+def test_plan_fuzz_bit_exact(lib):
+    rng = np.random.default_rng(1234)
+    for _ in range(3000):
+        B = int(rng.integers(1, 48))
+        hi = int(rng.choice([3, 40, 700, 9000]))
+        lens = rng.integers(1, hi + 1, size=B).astype(np.int32)
+        if rng.random() < 0.5:
+            tl, W = int(rng.integers(1, 300)), int(rng.integers(1, 400))
+            got = hda.hda_plan(lens, tl, W)
+            want = plan_dynamic(lens.tolist(), tl, W).to_list()
+        else:
+            S = int(rng.integers(1, 40))
+            got = hda.hda_plan_static(lens, S)
+            want = plan_static(lens.tolist(), S).to_list()
+        assert got.tolist() == want
+        assert hda.hda_plan_validate(got, lens) == hda.HDA_OK
+
+
+def test_plan_errors(lib):
+    with pytest.raises(hda.HdaError) as e:
+        hda.hda_plan(np.array([], dtype=np.int32), 16, 4)
+    assert e.value.status == hda.HDA_ERR_INVALID_ARG
+    for lens, tl, W in [([5, 0], 16, 4), ([5], 0, 4), ([5], 16, 0), ([-3], 16, 4)]:
+        with pytest.raises(hda.HdaError) as e:
+            hda.hda_plan(lens, tl, W)
+        assert e.value.status == hda.HDA_ERR_INVALID_ARG
+    with pytest.raises(hda.HdaError):
+        hda.hda_plan_static([5], 0)
+    # too-small buffer reports the size it needs
+    import ctypes
+    lens = np.array([17, 64, 200, 513], dtype=np.int32)
+    buf = np.zeros(10, dtype=np.int32)
+    n = ctypes.c_int64(0)
+    st = lib.hda_plan(hda._i32p(lens), 4, 64, 4, hda._i32p(buf), 10, ctypes.byref(n))
+    assert st == hda.HDA_ERR_CAPACITY and n.value == 46
+    assert (buf == 0).all()                      # nothing written on failure
+    assert lib.hda_plan_capacity(0, 4) == -1 and lib.hda_plan_capacity(4, 0) == -1
+
+
+def corrupt(plan, lens, fn):
+    p = plan.copy()
+    fn(p)
+    return hda.hda_plan_validate(p, lens)
+
+
+def test_validate_detects_corruption(lib):
+    lens = np.array([17, 64, 200, 513], dtype=np.int32)
+    plan = hda.hda_plan(lens, 64, 4)
+    W, N = plan[3], plan[5]
+    items = 8 + W + 1
+    assert hda.hda_plan_validate(plan, lens) == hda.HDA_OK
+    assert hda.hda_plan_validate(plan, lens[:3]) == hda.HDA_ERR_PLAN_MISMATCH
+    assert hda.hda_plan_validate(plan, lens + 1) == hda.HDA_ERR_PLAN_MISMATCH
+    assert corrupt(plan, lens, lambda p: p.__setitem__(0, 2)) == hda.HDA_ERR_BAD_PLAN
+    # overlap: second item of request 2 starts inside the first
+    assert corrupt(plan, lens, lambda p: p.__setitem__(items + 4 * 3 + 1, 100)) == hda.HDA_ERR_BAD_PLAN
+    # gap at the end of request 3
+    assert corrupt(plan, lens, lambda p: p.__setitem__(items + 4 * 6 + 2, 512)) == hda.HDA_ERR_PLAN_MISMATCH
+    # wrong slot
+    assert corrupt(plan, lens, lambda p: p.__setitem__(items + 4 * 2 + 3, 3)) == hda.HDA_ERR_BAD_PLAN
+    # slot on a single-item request
+    assert corrupt(plan, lens, lambda p: p.__setitem__(items + 3, 0)) == hda.HDA_ERR_BAD_PLAN
+    # wg_ptr not monotone
+    assert corrupt(plan, lens, lambda p: p.__setitem__(9, 6)) == hda.HDA_ERR_BAD_PLAN
+    # request index out of range
+    assert corrupt(plan, lens, lambda p: p.__setitem__(items, 9)) == hda.HDA_ERR_BAD_PLAN
+    # truncated
+    assert hda.hda_plan_validate(plan[:-1], lens) == hda.HDA_ERR_BAD_PLAN
+    assert hda.hda_plan_validate(plan[:4], lens) == hda.HDA_ERR_INVALID_ARG
+
+
+def test_workspace_bytes(lib):
+    lens = np.array([17, 64, 200, 513], dtype=np.int32)
+    plan = hda.hda_plan(lens, 64, 4)          # P = 5
+    up = lambda x: (x + 255) // 256 * 256
+    assert hda.hda_workspace_bytes(plan, 8, 2, 64) == up(5 * 8 * 64 * 4) + up(5 * 8 * 4) + up(4 * 2 * 4)
+    assert hda.hda_workspace_bytes(plan, 0, 2, 64) == -1
+
+
+# --- hda_decode argument errors: all are caught on the host before launch.
+# Fake, 256-byte aligned addresses stand in for device pointers; these tests
+# are skipped where a GPU is visible so that no path could ever launch on them.
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+FAKE = 0x7F0000000000
+
+
+def _params(**kw):
+    base = dict(batch=4, n_q_heads=8, n_kv_heads=2, head_dim=64, page_size=16,
+                max_pages_per_req=33, num_pages=52, kv_dtype=hda.HDA_KV_BF16,
+                sm_scale=0.125, k_scale=1.0, v_scale=1.0, prologue=0,
+                workspace=FAKE + 0x100000, workspace_bytes=1 << 20)
+    base.update(kw)
+    return hda.hda_params(**base)
+
+
+def _decode_status(lib, p, plan, **ptrs):
+    import ctypes
+    args = dict(q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, bt=FAKE + 0x3000, sl=FAKE + 0x4000,
+                pd=FAKE + 0x5000, out=FAKE + 0x6000)
+    args.update(ptrs)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return lib.hda_decode(ctypes.byref(p), vp(args["q"]), vp(args["k"]), vp(args["v"]),
+                          vp(args["bt"]), vp(args["sl"]), hda._i32p(plan), vp(args["pd"]),
+                          plan.size, vp(args["out"]), None)
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers are only used without a GPU")
+def test_decode_argument_errors(lib):
+    lens = np.array([17, 64, 200, 513], dtype=np.int32)
+    plan = hda.hda_plan(lens, 64, 4)
+    E = hda
+    assert _decode_status(lib, _params(), plan, q=None) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(), plan, out=None) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(batch=0), plan) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(n_q_heads=7), plan) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(sm_scale=0.0), plan) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(k_scale=float("nan")), plan) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(head_dim=96), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(n_q_heads=64, n_kv_heads=2), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(page_size=24), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(page_size=8), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(kv_dtype=5), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(), plan, q=FAKE + 8) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(prologue=1), plan) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(batch=5), plan) == E.HDA_ERR_PLAN_MISMATCH
+    assert _decode_status(lib, _params(), plan[:-1]) == E.HDA_ERR_BAD_PLAN
+    bad = plan.copy(); bad[0] = 9
+    assert _decode_status(lib, _params(), bad) == E.HDA_ERR_BAD_PLAN
+    assert _decode_status(lib, _params(workspace=None), plan) == E.HDA_ERR_WORKSPACE
+    assert _decode_status(lib, _params(workspace_bytes=100), plan) == E.HDA_ERR_WORKSPACE
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert lib.hda_status_string(s)
