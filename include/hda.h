@@ -121,9 +121,10 @@ int hda_plan_validate(const int32_t* plan, int64_t plan_len,
 
 /*
  * Bytes of workspace hda_decode needs for this plan: partial outputs
- * float32 [P][Hq][D], partial log-sum-exp float32 [P][Hq], and merge
- * counters int32 [B][Hkv], each region aligned to 256 bytes.  Returns -1 for
- * a malformed plan header or non-positive sizes.
+ * float32 [P][Hq][D] followed by partial log-sum-exp float32 [P][Hq], each
+ * region aligned to 256 bytes (at least 256 bytes in all).  Its contents
+ * need no initialisation.  Returns -1 for a malformed plan header or
+ * non-positive sizes.
  */
 int64_t hda_workspace_bytes(const int32_t* plan, int64_t plan_len,
                             int32_t n_q_heads, int32_t n_kv_heads,
@@ -151,12 +152,16 @@ typedef struct hda_params {
   const void* k_norm_w;       /* [device] bf16 [D] */
   const void* k_new;          /* [device] bf16 [B][Hkv][D], pre-norm k of the new token */
   const void* v_new;          /* [device] bf16 [B][Hkv][D] */
-  /* scratch: partials and merge counters, hda_workspace_bytes() bytes.
-   * Must be zero-filled before its first use; every completed hda_decode
-   * leaves the counters at zero again.  Calls that share a workspace must
-   * be ordered on one stream. */
+  /* scratch for split requests' partial results, hda_workspace_bytes()
+   * bytes, any contents */
   void* workspace;            /* [device] */
   int64_t workspace_bytes;
+  /* merge counters, int32, at least B * Hkv of them.  Zero-fill once before
+   * first use; every completed hda_decode leaves them at zero, so a buffer
+   * sized for the largest batch serves every later step.  Calls sharing
+   * workspace or counters must be ordered on one stream. */
+  int32_t* counters;          /* [device] */
+  int64_t counters_len;
 } hda_params;
 
 /*
@@ -179,7 +184,8 @@ typedef struct hda_params {
  * used, whatever they hold.
  * Errors (all detected on the host before any launch): HDA_ERR_INVALID_ARG,
  * HDA_ERR_UNSUPPORTED, HDA_ERR_PLAN_MISMATCH, HDA_ERR_BAD_PLAN,
- * HDA_ERR_WORKSPACE; HDA_ERR_HIP if the launch fails.  Device faults
+ * HDA_ERR_WORKSPACE (workspace or counters missing or too small);
+ * HDA_ERR_HIP if the launch fails.  Device faults
  * surface at the caller's next synchronisation.
  */
 int hda_decode(const hda_params* p, const void* q, void* k_pages,

@@ -588,6 +588,8 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
                                               p->head_dim);
   if (ws_need < 0) return HDA_ERR_BAD_PLAN;
   if (P > 0 && (!p->workspace || p->workspace_bytes < ws_need)) return HDA_ERR_WORKSPACE;
+  if (P > 0 && (!p->counters || p->counters_len < (int64_t)p->batch * p->n_kv_heads))
+    return HDA_ERR_WORKSPACE;
 
   const int D = p->head_dim;
   const int elem = p->kv_dtype == HDA_KV_FP8_E4M3 ? 1 : 2;
@@ -601,10 +603,9 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
   a.out = out;
   uint8_t* ws = static_cast<uint8_t*>(p->workspace);
   const int64_t o_bytes = (P * p->n_q_heads * D * 4 + 255) / 256 * 256;
-  const int64_t l_bytes = (P * p->n_q_heads * 4 + 255) / 256 * 256;
   a.part_o = ws ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_lse = ws ? reinterpret_cast<float*>(ws + o_bytes) : nullptr;
-  a.counters = ws ? reinterpret_cast<int32_t*>(ws + o_bytes + l_bytes) : nullptr;
+  a.counters = p->counters;
   a.q_norm_w = static_cast<const uint16_t*>(p->q_norm_w);
   a.k_norm_w = static_cast<const uint16_t*>(p->k_norm_w);
   a.k_new = static_cast<const uint16_t*>(p->k_new);

@@ -138,7 +138,8 @@ def test_workspace_bytes(lib):
     lens = np.array([17, 64, 200, 513], dtype=np.int32)
     plan = hda.hda_plan(lens, 64, 4)          # P = 5
     up = lambda x: (x + 255) // 256 * 256
-    assert hda.hda_workspace_bytes(plan, 8, 2, 64) == up(5 * 8 * 64 * 4) + up(5 * 8 * 4) + up(4 * 2 * 4)
+    assert hda.hda_workspace_bytes(plan, 8, 2, 64) == up(5 * 8 * 64 * 4) + up(5 * 8 * 4)
+    assert hda.hda_workspace_bytes(hda.hda_plan(lens, 64, 1), 8, 2, 64) == 256   # P = 0
     assert hda.hda_workspace_bytes(plan, 0, 2, 64) == -1
 
 
@@ -161,7 +162,8 @@ def _params(**kw):
     base = dict(batch=4, n_q_heads=8, n_kv_heads=2, head_dim=64, page_size=16,
                 max_pages_per_req=33, num_pages=52, kv_dtype=hda.HDA_KV_BF16,
                 sm_scale=0.125, k_scale=1.0, v_scale=1.0, prologue=0,
-                workspace=FAKE + 0x100000, workspace_bytes=1 << 20)
+                workspace=FAKE + 0x100000, workspace_bytes=1 << 20,
+                counters=FAKE + 0x200000, counters_len=8)
     base.update(kw)
     return hda.hda_params(**base)
 
@@ -201,5 +203,7 @@ def test_decode_argument_errors(lib):
     assert _decode_status(lib, _params(), bad) == E.HDA_ERR_BAD_PLAN
     assert _decode_status(lib, _params(workspace=None), plan) == E.HDA_ERR_WORKSPACE
     assert _decode_status(lib, _params(workspace_bytes=100), plan) == E.HDA_ERR_WORKSPACE
+    assert _decode_status(lib, _params(counters=None), plan) == E.HDA_ERR_WORKSPACE
+    assert _decode_status(lib, _params(counters_len=7), plan) == E.HDA_ERR_WORKSPACE
     for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.hda_status_string(s)

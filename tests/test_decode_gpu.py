@@ -93,17 +93,16 @@ def test_nan_poisoned_workspace():
     dev = hda.DeviceBatch.from_inputs(inp)
     plan = hda.hda_plan(inp["seq_lens"], 64, 40)
     need = hda.hda_workspace_bytes(plan, w.n_q_heads, w.n_kv_heads, w.head_dim)
-    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")   # NaN floats
-    cnt = w.batch * w.n_kv_heads * 4
-    ws[need - ((cnt + 255) // 256 * 256):] = 0                           # counters start at zero
-    dev._ws = ws
+    dev._ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")   # NaN floats
     out = dev.decode(plan)
     torch.cuda.synchronize()
     assert max_err(out, ref) <= 2e-2
-    # counters are left at zero for the next call
-    assert int(ws[need - ((cnt + 255) // 256 * 256):].sum()) == 0
-    out2 = dev.decode(plan)
+    assert int(dev.counters().abs().sum()) == 0          # left at zero for the next call
+    # a different plan (other partial count) reusing workspace and counters
+    out2 = dev.decode(hda.hda_plan(inp["seq_lens"], 32, 11))
     assert max_err(out2, ref) <= 2e-2
+    out3 = dev.decode(plan)
+    assert max_err(out3, ref) <= 2e-2
 
 
 EDGE = [
