@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Decode-attention step benchmark on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the host planner
+(hda_plan) rebuilds the tile plan from the current lengths, the plan goes to
+the device with an async copy from pinned memory, and hda_decode runs the
+attention kernel (tile loads, QK, online softmax, PV, log-sum-exp merge) on
+the torch stream.  Inputs are resident in HBM before timing starts.
+
+Default workload: the 1 x 131072 + 31 x 4096 extreme mix (bf16 cache, 64 q /
+8 kv heads, head dim 128, page 64, random page placement).  The KV pools are
+held in several copies and steps rotate over them so that no step finds the
+previous step's bytes in the 256 MB last-level cache.
+
+Prints one JSON line: value = KV bytes read per second (GB/s), plus the
+kernel's roofline position (HIP-event durations on the launch stream), the
+load-balance gain over static split plans, and the fp64 oracle timed on a
+bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E spec
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "load_balanced_split_step_amd", "csrc", "hda_decode.hip")
+METRIC = "decode-attn µs/step + KV GB/s (% HBM peak), 1×128K+31×4K mix, 1 GPU"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="extreme")
+    ap.add_argument("--tile-len", type=int, default=None)
+    ap.add_argument("--workgroups", type=int, default=None)
+    ap.add_argument("--copies", type=int, default=4, help="KV pool copies rotated over")
+    ap.add_argument("--no-static", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(inp, plan_len):
+    """Bytes one launch must move: every cached K/V row of every kv head,
+    q, the output, the block-table entries in use, lengths and plan."""
+    from load_balanced_split_step_amd.workloads import kv_bytes
+    w = inp["workload"]
+    B = len(inp["seq_lens"])
+    pages_used = int(sum(-(-int(L) // w.page_size) for L in inp["seq_lens"]))
+    return (kv_bytes(inp) + B * w.n_q_heads * w.head_dim * 2 + B * w.n_q_heads * w.head_dim * 4
+            + pages_used * 4 + B * 4 + plan_len * 4)
+
+
+def traffic_from_profiles(workload):
+    """Measured HBM bytes per launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"hda_decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_plan_kernel(dev, plan, copies, steps, warmup):
+    """Kernel-only durations (ms) of hda_decode for a fixed plan."""
+    import numpy as np
+    import torch
+    pd = torch.from_numpy(np.ascontiguousarray(plan)).to(dev.device)
+    out = torch.empty((dev.kw["batch"], dev.kw["n_q_heads"], dev.kw["head_dim"]),
+                      dtype=torch.float32, device=dev.device)
+    evs = []
+    for s in range(warmup + steps):
+        kp, vp = copies[s % len(copies)]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dev.decode(plan, out=out, plan_dev=pd, k_pages=kp, v_pages=vp)
+        e1.record()
+        if s >= warmup:
+            evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(inp, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    whole requests, shortest first, cycling over the batch until the time
+    budget is spent.  Rate = KV bytes of the requests done / seconds."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    w = inp["workload"]
+    order = np.argsort(inp["seq_lens"], kind="stable")
+    q64 = oracle.bf16_to_f64(inp["q"])
+    done, toks, t0 = [], 0, time.perf_counter()
+    seq = order.tolist() * 64
+    for b in seq:
+        sub = [b]
+        oracle.attention_reference(q64[sub], inp["k_pages"], inp["v_pages"],
+                                   inp["block_table"][sub], inp["seq_lens"][sub], w.kv_dtype,
+                                   float(inp["sm_scale"]), float(inp["k_scale"]),
+                                   float(inp["v_scale"]))
+        done.append(b)
+        toks += int(inp["seq_lens"][b])
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    secs = time.perf_counter() - t0
+    elem = 1 if w.kv_dtype == "fp8" else 2
+    kvb = toks * w.n_kv_heads * w.head_dim * 2 * elem
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(kvb / secs / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(done)} request passes over the {len(inp['seq_lens'])}-request "
+                      f"batch, shortest first ({toks} KV tokens) in {secs:.1f} s; "
+                      f"numpy fp64, BLAS threads {threads}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import load_balanced_split_step_amd.hda as hda
+    from load_balanced_split_step_amd.workloads import CONFIGS, make_inputs, kv_bytes
+
+    w = CONFIGS[args.workload]
+    t = time.time()
+    inp = make_inputs(w)
+    log(f"generated {args.workload} inputs in {time.time() - t:.1f}s")
+    lens = inp["seq_lens"]
+    dev = hda.DeviceBatch.from_inputs(inp, device="cuda:0")
+    copies = [(dev.t["k_pages"], dev.t["v_pages"])]
+    for _ in range(max(0, args.copies - 1)):
+        copies.append((dev.t["k_pages"].clone(), dev.t["v_pages"].clone()))
+    torch.cuda.synchronize()
+
+    tl, W = hda.launch_config(lens, w.n_kv_heads)
+    tl = args.tile_len or tl
+    W = args.workgroups or W
+    cap = hda.hda_plan_capacity(len(lens), W)
+    NB = 3                                     # pinned plan buffers in rotation
+    pinned = [torch.empty(cap, dtype=torch.int32).pin_memory() for _ in range(NB)]
+    plan_dev = [torch.empty(cap, dtype=torch.int32, device="cuda:0") for _ in range(NB)]
+    copied = [None] * NB
+    out = torch.empty((len(lens), w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    kv = kv_bytes(inp)
+
+    def step(s, events=None):
+        j = s % NB
+        if copied[j] is not None:
+            copied[j].synchronize()            # its previous upload has finished
+        host = pinned[j].numpy()
+        n = hda.hda_plan_into(lens, tl, W, host)      # a1: plan from current lengths
+        plan_dev[j][:n].copy_(pinned[j][:n], non_blocking=True)   # a2: upload
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        copied[j] = ev
+        kp, vp = copies[s % len(copies)]
+        if events is not None:
+            events[0].record(stream)
+        p = dev.params(host[:n])
+        hda.hda_decode(p, dev.t["q"], kp, vp, dev.t["block_table"], dev.t["seq_lens"],
+                       host[:n], plan_dev[j], out, stream)
+        if events is not None:
+            events[1].record(stream)
+        return n
+
+    for s in range(args.warmup):
+        plan_len = step(s)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        plan_len = step(args.warmup + s, evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    ms_per_step = wall * 1e3 / args.steps
+    kmean = sum(kern_ms) / len(kern_ms)
+    pct = lambda p: kern_ms[min(len(kern_ms) - 1, int(round(p * (len(kern_ms) - 1))))]
+    log(f"step {ms_per_step * 1e3:.1f} us wall, kernel mean {kmean * 1e3:.1f} us "
+        f"(p10 {pct(0.1) * 1e3:.1f}, p50 {pct(0.5) * 1e3:.1f}, p90 {pct(0.9) * 1e3:.1f})")
+
+    # parity spot check on the timed output (sampled rows, fp64 oracle)
+    import oracle
+    pairs = [(0, 0), (0, 37), (int(np.argmax(lens)), 63), (len(lens) - 1, 5)]
+    ref = oracle.attention_selected(oracle.bf16_to_f64(inp["q"]), inp["k_pages"], inp["v_pages"],
+                                    inp["block_table"], lens, w.kv_dtype, float(inp["sm_scale"]),
+                                    pairs, float(inp["k_scale"]), float(inp["v_scale"])) \
+        if not w.prologue else None
+    max_err = None
+    if ref is not None:
+        o = out.cpu().numpy()
+        max_err = max(float(np.abs(o[b, h] - ref[(b, h)]).max()) for b, h in pairs)
+        log(f"sampled parity vs oracle: max err {max_err:.3e}")
+
+    algo = algorithmic_bytes(inp, plan_len)
+    achieved = algo / (kmean * 1e-3) / 1e9
+    traffic = traffic_from_profiles(args.workload)
+    res = {
+        "metric": METRIC,
+        "value": round(kv / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: " + (
+            "1x131072 + 31x4096 KV tokens" if args.workload == "extreme" else
+            f"{len(lens)} requests, {int(lens.sum())} KV tokens"),
+            "batch": int(len(lens)), "kv_tokens": int(lens.sum()),
+            "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+            "page_size": w.page_size, "kv_dtype": w.kv_dtype, "tile_len": tl,
+            "n_workgroups": W, "kv_bytes": kv},
+        "us_per_step": {"wall": round(ms_per_step * 1e3, 2),
+                        "kernel_mean": round(kmean * 1e3, 2),
+                        "kernel_p10": round(pct(0.1) * 1e3, 2),
+                        "kernel_p50": round(pct(0.5) * 1e3, 2),
+                        "kernel_p90": round(pct(0.9) * 1e3, 2)},
+        "kv_gbs_kernel": round(kv / (kmean * 1e-3) / 1e9, 2),
+        "hbm_peak_frac_kernel": round(kv / (kmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": algo,
+                     "kernel": "hda_decode_kernel"},
+        "parity_max_err_sampled": max_err,
+    }
+
+    if not args.no_static:
+        static = {}
+        for S in (1, 2, 4, 8, 16, 32, 64):
+            plan = hda.hda_plan_static(lens, S)
+            ms = time_plan_kernel(dev, plan, copies, steps=8, warmup=2)
+            static[S] = sum(ms) / len(ms)
+            log(f"static S={S}: {static[S] * 1e3:.1f} us")
+        best = min(static, key=static.get)
+        S_h = max(1, min(64, math.ceil(256 * 2 / (len(lens) * w.n_kv_heads))))
+        S_h = 1 << (S_h - 1).bit_length()
+        res["load_balance"] = {
+            "dynamic_kernel_us": round(kmean * 1e3, 2),
+            "static_us": {str(k): round(v * 1e3, 2) for k, v in static.items()},
+            "static_best_S": best,
+            "gain_vs_best_static": round(static[best] / kmean, 3),
+            "static_heuristic_S": S_h,
+            "gain_vs_heuristic_static": round(static[S_h] / kmean, 3),
+        }
+
+    if not args.no_cpu:
+        log("timing the fp64 oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

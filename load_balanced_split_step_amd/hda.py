@@ -150,6 +150,19 @@ def hda_plan(seq_lens, tile_len: int, n_workgroups: int) -> np.ndarray:
     return _plan_call(lib.hda_plan, _lens(seq_lens), int(tile_len), int(n_workgroups))
 
 
+def hda_plan_into(seq_lens, tile_len: int, n_workgroups: int, out: np.ndarray) -> int:
+    """Dynamic plan written into a caller buffer (int32, e.g. a pinned host
+    tensor's numpy view); returns the number of ints used.  No allocation."""
+    lib = load_library()
+    lens = _lens(seq_lens)
+    n = ctypes.c_int64(0)
+    st = lib.hda_plan(_i32p(lens), len(lens), int(tile_len), int(n_workgroups), _i32p(out),
+                      out.size, ctypes.byref(n))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_plan")
+    return n.value
+
+
 def hda_plan_static(seq_lens, n_splits: int) -> np.ndarray:
     """Static split baseline plan (int32 array)."""
     lib = load_library()
