@@ -153,21 +153,20 @@ typedef struct hda_params {
   const void* k_new;          /* [device] bf16 [B][Hkv][D], pre-norm k of the new token */
   const void* v_new;          /* [device] bf16 [B][Hkv][D] */
   /* scratch for split requests' partial results, hda_workspace_bytes()
-   * bytes, any contents */
+   * bytes, any contents; calls sharing a workspace must be ordered on one
+   * stream */
   void* workspace;            /* [device] */
   int64_t workspace_bytes;
-  /* merge counters, int32, at least B * Hkv of them.  Zero-fill once before
-   * first use; every completed hda_decode leaves them at zero, so a buffer
-   * sized for the largest batch serves every later step.  Calls sharing
-   * workspace or counters must be ordered on one stream. */
-  int32_t* counters;          /* [device] */
-  int64_t counters_len;
+  /* optional profiling hook: a hipEvent_t recorded on the stream between the
+   * tile kernel and the merge kernel; NULL for none */
+  void* split_event;
 } hda_params;
 
 /*
- * One decode step: (optional prologue) + tile attention + log-sum-exp merge,
- * enqueued as a single kernel launch on `stream`.  Asynchronous; no host
- * synchronisation, no allocation.
+ * One decode step: (optional prologue) + tile attention, then the
+ * log-sum-exp merge of split requests, enqueued as two kernel launches on
+ * `stream` (the merge only when the plan has partial slots).  Asynchronous;
+ * no host synchronisation, no allocation.
  *
  *   q            [device] bf16 [B][Hq][D] (pre-norm when the prologue is on)
  *   k_pages,
@@ -184,8 +183,8 @@ typedef struct hda_params {
  * used, whatever they hold.
  * Errors (all detected on the host before any launch): HDA_ERR_INVALID_ARG,
  * HDA_ERR_UNSUPPORTED, HDA_ERR_PLAN_MISMATCH, HDA_ERR_BAD_PLAN,
- * HDA_ERR_WORKSPACE (workspace or counters missing or too small);
- * HDA_ERR_HIP if the launch fails.  Device faults
+ * HDA_ERR_WORKSPACE (workspace missing or too small); HDA_ERR_HIP if a
+ * launch fails.  Device faults
  * surface at the caller's next synchronisation.
  */
 int hda_decode(const hda_params* p, const void* q, void* k_pages,

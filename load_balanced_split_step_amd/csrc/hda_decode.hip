@@ -1,13 +1,13 @@
 // Dynamic split-KV paged decode attention for MI355X (gfx950 / CDNA4).
 //
-// One launch per decode step.  Workgroup (w, h) handles the work items that
+// Two launches per decode step.  Workgroup (w, h) handles the work items that
 // the host plan gives workgroup w, for kv head h (grid = W * Hkv, kv head
 // fastest).  Each workgroup is 4 waves; the waves of a workgroup take the
 // 32-token chunks of an item round-robin, keep their own online-softmax
 // state, and combine through LDS when the item ends.  An item that covers a
 // whole request writes its output; the other items write a normalised
-// partial and its log-sum-exp, and the last workgroup to finish a request
-// (per kv head) merges that request's partials.
+// partial and its log-sum-exp, which a second, small kernel merges per
+// request in slot order.
 //
 // Method: page "Tencent HPC llega a SGLang y desafía a los kernels de
 // inferencia predeterminados" (remio.ai), section "Por qué Tencent HPC
@@ -58,13 +58,12 @@ struct Args {
   float* out;
   float* part_o;
   float* part_lse;
-  int32_t* counters;
   const uint16_t* q_norm_w;
   const uint16_t* k_norm_w;
   const uint16_t* k_new;
   const uint16_t* v_new;
   int64_t page_stride;   // bytes per page (all kv heads)
-  int64_t num_pages;
+  int32_t num_pages;     // page ids are int32; clamped on the host
   int32_t head_stride;   // bytes per (page, kv head) slab
   int32_t batch, n_q_heads, n_kv_heads, group;
   int32_t page_size, log2_ps, max_pages;
@@ -186,7 +185,8 @@ __device__ inline bf16x8 k_operand(const Chunk<D, FP8>& ch, int hf, int s) {
 // kv head h).  A half with no valid rows (past len, outside the block table
 // or an out-of-range page id) gets an empty resource and reads zeros.
 template <int D, bool FP8>
-__device__ inline void chunk_rsrc(const Args& a, int b, int L, int h, int c, bool live,
+__device__ inline void chunk_rsrc(const Args& a, const int32_t* __restrict__ block_table, int b,
+                                  int L, int h, int c, bool live,
                                   __amdgpu_buffer_rsrc_t (&kr)[2],
                                   __amdgpu_buffer_rsrc_t (&vr)[2]) {
   using G = Geo<D, FP8>;
@@ -200,9 +200,9 @@ __device__ inline void chunk_rsrc(const Args& a, int b, int L, int h, int c, boo
     if (live && rows > 0) {
       const int pidx = t >> a.log2_ps;
       if (pidx < a.max_pages) {
-        const int64_t page = a.block_table[(int64_t)b * a.max_pages + pidx];
+        const int page = block_table[(int64_t)b * a.max_pages + pidx];
         if (page >= 0 && page < a.num_pages) {
-          off = page * a.page_stride + (int64_t)h * a.head_stride +
+          off = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
                 (int64_t)(t & (a.page_size - 1)) * G::RB;
           bytes = rows * G::RB;
         }
@@ -213,6 +213,10 @@ __device__ inline void chunk_rsrc(const Args& a, int b, int L, int h, int c, boo
   }
 }
 
+// K/V rows are read once per step and never again by this launch: load them
+// non-temporally (cache policy aux = nt) so they do not displace anything.
+constexpr int kStreamAux = 2;
+
 template <int D, bool FP8>
 __device__ inline void issue_chunk(Chunk<D, FP8>& ch, const __amdgpu_buffer_rsrc_t (&kr)[2],
                                    const __amdgpu_buffer_rsrc_t (&vr)[2], int i, int kg) {
@@ -222,19 +226,19 @@ __device__ inline void issue_chunk(Chunk<D, FP8>& ch, const __amdgpu_buffer_rsrc
 #pragma unroll
     for (int u = 0; u < G::KL; ++u)
       ch.k[hf][u] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr[hf], i * G::RB + 64 * u + 16 * kg, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr[hf], i * G::RB + 64 * u + 16 * kg, 0, kStreamAux));
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int hf = j >> 2;
     const int off = (4 * kg + (j & 3)) * G::RB + i * G::VW * 4;
     if constexpr (G::VW == 4) {
-      const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr[hf], off, 0, 0));
+      const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr[hf], off, 0, kStreamAux));
       ch.v[j][0] = x[0]; ch.v[j][1] = x[1]; ch.v[j][2] = x[2]; ch.v[j][3] = x[3];
     } else if constexpr (G::VW == 2) {
-      const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr[hf], off, 0, 0));
+      const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr[hf], off, 0, kStreamAux));
       ch.v[j][0] = x[0]; ch.v[j][1] = x[1];
     } else {
-      ch.v[j][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(vr[hf], off, 0, 0);
+      ch.v[j][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(vr[hf], off, 0, kStreamAux);
     }
   }
 }
@@ -319,20 +323,26 @@ __device__ inline void compute_chunk(const Chunk<D, FP8>& ch, const bf16x8 (&qop
 }
 
 template <int D, bool FP8, bool PRO>
-__global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(Args a) {
+__global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
+    Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ plan) {
+  // The plan, lengths and block table are read-only here and reached by
+  // wave-uniform addresses, so they load through the scalar cache.
   using G = Geo<D, FP8>;
   __shared__ float sm_acc[kWaves][kMaxGroup][D];
   __shared__ float sm_m[kWaves][kMaxGroup];
   __shared__ float sm_l[kWaves][kMaxGroup];
   __shared__ __attribute__((aligned(16))) uint16_t sm_q[kMaxGroup][D];
-  __shared__ int sm_last;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index is uniform within a wave: keep it (and everything derived
+  // from it: chunk index, page id, buffer resources) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, kg = lane >> 4;
   const int h = blockIdx.x % a.n_kv_heads;
   const int w = blockIdx.x / a.n_kv_heads;
   const int g = a.group;
-  const int32_t* wg_ptr = a.plan + HDA_PLAN_HEADER_INTS;
+  const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
   const int32_t* items = wg_ptr + a.n_wg + 1;
   const int32_t* rpp = items + 4 * a.n_items;
   const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
@@ -347,11 +357,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(Args a) {
       for (int it = it_begin; it < it_end; ++it) {
         const int b = items[4 * it], k1 = items[4 * it + 2];
         if ((unsigned)b >= (unsigned)a.batch) continue;
-        const int L = a.seq_lens[b];
+        const int L = seq_lens[b];
         if (k1 != L || L < 1) continue;
         const int pos = L - 1, pidx = pos >> a.log2_ps;
         if (pidx >= a.max_pages) continue;
-        const int64_t page = a.block_table[(int64_t)b * a.max_pages + pidx];
+        const int page = block_table[(int64_t)b * a.max_pages + pidx];
         if (page < 0 || page >= a.num_pages) continue;
         const bool act = lane < D / 2;
         float c = 1.f, s = 0.f;
@@ -363,7 +373,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(Args a) {
         if (act) {
           const float v0 = bf16_bits_to_float(a.v_new[src + lane]);
           const float v1 = bf16_bits_to_float(a.v_new[src + lane + D / 2]);
-          const int64_t row = page * a.page_stride + (int64_t)h * a.head_stride +
+          const int64_t row = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
                               (int64_t)(pos & (a.page_size - 1)) * G::RB;
           if constexpr (FP8) {
             a.k_pages[row + lane] = (uint8_t)fp8_encode(k0v / a.k_scale);
@@ -381,15 +391,18 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(Args a) {
         }
       }
     }
-    __threadfence();
+    // This workgroup's stores are complete before the barrier; the acquire
+    // drops any cached copy of the written rows before the chunk loads.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
 
   for (int it = it_begin; it < it_end; ++it) {
     const int b = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
               slot = items[4 * it + 3];
     if ((unsigned)b >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
-    const int L = a.seq_lens[b];
+    const int L = seq_lens[b];
     const int64_t qrow0 = ((int64_t)b * a.n_q_heads + (int64_t)h * g) * D;
 
     // q operand (MFMA B): lane (i, kg) holds q head i, dims qk_dim(s, kg) + 0..7.
@@ -434,18 +447,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(Args a) {
     if (c <= c_last) {
       Chunk<D, FP8> A, B;
       __amdgpu_buffer_rsrc_t kr[2], vr[2];
-      chunk_rsrc<D, FP8>(a, b, L, h, c, true, kr, vr);
+      chunk_rsrc<D, FP8>(a, block_table, b, L, h, c, true, kr, vr);
       issue_chunk<D, FP8>(A, kr, vr, i, kg);
+      // The next chunk's loads are issued before this chunk's math; the
+      // scheduling barrier keeps the compiler from sinking them below it.
       while (true) {
         int cn = c + kWaves;
-        chunk_rsrc<D, FP8>(a, b, L, h, cn, cn <= c_last, kr, vr);
+        chunk_rsrc<D, FP8>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr);
         issue_chunk<D, FP8>(B, kr, vr, i, kg);
+        __builtin_amdgcn_sched_barrier(0);
         compute_chunk<D, FP8>(A, qop, c, k0, k1, a.qk_scale_log2, kg, m_run, l_run, acc);
         c = cn;
         if (c > c_last) break;
         cn = c + kWaves;
-        chunk_rsrc<D, FP8>(a, b, L, h, cn, cn <= c_last, kr, vr);
+        chunk_rsrc<D, FP8>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr);
         issue_chunk<D, FP8>(A, kr, vr, i, kg);
+        __builtin_amdgcn_sched_barrier(0);
         compute_chunk<D, FP8>(B, qop, c, k0, k1, a.qk_scale_log2, kg, m_run, l_run, acc);
         c = cn;
         if (c > c_last) break;
@@ -495,57 +512,92 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(Args a) {
       }
     }
 
-    if (slot >= 0) {
-      // Last workgroup to finish request b (for this kv head) merges its
-      // partials in slot order.
-      const int s0 = max(0, rpp[b]), s1 = min(a.n_parts, rpp[b + 1]);
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) {
-        const int old = atomicAdd(&a.counters[(int64_t)b * a.n_kv_heads + h], 1);
-        sm_last = (old == s1 - s0 - 1);
-      }
-      __syncthreads();
-      if (sm_last) {
-        __threadfence();
-        for (int idx = tid; idx < g * D; idx += 64 * kWaves) {
-          const int hh = idx / D, d = idx - hh * D;
-          const int64_t hq = (int64_t)h * g + hh;
-          float M = -INFINITY;
-          for (int sl = s0; sl < s1; ++sl)
-            M = fmaxf(M, __hip_atomic_load(&a.part_lse[(int64_t)sl * a.n_q_heads + hq],
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-          float wsum = 0.f, o = 0.f;
-          for (int sl = s0; sl < s1; ++sl) {
-            const float lse = __hip_atomic_load(&a.part_lse[(int64_t)sl * a.n_q_heads + hq],
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float po = __hip_atomic_load(&a.part_o[((int64_t)sl * a.n_q_heads + hq) * D + d],
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float wt = expf(lse - M);
-            wsum += wt;
-            o += wt * po;
-          }
-          a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = o / wsum;
-        }
-        if (tid == 0)
-          __hip_atomic_store(&a.counters[(int64_t)b * a.n_kv_heads + h], 0, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
     __syncthreads();  // LDS is reused by the next item
   }
 }
 
+// Log-sum-exp merge of split requests: workgroup (b, q head) combines the
+// partials of request b in slot order,
+//   out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M),  M = max_s lse_s.
+// A separate launch: the kernel boundary makes every partial written by the
+// tile kernel (on any XCD) visible here without cross-XCD fences.  Thread d
+// owns output dim d; the slot loop is unrolled so that many partial rows are
+// in flight at once.
+constexpr int kMergeStage = 512;   // slot weights staged in LDS per pass
+
+template <int D>
+__global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __restrict__ plan) {
+  __shared__ float sm_w[kMergeStage];
+  __shared__ float sm_red[2][D / 64];
+  const int d = threadIdx.x, lane = d & 63, wave = d >> 6;
+  const int b = blockIdx.x / a.n_q_heads, hq = blockIdx.x % a.n_q_heads;
+  const int32_t* rpp = plan + HDA_PLAN_HEADER_INTS + a.n_wg + 1 + 4 * a.n_items;
+  const int s0 = max(0, rpp[b]), s1 = min(a.n_parts, rpp[b + 1]);
+  if (s1 <= s0) return;
+  const float* lse = a.part_lse + hq;               // stride n_q_heads
+  float m = -INFINITY;
+  for (int sl = s0 + d; sl < s1; sl += D) m = fmaxf(m, lse[(int64_t)sl * a.n_q_heads]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) sm_red[0][wave] = m;
+  __syncthreads();
+  float M = sm_red[0][0];
+#pragma unroll
+  for (int w = 1; w < D / 64; ++w) M = fmaxf(M, sm_red[0][w]);
+  float t = 0.f;
+  for (int sl = s0 + d; sl < s1; sl += D) t += expf(lse[(int64_t)sl * a.n_q_heads] - M);
+  t = wave_sum(t);
+  if (lane == 0) sm_red[1][wave] = t;
+  __syncthreads();
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < D / 64; ++w) total += sm_red[1][w];
+  const float inv_total = 1.0f / total;
+
+  const int64_t row_stride = (int64_t)a.n_q_heads * D;
+  const float* po = a.part_o + (int64_t)hq * D + d;
+  float acc = 0.f;
+  for (int c0 = s0; c0 < s1; c0 += kMergeStage) {
+    const int n = min(kMergeStage, s1 - c0);
+    __syncthreads();
+    for (int k = d; k < n; k += D)
+      sm_w[k] = expf(lse[(int64_t)(c0 + k) * a.n_q_heads] - M) * inv_total;
+    __syncthreads();
+    int k = 0;
+    for (; k + 16 <= n; k += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = po[(int64_t)(c0 + k + u) * row_stride];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc += sm_w[k + u] * v[u];
+    }
+    for (; k < n; ++k) acc += sm_w[k] * po[(int64_t)(c0 + k) * row_stride];
+  }
+  a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = acc;
+}
+
 template <int D, bool FP8, bool PRO>
-hipError_t launch(const Args& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, PRO>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
-  return hipGetLastError();
+hipError_t launch(const Args& a, int grid, hipStream_t stream, void* split_event) {
+  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, PRO>), dim3(grid), dim3(64 * kWaves), 0, stream, a,
+                     a.block_table, a.seq_lens, a.plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (split_event) {
+    e = hipEventRecord(static_cast<hipEvent_t>(split_event), stream);
+    if (e != hipSuccess) return e;
+  }
+  if (a.n_parts > 0) {
+    hipLaunchKernelGGL((hda_merge_kernel<D>), dim3(a.batch * a.n_q_heads), dim3(D), 0, stream,
+                       a, a.plan);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 template <int D>
-hipError_t launch_d(const Args& a, bool fp8, bool pro, int grid, hipStream_t st) {
-  if (fp8) return pro ? launch<D, true, true>(a, grid, st) : launch<D, true, false>(a, grid, st);
-  return pro ? launch<D, false, true>(a, grid, st) : launch<D, false, false>(a, grid, st);
+hipError_t launch_d(const Args& a, bool fp8, bool pro, int grid, hipStream_t st, void* ev) {
+  if (fp8) return pro ? launch<D, true, true>(a, grid, st, ev) : launch<D, true, false>(a, grid, st, ev);
+  return pro ? launch<D, false, true>(a, grid, st, ev) : launch<D, false, false>(a, grid, st, ev);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -588,8 +640,6 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
                                               p->head_dim);
   if (ws_need < 0) return HDA_ERR_BAD_PLAN;
   if (P > 0 && (!p->workspace || p->workspace_bytes < ws_need)) return HDA_ERR_WORKSPACE;
-  if (P > 0 && (!p->counters || p->counters_len < (int64_t)p->batch * p->n_kv_heads))
-    return HDA_ERR_WORKSPACE;
 
   const int D = p->head_dim;
   const int elem = p->kv_dtype == HDA_KV_FP8_E4M3 ? 1 : 2;
@@ -605,14 +655,13 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
   const int64_t o_bytes = (P * p->n_q_heads * D * 4 + 255) / 256 * 256;
   a.part_o = ws ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_lse = ws ? reinterpret_cast<float*>(ws + o_bytes) : nullptr;
-  a.counters = p->counters;
   a.q_norm_w = static_cast<const uint16_t*>(p->q_norm_w);
   a.k_norm_w = static_cast<const uint16_t*>(p->k_norm_w);
   a.k_new = static_cast<const uint16_t*>(p->k_new);
   a.v_new = static_cast<const uint16_t*>(p->v_new);
   a.head_stride = p->page_size * D * elem;
   a.page_stride = (int64_t)a.head_stride * p->n_kv_heads;
-  a.num_pages = p->num_pages;
+  a.num_pages = (int32_t)(p->num_pages < 0x7fffffffLL ? p->num_pages : 0x7fffffffLL);
   a.batch = p->batch;
   a.n_q_heads = p->n_q_heads;
   a.n_kv_heads = p->n_kv_heads;
@@ -631,7 +680,7 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
-  hipError_t e = D == 64 ? launch_d<64>(a, fp8, p->prologue != 0, (int)grid, st)
-                         : launch_d<128>(a, fp8, p->prologue != 0, (int)grid, st);
+  hipError_t e = D == 64 ? launch_d<64>(a, fp8, p->prologue != 0, (int)grid, st, p->split_event)
+                         : launch_d<128>(a, fp8, p->prologue != 0, (int)grid, st, p->split_event);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
 }

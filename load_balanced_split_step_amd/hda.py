@@ -64,8 +64,7 @@ class hda_params(ctypes.Structure):
         ("v_new", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_int64),
-        ("counters", ctypes.c_void_p),
-        ("counters_len", ctypes.c_int64),
+        ("split_event", ctypes.c_void_p),
     ]
 
 
@@ -220,7 +219,6 @@ class DeviceBatch:
         self.kw = params_kw
         self.device = device
         self._ws = None
-        self._cnt = None
 
     @classmethod
     def from_inputs(cls, inp, device="cuda:0"):
@@ -249,17 +247,8 @@ class DeviceBatch:
     def workspace(self, nbytes):
         import torch
         if self._ws is None or self._ws.numel() < nbytes:
-            self._ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
         return self._ws
-
-    def counters(self):
-        """Merge counters for this batch: zero-filled once, left zero by
-        every completed decode."""
-        import torch
-        n = self.kw["batch"] * self.kw["n_kv_heads"]
-        if self._cnt is None or self._cnt.numel() < n:
-            self._cnt = torch.zeros(n, dtype=torch.int32, device=self.device)
-        return self._cnt
 
     def params(self, plan, workspace=None):
         p = hda_params(**self.kw)
@@ -274,9 +263,6 @@ class DeviceBatch:
         ws = workspace if workspace is not None else self.workspace(need)
         p.workspace = ws.data_ptr()
         p.workspace_bytes = ws.numel() * ws.element_size()
-        cnt = self.counters()
-        p.counters = cnt.data_ptr()
-        p.counters_len = cnt.numel()
         return p
 
     def decode(self, plan, out=None, plan_dev=None, stream=None, k_pages=None, v_pages=None,

@@ -162,8 +162,7 @@ def _params(**kw):
     base = dict(batch=4, n_q_heads=8, n_kv_heads=2, head_dim=64, page_size=16,
                 max_pages_per_req=33, num_pages=52, kv_dtype=hda.HDA_KV_BF16,
                 sm_scale=0.125, k_scale=1.0, v_scale=1.0, prologue=0,
-                workspace=FAKE + 0x100000, workspace_bytes=1 << 20,
-                counters=FAKE + 0x200000, counters_len=8)
+                workspace=FAKE + 0x100000, workspace_bytes=1 << 20)
     base.update(kw)
     return hda.hda_params(**base)
 
@@ -203,7 +202,5 @@ def test_decode_argument_errors(lib):
     assert _decode_status(lib, _params(), bad) == E.HDA_ERR_BAD_PLAN
     assert _decode_status(lib, _params(workspace=None), plan) == E.HDA_ERR_WORKSPACE
     assert _decode_status(lib, _params(workspace_bytes=100), plan) == E.HDA_ERR_WORKSPACE
-    assert _decode_status(lib, _params(counters=None), plan) == E.HDA_ERR_WORKSPACE
-    assert _decode_status(lib, _params(counters_len=7), plan) == E.HDA_ERR_WORKSPACE
     for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.hda_status_string(s)
