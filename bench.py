@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-static", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -273,6 +275,26 @@ def main():
                      "kernel": "hda_decode_kernel (tile kernel; HIP events on its stream)"},
         "parity_max_err_sampled": max_err,
     }
+
+    if args.copy_probe:
+        # a plain copy kernel of known size: reads and writes 2^30 bytes per
+        # launch; the HBM counters of this launch calibrate the kernel's
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dst.copy_(src)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        res["copy_probe"] = {"bytes_read": nbytes, "bytes_written": nbytes,
+                             "us": round(ms * 1e3, 2),
+                             "read_plus_write_gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+        log(f"copy probe: 1 GiB copy {ms * 1e3:.1f} us")
+        del src, dst
 
     if not args.no_static:
         static = {}
