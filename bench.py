@@ -226,7 +226,8 @@ def main():
 
     # parity spot check on the timed output (sampled rows, fp64 oracle)
     import oracle
-    pairs = [(0, 0), (0, 37), (int(np.argmax(lens)), 63), (len(lens) - 1, 5)]
+    Hq = w.n_q_heads
+    pairs = [(0, 0), (0, (37 % Hq)), (int(np.argmax(lens)), Hq - 1), (len(lens) - 1, 5 % Hq)]
     ref = oracle.attention_selected(oracle.bf16_to_f64(inp["q"]), inp["k_pages"], inp["v_pages"],
                                     inp["block_table"], lens, w.kv_dtype, float(inp["sm_scale"]),
                                     pairs, float(inp["k_scale"]), float(inp["v_scale"])) \
