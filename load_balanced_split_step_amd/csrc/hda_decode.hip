@@ -135,13 +135,19 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// cos/sin of pos * theta^(-2l/D) for lane l < D/2, in double precision.
-__device__ inline void rope_angle(int pos, int lane, int D, float theta, float& c, float& s) {
-  const double inv = exp(-(2.0 * (double)lane / (double)D) * log((double)theta));
-  double sd, cd;
-  sincos((double)pos * inv, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+// Rotary angles: inverse frequency theta^(-2l/D) for lane l < D/2 in double
+// precision (computed once per wave), the angle pos * inv_freq in double,
+// reduced to [-pi, pi] in double, then cos/sin in float.  The reduction keeps
+// the float rounding of the angle at ~1e-7 rad for positions up to 2^31.
+__device__ inline double rope_inv_freq(int lane, int D, float theta) {
+  return exp(-(2.0 * (double)lane / (double)D) * log((double)theta));
+}
+
+__device__ inline void rope_cos_sin(int pos, double inv_freq, float& c, float& s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  const double phi = (double)pos * inv_freq;
+  const double r = phi - rint(phi / two_pi) * two_pi;
+  sincosf((float)r, &s, &c);
 }
 
 // RMSNorm (over D, weight w) then rotate-half RoPE of one head vector held as
@@ -348,6 +354,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
   const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
   if (it_begin >= it_end) return;
 
+  // rotary inverse frequency of this lane (prologue only)
+  const double inv_freq = PRO && lane < D / 2 ? rope_inv_freq(lane, D, a.rope_theta) : 0.0;
+
   if constexpr (PRO) {
     // New token of each request whose last item is ours: k' = RoPE(RMSNorm(k)),
     // v as given, both stored into slot len-1 for this kv head.  Only this
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
         if (page < 0 || page >= a.num_pages) continue;
         const bool act = lane < D / 2;
         float c = 1.f, s = 0.f;
-        if (act) rope_angle(pos, lane, D, a.rope_theta, c, s);
+        if (act) rope_cos_sin(pos, inv_freq, c, s);
         const int64_t src = ((int64_t)b * a.n_kv_heads + h) * D;
         float k0v = act ? bf16_bits_to_float(a.k_new[src + lane]) : 0.f;
         float k1v = act ? bf16_bits_to_float(a.k_new[src + lane + D / 2]) : 0.f;
@@ -405,16 +414,23 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
     const int L = seq_lens[b];
     const int64_t qrow0 = ((int64_t)b * a.n_q_heads + (int64_t)h * g) * D;
 
+    // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
+    const int c_last = (k1 - 1) / kChunk;
+    int c = k0 / kChunk + wave;
+    const bool has_chunks = c <= c_last;   // uniform per wave
+    Chunk<D, FP8> A, B;
+    __amdgpu_buffer_rsrc_t kr[2], vr[2];
+
     // q operand (MFMA B): lane (i, kg) holds q head i, dims qk_dim(s, kg) + 0..7.
     bf16x8 qop[G::STEPS];
     if constexpr (PRO) {
       const bool act = lane < D / 2;
-      float c = 1.f, s = 0.f;
-      if (act) rope_angle(L - 1, lane, D, a.rope_theta, c, s);
+      float cs = 1.f, sn = 0.f;
+      if (act) rope_cos_sin(L - 1, inv_freq, cs, sn);
       for (int hh = wave; hh < g; hh += kWaves) {
         float x0 = act ? bf16_bits_to_float(a.q[qrow0 + (int64_t)hh * D + lane]) : 0.f;
         float x1 = act ? bf16_bits_to_float(a.q[qrow0 + (int64_t)hh * D + lane + D / 2]) : 0.f;
-        norm_rope(x0, x1, act, a.q_norm_w, lane, D, a.rms_eps, c, s);
+        norm_rope(x0, x1, act, a.q_norm_w, lane, D, a.rms_eps, cs, sn);
         if (act) {
           sm_q[hh][lane] = __builtin_bit_cast(uint16_t, (__bf16)x0);
           sm_q[hh][lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)x1);
@@ -441,12 +457,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
 #pragma unroll
     for (int nb = 0; nb < G::DPL; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
-    const int c_last = (k1 - 1) / kChunk;
-    int c = k0 / kChunk + wave;
-    if (c <= c_last) {
-      Chunk<D, FP8> A, B;
-      __amdgpu_buffer_rsrc_t kr[2], vr[2];
+    if (has_chunks) {
       chunk_rsrc<D, FP8>(a, block_table, b, L, h, c, true, kr, vr);
       issue_chunk<D, FP8>(A, kr, vr, i, kg);
       // The next chunk's loads are issued before this chunk's math; the
@@ -521,8 +532,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
 //   out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M),  M = max_s lse_s.
 // A separate launch: the kernel boundary makes every partial written by the
 // tile kernel (on any XCD) visible here without cross-XCD fences.  Thread d
-// owns output dim d; the slot loop is unrolled so that many partial rows are
-// in flight at once.
+// owns output dim d.  The first kMergeEarly partial rows are loaded up front,
+// before the weights are known, so that the whole merge costs about one
+// memory round trip for typical slot counts.
+constexpr int kMergeEarly = 32;    // partial rows loaded before the weights
 constexpr int kMergeStage = 512;   // slot weights staged in LDS per pass
 
 template <int D>
@@ -534,9 +547,18 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
   const int32_t* rpp = plan + HDA_PLAN_HEADER_INTS + a.n_wg + 1 + 4 * a.n_items;
   const int s0 = max(0, rpp[b]), s1 = min(a.n_parts, rpp[b + 1]);
   if (s1 <= s0) return;
-  const float* lse = a.part_lse + hq;               // stride n_q_heads
-  float m = -INFINITY;
-  for (int sl = s0 + d; sl < s1; sl += D) m = fmaxf(m, lse[(int64_t)sl * a.n_q_heads]);
+  const int n = s1 - s0;
+  const int64_t row_stride = (int64_t)a.n_q_heads * D;
+  const float* po = a.part_o + (int64_t)s0 * row_stride + (int64_t)hq * D + d;
+  const float* lse = a.part_lse + (int64_t)s0 * a.n_q_heads + hq;   // stride n_q_heads
+
+  float early[kMergeEarly];
+#pragma unroll
+  for (int u = 0; u < kMergeEarly; ++u) early[u] = u < n ? po[(int64_t)u * row_stride] : 0.f;
+  float my_lse = d < n ? lse[(int64_t)d * a.n_q_heads] : -INFINITY;
+
+  float m = my_lse;
+  for (int k = d + D; k < n; k += D) m = fmaxf(m, lse[(int64_t)k * a.n_q_heads]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if (lane == 0) sm_red[0][wave] = m;
@@ -544,8 +566,8 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
   float M = sm_red[0][0];
 #pragma unroll
   for (int w = 1; w < D / 64; ++w) M = fmaxf(M, sm_red[0][w]);
-  float t = 0.f;
-  for (int sl = s0 + d; sl < s1; sl += D) t += expf(lse[(int64_t)sl * a.n_q_heads] - M);
+  float t = d < n ? expf(my_lse - M) : 0.f;
+  for (int k = d + D; k < n; k += D) t += expf(lse[(int64_t)k * a.n_q_heads] - M);
   t = wave_sum(t);
   if (lane == 0) sm_red[1][wave] = t;
   __syncthreads();
@@ -554,24 +576,30 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
   for (int w = 0; w < D / 64; ++w) total += sm_red[1][w];
   const float inv_total = 1.0f / total;
 
-  const int64_t row_stride = (int64_t)a.n_q_heads * D;
-  const float* po = a.part_o + (int64_t)hq * D + d;
   float acc = 0.f;
-  for (int c0 = s0; c0 < s1; c0 += kMergeStage) {
-    const int n = min(kMergeStage, s1 - c0);
-    __syncthreads();
-    for (int k = d; k < n; k += D)
-      sm_w[k] = expf(lse[(int64_t)(c0 + k) * a.n_q_heads] - M) * inv_total;
+  for (int c0 = 0; c0 < n; c0 += kMergeStage) {
+    const int cn = min(kMergeStage, n - c0);
+    if (c0 > 0) __syncthreads();
+    for (int k = d; k < cn; k += D) {
+      const float l = (c0 == 0 && k == d) ? my_lse : lse[(int64_t)(c0 + k) * a.n_q_heads];
+      sm_w[k] = expf(l - M) * inv_total;
+    }
     __syncthreads();
     int k = 0;
-    for (; k + 16 <= n; k += 16) {
+    if (c0 == 0) {
+#pragma unroll
+      for (int u = 0; u < kMergeEarly; ++u)
+        if (u < cn) acc += sm_w[u] * early[u];
+      k = kMergeEarly;
+    }
+    for (; k + 16 <= cn; k += 16) {
       float v[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) v[u] = po[(int64_t)(c0 + k + u) * row_stride];
 #pragma unroll
       for (int u = 0; u < 16; ++u) acc += sm_w[k + u] * v[u];
     }
-    for (; k < n; ++k) acc += sm_w[k] * po[(int64_t)(c0 + k) * row_stride];
+    for (; k < cn; ++k) acc += sm_w[k] * po[(int64_t)(c0 + k) * row_stride];
   }
   a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = acc;
 }
