@@ -193,6 +193,44 @@ int hda_decode(const hda_params* p, const void* q, void* k_pages,
                const int32_t* plan_dev, int64_t plan_len, float* out,
                void* stream);
 
+/*
+ * The same decode step with the plan built on the device: each workgroup
+ * derives its own items from the device lengths with exactly the hda_plan
+ * rule (request-major tiles of tile_len, contiguous balanced split over
+ * n_workgroups), so no host planning or plan upload is needed per step and
+ * the step has fixed arguments (it can be captured in a HIP graph while the
+ * lengths change in device memory).  This follows the persistent kernel of
+ * the arex-research page that allocates tiles every decode step by the
+ * actual KV length.
+ *
+ *   seq_lens    [device] int32 [B], every length >= 1 (a request with a
+ *               length < 1 gets no item and its output rows are not written)
+ *   workspace   at least hda_workspace_bytes_bound(B, n_workgroups, Hq, D)
+ * Other arguments and errors as hda_decode.  Outputs are bitwise identical
+ * to hda_decode with hda_plan(seq_lens, B, tile_len, n_workgroups).
+ */
+int hda_decode_auto(const hda_params* p, const void* q, void* k_pages, void* v_pages,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int32_t tile_len, int32_t n_workgroups, float* out, void* stream);
+
+/*
+ * Workspace bytes that suffice for any plan over `batch` requests and
+ * `n_workgroups` workgroups (partial slots <= W + B - 1).  -1 for
+ * non-positive arguments.
+ */
+int64_t hda_workspace_bytes_bound(int32_t batch, int32_t n_workgroups,
+                                  int32_t n_q_heads, int32_t head_dim);
+
+/*
+ * Writes, on `stream`, the hda_plan-format plan for the device lengths
+ * `seq_lens` [device] into `plan` [device] (capacity ints, at least
+ * hda_plan_capacity(batch, n_workgroups)), computed on the GPU with the
+ * device-side planning of hda_decode_auto.  Asynchronous.  Errors:
+ * HDA_ERR_INVALID_ARG, HDA_ERR_CAPACITY, HDA_ERR_HIP.
+ */
+int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
+                    int32_t n_workgroups, int32_t* plan, int64_t capacity, void* stream);
+
 /* Static description of a status code. */
 const char* hda_status_string(int status);
 

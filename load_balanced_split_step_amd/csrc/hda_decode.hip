@@ -68,6 +68,7 @@ struct Args {
   int32_t batch, n_q_heads, n_kv_heads, group;
   int32_t page_size, log2_ps, max_pages;
   int32_t n_wg, n_items, n_parts;
+  int32_t tile_len;      // device-planned launches only
   float qk_scale_log2;   // sm_scale * k_scale * log2(e)
   float v_scale;
   float k_scale, rms_eps, rope_theta;
@@ -328,90 +329,63 @@ __device__ inline void compute_chunk(const Chunk<D, FP8>& ch, const bf16x8 (&qop
   }
 }
 
-template <int D, bool FP8, bool PRO>
-__global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
-    Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ plan) {
-  // The plan, lengths and block table are read-only here and reached by
-  // wave-uniform addresses, so they load through the scalar cache.
+// LDS of one tile workgroup.
+template <int D>
+struct TileSmem {
+  float acc[kWaves][kMaxGroup][D];
+  float m[kWaves][kMaxGroup];
+  float l[kWaves][kMaxGroup];
+  __attribute__((aligned(16))) uint16_t q[kMaxGroup][D];
+};
+
+// Prologue store for the new token of request b (length L) and kv head h:
+// k' = RoPE(RMSNorm(k_new)) and v_new, divided by their scales, written to
+// row L-1 of the cache.  Executed by one wave.
+template <int D, bool FP8>
+__device__ inline void store_new_token(const Args& a, const int32_t* __restrict__ block_table,
+                                       int b, int L, int h, int lane, double inv_freq) {
   using G = Geo<D, FP8>;
-  __shared__ float sm_acc[kWaves][kMaxGroup][D];
-  __shared__ float sm_m[kWaves][kMaxGroup];
-  __shared__ float sm_l[kWaves][kMaxGroup];
-  __shared__ __attribute__((aligned(16))) uint16_t sm_q[kMaxGroup][D];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  // wave index is uniform within a wave: keep it (and everything derived
-  // from it: chunk index, page id, buffer resources) in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int i = lane & 15, kg = lane >> 4;
-  const int h = blockIdx.x % a.n_kv_heads;
-  const int w = blockIdx.x / a.n_kv_heads;
-  const int g = a.group;
-  const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
-  const int32_t* items = wg_ptr + a.n_wg + 1;
-  const int32_t* rpp = items + 4 * a.n_items;
-  const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
-  if (it_begin >= it_end) return;
-
-  // rotary inverse frequency of this lane (prologue only)
-  const double inv_freq = PRO && lane < D / 2 ? rope_inv_freq(lane, D, a.rope_theta) : 0.0;
-
-  if constexpr (PRO) {
-    // New token of each request whose last item is ours: k' = RoPE(RMSNorm(k)),
-    // v as given, both stored into slot len-1 for this kv head.  Only this
-    // workgroup reads that row (it lies inside its item), so a fence and a
-    // barrier order the write before the chunk loads.
-    if (wave == 0) {
-      for (int it = it_begin; it < it_end; ++it) {
-        const int b = items[4 * it], k1 = items[4 * it + 2];
-        if ((unsigned)b >= (unsigned)a.batch) continue;
-        const int L = seq_lens[b];
-        if (k1 != L || L < 1) continue;
-        const int pos = L - 1, pidx = pos >> a.log2_ps;
-        if (pidx >= a.max_pages) continue;
-        const int page = block_table[(int64_t)b * a.max_pages + pidx];
-        if (page < 0 || page >= a.num_pages) continue;
-        const bool act = lane < D / 2;
-        float c = 1.f, s = 0.f;
-        if (act) rope_cos_sin(pos, inv_freq, c, s);
-        const int64_t src = ((int64_t)b * a.n_kv_heads + h) * D;
-        float k0v = act ? bf16_bits_to_float(a.k_new[src + lane]) : 0.f;
-        float k1v = act ? bf16_bits_to_float(a.k_new[src + lane + D / 2]) : 0.f;
-        norm_rope(k0v, k1v, act, a.k_norm_w, lane, D, a.rms_eps, c, s);
-        if (act) {
-          const float v0 = bf16_bits_to_float(a.v_new[src + lane]);
-          const float v1 = bf16_bits_to_float(a.v_new[src + lane + D / 2]);
-          const int64_t row = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
-                              (int64_t)(pos & (a.page_size - 1)) * G::RB;
-          if constexpr (FP8) {
-            a.k_pages[row + lane] = (uint8_t)fp8_encode(k0v / a.k_scale);
-            a.k_pages[row + lane + D / 2] = (uint8_t)fp8_encode(k1v / a.k_scale);
-            a.v_pages[row + lane] = (uint8_t)fp8_encode(v0 / a.v_scale);
-            a.v_pages[row + lane + D / 2] = (uint8_t)fp8_encode(v1 / a.v_scale);
-          } else {
-            uint16_t* kp = reinterpret_cast<uint16_t*>(a.k_pages + row);
-            uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pages + row);
-            kp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(k0v / a.k_scale));
-            kp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(k1v / a.k_scale));
-            vp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(v0 / a.v_scale));
-            vp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(v1 / a.v_scale));
-          }
-        }
-      }
+  const int pos = L - 1, pidx = pos >> a.log2_ps;
+  if (L < 1 || pidx >= a.max_pages) return;
+  const int page = block_table[(int64_t)b * a.max_pages + pidx];
+  if (page < 0 || page >= a.num_pages) return;
+  const bool act = lane < D / 2;
+  float c = 1.f, s = 0.f;
+  if (act) rope_cos_sin(pos, inv_freq, c, s);
+  const int64_t src = ((int64_t)b * a.n_kv_heads + h) * D;
+  float k0v = act ? bf16_bits_to_float(a.k_new[src + lane]) : 0.f;
+  float k1v = act ? bf16_bits_to_float(a.k_new[src + lane + D / 2]) : 0.f;
+  norm_rope(k0v, k1v, act, a.k_norm_w, lane, D, a.rms_eps, c, s);
+  if (act) {
+    const float v0 = bf16_bits_to_float(a.v_new[src + lane]);
+    const float v1 = bf16_bits_to_float(a.v_new[src + lane + D / 2]);
+    const int64_t row = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
+                        (int64_t)(pos & (a.page_size - 1)) * G::RB;
+    if constexpr (FP8) {
+      a.k_pages[row + lane] = (uint8_t)fp8_encode(k0v / a.k_scale);
+      a.k_pages[row + lane + D / 2] = (uint8_t)fp8_encode(k1v / a.k_scale);
+      a.v_pages[row + lane] = (uint8_t)fp8_encode(v0 / a.v_scale);
+      a.v_pages[row + lane + D / 2] = (uint8_t)fp8_encode(v1 / a.v_scale);
+    } else {
+      uint16_t* kp = reinterpret_cast<uint16_t*>(a.k_pages + row);
+      uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pages + row);
+      kp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(k0v / a.k_scale));
+      kp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(k1v / a.k_scale));
+      vp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(v0 / a.v_scale));
+      vp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(v1 / a.v_scale));
     }
-    // This workgroup's stores are complete before the barrier; the acquire
-    // drops any cached copy of the written rows before the chunk loads.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
+}
 
-  for (int it = it_begin; it < it_end; ++it) {
-    const int b = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
-              slot = items[4 * it + 3];
-    if ((unsigned)b >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
-    const int L = seq_lens[b];
+// One plan item (b, [k0, k1), slot) for kv head h: the waves stream the
+// item's chunks, combine in LDS, and write the output (slot -1) or a partial.
+template <int D, bool FP8, bool PRO>
+__device__ inline void process_item(const Args& a, const int32_t* __restrict__ block_table,
+                                    TileSmem<D>& sm, int b, int k0, int k1, int slot, int L,
+                                    int h, int wave, int lane, int tid, double inv_freq) {
+  using G = Geo<D, FP8>;
+  const int i = lane & 15, kg = lane >> 4;
+  const int g = a.group;
     const int64_t qrow0 = ((int64_t)b * a.n_q_heads + (int64_t)h * g) * D;
 
     // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
@@ -432,15 +406,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
         float x1 = act ? bf16_bits_to_float(a.q[qrow0 + (int64_t)hh * D + lane + D / 2]) : 0.f;
         norm_rope(x0, x1, act, a.q_norm_w, lane, D, a.rms_eps, cs, sn);
         if (act) {
-          sm_q[hh][lane] = __builtin_bit_cast(uint16_t, (__bf16)x0);
-          sm_q[hh][lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)x1);
+          sm.q[hh][lane] = __builtin_bit_cast(uint16_t, (__bf16)x0);
+          sm.q[hh][lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)x1);
         }
       }
       __syncthreads();
 #pragma unroll
       for (int s2 = 0; s2 < G::STEPS; ++s2) {
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (i < g) v = *reinterpret_cast<const u32x4*>(&sm_q[i][qk_dim<FP8>(s2, kg)]);
+        if (i < g) v = *reinterpret_cast<const u32x4*>(&sm.q[i][qk_dim<FP8>(s2, kg)]);
         qop[s2] = __builtin_bit_cast(bf16x8, v);
       }
     } else {
@@ -485,8 +459,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
     l_tot += __shfl_xor(l_tot, 16);
     l_tot += __shfl_xor(l_tot, 32);
     if (kg == 0) {
-      sm_m[wave][i] = m_run;
-      sm_l[wave][i] = l_tot;
+      sm.m[wave][i] = m_run;
+      sm.l[wave][i] = l_tot;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -495,22 +469,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
 #pragma unroll
         for (int v4 = 0; v4 < G::DPL / 4; ++v4) {
           f32x4 o = {acc[4 * v4][r], acc[4 * v4 + 1][r], acc[4 * v4 + 2][r], acc[4 * v4 + 3][r]};
-          *reinterpret_cast<f32x4*>(&sm_acc[wave][hh][G::DPL * i + 4 * v4]) = o;
+          *reinterpret_cast<f32x4*>(&sm.acc[wave][hh][G::DPL * i + 4 * v4]) = o;
         }
       }
     }
     __syncthreads();
     for (int idx = tid; idx < g * D; idx += 64 * kWaves) {
       const int hh = idx / D, d = idx - hh * D;
-      float M = sm_m[0][hh];
+      float M = sm.m[0][hh];
 #pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][hh]);
       float lsum = 0.f, o = 0.f;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
-        const float wt = __builtin_amdgcn_exp2f(sm_m[ww][hh] - M);
-        lsum += wt * sm_l[ww][hh];
-        o += wt * sm_acc[ww][hh][d];
+        const float wt = __builtin_amdgcn_exp2f(sm.m[ww][hh] - M);
+        lsum += wt * sm.l[ww][hh];
+        o += wt * sm.acc[ww][hh][d];
       }
       o = o / lsum * a.v_scale;
       const int64_t hq = (int64_t)h * g + hh;
@@ -523,7 +497,167 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
       }
     }
 
-    __syncthreads();  // LDS is reused by the next item
+}
+
+// ---- device-side planning: the host planner's arithmetic, per wave ----
+// T tiles over W workgroups, the first r = T mod W taking q + 1 tiles.
+struct SplitDev {
+  uint32_t q, r;
+  __device__ uint32_t first_tile(uint32_t w) const { return w * q + min(w, r); }
+  __device__ uint32_t owner(uint32_t t) const {
+    const uint32_t big = r * (q + 1);
+    return t < big ? t / (q + 1) : r + (t - big) / q;
+  }
+};
+
+__device__ inline uint32_t tiles_of(int len, int tile_len) {
+  return len > 0 ? (uint32_t)((len - 1) / tile_len + 1) : 0u;
+}
+
+__device__ inline uint32_t wave_incl_scan(uint32_t x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ inline uint32_t wave_total_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Per-request plan facts for the 64 requests cb + lane, given the running
+// totals over earlier requests: first tile, tile count, item count and the
+// first partial slot.
+struct ReqScan {
+  int b, len;
+  uint32_t n, first, k, slot_base;
+};
+
+__device__ inline ReqScan scan_requests(const int32_t* __restrict__ seq_lens, int batch,
+                                        int tile_len, const SplitDev& sp, int cb, int lane,
+                                        uint32_t first_carry, uint32_t slot_carry,
+                                        uint32_t& first_total, uint32_t& split_total) {
+  ReqScan r;
+  r.b = cb + lane;
+  r.len = r.b < batch ? seq_lens[r.b] : 0;
+  r.n = tiles_of(r.len, tile_len);
+  const uint32_t incl = wave_incl_scan(r.n, lane);
+  r.first = first_carry + incl - r.n;
+  r.k = r.n ? sp.owner(r.first + r.n - 1) - sp.owner(r.first) + 1 : 0u;
+  const uint32_t split_k = r.k > 1 ? r.k : 0u;
+  const uint32_t sincl = wave_incl_scan(split_k, lane);
+  r.slot_base = slot_carry + sincl - split_k;
+  first_total = __shfl(incl, 63);
+  split_total = __shfl(sincl, 63);
+  return r;
+}
+
+__device__ inline uint32_t total_tiles(const int32_t* __restrict__ seq_lens, int batch,
+                                       int tile_len, int lane) {
+  uint32_t T = 0;
+  for (int cb = 0; cb < batch; cb += 64) {
+    const int b = cb + lane;
+    T += wave_total_u32(b < batch ? tiles_of(seq_lens[b], tile_len) : 0u);
+  }
+  return __builtin_amdgcn_readfirstlane(T);
+}
+
+// Workgroup (w, h): W * Hkv workgroups, kv head fastest.  Items come from the
+// host plan (DEVPLAN false) or are derived here from the device lengths with
+// the same rule (DEVPLAN true), in the same order.
+template <int D, bool FP8, bool PRO, bool DEVPLAN>
+__global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
+    Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ plan) {
+  // The plan, lengths and block table are read-only here and reached by
+  // wave-uniform addresses, so they load through the scalar cache.
+  __shared__ TileSmem<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index is uniform within a wave: keep it (and everything derived
+  // from it: chunk index, page id, buffer resources) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x % a.n_kv_heads;
+  const int w = blockIdx.x / a.n_kv_heads;
+  // rotary inverse frequency of this lane (prologue only)
+  const double inv_freq = PRO && lane < D / 2 ? rope_inv_freq(lane, D, a.rope_theta) : 0.0;
+
+  if constexpr (!DEVPLAN) {
+    const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
+    const int32_t* items = wg_ptr + a.n_wg + 1;
+    const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
+    if (it_begin >= it_end) return;
+    if constexpr (PRO) {
+      // New token of each request whose last item is ours.  Only this
+      // workgroup reads that row (it lies inside its item).
+      if (wave == 0) {
+        for (int it = it_begin; it < it_end; ++it) {
+          const int b = items[4 * it], k1 = items[4 * it + 2];
+          if ((unsigned)b >= (unsigned)a.batch) continue;
+          const int L = seq_lens[b];
+          if (k1 == L) store_new_token<D, FP8>(a, block_table, b, L, h, lane, inv_freq);
+        }
+      }
+      // This workgroup's stores are complete before the barrier; the acquire
+      // drops any cached copy of the written rows before the chunk loads.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    for (int it = it_begin; it < it_end; ++it) {
+      const int b = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
+                slot = items[4 * it + 3];
+      if ((unsigned)b >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
+      process_item<D, FP8, PRO>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], h, wave, lane,
+                                tid, inv_freq);
+    }
+  } else {
+    // Every wave derives the same plan facts; they stay wave-uniform.
+    const uint32_t T = total_tiles(seq_lens, a.batch, a.tile_len, lane);
+    const SplitDev sp{T / (uint32_t)a.n_wg, T % (uint32_t)a.n_wg};
+    const uint32_t t0 = sp.first_tile(w), t1 = sp.first_tile(w + 1);
+    if (t0 >= t1) return;
+    for (int pass = PRO ? 0 : 1; pass < 2; ++pass) {
+      // pass 0 (prologue only): store the new tokens this workgroup owns;
+      // pass 1: the attention items.
+      uint32_t first_carry = 0, slot_carry = 0;
+      for (int cb = 0; cb < a.batch && first_carry < t1; cb += 64) {
+        uint32_t ft, st;
+        const ReqScan r = scan_requests(seq_lens, a.batch, a.tile_len, sp, cb, lane, first_carry,
+                                        slot_carry, ft, st);
+        uint64_t mask = __ballot(r.n > 0 && r.first < t1 && r.first + r.n > t0);
+        while (mask) {
+          const int j = __builtin_ctzll(mask);
+          mask &= mask - 1;
+          const int b = __builtin_amdgcn_readlane(r.b, j);
+          const int L = __builtin_amdgcn_readlane(r.len, j);
+          const uint32_t first = __builtin_amdgcn_readlane(r.first, j);
+          const uint32_t n = __builtin_amdgcn_readlane(r.n, j);
+          const uint32_t k = __builtin_amdgcn_readlane(r.k, j);
+          const uint32_t sb = __builtin_amdgcn_readlane(r.slot_base, j);
+          const uint32_t lo = max(t0, first), hi = min(t1, first + n);
+          const int k0 = (int)((int64_t)(lo - first) * a.tile_len);
+          const int k1 = (int)min((int64_t)(hi - first) * a.tile_len, (int64_t)L);
+          if (pass == 0) {
+            if (wave == 0 && k1 == L) store_new_token<D, FP8>(a, block_table, b, L, h, lane, inv_freq);
+          } else {
+            const int slot = k > 1 ? (int)(sb + (uint32_t)w - sp.owner(first)) : -1;
+            process_item<D, FP8, PRO>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane,
+                                      tid, inv_freq);
+          }
+        }
+        first_carry += ft;
+        slot_carry += st;
+      }
+      if (pass == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+    }
   }
 }
 
@@ -538,14 +672,37 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
 constexpr int kMergeEarly = 32;    // partial rows loaded before the weights
 constexpr int kMergeStage = 512;   // slot weights staged in LDS per pass
 
-template <int D>
-__global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __restrict__ plan) {
+template <int D, bool DEVPLAN>
+__global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __restrict__ plan,
+                                                      const int32_t* __restrict__ seq_lens) {
   __shared__ float sm_w[kMergeStage];
   __shared__ float sm_red[2][D / 64];
   const int d = threadIdx.x, lane = d & 63, wave = d >> 6;
   const int b = blockIdx.x / a.n_q_heads, hq = blockIdx.x % a.n_q_heads;
-  const int32_t* rpp = plan + HDA_PLAN_HEADER_INTS + a.n_wg + 1 + 4 * a.n_items;
-  const int s0 = max(0, rpp[b]), s1 = min(a.n_parts, rpp[b + 1]);
+  int s0, s1;
+  if constexpr (!DEVPLAN) {
+    const int32_t* rpp = plan + HDA_PLAN_HEADER_INTS + a.n_wg + 1 + 4 * a.n_items;
+    s0 = max(0, rpp[b]);
+    s1 = min(a.n_parts, rpp[b + 1]);
+  } else {
+    // slot range of request b under the device plan: scan up to b's chunk
+    const uint32_t T = total_tiles(seq_lens, a.batch, a.tile_len, lane);
+    const SplitDev sp{T / (uint32_t)a.n_wg, T % (uint32_t)a.n_wg};
+    uint32_t first_carry = 0, slot_carry = 0, k = 0, sb = 0;
+    for (int cb = 0; cb <= b; cb += 64) {
+      uint32_t ft, st;
+      const ReqScan r = scan_requests(seq_lens, a.batch, a.tile_len, sp, cb, lane, first_carry,
+                                      slot_carry, ft, st);
+      if (b < cb + 64) {
+        k = __builtin_amdgcn_readlane(r.k, b - cb);
+        sb = __builtin_amdgcn_readlane(r.slot_base, b - cb);
+      }
+      first_carry += ft;
+      slot_carry += st;
+    }
+    s0 = (int)sb;
+    s1 = k > 1 ? min(a.n_parts, (int)(sb + k)) : s0;
+  }
   if (s1 <= s0) return;
   const int n = s1 - s0;
   const int64_t row_stride = (int64_t)a.n_q_heads * D;
@@ -604,40 +761,119 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
   a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = acc;
 }
 
-template <int D, bool FP8, bool PRO>
+// The plan in the host format, built from device lengths by one wave with
+// the device-side planning arithmetic (the same items the tile kernel derives
+// for itself in a device-planned launch).
+__global__ __launch_bounds__(64) void hda_plan_kernel(const int32_t* __restrict__ seq_lens,
+                                                      int batch, int tile_len, int W,
+                                                      int32_t* __restrict__ plan) {
+  const int lane = threadIdx.x;
+  const uint32_t T = total_tiles(seq_lens, batch, tile_len, lane);
+  const SplitDev sp{T / (uint32_t)W, T % (uint32_t)W};
+  int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
+  int32_t* items = wg_ptr + W + 1;
+  // pass 1: item count N (items sit between wg_ptr and req_part_ptr)
+  uint32_t N = 0, P = 0;
+  {
+    uint32_t fc = 0, sc = 0;
+    for (int cb = 0; cb < batch; cb += 64) {
+      uint32_t ft, st;
+      const ReqScan r = scan_requests(seq_lens, batch, tile_len, sp, cb, lane, fc, sc, ft, st);
+      N += wave_total_u32(r.k);
+      fc += ft;
+      sc += st;
+    }
+    P = sc;
+  }
+  int32_t* rpp = items + 4 * N;
+  // pass 2: items, req_part_ptr, and wg_ptr contributions
+  uint32_t fc = 0, sc = 0, ic = 0;
+  for (int cb = 0; cb < batch; cb += 64) {
+    uint32_t ft, st;
+    const ReqScan r = scan_requests(seq_lens, batch, tile_len, sp, cb, lane, fc, sc, ft, st);
+    const uint32_t iincl = wave_incl_scan(r.k, lane);
+    const uint32_t ibase = ic + iincl - r.k;
+    if (r.b < batch) {
+      const uint32_t w0 = r.n ? sp.owner(r.first) : 0u;
+      for (uint32_t j = 0; j < r.k; ++j) {
+        const uint32_t wg = w0 + j;
+        const uint32_t lo = max(r.first, sp.first_tile(wg));
+        const uint32_t hi = min(r.first + r.n, sp.first_tile(wg + 1));
+        int32_t* it = items + 4 * (ibase + j);
+        it[0] = r.b;
+        it[1] = (int32_t)((int64_t)(lo - r.first) * tile_len);
+        it[2] = (int32_t)min((int64_t)(hi - r.first) * tile_len, (int64_t)r.len);
+        it[3] = r.k > 1 ? (int32_t)(r.slot_base + j) : -1;
+      }
+      rpp[r.b + 1] = (int32_t)(r.slot_base + (r.k > 1 ? r.k : 0u));
+    }
+    fc += ft;
+    sc += st;
+    ic += __shfl(iincl, 63);
+  }
+  // wg_ptr[w] = number of items held by workgroups before w
+  for (int w = 0; w <= W; ++w) {
+    uint32_t cnt = 0, fc2 = 0, sc2 = 0;
+    for (int cb = 0; cb < batch; cb += 64) {
+      uint32_t ft, st;
+      const ReqScan r = scan_requests(seq_lens, batch, tile_len, sp, cb, lane, fc2, sc2, ft, st);
+      uint32_t c = 0;
+      if (r.k) {
+        const uint32_t w0 = sp.owner(r.first);
+        c = (uint32_t)w > w0 ? min((uint32_t)w - w0, r.k) : 0u;
+      }
+      cnt += wave_total_u32(c);
+      fc2 += ft;
+      sc2 += st;
+    }
+    if (lane == 0) wg_ptr[w] = (int32_t)cnt;
+  }
+  if (lane == 0) {
+    rpp[0] = 0;
+    plan[0] = HDA_PLAN_VERSION;
+    plan[1] = batch;
+    plan[2] = tile_len;
+    plan[3] = W;
+    plan[4] = (int32_t)T;
+    plan[5] = (int32_t)N;
+    plan[6] = (int32_t)P;
+    plan[7] = 0;
+  }
+}
+
+template <int D, bool FP8, bool PRO, bool DEVPLAN>
 hipError_t launch(const Args& a, int grid, hipStream_t stream, void* split_event) {
-  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, PRO>), dim3(grid), dim3(64 * kWaves), 0, stream, a,
-                     a.block_table, a.seq_lens, a.plan);
+  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, PRO, DEVPLAN>), dim3(grid), dim3(64 * kWaves), 0,
+                     stream, a, a.block_table, a.seq_lens, a.plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (split_event) {
     e = hipEventRecord(static_cast<hipEvent_t>(split_event), stream);
     if (e != hipSuccess) return e;
   }
-  if (a.n_parts > 0) {
-    hipLaunchKernelGGL((hda_merge_kernel<D>), dim3(a.batch * a.n_q_heads), dim3(D), 0, stream,
-                       a, a.plan);
+  if (DEVPLAN || a.n_parts > 0) {
+    hipLaunchKernelGGL((hda_merge_kernel<D, DEVPLAN>), dim3(a.batch * a.n_q_heads), dim3(D), 0,
+                       stream, a, a.plan, a.seq_lens);
     e = hipGetLastError();
   }
   return e;
 }
 
-template <int D>
+template <int D, bool DEVPLAN>
 hipError_t launch_d(const Args& a, bool fp8, bool pro, int grid, hipStream_t st, void* ev) {
-  if (fp8) return pro ? launch<D, true, true>(a, grid, st, ev) : launch<D, true, false>(a, grid, st, ev);
-  return pro ? launch<D, false, true>(a, grid, st, ev) : launch<D, false, false>(a, grid, st, ev);
+  if (fp8)
+    return pro ? launch<D, true, true, DEVPLAN>(a, grid, st, ev)
+               : launch<D, true, false, DEVPLAN>(a, grid, st, ev);
+  return pro ? launch<D, false, true, DEVPLAN>(a, grid, st, ev)
+             : launch<D, false, false, DEVPLAN>(a, grid, st, ev);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-}  // namespace
-
-extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, void* v_pages,
-                          const int32_t* block_table, const int32_t* seq_lens,
-                          const int32_t* plan_host, const int32_t* plan_dev, int64_t plan_len,
-                          float* out, void* stream) {
-  if (!p || !q || !k_pages || !v_pages || !block_table || !seq_lens || !plan_host ||
-      !plan_dev || !out)
+// Checks shared by both decode entry points (host only, before any launch).
+int check_params(const hda_params* p, const void* q, const void* k_pages, const void* v_pages,
+                 const void* block_table, const void* seq_lens, const void* out) {
+  if (!p || !q || !k_pages || !v_pages || !block_table || !seq_lens || !out)
     return HDA_ERR_INVALID_ARG;
   if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1 || p->head_dim < 1 ||
       p->page_size < 1 || p->max_pages_per_req < 1 || p->num_pages < 1)
@@ -646,8 +882,7 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
       !isfinite(p->sm_scale) || !isfinite(p->k_scale) || !isfinite(p->v_scale))
     return HDA_ERR_INVALID_ARG;
   if (p->n_q_heads % p->n_kv_heads != 0) return HDA_ERR_INVALID_ARG;
-  const int g = p->n_q_heads / p->n_kv_heads;
-  if (g > kMaxGroup) return HDA_ERR_UNSUPPORTED;
+  if (p->n_q_heads / p->n_kv_heads > kMaxGroup) return HDA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return HDA_ERR_UNSUPPORTED;
   if (p->page_size < 16 || p->page_size > 1024 || (p->page_size & (p->page_size - 1)))
     return HDA_ERR_UNSUPPORTED;
@@ -657,18 +892,12 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
     if (!p->q_norm_w || !p->k_norm_w || !p->k_new || !p->v_new) return HDA_ERR_INVALID_ARG;
     if (!(p->rms_eps >= 0.f) || !(p->rope_theta > 0.f)) return HDA_ERR_INVALID_ARG;
   }
-  if (plan_len < HDA_PLAN_HEADER_INTS || plan_host[0] != HDA_PLAN_VERSION) return HDA_ERR_BAD_PLAN;
-  if (plan_host[1] != p->batch) return HDA_ERR_PLAN_MISMATCH;
-  const int64_t W = plan_host[3], N = plan_host[5], P = plan_host[6];
-  if (W < 1 || N < 1 || P < 0 || plan_len != HDA_PLAN_HEADER_INTS + (W + 1) + 4 * N + p->batch + 1)
-    return HDA_ERR_BAD_PLAN;
-  const int64_t grid = W * p->n_kv_heads;
-  if (grid > 0x7fffffffLL) return HDA_ERR_UNSUPPORTED;
-  const int64_t ws_need = hda_workspace_bytes(plan_host, plan_len, p->n_q_heads, p->n_kv_heads,
-                                              p->head_dim);
-  if (ws_need < 0) return HDA_ERR_BAD_PLAN;
-  if (P > 0 && (!p->workspace || p->workspace_bytes < ws_need)) return HDA_ERR_WORKSPACE;
+  return HDA_OK;
+}
 
+Args make_args(const hda_params* p, const void* q, void* k_pages, void* v_pages,
+               const int32_t* block_table, const int32_t* seq_lens, float* out, int64_t W,
+               int64_t P) {
   const int D = p->head_dim;
   const int elem = p->kv_dtype == HDA_KV_FP8_E4M3 ? 1 : 2;
   Args a{};
@@ -677,7 +906,6 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
   a.v_pages = static_cast<uint8_t*>(v_pages);
   a.block_table = block_table;
   a.seq_lens = seq_lens;
-  a.plan = plan_dev;
   a.out = out;
   uint8_t* ws = static_cast<uint8_t*>(p->workspace);
   const int64_t o_bytes = (P * p->n_q_heads * D * 4 + 255) / 256 * 256;
@@ -693,22 +921,96 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
   a.batch = p->batch;
   a.n_q_heads = p->n_q_heads;
   a.n_kv_heads = p->n_kv_heads;
-  a.group = g;
+  a.group = p->n_q_heads / p->n_kv_heads;
   a.page_size = p->page_size;
   a.log2_ps = __builtin_ctz((unsigned)p->page_size);
   a.max_pages = p->max_pages_per_req;
   a.n_wg = (int32_t)W;
-  a.n_items = (int32_t)N;
   a.n_parts = (int32_t)P;
   a.qk_scale_log2 = (float)((double)p->sm_scale * (double)p->k_scale * 1.4426950408889634);
   a.v_scale = p->v_scale;
   a.k_scale = p->k_scale;
   a.rms_eps = p->rms_eps;
   a.rope_theta = p->rope_theta;
+  return a;
+}
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, void* v_pages,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          const int32_t* plan_host, const int32_t* plan_dev, int64_t plan_len,
+                          float* out, void* stream) {
+  int st = check_params(p, q, k_pages, v_pages, block_table, seq_lens, out);
+  if (st != HDA_OK) return st;
+  if (!plan_host || !plan_dev) return HDA_ERR_INVALID_ARG;
+  if (plan_len < HDA_PLAN_HEADER_INTS || plan_host[0] != HDA_PLAN_VERSION) return HDA_ERR_BAD_PLAN;
+  if (plan_host[1] != p->batch) return HDA_ERR_PLAN_MISMATCH;
+  const int64_t W = plan_host[3], N = plan_host[5], P = plan_host[6];
+  if (W < 1 || N < 1 || P < 0 || plan_len != HDA_PLAN_HEADER_INTS + (W + 1) + 4 * N + p->batch + 1)
+    return HDA_ERR_BAD_PLAN;
+  const int64_t grid = W * p->n_kv_heads;
+  if (grid > 0x7fffffffLL) return HDA_ERR_UNSUPPORTED;
+  const int64_t ws_need = hda_workspace_bytes(plan_host, plan_len, p->n_q_heads, p->n_kv_heads,
+                                              p->head_dim);
+  if (ws_need < 0) return HDA_ERR_BAD_PLAN;
+  if (P > 0 && (!p->workspace || p->workspace_bytes < ws_need)) return HDA_ERR_WORKSPACE;
+
+  Args a = make_args(p, q, k_pages, v_pages, block_table, seq_lens, out, W, P);
+  a.plan = plan_dev;
+  a.n_items = (int32_t)N;
+  a.tile_len = plan_host[2];
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
-  hipError_t e = D == 64 ? launch_d<64>(a, fp8, p->prologue != 0, (int)grid, st, p->split_event)
-                         : launch_d<128>(a, fp8, p->prologue != 0, (int)grid, st, p->split_event);
+  const bool pro = p->prologue != 0;
+  hipError_t e = p->head_dim == 64 ? launch_d<64, false>(a, fp8, pro, (int)grid, hs, p->split_event)
+                                   : launch_d<128, false>(a, fp8, pro, (int)grid, hs, p->split_event);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
+}
+
+extern "C" int64_t hda_workspace_bytes_bound(int32_t batch, int32_t n_workgroups,
+                                             int32_t n_q_heads, int32_t head_dim) {
+  if (batch < 1 || n_workgroups < 1 || n_q_heads < 1 || head_dim < 1) return -1;
+  const int64_t P = (int64_t)n_workgroups + batch - 1;   // partial slots <= items <= W + B - 1
+  const int64_t n = round256(P * n_q_heads * head_dim * 4) + round256(P * n_q_heads * 4);
+  return n > 256 ? n : 256;
+}
+
+extern "C" int hda_decode_auto(const hda_params* p, const void* q, void* k_pages, void* v_pages,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               int32_t tile_len, int32_t n_workgroups, float* out, void* stream) {
+  int st = check_params(p, q, k_pages, v_pages, block_table, seq_lens, out);
+  if (st != HDA_OK) return st;
+  if (tile_len < 1 || n_workgroups < 1) return HDA_ERR_INVALID_ARG;
+  if ((int64_t)n_workgroups + p->batch > 0x7fffffffLL) return HDA_ERR_INVALID_ARG;
+  const int64_t grid = (int64_t)n_workgroups * p->n_kv_heads;
+  if (grid > 0x7fffffffLL) return HDA_ERR_UNSUPPORTED;
+  const int64_t ws_need = hda_workspace_bytes_bound(p->batch, n_workgroups, p->n_q_heads,
+                                                    p->head_dim);
+  if (!p->workspace || p->workspace_bytes < ws_need) return HDA_ERR_WORKSPACE;
+  const int64_t P = (int64_t)n_workgroups + p->batch - 1;
+  Args a = make_args(p, q, k_pages, v_pages, block_table, seq_lens, out, n_workgroups, P);
+  a.plan = nullptr;
+  a.n_items = 0;
+  a.tile_len = tile_len;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
+  const bool pro = p->prologue != 0;
+  hipError_t e = p->head_dim == 64 ? launch_d<64, true>(a, fp8, pro, (int)grid, hs, p->split_event)
+                                   : launch_d<128, true>(a, fp8, pro, (int)grid, hs, p->split_event);
+  return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
+}
+
+extern "C" int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
+                               int32_t n_workgroups, int32_t* plan, int64_t capacity,
+                               void* stream) {
+  if (!seq_lens || !plan || batch < 1 || tile_len < 1 || n_workgroups < 1)
+    return HDA_ERR_INVALID_ARG;
+  if ((int64_t)n_workgroups + batch > 0x7fffffffLL) return HDA_ERR_INVALID_ARG;
+  if (capacity < hda_plan_capacity(batch, n_workgroups)) return HDA_ERR_CAPACITY;
+  hipLaunchKernelGGL(hda_plan_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     seq_lens, batch, tile_len, n_workgroups, plan);
+  return hipGetLastError() == hipSuccess ? HDA_OK : HDA_ERR_HIP;
 }

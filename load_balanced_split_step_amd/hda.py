@@ -32,8 +32,8 @@ PLAN_HEADER_INTS = 8
 
 # every symbol include/hda.h declares
 EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_plan_static", "hda_plan_validate",
-           "hda_workspace_bytes", "hda_decode", "hda_status_string", "hda_version",
-           "hda_params_bytes")
+           "hda_workspace_bytes", "hda_decode", "hda_decode_auto", "hda_workspace_bytes_bound",
+           "hda_plan_device", "hda_status_string", "hda_version", "hda_params_bytes")
 
 
 class HdaError(RuntimeError):
@@ -91,6 +91,10 @@ def load_library(path: Optional[str] = None):
         "hda_workspace_bytes": (i64, [pi32, i64, i32, i32, i32]),
         "hda_decode": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp, pi32, vp,
                                       i64, vp, vp]),
+        "hda_decode_auto": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp, i32, i32,
+                                           vp, vp]),
+        "hda_workspace_bytes_bound": (i64, [i32, i32, i32, i32]),
+        "hda_plan_device": (ctypes.c_int, [vp, i32, i32, i32, vp, i64, vp]),
         "hda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "hda_version": (ctypes.c_int, []),
         "hda_params_bytes": (i64, []),
@@ -190,16 +194,46 @@ def hda_decode(params: hda_params, q, k_pages, v_pages, block_table, seq_lens, p
     hipStream_t (int) or a torch stream, default the current torch stream."""
     lib = load_library()
     plan_host = np.ascontiguousarray(plan_host, dtype=np.int32)
+    st = lib.hda_decode(ctypes.byref(params), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                        _ptr(block_table), _ptr(seq_lens), _i32p(plan_host), _ptr(plan_dev),
+                        plan_host.size, _ptr(out), _stream(stream))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_decode")
+
+
+def hda_workspace_bytes_bound(batch: int, n_workgroups: int, n_q_heads: int, head_dim: int) -> int:
+    return load_library().hda_workspace_bytes_bound(int(batch), int(n_workgroups), int(n_q_heads),
+                                                    int(head_dim))
+
+
+def _stream(stream):
     if stream is None:
         import torch
         stream = torch.cuda.current_stream()
     if hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    st = lib.hda_decode(ctypes.byref(params), _ptr(q), _ptr(k_pages), _ptr(v_pages),
-                        _ptr(block_table), _ptr(seq_lens), _i32p(plan_host), _ptr(plan_dev),
-                        plan_host.size, _ptr(out), ctypes.c_void_p(int(stream) if stream else 0))
+    return ctypes.c_void_p(int(stream) if stream else 0)
+
+
+def hda_decode_auto(params: hda_params, q, k_pages, v_pages, block_table, seq_lens,
+                    tile_len: int, n_workgroups: int, out, stream=None) -> None:
+    """Enqueue one decode step planned on the device from the device lengths."""
+    lib = load_library()
+    st = lib.hda_decode_auto(ctypes.byref(params), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                             _ptr(block_table), _ptr(seq_lens), int(tile_len), int(n_workgroups),
+                             _ptr(out), _stream(stream))
     if st != HDA_OK:
-        raise HdaError(st, "hda_decode")
+        raise HdaError(st, "hda_decode_auto")
+
+
+def hda_plan_device(seq_lens, batch: int, tile_len: int, n_workgroups: int, plan, capacity: int,
+                    stream=None) -> None:
+    """Enqueue the device-side planner writing the hda_plan format into `plan`."""
+    lib = load_library()
+    st = lib.hda_plan_device(_ptr(seq_lens), int(batch), int(tile_len), int(n_workgroups),
+                             _ptr(plan), int(capacity), _stream(stream))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_plan_device")
 
 
 def _ptr(x):
@@ -250,7 +284,7 @@ class DeviceBatch:
             self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
         return self._ws
 
-    def params(self, plan, workspace=None):
+    def params(self, plan, workspace=None, need=None):
         p = hda_params(**self.kw)
         t = self.t
         if self.kw.get("prologue"):
@@ -258,12 +292,31 @@ class DeviceBatch:
             p.k_norm_w = t["k_norm_w"].data_ptr()
             p.k_new = t["k_new"].data_ptr()
             p.v_new = t["v_new"].data_ptr()
-        need = hda_workspace_bytes(plan, self.kw["n_q_heads"], self.kw["n_kv_heads"],
-                                   self.kw["head_dim"])
+        if need is None:
+            need = hda_workspace_bytes(plan, self.kw["n_q_heads"], self.kw["n_kv_heads"],
+                                       self.kw["head_dim"])
         ws = workspace if workspace is not None else self.workspace(need)
         p.workspace = ws.data_ptr()
         p.workspace_bytes = ws.numel() * ws.element_size()
         return p
+
+    def params_auto(self, tile_len, n_workgroups, workspace=None):
+        p = self.params(None, workspace=workspace, need=hda_workspace_bytes_bound(
+            self.kw["batch"], n_workgroups, self.kw["n_q_heads"], self.kw["head_dim"]))
+        return p
+
+    def decode_auto(self, tile_len, n_workgroups, out=None, stream=None, k_pages=None,
+                    v_pages=None):
+        import torch
+        t = self.t
+        if out is None:
+            out = torch.empty((self.kw["batch"], self.kw["n_q_heads"], self.kw["head_dim"]),
+                              dtype=torch.float32, device=self.device)
+        p = self.params_auto(tile_len, n_workgroups)
+        hda_decode_auto(p, t["q"], t["k_pages"] if k_pages is None else k_pages,
+                        t["v_pages"] if v_pages is None else v_pages, t["block_table"],
+                        t["seq_lens"], tile_len, n_workgroups, out, stream)
+        return out
 
     def decode(self, plan, out=None, plan_dev=None, stream=None, k_pages=None, v_pages=None,
                block_table=None):

@@ -204,3 +204,41 @@ def test_decode_argument_errors(lib):
     assert _decode_status(lib, _params(workspace_bytes=100), plan) == E.HDA_ERR_WORKSPACE
     for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.hda_status_string(s)
+
+
+def test_workspace_bound(lib):
+    up = lambda x: (x + 255) // 256 * 256
+    assert hda.hda_workspace_bytes_bound(4, 8, 8, 64) == up(11 * 8 * 64 * 4) + up(11 * 8 * 4)
+    assert hda.hda_workspace_bytes_bound(0, 8, 8, 64) == -1
+    # the bound covers every plan over the same batch and workgroup count
+    rng = np.random.default_rng(9)
+    for _ in range(200):
+        B, W = int(rng.integers(1, 40)), int(rng.integers(1, 200))
+        lens = rng.integers(1, 3000, size=B).astype(np.int32)
+        plan = hda.hda_plan(lens, int(rng.integers(1, 300)), W)
+        assert hda.hda_workspace_bytes(plan, 8, 2, 128) <= hda.hda_workspace_bytes_bound(B, W, 8, 128)
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers are only used without a GPU")
+def test_decode_auto_and_plan_device_argument_errors(lib):
+    import ctypes
+    E = hda
+    vp = ctypes.c_void_p
+
+    def auto(p, tl=64, W=4, **ptrs):
+        a = dict(q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, bt=FAKE + 0x3000, sl=FAKE + 0x4000,
+                 out=FAKE + 0x6000)
+        a.update(ptrs)
+        f = lambda x: vp(x) if x is not None else None
+        return lib.hda_decode_auto(ctypes.byref(p), f(a["q"]), f(a["k"]), f(a["v"]), f(a["bt"]),
+                                   f(a["sl"]), tl, W, f(a["out"]), None)
+
+    assert auto(_params(), sl=None) == E.HDA_ERR_INVALID_ARG
+    assert auto(_params(), tl=0) == E.HDA_ERR_INVALID_ARG
+    assert auto(_params(), W=0) == E.HDA_ERR_INVALID_ARG
+    assert auto(_params(head_dim=80)) == E.HDA_ERR_UNSUPPORTED
+    assert auto(_params(workspace=None)) == E.HDA_ERR_WORKSPACE
+    assert auto(_params(workspace_bytes=1000), W=64) == E.HDA_ERR_WORKSPACE
+    assert lib.hda_plan_device(None, 4, 64, 4, vp(FAKE), 1000, None) == E.HDA_ERR_INVALID_ARG
+    assert lib.hda_plan_device(vp(FAKE), 4, 0, 4, vp(FAKE), 1000, None) == E.HDA_ERR_INVALID_ARG
+    assert lib.hda_plan_device(vp(FAKE), 4, 64, 4, vp(FAKE), 10, None) == E.HDA_ERR_CAPACITY

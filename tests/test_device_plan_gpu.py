@@ -1,0 +1,104 @@
+"""Device-side planning on the GPU: hda_plan_device writes exactly the plan
+hda_plan builds on the host, and hda_decode_auto (items derived inside the
+tile kernel) gives outputs bitwise identical to hda_decode with the host
+plan, also across decode steps with growing lengths."""
+
+import numpy as np
+import pytest
+import torch
+
+import load_balanced_split_step_amd.hda as hda
+from load_balanced_split_step_amd.workloads import CONFIGS, Workload, draw_lengths, make_inputs
+from tests.gpu_util import TOL, need_gpu, oracle_out, max_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def device_plan(lens, tile_len, W):
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    cap = hda.hda_plan_capacity(len(lens), W)
+    d_lens = torch.from_numpy(lens).cuda()
+    d_plan = torch.full((cap,), -7, dtype=torch.int32, device="cuda:0")
+    hda.hda_plan_device(d_lens, len(lens), tile_len, W, d_plan, cap)
+    torch.cuda.synchronize()
+    return d_plan.cpu().numpy()
+
+
+def test_device_plan_matches_host_plan():
+    cases = []
+    for name, w in CONFIGS.items():
+        lens = draw_lengths(w, w.seed)
+        for tl in (16, 128, 512):
+            for W in (1, 7, 64, 1024):
+                cases.append((lens, tl, W))
+    rng = np.random.default_rng(3)
+    for _ in range(150):
+        B = int(rng.integers(1, 300))
+        lens = rng.integers(1, int(rng.choice([5, 200, 20000])) + 1, size=B)
+        cases.append((lens, int(rng.integers(1, 400)), int(rng.integers(1, 700))))
+    for lens, tl, W in cases:
+        want = hda.hda_plan(lens, tl, W)
+        got = device_plan(lens, tl, W)
+        assert np.array_equal(got[:want.size], want), (len(lens), tl, W)
+    print(f"{len(cases)} plans bit-exact", flush=True)
+
+
+AUTO = [
+    ("tiny", CONFIGS["tiny"], None, [(64, 8), (16, 1), (1, 97)]),
+    ("extreme_s", CONFIGS["extreme"].with_(name="extreme_s", batch=8), [16384] + [1000] * 7,
+     [(128, 64), (64, 7), (100, 300)]),
+    ("many", Workload("many", 150, 16, 2, 128, 16, seed=61), None, [(32, 64), (16, 500), (256, 3)]),
+    ("fp8_s", CONFIGS["fp8"].with_(name="fp8_s", batch=70, len_range=(20, 2000)), None,
+     [(128, 64), (64, 13)]),
+]
+
+
+@pytest.mark.parametrize("name,w,lens,plans", AUTO, ids=[a[0] for a in AUTO])
+def test_decode_auto_bitwise_equals_host_plan(name, w, lens, plans):
+    if lens is None and w.lengths is None and w.len_range is None:
+        lens = list(np.random.default_rng(w.seed).integers(1, 900, size=w.batch))
+    inp = make_inputs(w, lengths=lens)
+    L = inp["seq_lens"]
+    ref = oracle_out(inp)
+    dev = hda.DeviceBatch.from_inputs(inp)
+    for tl, W in plans:
+        a = dev.decode(hda.hda_plan(L, tl, W))
+        b = dev.decode_auto(tl, W)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (name, tl, W)
+        err = max_err(b, ref)
+        print(f"{name} auto tl={tl} W={W}: bitwise equal to host plan, max err {err:.3e}", flush=True)
+        assert err <= TOL[w.kv_dtype]
+
+
+def test_decode_auto_growth_steps():
+    """Lengths change in device memory between steps; no host planning."""
+    import oracle
+    from oracle.prologue import prologue_step, write_new_token
+    steps = 3
+    w = CONFIGS["fp8"].with_(name="grow_auto", batch=5, len_range=(30, 400))
+    L0 = make_inputs(w)["seq_lens"].copy()
+    inp = make_inputs(w, lengths=L0 + steps)
+    dev = hda.DeviceBatch.from_inputs(inp)
+    kp_ref, vp_ref = inp["k_pages"].copy(), inp["v_pages"].copy()
+    for s in range(steps + 1):
+        lens = (L0 + s).astype(np.int32)
+        dev.t["seq_lens"].copy_(torch.from_numpy(lens))
+        out = dev.decode_auto(64, 11)
+        q_p, _, _, kc, vc = prologue_step(inp["q"], inp["k_new"], inp["v_new"], inp["q_norm_w"],
+                                          inp["k_norm_w"], lens, float(inp["rms_eps"]),
+                                          float(inp["rope_theta"]), "fp8", float(inp["k_scale"]),
+                                          float(inp["v_scale"]))
+        kp_ref, vp_ref = write_new_token(kp_ref, vp_ref, inp["block_table"], lens, kc, vc)
+        ref = oracle.attention_reference(q_p, kp_ref, vp_ref, inp["block_table"], lens, "fp8",
+                                         float(inp["sm_scale"]), float(inp["k_scale"]),
+                                         float(inp["v_scale"]))
+        torch.cuda.synchronize()
+        err = max_err(out, ref)
+        print(f"auto growth step {s}: max err {err:.3e}", flush=True)
+        assert err <= TOL["fp8"]
