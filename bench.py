@@ -224,6 +224,48 @@ def main():
         f"(p10 {pct(dec_ms, 0.1) * 1e3:.1f}, p50 {pct(dec_ms, 0.5) * 1e3:.1f}, "
         f"p90 {pct(dec_ms, 0.9) * 1e3:.1f}), tile kernel {kmean * 1e3:.1f} us")
 
+    # NEXT: device-planned step (no host plan, no upload), eager and as a
+    # replayed HIP graph (its arguments are fixed; lengths live on the device)
+    pa = dev.params_auto(tl, W)
+
+    def step_auto(s):
+        kp, vp = copies[s % len(copies)]
+        # the current stream: the launch stream, or the capture stream inside torch.cuda.graph
+        hda.hda_decode_auto(pa, dev.t["q"], kp, vp, dev.t["block_table"], dev.t["seq_lens"],
+                            tl, W, out, torch.cuda.current_stream())
+
+    for s in range(args.warmup):
+        step_auto(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step_auto(s)
+    torch.cuda.synchronize()
+    auto_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    graphs = []
+    for c in range(len(copies)):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step_auto(c)
+        graphs.append(gr)
+    graphs[0].replay()                 # the replayed step reproduces the eager output
+    torch.cuda.synchronize()
+    o_graph = out.clone()
+    step_auto(0)
+    torch.cuda.synchronize()
+    if not torch.equal(o_graph, out):
+        raise RuntimeError("graph replay differs from the eager device-planned step")
+    for s in range(args.warmup):
+        graphs[s % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        graphs[s % len(graphs)].replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"device-planned step {auto_ms * 1e3:.1f} us wall, as HIP graph {graph_ms * 1e3:.1f} us")
+    del graphs
+
     # parity spot check on the timed output (sampled rows, fp64 oracle)
     import oracle
     Hq = w.n_q_heads
@@ -275,6 +317,9 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": algo,
                      "kernel": "hda_decode_kernel (tile kernel; HIP events on its stream)"},
         "parity_max_err_sampled": max_err,
+        "device_planned_step": {"wall_us": round(auto_ms * 1e3, 2),
+                                "graph_replay_wall_us": round(graph_ms * 1e3, 2),
+                                "kv_gbs_graph": round(kv / (graph_ms * 1e-3) / 1e9, 2)},
     }
 
     if args.copy_probe:

@@ -102,3 +102,33 @@ def test_decode_auto_growth_steps():
         err = max_err(out, ref)
         print(f"auto growth step {s}: max err {err:.3e}", flush=True)
         assert err <= TOL["fp8"]
+
+
+def test_graph_replay_of_device_planned_step():
+    """One device-planned step captured in a HIP graph; each replay, with
+    eager work and synchronisation between replays, equals the eager step,
+    also after the lengths change in device memory (re-planned on replay)."""
+    w = CONFIGS["extreme"].with_(name="graph_s", batch=8)
+    lens0 = np.array([9000] + [700] * 7, dtype=np.int32)
+    inp = make_inputs(w, lengths=lens0 + 40)            # room to grow
+    dev = hda.DeviceBatch.from_inputs(inp)
+    tl, W = 128, 24
+    out_g = torch.empty((8, 64, 128), dtype=torch.float32, device="cuda:0")
+    dev.t["seq_lens"].copy_(torch.from_numpy(lens0))
+    p = dev.params_auto(tl, W)
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        hda.hda_decode_auto(p, dev.t["q"], dev.t["k_pages"], dev.t["v_pages"], dev.t["block_table"],
+                            dev.t["seq_lens"], tl, W, out_g)
+    torch.cuda.synchronize()
+    for step, grow in enumerate([0, 0, 5, 17, 40, 3]):
+        lens = lens0 + grow
+        dev.t["seq_lens"].copy_(torch.from_numpy(lens))
+        g.replay()
+        torch.cuda.synchronize()
+        eager = dev.decode(hda.hda_plan(lens, tl, W))       # eager work between replays
+        _ = (eager * 2).sum().item()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, eager), step
+        print(f"graph replay {step} (lengths +{grow}): equal to eager", flush=True)
