@@ -121,10 +121,11 @@ int hda_plan_validate(const int32_t* plan, int64_t plan_len,
 
 /*
  * Bytes of workspace hda_decode needs for this plan: partial outputs
- * float32 [P][Hq][D] followed by partial log-sum-exp float32 [P][Hq], each
- * region aligned to 256 bytes (at least 256 bytes in all).  Its contents
- * need no initialisation.  Returns -1 for a malformed plan header or
- * non-positive sizes.
+ * float32 [P][Hq][D], partial log-sum-exp float32 [P][Hq], then the
+ * prologue's normalised, rotated q as bf16 [B][Hq][D] (used only when the
+ * prologue is on), each region aligned to 256 bytes.  Its contents need no
+ * initialisation.  Returns -1 for a malformed plan header or non-positive
+ * sizes.
  */
 int64_t hda_workspace_bytes(const int32_t* plan, int64_t plan_len,
                             int32_t n_q_heads, int32_t n_kv_heads,
@@ -163,10 +164,11 @@ typedef struct hda_params {
 } hda_params;
 
 /*
- * One decode step: (optional prologue) + tile attention, then the
- * log-sum-exp merge of split requests, enqueued as two kernel launches on
- * `stream` (the merge only when the plan has partial slots).  Asynchronous;
- * no host synchronisation, no allocation.
+ * One decode step enqueued on `stream`: the optional new-token prologue
+ * kernel (RMSNorm + RoPE of q and k, k/v stored to slot len-1, all fused in
+ * one kernel), the tile attention kernel, then the log-sum-exp merge of
+ * split requests (only when the plan has partial slots).  Asynchronous; no
+ * host synchronisation, no allocation.
  *
  *   q            [device] bf16 [B][Hq][D] (pre-norm when the prologue is on)
  *   k_pages,
@@ -215,8 +217,8 @@ int hda_decode_auto(const hda_params* p, const void* q, void* k_pages, void* v_p
 
 /*
  * Workspace bytes that suffice for any plan over `batch` requests and
- * `n_workgroups` workgroups (partial slots <= W + B - 1).  -1 for
- * non-positive arguments.
+ * `n_workgroups` workgroups (partial slots <= W + B - 1), in the layout of
+ * hda_workspace_bytes.  -1 for non-positive arguments.
  */
 int64_t hda_workspace_bytes_bound(int32_t batch, int32_t n_workgroups,
                                   int32_t n_q_heads, int32_t head_dim);

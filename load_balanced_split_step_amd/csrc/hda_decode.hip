@@ -58,6 +58,7 @@ struct Args {
   float* out;
   float* part_o;
   float* part_lse;
+  uint16_t* q_prime;     // workspace copy of the prologue's q' (bf16 [B][Hq][D])
   const uint16_t* q_norm_w;
   const uint16_t* k_norm_w;
   const uint16_t* k_new;
@@ -82,6 +83,9 @@ struct Geo {
   static constexpr int VW = D * ELEM / 64;   // dwords of V per token per lane
   static constexpr int DPL = D / 16;         // output d values per lane (PV N blocks)
   static constexpr int STEPS = D / 32;       // QK k-steps of 32
+  // register sets in the per-wave chunk ring (a third set for fp8 pushed the
+  // kernel past 256 VGPRs into spills and measured slower)
+  static constexpr int NBUF = 2;
 };
 
 // Registers of one in-flight chunk.
@@ -338,51 +342,78 @@ struct TileSmem {
   __attribute__((aligned(16))) uint16_t q[kMaxGroup][D];
 };
 
-// Prologue store for the new token of request b (length L) and kv head h:
-// k' = RoPE(RMSNorm(k_new)) and v_new, divided by their scales, written to
-// row L-1 of the cache.  Executed by one wave.
+// New-token prologue, one workgroup (one wave) per (request b, kv head h):
+// q' = RoPE(RMSNorm(q)) for the group's q heads into the workspace (bf16,
+// the precision the QK product takes), k' = RoPE(RMSNorm(k_new)) and v_new,
+// divided by their scales, stored into cache row len-1.  RMSNorm per head
+// over D, then rotate-half RoPE at pos = len-1.  All loads are issued before
+// any arithmetic.  Runs before the tile kernel, whose launch then sees the
+// written rows.
 template <int D, bool FP8>
-__device__ inline void store_new_token(const Args& a, const int32_t* __restrict__ block_table,
-                                       int b, int L, int h, int lane, double inv_freq) {
+__global__ __launch_bounds__(64) void hda_prologue_kernel(Args a,
+                                                          const int32_t* __restrict__ block_table,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          uint16_t* __restrict__ q_out) {
   using G = Geo<D, FP8>;
-  const int pos = L - 1, pidx = pos >> a.log2_ps;
-  if (L < 1 || pidx >= a.max_pages) return;
-  const int page = block_table[(int64_t)b * a.max_pages + pidx];
-  if (page < 0 || page >= a.num_pages) return;
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / a.n_kv_heads, h = blockIdx.x % a.n_kv_heads;
+  const int g = a.group;
+  const int L = seq_lens[b];
+  if (L < 1) return;
   const bool act = lane < D / 2;
-  float c = 1.f, s = 0.f;
-  if (act) rope_cos_sin(pos, inv_freq, c, s);
+  const int64_t q0 = ((int64_t)b * a.n_q_heads + (int64_t)h * g) * D;
   const int64_t src = ((int64_t)b * a.n_kv_heads + h) * D;
+  float qx[kMaxGroup][2];
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) {
+    qx[hh][0] = act && hh < g ? bf16_bits_to_float(a.q[q0 + (int64_t)hh * D + lane]) : 0.f;
+    qx[hh][1] = act && hh < g ? bf16_bits_to_float(a.q[q0 + (int64_t)hh * D + lane + D / 2]) : 0.f;
+  }
   float k0v = act ? bf16_bits_to_float(a.k_new[src + lane]) : 0.f;
   float k1v = act ? bf16_bits_to_float(a.k_new[src + lane + D / 2]) : 0.f;
-  norm_rope(k0v, k1v, act, a.k_norm_w, lane, D, a.rms_eps, c, s);
-  if (act) {
-    const float v0 = bf16_bits_to_float(a.v_new[src + lane]);
-    const float v1 = bf16_bits_to_float(a.v_new[src + lane + D / 2]);
-    const int64_t row = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
-                        (int64_t)(pos & (a.page_size - 1)) * G::RB;
-    if constexpr (FP8) {
-      a.k_pages[row + lane] = (uint8_t)fp8_encode(k0v / a.k_scale);
-      a.k_pages[row + lane + D / 2] = (uint8_t)fp8_encode(k1v / a.k_scale);
-      a.v_pages[row + lane] = (uint8_t)fp8_encode(v0 / a.v_scale);
-      a.v_pages[row + lane + D / 2] = (uint8_t)fp8_encode(v1 / a.v_scale);
-    } else {
-      uint16_t* kp = reinterpret_cast<uint16_t*>(a.k_pages + row);
-      uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pages + row);
-      kp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(k0v / a.k_scale));
-      kp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(k1v / a.k_scale));
-      vp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(v0 / a.v_scale));
-      vp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(v1 / a.v_scale));
+  const float v0 = act ? bf16_bits_to_float(a.v_new[src + lane]) : 0.f;
+  const float v1 = act ? bf16_bits_to_float(a.v_new[src + lane + D / 2]) : 0.f;
+  const int pos = L - 1;
+  float c = 1.f, s = 0.f;
+  if (act) rope_cos_sin(pos, rope_inv_freq(lane, D, a.rope_theta), c, s);
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) {
+    if (hh < g) {
+      norm_rope(qx[hh][0], qx[hh][1], act, a.q_norm_w, lane, D, a.rms_eps, c, s);
+      if (act) {
+        q_out[q0 + (int64_t)hh * D + lane] = __builtin_bit_cast(uint16_t, (__bf16)qx[hh][0]);
+        q_out[q0 + (int64_t)hh * D + lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)qx[hh][1]);
+      }
     }
+  }
+  norm_rope(k0v, k1v, act, a.k_norm_w, lane, D, a.rms_eps, c, s);
+  const int pidx = pos >> a.log2_ps;
+  if (pidx >= a.max_pages) return;
+  const int page = block_table[(int64_t)b * a.max_pages + pidx];
+  if (page < 0 || page >= a.num_pages || !act) return;
+  const int64_t row = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
+                      (int64_t)(pos & (a.page_size - 1)) * G::RB;
+  if constexpr (FP8) {
+    a.k_pages[row + lane] = (uint8_t)fp8_encode(k0v / a.k_scale);
+    a.k_pages[row + lane + D / 2] = (uint8_t)fp8_encode(k1v / a.k_scale);
+    a.v_pages[row + lane] = (uint8_t)fp8_encode(v0 / a.v_scale);
+    a.v_pages[row + lane + D / 2] = (uint8_t)fp8_encode(v1 / a.v_scale);
+  } else {
+    uint16_t* kp = reinterpret_cast<uint16_t*>(a.k_pages + row);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pages + row);
+    kp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(k0v / a.k_scale));
+    kp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(k1v / a.k_scale));
+    vp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(v0 / a.v_scale));
+    vp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(v1 / a.v_scale));
   }
 }
 
 // One plan item (b, [k0, k1), slot) for kv head h: the waves stream the
 // item's chunks, combine in LDS, and write the output (slot -1) or a partial.
-template <int D, bool FP8, bool PRO>
+template <int D, bool FP8>
 __device__ inline void process_item(const Args& a, const int32_t* __restrict__ block_table,
                                     TileSmem<D>& sm, int b, int k0, int k1, int slot, int L,
-                                    int h, int wave, int lane, int tid, double inv_freq) {
+                                    int h, int wave, int lane, int tid) {
   using G = Geo<D, FP8>;
   const int i = lane & 15, kg = lane >> 4;
   const int g = a.group;
@@ -392,38 +423,16 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
     const int c_last = (k1 - 1) / kChunk;
     int c = k0 / kChunk + wave;
     const bool has_chunks = c <= c_last;   // uniform per wave
-    Chunk<D, FP8> A, B;
+    Chunk<D, FP8> ring[G::NBUF];
     __amdgpu_buffer_rsrc_t kr[2], vr[2];
 
     // q operand (MFMA B): lane (i, kg) holds q head i, dims qk_dim(s, kg) + 0..7.
     bf16x8 qop[G::STEPS];
-    if constexpr (PRO) {
-      const bool act = lane < D / 2;
-      float cs = 1.f, sn = 0.f;
-      if (act) rope_cos_sin(L - 1, inv_freq, cs, sn);
-      for (int hh = wave; hh < g; hh += kWaves) {
-        float x0 = act ? bf16_bits_to_float(a.q[qrow0 + (int64_t)hh * D + lane]) : 0.f;
-        float x1 = act ? bf16_bits_to_float(a.q[qrow0 + (int64_t)hh * D + lane + D / 2]) : 0.f;
-        norm_rope(x0, x1, act, a.q_norm_w, lane, D, a.rms_eps, cs, sn);
-        if (act) {
-          sm.q[hh][lane] = __builtin_bit_cast(uint16_t, (__bf16)x0);
-          sm.q[hh][lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)x1);
-        }
-      }
-      __syncthreads();
 #pragma unroll
-      for (int s2 = 0; s2 < G::STEPS; ++s2) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (i < g) v = *reinterpret_cast<const u32x4*>(&sm.q[i][qk_dim<FP8>(s2, kg)]);
-        qop[s2] = __builtin_bit_cast(bf16x8, v);
-      }
-    } else {
-#pragma unroll
-      for (int s2 = 0; s2 < G::STEPS; ++s2) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (i < g) v = *reinterpret_cast<const u32x4*>(a.q + qrow0 + (int64_t)i * D + qk_dim<FP8>(s2, kg));
-        qop[s2] = __builtin_bit_cast(bf16x8, v);
-      }
+    for (int s2 = 0; s2 < G::STEPS; ++s2) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (i < g) v = *reinterpret_cast<const u32x4*>(a.q + qrow0 + (int64_t)i * D + qk_dim<FP8>(s2, kg));
+      qop[s2] = __builtin_bit_cast(bf16x8, v);
     }
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -432,27 +441,33 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
     for (int nb = 0; nb < G::DPL; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (has_chunks) {
-      chunk_rsrc<D, FP8>(a, block_table, b, L, h, c, true, kr, vr);
-      issue_chunk<D, FP8>(A, kr, vr, i, kg);
-      // The next chunk's loads are issued before this chunk's math; the
-      // scheduling barrier keeps the compiler from sinking them below it.
-      while (true) {
-        int cn = c + kWaves;
-        chunk_rsrc<D, FP8>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr);
-        issue_chunk<D, FP8>(B, kr, vr, i, kg);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_chunk<D, FP8>(A, qop, c, k0, k1, a.qk_scale_log2, kg, m_run, l_run, acc);
-        c = cn;
-        if (c > c_last) break;
-        cn = c + kWaves;
-        chunk_rsrc<D, FP8>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr);
-        issue_chunk<D, FP8>(A, kr, vr, i, kg);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_chunk<D, FP8>(B, qop, c, k0, k1, a.qk_scale_log2, kg, m_run, l_run, acc);
-        c = cn;
-        if (c > c_last) break;
+      // A ring of G::NBUF register sets: the loads of the chunk NBUF-1 steps
+      // ahead are issued before this chunk's math (the scheduling barrier
+      // keeps the compiler from sinking them below it).
+#pragma unroll
+      for (int k = 0; k < G::NBUF - 1; ++k) {
+        const int ck = c + k * kWaves;
+        chunk_rsrc<D, FP8>(a, block_table, b, L, h, ck, ck <= c_last, kr, vr);
+        issue_chunk<D, FP8>(ring[k], kr, vr, i, kg);
+      }
+      bool done = false;
+      while (!done) {
+#pragma unroll
+        for (int k = 0; k < G::NBUF; ++k) {
+          const int cn = c + (G::NBUF - 1) * kWaves;
+          chunk_rsrc<D, FP8>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr);
+          issue_chunk<D, FP8>(ring[(k + G::NBUF - 1) % G::NBUF], kr, vr, i, kg);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_chunk<D, FP8>(ring[k], qop, c, k0, k1, a.qk_scale_log2, kg, m_run, l_run, acc);
+          c += kWaves;
+          if (c > c_last) {
+            done = true;
+            break;
+          }
+        }
       }
     }
+
 
     // Combine the waves of this workgroup.
     float l_tot = l_run;
@@ -569,7 +584,7 @@ __device__ inline uint32_t total_tiles(const int32_t* __restrict__ seq_lens, int
 // Workgroup (w, h): W * Hkv workgroups, kv head fastest.  Items come from the
 // host plan (DEVPLAN false) or are derived here from the device lengths with
 // the same rule (DEVPLAN true), in the same order.
-template <int D, bool FP8, bool PRO, bool DEVPLAN>
+template <int D, bool FP8, bool DEVPLAN>
 __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
     Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ plan) {
@@ -582,37 +597,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x % a.n_kv_heads;
   const int w = blockIdx.x / a.n_kv_heads;
-  // rotary inverse frequency of this lane (prologue only)
-  const double inv_freq = PRO && lane < D / 2 ? rope_inv_freq(lane, D, a.rope_theta) : 0.0;
 
   if constexpr (!DEVPLAN) {
     const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
     const int32_t* items = wg_ptr + a.n_wg + 1;
     const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
-    if (it_begin >= it_end) return;
-    if constexpr (PRO) {
-      // New token of each request whose last item is ours.  Only this
-      // workgroup reads that row (it lies inside its item).
-      if (wave == 0) {
-        for (int it = it_begin; it < it_end; ++it) {
-          const int b = items[4 * it], k1 = items[4 * it + 2];
-          if ((unsigned)b >= (unsigned)a.batch) continue;
-          const int L = seq_lens[b];
-          if (k1 == L) store_new_token<D, FP8>(a, block_table, b, L, h, lane, inv_freq);
-        }
-      }
-      // This workgroup's stores are complete before the barrier; the acquire
-      // drops any cached copy of the written rows before the chunk loads.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
     for (int it = it_begin; it < it_end; ++it) {
       const int b = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
                 slot = items[4 * it + 3];
       if ((unsigned)b >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
-      process_item<D, FP8, PRO>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], h, wave, lane,
-                                tid, inv_freq);
+      process_item<D, FP8>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], h, wave, lane, tid);
     }
   } else {
     // Every wave derives the same plan facts; they stay wave-uniform.
@@ -620,43 +614,29 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
     const SplitDev sp{T / (uint32_t)a.n_wg, T % (uint32_t)a.n_wg};
     const uint32_t t0 = sp.first_tile(w), t1 = sp.first_tile(w + 1);
     if (t0 >= t1) return;
-    for (int pass = PRO ? 0 : 1; pass < 2; ++pass) {
-      // pass 0 (prologue only): store the new tokens this workgroup owns;
-      // pass 1: the attention items.
-      uint32_t first_carry = 0, slot_carry = 0;
-      for (int cb = 0; cb < a.batch && first_carry < t1; cb += 64) {
-        uint32_t ft, st;
-        const ReqScan r = scan_requests(seq_lens, a.batch, a.tile_len, sp, cb, lane, first_carry,
-                                        slot_carry, ft, st);
-        uint64_t mask = __ballot(r.n > 0 && r.first < t1 && r.first + r.n > t0);
-        while (mask) {
-          const int j = __builtin_ctzll(mask);
-          mask &= mask - 1;
-          const int b = __builtin_amdgcn_readlane(r.b, j);
-          const int L = __builtin_amdgcn_readlane(r.len, j);
-          const uint32_t first = __builtin_amdgcn_readlane(r.first, j);
-          const uint32_t n = __builtin_amdgcn_readlane(r.n, j);
-          const uint32_t k = __builtin_amdgcn_readlane(r.k, j);
-          const uint32_t sb = __builtin_amdgcn_readlane(r.slot_base, j);
-          const uint32_t lo = max(t0, first), hi = min(t1, first + n);
-          const int k0 = (int)((int64_t)(lo - first) * a.tile_len);
-          const int k1 = (int)min((int64_t)(hi - first) * a.tile_len, (int64_t)L);
-          if (pass == 0) {
-            if (wave == 0 && k1 == L) store_new_token<D, FP8>(a, block_table, b, L, h, lane, inv_freq);
-          } else {
-            const int slot = k > 1 ? (int)(sb + (uint32_t)w - sp.owner(first)) : -1;
-            process_item<D, FP8, PRO>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane,
-                                      tid, inv_freq);
-          }
-        }
-        first_carry += ft;
-        slot_carry += st;
+    uint32_t first_carry = 0, slot_carry = 0;
+    for (int cb = 0; cb < a.batch && first_carry < t1; cb += 64) {
+      uint32_t ft, st;
+      const ReqScan r = scan_requests(seq_lens, a.batch, a.tile_len, sp, cb, lane, first_carry,
+                                      slot_carry, ft, st);
+      uint64_t mask = __ballot(r.n > 0 && r.first < t1 && r.first + r.n > t0);
+      while (mask) {
+        const int j = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const int b = __builtin_amdgcn_readlane(r.b, j);
+        const int L = __builtin_amdgcn_readlane(r.len, j);
+        const uint32_t first = __builtin_amdgcn_readlane(r.first, j);
+        const uint32_t n = __builtin_amdgcn_readlane(r.n, j);
+        const uint32_t k = __builtin_amdgcn_readlane(r.k, j);
+        const uint32_t sb = __builtin_amdgcn_readlane(r.slot_base, j);
+        const uint32_t lo = max(t0, first), hi = min(t1, first + n);
+        const int k0 = (int)((int64_t)(lo - first) * a.tile_len);
+        const int k1 = (int)min((int64_t)(hi - first) * a.tile_len, (int64_t)L);
+        const int slot = k > 1 ? (int)(sb + (uint32_t)w - sp.owner(first)) : -1;
+        process_item<D, FP8>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
       }
-      if (pass == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      }
+      first_carry += ft;
+      slot_carry += st;
     }
   }
 }
@@ -841,11 +821,20 @@ __global__ __launch_bounds__(64) void hda_plan_kernel(const int32_t* __restrict_
   }
 }
 
-template <int D, bool FP8, bool PRO, bool DEVPLAN>
-hipError_t launch(const Args& a, int grid, hipStream_t stream, void* split_event) {
-  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, PRO, DEVPLAN>), dim3(grid), dim3(64 * kWaves), 0,
+template <int D, bool FP8, bool DEVPLAN>
+hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_t stream,
+                  void* split_event) {
+  hipError_t e;
+  if (prologue) {
+    hipLaunchKernelGGL((hda_prologue_kernel<D, FP8>), dim3(a.batch * a.n_kv_heads), dim3(64), 0,
+                       stream, a, a.block_table, a.seq_lens, q_prime);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.q = q_prime;   // attention reads the normalised, rotated q
+  }
+  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, DEVPLAN>), dim3(grid), dim3(64 * kWaves), 0,
                      stream, a, a.block_table, a.seq_lens, a.plan);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (split_event) {
     e = hipEventRecord(static_cast<hipEvent_t>(split_event), stream);
@@ -860,12 +849,10 @@ hipError_t launch(const Args& a, int grid, hipStream_t stream, void* split_event
 }
 
 template <int D, bool DEVPLAN>
-hipError_t launch_d(const Args& a, bool fp8, bool pro, int grid, hipStream_t st, void* ev) {
-  if (fp8)
-    return pro ? launch<D, true, true, DEVPLAN>(a, grid, st, ev)
-               : launch<D, true, false, DEVPLAN>(a, grid, st, ev);
-  return pro ? launch<D, false, true, DEVPLAN>(a, grid, st, ev)
-             : launch<D, false, false, DEVPLAN>(a, grid, st, ev);
+hipError_t launch_d(const Args& a, bool fp8, int grid, bool pro, uint16_t* qp, hipStream_t st,
+                    void* ev) {
+  return fp8 ? launch<D, true, DEVPLAN>(a, grid, pro, qp, st, ev)
+             : launch<D, false, DEVPLAN>(a, grid, pro, qp, st, ev);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -909,8 +896,11 @@ Args make_args(const hda_params* p, const void* q, void* k_pages, void* v_pages,
   a.out = out;
   uint8_t* ws = static_cast<uint8_t*>(p->workspace);
   const int64_t o_bytes = (P * p->n_q_heads * D * 4 + 255) / 256 * 256;
+  const int64_t l_bytes = (P * p->n_q_heads * 4 + 255) / 256 * 256;
   a.part_o = ws ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_lse = ws ? reinterpret_cast<float*>(ws + o_bytes) : nullptr;
+  // q' of the prologue follows the partials
+  a.q_prime = ws ? reinterpret_cast<uint16_t*>(ws + o_bytes + l_bytes) : nullptr;
   a.q_norm_w = static_cast<const uint16_t*>(p->q_norm_w);
   a.k_norm_w = static_cast<const uint16_t*>(p->k_norm_w);
   a.k_new = static_cast<const uint16_t*>(p->k_new);
@@ -956,7 +946,8 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
   const int64_t ws_need = hda_workspace_bytes(plan_host, plan_len, p->n_q_heads, p->n_kv_heads,
                                               p->head_dim);
   if (ws_need < 0) return HDA_ERR_BAD_PLAN;
-  if (P > 0 && (!p->workspace || p->workspace_bytes < ws_need)) return HDA_ERR_WORKSPACE;
+  if ((P > 0 || p->prologue) && (!p->workspace || p->workspace_bytes < ws_need))
+    return HDA_ERR_WORKSPACE;
 
   Args a = make_args(p, q, k_pages, v_pages, block_table, seq_lens, out, W, P);
   a.plan = plan_dev;
@@ -965,8 +956,9 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
   const bool pro = p->prologue != 0;
-  hipError_t e = p->head_dim == 64 ? launch_d<64, false>(a, fp8, pro, (int)grid, hs, p->split_event)
-                                   : launch_d<128, false>(a, fp8, pro, (int)grid, hs, p->split_event);
+  hipError_t e = p->head_dim == 64
+                     ? launch_d<64, false>(a, fp8, (int)grid, pro, a.q_prime, hs, p->split_event)
+                     : launch_d<128, false>(a, fp8, (int)grid, pro, a.q_prime, hs, p->split_event);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
 }
 
@@ -974,8 +966,8 @@ extern "C" int64_t hda_workspace_bytes_bound(int32_t batch, int32_t n_workgroups
                                              int32_t n_q_heads, int32_t head_dim) {
   if (batch < 1 || n_workgroups < 1 || n_q_heads < 1 || head_dim < 1) return -1;
   const int64_t P = (int64_t)n_workgroups + batch - 1;   // partial slots <= items <= W + B - 1
-  const int64_t n = round256(P * n_q_heads * head_dim * 4) + round256(P * n_q_heads * 4);
-  return n > 256 ? n : 256;
+  return round256(P * n_q_heads * head_dim * 4) + round256(P * n_q_heads * 4) +
+         round256((int64_t)batch * n_q_heads * head_dim * 2);
 }
 
 extern "C" int hda_decode_auto(const hda_params* p, const void* q, void* k_pages, void* v_pages,
@@ -998,8 +990,9 @@ extern "C" int hda_decode_auto(const hda_params* p, const void* q, void* k_pages
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
   const bool pro = p->prologue != 0;
-  hipError_t e = p->head_dim == 64 ? launch_d<64, true>(a, fp8, pro, (int)grid, hs, p->split_event)
-                                   : launch_d<128, true>(a, fp8, pro, (int)grid, hs, p->split_event);
+  hipError_t e = p->head_dim == 64
+                     ? launch_d<64, true>(a, fp8, (int)grid, pro, a.q_prime, hs, p->split_event)
+                     : launch_d<128, true>(a, fp8, (int)grid, pro, a.q_prime, hs, p->split_event);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
 }
 

@@ -277,9 +277,9 @@ int64_t hda_workspace_bytes(const int32_t* plan, int64_t plan_len,
       n_kv_heads < 1 || head_dim < 1)
     return -1;
   if (plan[0] != HDA_PLAN_VERSION || plan[1] < 1 || plan[6] < 0) return -1;
-  const int64_t P = plan[6];
-  return std::max<int64_t>(256, round_up(P * n_q_heads * head_dim * 4, 256) +
-                                    round_up(P * n_q_heads * 4, 256));
+  const int64_t B = plan[1], P = plan[6];
+  return round_up(P * n_q_heads * head_dim * 4, 256) + round_up(P * n_q_heads * 4, 256) +
+         round_up(B * n_q_heads * head_dim * 2, 256);
 }
 
 const char* hda_status_string(int status) {
