@@ -104,17 +104,14 @@ __device__ inline float bf16_bits_to_float(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }
 
-// Two fp32 values that are exact in bf16 -> one dword of two bf16 (lo first).
-__device__ inline uint32_t pack_bf16_exact(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-}
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 // Four OCP E4M3FN codes -> four bf16 (exact: every code is a bf16 value).
+// gfx950's scaled pair conversion with scale 1.0 writes two bf16 per
+// instruction; it agrees with the exact decode on all 256 codes.
 __device__ inline void fp8x4_to_bf16x4(uint32_t c, uint32_t& lo, uint32_t& hi) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
-  lo = pack_bf16_exact(a.x, a.y);
-  hi = pack_bf16_exact(b.x, b.y);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true));
 }
 
 // fp32 -> OCP E4M3FN code: round to nearest, ties to even, saturating at
