@@ -121,9 +121,10 @@ int hda_plan_validate(const int32_t* plan, int64_t plan_len,
 
 /*
  * Bytes of workspace hda_decode needs for this plan: partial outputs
- * float32 [P][Hq][D], partial log-sum-exp float32 [P][Hq], then the
- * prologue's normalised, rotated q as bf16 [B][Hq][D] (used only when the
- * prologue is on), each region aligned to 256 bytes.  Its contents need no
+ * float32 [P][Hq][D], partial log-sum-exp float32 [P][Hq], the prologue's
+ * normalised, rotated q as bf16 [B][Hq][D] (used only when the prologue is
+ * on), and per-request slot ranges int32 [B][2] (used only by
+ * hda_decode_auto), each region aligned to 256 bytes.  Its contents need no
  * initialisation.  Returns -1 for a malformed plan header or non-positive
  * sizes.
  */

@@ -59,6 +59,7 @@ struct Args {
   float* part_o;
   float* part_lse;
   uint16_t* q_prime;     // workspace copy of the prologue's q' (bf16 [B][Hq][D])
+  int32_t* req_slots;    // device-planned launches: per request (first slot, slot count)
   const uint16_t* q_norm_w;
   const uint16_t* k_norm_w;
   const uint16_t* k_new;
@@ -147,8 +148,9 @@ __device__ inline double rope_inv_freq(int lane, int D, float theta) {
 
 __device__ inline void rope_cos_sin(int pos, double inv_freq, float& c, float& s) {
   const double two_pi = 6.283185307179586476925286766559;
+  const double inv_two_pi = 0.15915494309189533576888376337251;
   const double phi = (double)pos * inv_freq;
-  const double r = phi - rint(phi / two_pi) * two_pi;
+  const double r = phi - rint(phi * inv_two_pi) * two_pi;
   sincosf((float)r, &s, &c);
 }
 
@@ -339,7 +341,7 @@ struct TileSmem {
   __attribute__((aligned(16))) uint16_t q[kMaxGroup][D];
 };
 
-// New-token prologue, one workgroup (one wave) per (request b, kv head h):
+// New-token prologue, one workgroup (4 waves) per (request b, kv head h):
 // q' = RoPE(RMSNorm(q)) for the group's q heads into the workspace (bf16,
 // the precision the QK product takes), k' = RoPE(RMSNorm(k_new)) and v_new,
 // divided by their scales, stored into cache row len-1.  RMSNorm per head
@@ -347,12 +349,14 @@ struct TileSmem {
 // any arithmetic.  Runs before the tile kernel, whose launch then sees the
 // written rows.
 template <int D, bool FP8>
-__global__ __launch_bounds__(64) void hda_prologue_kernel(Args a,
-                                                          const int32_t* __restrict__ block_table,
-                                                          const int32_t* __restrict__ seq_lens,
-                                                          uint16_t* __restrict__ q_out) {
+__global__ __launch_bounds__(256) void hda_prologue_kernel(Args a,
+                                                           const int32_t* __restrict__ block_table,
+                                                           const int32_t* __restrict__ seq_lens,
+                                                           uint16_t* __restrict__ q_out) {
   using G = Geo<D, FP8>;
-  const int lane = threadIdx.x;
+  constexpr int kHeadsPerWave = kMaxGroup / 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.x / a.n_kv_heads, h = blockIdx.x % a.n_kv_heads;
   const int g = a.group;
   const int L = seq_lens[b];
@@ -360,29 +364,34 @@ __global__ __launch_bounds__(64) void hda_prologue_kernel(Args a,
   const bool act = lane < D / 2;
   const int64_t q0 = ((int64_t)b * a.n_q_heads + (int64_t)h * g) * D;
   const int64_t src = ((int64_t)b * a.n_kv_heads + h) * D;
-  float qx[kMaxGroup][2];
+  // wave w normalises and rotates q heads w, w+4, ...; wave 0 also k and v
+  float qx[kHeadsPerWave][2];
 #pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) {
-    qx[hh][0] = act && hh < g ? bf16_bits_to_float(a.q[q0 + (int64_t)hh * D + lane]) : 0.f;
-    qx[hh][1] = act && hh < g ? bf16_bits_to_float(a.q[q0 + (int64_t)hh * D + lane + D / 2]) : 0.f;
+  for (int j = 0; j < kHeadsPerWave; ++j) {
+    const int hh = wave + 4 * j;
+    qx[j][0] = act && hh < g ? bf16_bits_to_float(a.q[q0 + (int64_t)hh * D + lane]) : 0.f;
+    qx[j][1] = act && hh < g ? bf16_bits_to_float(a.q[q0 + (int64_t)hh * D + lane + D / 2]) : 0.f;
   }
-  float k0v = act ? bf16_bits_to_float(a.k_new[src + lane]) : 0.f;
-  float k1v = act ? bf16_bits_to_float(a.k_new[src + lane + D / 2]) : 0.f;
-  const float v0 = act ? bf16_bits_to_float(a.v_new[src + lane]) : 0.f;
-  const float v1 = act ? bf16_bits_to_float(a.v_new[src + lane + D / 2]) : 0.f;
+  const bool kv_wave = wave == 0;
+  float k0v = act && kv_wave ? bf16_bits_to_float(a.k_new[src + lane]) : 0.f;
+  float k1v = act && kv_wave ? bf16_bits_to_float(a.k_new[src + lane + D / 2]) : 0.f;
+  const float v0 = act && kv_wave ? bf16_bits_to_float(a.v_new[src + lane]) : 0.f;
+  const float v1 = act && kv_wave ? bf16_bits_to_float(a.v_new[src + lane + D / 2]) : 0.f;
   const int pos = L - 1;
   float c = 1.f, s = 0.f;
   if (act) rope_cos_sin(pos, rope_inv_freq(lane, D, a.rope_theta), c, s);
 #pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) {
+  for (int j = 0; j < kHeadsPerWave; ++j) {
+    const int hh = wave + 4 * j;
     if (hh < g) {
-      norm_rope(qx[hh][0], qx[hh][1], act, a.q_norm_w, lane, D, a.rms_eps, c, s);
+      norm_rope(qx[j][0], qx[j][1], act, a.q_norm_w, lane, D, a.rms_eps, c, s);
       if (act) {
-        q_out[q0 + (int64_t)hh * D + lane] = __builtin_bit_cast(uint16_t, (__bf16)qx[hh][0]);
-        q_out[q0 + (int64_t)hh * D + lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)qx[hh][1]);
+        q_out[q0 + (int64_t)hh * D + lane] = __builtin_bit_cast(uint16_t, (__bf16)qx[j][0]);
+        q_out[q0 + (int64_t)hh * D + lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)qx[j][1]);
       }
     }
   }
+  if (!kv_wave) return;
   norm_rope(k0v, k1v, act, a.k_norm_w, lane, D, a.rms_eps, c, s);
   const int pidx = pos >> a.log2_ps;
   if (pidx >= a.max_pages) return;
@@ -616,6 +625,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
       uint32_t ft, st;
       const ReqScan r = scan_requests(seq_lens, a.batch, a.tile_len, sp, cb, lane, first_carry,
                                       slot_carry, ft, st);
+      // the workgroup holding a request's first tile records its slot range
+      // for the merge launch (kv head 0 only; every head would write the same)
+      if (h == 0 && r.n > 0 && r.first >= t0 && r.first < t1) {
+        a.req_slots[2 * r.b] = (int32_t)r.slot_base;
+        a.req_slots[2 * r.b + 1] = r.k > 1 ? (int32_t)r.k : 0;
+      }
       uint64_t mask = __ballot(r.n > 0 && r.first < t1 && r.first + r.n > t0);
       while (mask) {
         const int j = __builtin_ctzll(mask);
@@ -645,7 +660,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
 // tile kernel (on any XCD) visible here without cross-XCD fences.  Thread d
 // owns output dim d.  The first kMergeEarly partial rows are loaded up front,
 // before the weights are known, so that the whole merge costs about one
-// memory round trip for typical slot counts.
+// memory round trip for typical slot counts.  (One workgroup per kv head
+// instead was measured 3x slower on a request split 32 ways.)
 constexpr int kMergeEarly = 32;    // partial rows loaded before the weights
 constexpr int kMergeStage = 512;   // slot weights staged in LDS per pass
 
@@ -662,23 +678,9 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
     s0 = max(0, rpp[b]);
     s1 = min(a.n_parts, rpp[b + 1]);
   } else {
-    // slot range of request b under the device plan: scan up to b's chunk
-    const uint32_t T = total_tiles(seq_lens, a.batch, a.tile_len, lane);
-    const SplitDev sp{T / (uint32_t)a.n_wg, T % (uint32_t)a.n_wg};
-    uint32_t first_carry = 0, slot_carry = 0, k = 0, sb = 0;
-    for (int cb = 0; cb <= b; cb += 64) {
-      uint32_t ft, st;
-      const ReqScan r = scan_requests(seq_lens, a.batch, a.tile_len, sp, cb, lane, first_carry,
-                                      slot_carry, ft, st);
-      if (b < cb + 64) {
-        k = __builtin_amdgcn_readlane(r.k, b - cb);
-        sb = __builtin_amdgcn_readlane(r.slot_base, b - cb);
-      }
-      first_carry += ft;
-      slot_carry += st;
-    }
-    s0 = (int)sb;
-    s1 = k > 1 ? min(a.n_parts, (int)(sb + k)) : s0;
+    if (seq_lens[b] < 1) return;                    // no item, nothing recorded
+    s0 = max(0, a.req_slots[2 * b]);
+    s1 = min(a.n_parts, s0 + a.req_slots[2 * b + 1]);
   }
   if (s1 <= s0) return;
   const int n = s1 - s0;
@@ -823,7 +825,7 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
                   void* split_event) {
   hipError_t e;
   if (prologue) {
-    hipLaunchKernelGGL((hda_prologue_kernel<D, FP8>), dim3(a.batch * a.n_kv_heads), dim3(64), 0,
+    hipLaunchKernelGGL((hda_prologue_kernel<D, FP8>), dim3(a.batch * a.n_kv_heads), dim3(256), 0,
                        stream, a, a.block_table, a.seq_lens, q_prime);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -896,8 +898,10 @@ Args make_args(const hda_params* p, const void* q, void* k_pages, void* v_pages,
   const int64_t l_bytes = (P * p->n_q_heads * 4 + 255) / 256 * 256;
   a.part_o = ws ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_lse = ws ? reinterpret_cast<float*>(ws + o_bytes) : nullptr;
-  // q' of the prologue follows the partials
+  // q' of the prologue follows the partials, then the per-request slot ranges
   a.q_prime = ws ? reinterpret_cast<uint16_t*>(ws + o_bytes + l_bytes) : nullptr;
+  const int64_t qp_bytes = ((int64_t)p->batch * p->n_q_heads * D * 2 + 255) / 256 * 256;
+  a.req_slots = ws ? reinterpret_cast<int32_t*>(ws + o_bytes + l_bytes + qp_bytes) : nullptr;
   a.q_norm_w = static_cast<const uint16_t*>(p->q_norm_w);
   a.k_norm_w = static_cast<const uint16_t*>(p->k_norm_w);
   a.k_new = static_cast<const uint16_t*>(p->k_new);
@@ -964,7 +968,7 @@ extern "C" int64_t hda_workspace_bytes_bound(int32_t batch, int32_t n_workgroups
   if (batch < 1 || n_workgroups < 1 || n_q_heads < 1 || head_dim < 1) return -1;
   const int64_t P = (int64_t)n_workgroups + batch - 1;   // partial slots <= items <= W + B - 1
   return round256(P * n_q_heads * head_dim * 4) + round256(P * n_q_heads * 4) +
-         round256((int64_t)batch * n_q_heads * head_dim * 2);
+         round256((int64_t)batch * n_q_heads * head_dim * 2) + round256((int64_t)batch * 8);
 }
 
 extern "C" int hda_decode_auto(const hda_params* p, const void* q, void* k_pages, void* v_pages,

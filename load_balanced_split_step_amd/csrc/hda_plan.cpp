@@ -279,7 +279,7 @@ int64_t hda_workspace_bytes(const int32_t* plan, int64_t plan_len,
   if (plan[0] != HDA_PLAN_VERSION || plan[1] < 1 || plan[6] < 0) return -1;
   const int64_t B = plan[1], P = plan[6];
   return round_up(P * n_q_heads * head_dim * 4, 256) + round_up(P * n_q_heads * 4, 256) +
-         round_up(B * n_q_heads * head_dim * 2, 256);
+         round_up(B * n_q_heads * head_dim * 2, 256) + round_up(B * 8, 256);
 }
 
 const char* hda_status_string(int status) {

@@ -138,7 +138,7 @@ def test_workspace_bytes(lib):
     lens = np.array([17, 64, 200, 513], dtype=np.int32)
     plan = hda.hda_plan(lens, 64, 4)          # P = 5
     up = lambda x: (x + 255) // 256 * 256
-    q_prime = up(4 * 8 * 64 * 2)              # prologue's q' region, B x Hq x D bf16
+    q_prime = up(4 * 8 * 64 * 2) + up(4 * 8)  # prologue's q' (B x Hq x D bf16) + slot ranges
     assert hda.hda_workspace_bytes(plan, 8, 2, 64) == up(5 * 8 * 64 * 4) + up(5 * 8 * 4) + q_prime
     assert hda.hda_workspace_bytes(hda.hda_plan(lens, 64, 1), 8, 2, 64) == q_prime   # P = 0
     assert hda.hda_workspace_bytes(plan, 0, 2, 64) == -1
@@ -210,7 +210,7 @@ def test_decode_argument_errors(lib):
 def test_workspace_bound(lib):
     up = lambda x: (x + 255) // 256 * 256
     assert hda.hda_workspace_bytes_bound(4, 8, 8, 64) == (up(11 * 8 * 64 * 4) + up(11 * 8 * 4)
-                                                          + up(4 * 8 * 64 * 2))
+                                                          + up(4 * 8 * 64 * 2) + up(4 * 8))
     assert hda.hda_workspace_bytes_bound(0, 8, 8, 64) == -1
     # the bound covers every plan over the same batch and workgroup count
     rng = np.random.default_rng(9)
