@@ -19,6 +19,8 @@ Five workloads, all single-token grouped-query decode over a paged cache:
             cache with per-tensor fp32 scales, and a new token per request
             that the fused prologue (RMSNorm with weights ~ N(1, 0.1),
             RoPE with theta 1e6) must write before attention reads it
+  fp8_page  the long-tail lengths and per-head magnitudes, fp8 E4M3FN cache
+            with one fp32 scale per (page, kv head) slab, and the prologue
 
 Recipe (the pages use no dataset; these stand in for a serving batch):
   * numpy PCG64 streams spawned from SeedSequence(seed), one stream per
@@ -31,8 +33,9 @@ Recipe (the pages use no dataset; these stand in for a serving batch):
   * random placement: the pool holds exactly sum_b ceil(len_b / page) pages
     and logical page p of request b lives in physical page
     perm[sum_{b'<b} pages_b' + p]; unused block-table entries are -1;
-  * fp8: per-tensor scale = amax(drawn values) / 448 in float32, codes from
-    torch's float8_e4m3fn cast of clip(x / scale, +-448);
+  * fp8: scale = amax / 448 in float32 over the drawn values of the whole
+    pool ("tensor"), of one kv head ("head") or of one (page, kv head) slab
+    ("page"); codes from torch's float8_e4m3fn cast of clip(x / scale, +-448);
   * rows past len_b in a request's last page hold NaN (when poisoned), and
     for the prologue workload so does the new token's slot len_b - 1.
 """
@@ -68,6 +71,7 @@ class Workload:
     placement: str = "random"           # "random" or "contiguous"
     head_scale: bool = False            # per-kv-head U(0.5, 2) on K and V
     prologue: bool = False              # new token written by the prologue
+    kv_scale: str = "tensor"            # fp8 scale granularity: tensor, head, page
     seed: int = 0
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
@@ -90,6 +94,9 @@ CONFIGS = {
                          head_scale=True, seed=3),
     "fp8": Workload("fp8", 128, 64, 8, 128, 64, kv_dtype="fp8",
                     len_range=(1024, 32768), prologue=True, seed=4),
+    "fp8_page": Workload("fp8_page", 64, 64, 8, 128, 64, kv_dtype="fp8",
+                         len_range=(256, 65536), head_scale=True, prologue=True,
+                         kv_scale="page", seed=5),
 }
 
 _CHUNK_SLABS = 256
@@ -132,30 +139,48 @@ def draw_lengths(w: Workload, seed: int):
 
 def _draw_pool(ss, n_pages, w: Workload, head_scales, fp8_scale=None):
     """One page pool [n_pages, Hkv, ps, D], drawn in chunks of whole
-    (page, head) slabs.  Returns float32 amax when fp8_scale is None and the
-    cache is fp8 (first pass), else the stored bits."""
+    (page, head) slabs.
+
+    For an fp8 cache with "tensor" or "head" scales this runs twice: first
+    with fp8_scale None, returning the float32 amax per kv head [Hkv]; then
+    with the scale (a scalar, or [Hkv]), returning the stored bits.  With
+    "page" scales one pass returns (bits, scales [n_pages, Hkv]), each slab's
+    scale being its own amax / 448.  A bf16 cache returns the bits."""
     Hkv, ps, D = w.n_kv_heads, w.page_size, w.head_dim
     slab = ps * D
     n_slabs = n_pages * Hkv
     n_chunks = max(1, (n_slabs + _CHUNK_SLABS - 1) // _CHUNK_SLABS)
-    children = ss.spawn(n_chunks)
+    # child c of ss, built from its spawn key: the same streams on every pass
+    # (ss.spawn would hand out new children on a second call)
+    children = [np.random.SeedSequence(ss.entropy, spawn_key=ss.spawn_key + (c,))
+                for c in range(n_chunks)]
     fp8 = w.kv_dtype == "fp8"
-    amax_pass = fp8 and fp8_scale is None
+    page_mode = fp8 and w.kv_scale == "page"
+    amax_pass = fp8 and not page_mode and fp8_scale is None
     if not amax_pass:
         out = np.empty((n_slabs, slab), dtype=np.uint8 if fp8 else np.uint16)
+    slab_scale = np.empty(n_slabs, dtype=np.float32) if page_mode else None
+    if fp8 and not page_mode and not amax_pass:
+        fp8_scale = np.broadcast_to(np.asarray(fp8_scale, dtype=np.float32), (Hkv,))
 
     def work(c):
         s0 = c * _CHUNK_SLABS
         s1 = min(n_slabs, s0 + _CHUNK_SLABS)
         x = np.empty((s1 - s0, slab), dtype=np.float32)
         _rng(children[c]).standard_normal(out=x, dtype=np.float32)
+        heads = np.arange(s0, s1) % Hkv
         if head_scales is not None:
-            heads = np.arange(s0, s1) % Hkv
             x *= head_scales[heads][:, None]
         if amax_pass:
-            return float(np.abs(x).max())
-        if fp8:
-            out[s0:s1] = _fp8_bits(x / np.float32(fp8_scale))
+            am = np.abs(x).max(axis=1)
+            return np.array([am[heads == h].max(initial=0.0) for h in range(Hkv)],
+                            dtype=np.float32)
+        if page_mode:
+            sc = np.abs(x).max(axis=1) / np.float32(448.0)
+            slab_scale[s0:s1] = sc
+            out[s0:s1] = _fp8_bits(x / sc[:, None])
+        elif fp8:
+            out[s0:s1] = _fp8_bits(x / fp8_scale[heads][:, None])
         else:
             out[s0:s1] = _bf16_bits(x)
         return None
@@ -163,8 +188,11 @@ def _draw_pool(ss, n_pages, w: Workload, head_scales, fp8_scale=None):
     with ThreadPoolExecutor(_threads()) as ex:
         res = list(ex.map(work, range(n_chunks)))
     if amax_pass:
-        return np.float32(max(res))
-    return out.reshape(n_pages, Hkv, ps, D)
+        return np.max(np.stack(res), axis=0).astype(np.float32)
+    bits = out.reshape(n_pages, Hkv, ps, D)
+    if page_mode:
+        return bits, slab_scale.reshape(n_pages, Hkv)
+    return bits
 
 
 def make_inputs(w: Workload, seed: Optional[int] = None, poison: bool = True,
@@ -173,7 +201,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None, poison: bool = True,
 
     q [B, Hq, D] u16 (bf16), k_pages / v_pages [NP, Hkv, ps, D] (u16 bf16 or
     u8 fp8), block_table [B, max_pages] i32, seq_lens [B] i32, sm_scale,
-    k_scale, v_scale (float32), and for the prologue workload q_norm_w,
+    k_scale, v_scale (float32), scale_mode with k_scales / v_scales (None,
+    float32 [Hkv] or [NP, Hkv]), and for the prologue workload q_norm_w,
     k_norm_w [D] u16, k_new, v_new [B, Hkv, D] u16, rms_eps, rope_theta.
     """
     seed = w.seed if seed is None else seed
@@ -202,19 +231,33 @@ def make_inputs(w: Workload, seed: Optional[int] = None, poison: bool = True,
         head_k, head_v = hs[0], hs[1]
 
     k_scale = v_scale = np.float32(1.0)
+    k_scales = v_scales = None
+    scale_mode = w.kv_scale if w.kv_dtype == "fp8" else "tensor"
+    assert scale_mode in ("tensor", "head", "page")
     k_ss, v_ss = ss[_S_K], ss[_S_V]
-    if w.kv_dtype == "fp8":
-        k_scale = np.float32(_draw_pool(k_ss, n_pages, w, head_k) / np.float32(448.0))
-        v_scale = np.float32(_draw_pool(v_ss, n_pages, w, head_v) / np.float32(448.0))
-    k_pages = _draw_pool(k_ss, n_pages, w, head_k, fp8_scale=k_scale)
-    v_pages = _draw_pool(v_ss, n_pages, w, head_v, fp8_scale=v_scale)
+    if scale_mode == "page":
+        k_pages, k_scales = _draw_pool(k_ss, n_pages, w, head_k)
+        v_pages, v_scales = _draw_pool(v_ss, n_pages, w, head_v)
+    else:
+        if w.kv_dtype == "fp8":
+            ka = _draw_pool(k_ss, n_pages, w, head_k) / np.float32(448.0)
+            va = _draw_pool(v_ss, n_pages, w, head_v) / np.float32(448.0)
+            if scale_mode == "head":
+                k_scales, v_scales = ka.astype(np.float32), va.astype(np.float32)
+            else:
+                k_scale, v_scale = np.float32(ka.max()), np.float32(va.max())
+        k_pages = _draw_pool(k_ss, n_pages, w, head_k,
+                             fp8_scale=k_scales if scale_mode == "head" else k_scale)
+        v_pages = _draw_pool(v_ss, n_pages, w, head_v,
+                             fp8_scale=v_scales if scale_mode == "head" else v_scale)
 
     q = _bf16_bits(_rng(ss[_S_Q]).standard_normal((B, Hq, D), dtype=np.float32))
 
     inp = dict(workload=w, seed=seed, q=q, k_pages=k_pages, v_pages=v_pages,
                block_table=block_table, seq_lens=lens.astype(np.int32),
                sm_scale=np.float32(1.0 / math.sqrt(D)),
-               k_scale=k_scale, v_scale=v_scale, kv_dtype=w.kv_dtype)
+               k_scale=k_scale, v_scale=v_scale, kv_dtype=w.kv_dtype,
+               scale_mode=scale_mode, k_scales=k_scales, v_scales=v_scales)
 
     if w.prologue:
         r = _rng(ss[_S_NORMW])

@@ -40,13 +40,17 @@ from .attention import (
     attention_bruteforce,
     split_merge_reference,
     decode_kv,
+    row_scales,
+    SCALE_MODES,
 )
-from .prologue import rms_norm, rope, prologue_step, bf16_encode, write_new_token
+from .prologue import (rms_norm, rope, prologue_step, bf16_encode, write_new_token,
+                       slot_scales)
 
 __all__ = [
     "bf16_to_f64", "fp8_decode", "fp8_encode", "FP8_MAX",
     "plan_dynamic", "plan_static", "Plan",
     "gather_request", "attention_reference", "attention_selected",
-    "attention_bruteforce", "split_merge_reference", "decode_kv",
-    "rms_norm", "rope", "prologue_step", "bf16_encode", "write_new_token",
+    "attention_bruteforce", "split_merge_reference", "decode_kv", "row_scales",
+    "SCALE_MODES", "rms_norm", "rope", "prologue_step", "bf16_encode", "write_new_token",
+    "slot_scales",
 ]

@@ -17,8 +17,11 @@ Readings taken:
     two apart;
   * the new token sits at position pos = len_b - 1 (len_b counts it); its k
     (normalised and rotated) and v are stored into that cache slot, in the
-    cache format as x / scale (per-tensor scale, 1 for a plain bf16 cache):
-    fp8 codes, or bf16 rounded to nearest-even;
+    cache format as x / scale: fp8 codes, or bf16 rounded to nearest-even.
+    The scale is the one the attention reads that slot with: the per-tensor
+    scalar times, per the scale mode, the kv head's entry ("head") or the
+    (physical page of the slot, kv head) entry ("page") -- an existing
+    page's scale is not changed by the write;
   * attention then uses the normalised, rotated q.
 """
 
@@ -75,12 +78,33 @@ def bf16_encode(x):
     return (v.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def slot_scales(scale, scale_mode, scales, block_table, seq_lens, page_size, n_kv_heads):
+    """Scale of the new token's cache slot (row len_b - 1) per request and
+    kv head: float64 [B, Hkv]."""
+    B = len(seq_lens)
+    out = np.full((B, n_kv_heads), np.float64(scale))
+    if scale_mode == "tensor":
+        return out
+    arr = np.asarray(scales, dtype=np.float64)
+    if scale_mode == "head":
+        return out * arr[None, :]
+    if scale_mode == "page":
+        for b, L in enumerate(np.asarray(seq_lens).tolist()):
+            page = int(block_table[b][(L - 1) // page_size])
+            out[b] *= arr[page]
+        return out
+    raise ValueError(scale_mode)
+
+
 def prologue_step(q, k_new, v_new, q_norm_w, k_norm_w, seq_lens, rms_eps,
-                  rope_theta, kv_dtype, k_scale=1.0, v_scale=1.0):
+                  rope_theta, kv_dtype, k_scale=1.0, v_scale=1.0, scale_mode="tensor",
+                  k_scales=None, v_scales=None, block_table=None, page_size=None):
     """Returns (q', k', v, k_codes, v_codes) for the new token of each request.
 
     q: bf16 bits [B, Hq, D]; k_new, v_new: bf16 bits [B, Hkv, D];
-    q_norm_w, k_norm_w: bf16 bits [D].
+    q_norm_w, k_norm_w: bf16 bits [D].  With "head" or "page" scales,
+    k_scales / v_scales hold the per-head or per-(page, head) factors, and
+    the "page" mode also needs block_table and page_size to find the slot.
     """
     pos = np.asarray(seq_lens, dtype=np.int64) - 1
     qf = bf16_to_f64(q)
@@ -90,12 +114,15 @@ def prologue_step(q, k_new, v_new, q_norm_w, k_norm_w, seq_lens, rms_eps,
     wk = bf16_to_f64(k_norm_w)
     q_p = rope(rms_norm(qf, wq, rms_eps), pos[:, None], rope_theta)
     k_p = rope(rms_norm(kf, wk, rms_eps), pos[:, None], rope_theta)
+    Hkv = kf.shape[1]
+    ks = slot_scales(k_scale, scale_mode, k_scales, block_table, seq_lens, page_size, Hkv)
+    vs = slot_scales(v_scale, scale_mode, v_scales, block_table, seq_lens, page_size, Hkv)
     if kv_dtype == "fp8":
-        k_codes = fp8_encode(k_p / np.float64(k_scale))
-        v_codes = fp8_encode(vf / np.float64(v_scale))
+        k_codes = fp8_encode(k_p / ks[:, :, None])
+        v_codes = fp8_encode(vf / vs[:, :, None])
     elif kv_dtype == "bf16":
-        k_codes = bf16_encode(k_p / np.float64(k_scale))
-        v_codes = bf16_encode(vf / np.float64(v_scale))
+        k_codes = bf16_encode(k_p / ks[:, :, None])
+        v_codes = bf16_encode(vf / vs[:, :, None])
     else:
         raise ValueError(kv_dtype)
     return q_p, k_p, vf, k_codes, v_codes

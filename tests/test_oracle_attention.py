@@ -25,7 +25,8 @@ def run_ref(inp, q=None, fn=attention_reference, **kw):
     q64 = oa.bf16_to_f64(inp["q"]) if q is None else q
     return fn(q64, inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
               inp["kv_dtype"], float(inp["sm_scale"]), k_scale=float(inp["k_scale"]),
-              v_scale=float(inp["v_scale"]), **kw)
+              v_scale=float(inp["v_scale"]), scale_mode=inp["scale_mode"],
+              k_scales=inp["k_scales"], v_scales=inp["v_scales"], **kw)
 
 
 SMALL = [

@@ -49,3 +49,25 @@ def test_kv_bytes_extreme():
     w = CONFIGS["extreme"]
     inp = {"workload": w, "seq_lens": np.array(w.lengths)}
     assert kv_bytes(inp) == 258048 * 8 * 128 * 2 * 2
+
+
+@pytest.mark.parametrize("mode", ["tensor", "head", "page"])
+def test_fp8_scale_granularity(mode):
+    from oracle.codec import fp8_decode
+    w = CONFIGS["tiny"].with_(kv_dtype="fp8", kv_scale=mode, head_scale=True, placement="random")
+    a = make_inputs(w, poison=False)
+    assert a["scale_mode"] == mode
+    for pool, sc in ((a["k_pages"], a["k_scales"]), (a["v_pages"], a["v_scales"])):
+        mag = np.abs(fp8_decode(pool))                       # [NP, Hkv, ps, D]
+        if mode == "tensor":
+            assert sc is None and mag.max() == 448.0
+        elif mode == "head":
+            assert sc.shape == (w.n_kv_heads,) and sc.dtype == np.float32
+            assert np.all(mag.max(axis=(0, 2, 3)) == 448.0)
+        else:
+            assert sc.shape == (pool.shape[0], w.n_kv_heads) and sc.dtype == np.float32
+            assert np.all(mag.max(axis=(2, 3)) == 448.0)
+    if mode == "tensor":
+        assert a["k_scale"] != 1.0
+    else:
+        assert a["k_scale"] == 1.0 and a["v_scale"] == 1.0
