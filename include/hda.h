@@ -58,6 +58,20 @@ extern "C" {
 #define HDA_KV_BF16 0      /* bfloat16 */
 #define HDA_KV_FP8_E4M3 1  /* OCP FP8 E4M3FN code, value = decode(code) * scale */
 
+/* Scale granularity (hda_params.scale_mode).  The value of a stored K
+ * element is decode(element) * k_scale * f, where f is
+ *   HDA_SCALE_TENSOR  1
+ *   HDA_SCALE_HEAD    k_scales[h]                    (float [Hkv])
+ *   HDA_SCALE_PAGE    k_scales[page * Hkv + h]       (float [num_pages][Hkv]),
+ *                     page = the physical page holding the row
+ * for kv head h; V likewise with v_scale and v_scales.  The pages name
+ * quantisation scales as a per-model integration parameter without fixing a
+ * granularity (remio.ai page, section "Lo que la afirmación de un 48,8 % de
+ * TPOT no demuestra"); these three cover the usual cache quantisers. */
+#define HDA_SCALE_TENSOR 0
+#define HDA_SCALE_HEAD 1
+#define HDA_SCALE_PAGE 2   /* fp8 cache only */
+
 /*
  * Plan format (int32 array), produced by hda_plan / hda_plan_static:
  *   [0..7]   header: VERSION, B, tile_len (0 for a static plan), W, T, N, P, 0
@@ -162,6 +176,14 @@ typedef struct hda_params {
   /* optional profiling hook: a hipEvent_t recorded on the stream between the
    * tile kernel and the merge kernel; NULL for none */
   void* split_event;
+  /* scale granularity (HDA_SCALE_*) and, for HEAD and PAGE, the factor
+   * arrays: positive finite floats, read on the device, never written.  The
+   * prologue stores the new token with the scale of its slot (it never
+   * changes a scale: a caller that rescales a page does so itself). */
+  int32_t scale_mode;
+  int32_t reserved0;          /* must be 0 */
+  const float* k_scales;      /* [device] [Hkv] or [num_pages][Hkv]; NULL for TENSOR */
+  const float* v_scales;      /* [device] likewise */
 } hda_params;
 
 /*

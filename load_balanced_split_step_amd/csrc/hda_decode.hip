@@ -64,6 +64,8 @@ struct Args {
   const uint16_t* k_norm_w;
   const uint16_t* k_new;
   const uint16_t* v_new;
+  const float* k_scales;   // per-head [Hkv] or per-page [num_pages][Hkv] factors
+  const float* v_scales;
   int64_t page_stride;   // bytes per page (all kv heads)
   int32_t num_pages;     // page ids are int32; clamped on the host
   int32_t head_stride;   // bytes per (page, kv head) slab
@@ -71,6 +73,7 @@ struct Args {
   int32_t page_size, log2_ps, max_pages;
   int32_t n_wg, n_items, n_parts;
   int32_t tile_len;      // device-planned launches only
+  int32_t scale_mode;    // HDA_SCALE_*
   float qk_scale_log2;   // sm_scale * k_scale * log2(e)
   float v_scale;
   float k_scale, rms_eps, rope_theta;
@@ -89,11 +92,13 @@ struct Geo {
   static constexpr int NBUF = 2;
 };
 
-// Registers of one in-flight chunk.
+// Registers of one in-flight chunk (ks, vs: the K and V scale factors of the
+// page under each 16-token half; used with per-page scales only).
 template <int D, bool FP8>
 struct Chunk {
   u32x4 k[2][Geo<D, FP8>::KL];
   uint32_t v[8][Geo<D, FP8>::VW];
+  float ks[2], vs[2];
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int32_t bytes) {
@@ -194,11 +199,16 @@ __device__ inline bf16x8 k_operand(const Chunk<D, FP8>& ch, int hf, int s) {
 // Buffer resources for the two 16-token halves of chunk c of (request b,
 // kv head h).  A half with no valid rows (past len, outside the block table
 // or an out-of-range page id) gets an empty resource and reads zeros.
-template <int D, bool FP8>
+// With PAGE, also the page's K and V scale factors of each half (1 for a
+// half without rows, whose tokens are masked).  They are vector loads that
+// nothing reads until the chunk is computed, so their wait is the one the
+// chunk's own K/V loads need anyway (consuming them here would stall on
+// every load in flight).
+template <int D, bool FP8, bool PAGE>
 __device__ inline void chunk_rsrc(const Args& a, const int32_t* __restrict__ block_table, int b,
                                   int L, int h, int c, bool live,
                                   __amdgpu_buffer_rsrc_t (&kr)[2],
-                                  __amdgpu_buffer_rsrc_t (&vr)[2]) {
+                                  __amdgpu_buffer_rsrc_t (&vr)[2], Chunk<D, FP8>& ch) {
   using G = Geo<D, FP8>;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -207,6 +217,7 @@ __device__ inline void chunk_rsrc(const Args& a, const int32_t* __restrict__ blo
     rows = rows > 16 ? 16 : rows;
     int64_t off = 0;
     int bytes = 0;
+    float ks = 1.f, vs = 1.f;
     if (live && rows > 0) {
       const int pidx = t >> a.log2_ps;
       if (pidx < a.max_pages) {
@@ -215,11 +226,20 @@ __device__ inline void chunk_rsrc(const Args& a, const int32_t* __restrict__ blo
           off = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
                 (int64_t)(t & (a.page_size - 1)) * G::RB;
           bytes = rows * G::RB;
+          if constexpr (PAGE) {
+            const int64_t si = (int64_t)page * a.n_kv_heads + h;
+            ks = a.k_scales[si];
+            vs = a.v_scales[si];
+          }
         }
       }
     }
     kr[hf] = make_rsrc(a.k_pages + off, bytes);
     vr[hf] = make_rsrc(a.v_pages + off, bytes);
+    if constexpr (PAGE) {
+      ch.ks[hf] = ks;
+      ch.vs[hf] = vs;
+    }
   }
 }
 
@@ -256,7 +276,12 @@ __device__ inline void issue_chunk(Chunk<D, FP8>& ch, const __amdgpu_buffer_rsrc
 // One chunk: S^T = K Q^T on MFMA, online-softmax update, acc += P V on MFMA.
 // Lane (i = lane % 16, kg = lane / 16): score of q head i for tokens
 // 16*hf + 4*kg + r; PV accumulator for q head 4*kg + r, head dim DPL*i + nb.
-template <int D, bool FP8>
+//
+// With PAGE, the scores of each half take its page's K factor, and the PV
+// weights its page's V factor: the MFMA gets bf16(p * vs), and the running
+// sum adds that rounded weight divided by vs, so the normaliser counts
+// exactly the weight each V row received.
+template <int D, bool FP8, bool PAGE>
 __device__ inline void compute_chunk(const Chunk<D, FP8>& ch, const bf16x8 (&qop)[Geo<D, FP8>::STEPS],
                                      int c, int k0, int k1, float qk_scale_log2, int kg,
                                      float& m_run, float& l_run, f32x4 (&acc)[Geo<D, FP8>::DPL]) {
@@ -270,9 +295,14 @@ __device__ inline void compute_chunk(const Chunk<D, FP8>& ch, const bf16x8 (&qop
       sacc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<D, FP8>(ch, hf, s), qop[s],
                                                          sacc[hf], 0, 0, 0);
   }
+  float qs[2] = {qk_scale_log2, qk_scale_log2};
+  if constexpr (PAGE) {
+    qs[0] *= ch.ks[0];
+    qs[1] *= ch.ks[1];
+  }
   float sc[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) sc[j] = sacc[j >> 2][j & 3] * qk_scale_log2;
+  for (int j = 0; j < 8; ++j) sc[j] = sacc[j >> 2][j & 3] * qs[j >> 2];
   const int t0 = c * kChunk;
   if (t0 < k0 || t0 + kChunk > k1) {  // partial chunk: mask tokens outside [k0, k1)
 #pragma unroll
@@ -290,11 +320,21 @@ __device__ inline void compute_chunk(const Chunk<D, FP8>& ch, const bf16x8 (&qop
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
   bf16x8 pop;
   float psum = 0.f;
+  if constexpr (!PAGE) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 p = (__bf16)__builtin_amdgcn_exp2f(sc[j] - m_new);
-    pop[j] = p;
-    psum += (float)p;   // normalise with the same rounded weights PV uses
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 p = (__bf16)__builtin_amdgcn_exp2f(sc[j] - m_new);
+      pop[j] = p;
+      psum += (float)p;   // normalise with the same rounded weights PV uses
+    }
+  } else {
+    const float rvs[2] = {__builtin_amdgcn_rcpf(ch.vs[0]), __builtin_amdgcn_rcpf(ch.vs[1])};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 p = (__bf16)(__builtin_amdgcn_exp2f(sc[j] - m_new) * ch.vs[j >> 2]);
+      pop[j] = p;
+      psum += (float)p * rvs[j >> 2];
+    }
   }
   l_run = l_run * alpha + psum;
   m_run = m_new;
@@ -399,30 +439,44 @@ __global__ __launch_bounds__(256) void hda_prologue_kernel(Args a,
   if (page < 0 || page >= a.num_pages || !act) return;
   const int64_t row = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
                       (int64_t)(pos & (a.page_size - 1)) * G::RB;
+  // the slot is written with the scale it is read with
+  float ksc = a.k_scale, vsc = a.v_scale;
+  if (a.scale_mode != HDA_SCALE_TENSOR) {
+    const int64_t si = a.scale_mode == HDA_SCALE_PAGE ? (int64_t)page * a.n_kv_heads + h : h;
+    ksc *= a.k_scales[si];
+    vsc *= a.v_scales[si];
+  }
   if constexpr (FP8) {
-    a.k_pages[row + lane] = (uint8_t)fp8_encode(k0v / a.k_scale);
-    a.k_pages[row + lane + D / 2] = (uint8_t)fp8_encode(k1v / a.k_scale);
-    a.v_pages[row + lane] = (uint8_t)fp8_encode(v0 / a.v_scale);
-    a.v_pages[row + lane + D / 2] = (uint8_t)fp8_encode(v1 / a.v_scale);
+    a.k_pages[row + lane] = (uint8_t)fp8_encode(k0v / ksc);
+    a.k_pages[row + lane + D / 2] = (uint8_t)fp8_encode(k1v / ksc);
+    a.v_pages[row + lane] = (uint8_t)fp8_encode(v0 / vsc);
+    a.v_pages[row + lane + D / 2] = (uint8_t)fp8_encode(v1 / vsc);
   } else {
     uint16_t* kp = reinterpret_cast<uint16_t*>(a.k_pages + row);
     uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pages + row);
-    kp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(k0v / a.k_scale));
-    kp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(k1v / a.k_scale));
-    vp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(v0 / a.v_scale));
-    vp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(v1 / a.v_scale));
+    kp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(k0v / ksc));
+    kp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(k1v / ksc));
+    vp[lane] = __builtin_bit_cast(uint16_t, (__bf16)(v0 / vsc));
+    vp[lane + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)(v1 / vsc));
   }
 }
 
 // One plan item (b, [k0, k1), slot) for kv head h: the waves stream the
 // item's chunks, combine in LDS, and write the output (slot -1) or a partial.
-template <int D, bool FP8>
+template <int D, bool FP8, bool PAGE>
 __device__ inline void process_item(const Args& a, const int32_t* __restrict__ block_table,
                                     TileSmem<D>& sm, int b, int k0, int k1, int slot, int L,
                                     int h, int wave, int lane, int tid) {
   using G = Geo<D, FP8>;
   const int i = lane & 15, kg = lane >> 4;
   const int g = a.group;
+  // score and output scales of this kv head (per-page factors are applied
+  // per half-chunk instead)
+  float qk = a.qk_scale_log2, vsc = a.v_scale;
+  if (!PAGE && a.scale_mode == HDA_SCALE_HEAD) {
+    qk *= a.k_scales[h];
+    vsc *= a.v_scales[h];
+  }
     const int64_t qrow0 = ((int64_t)b * a.n_q_heads + (int64_t)h * g) * D;
 
     // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
@@ -453,7 +507,7 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
 #pragma unroll
       for (int k = 0; k < G::NBUF - 1; ++k) {
         const int ck = c + k * kWaves;
-        chunk_rsrc<D, FP8>(a, block_table, b, L, h, ck, ck <= c_last, kr, vr);
+        chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, ck, ck <= c_last, kr, vr, ring[k]);
         issue_chunk<D, FP8>(ring[k], kr, vr, i, kg);
       }
       bool done = false;
@@ -461,10 +515,11 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
 #pragma unroll
         for (int k = 0; k < G::NBUF; ++k) {
           const int cn = c + (G::NBUF - 1) * kWaves;
-          chunk_rsrc<D, FP8>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr);
-          issue_chunk<D, FP8>(ring[(k + G::NBUF - 1) % G::NBUF], kr, vr, i, kg);
+          const int nx = (k + G::NBUF - 1) % G::NBUF;
+          chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr, ring[nx]);
+          issue_chunk<D, FP8>(ring[nx], kr, vr, i, kg);
           __builtin_amdgcn_sched_barrier(0);
-          compute_chunk<D, FP8>(ring[k], qop, c, k0, k1, a.qk_scale_log2, kg, m_run, l_run, acc);
+          compute_chunk<D, FP8, PAGE>(ring[k], qop, c, k0, k1, qk, kg, m_run, l_run, acc);
           c += kWaves;
           if (c > c_last) {
             done = true;
@@ -507,7 +562,7 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
         lsum += wt * sm.l[ww][hh];
         o += wt * sm.acc[ww][hh][d];
       }
-      o = o / lsum * a.v_scale;
+      o = o / lsum * vsc;
       const int64_t hq = (int64_t)h * g + hh;
       if (slot < 0) {
         a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = o;
@@ -590,7 +645,7 @@ __device__ inline uint32_t total_tiles(const int32_t* __restrict__ seq_lens, int
 // Workgroup (w, h): W * Hkv workgroups, kv head fastest.  Items come from the
 // host plan (DEVPLAN false) or are derived here from the device lengths with
 // the same rule (DEVPLAN true), in the same order.
-template <int D, bool FP8, bool DEVPLAN>
+template <int D, bool FP8, bool DEVPLAN, bool PAGE>
 __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
     Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ plan) {
@@ -612,7 +667,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
       const int b = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
                 slot = items[4 * it + 3];
       if ((unsigned)b >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
-      process_item<D, FP8>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], h, wave, lane, tid);
+      process_item<D, FP8, PAGE>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], h, wave, lane,
+                                 tid);
     }
   } else {
     // Every wave derives the same plan facts; they stay wave-uniform.
@@ -645,7 +701,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
         const int k0 = (int)((int64_t)(lo - first) * a.tile_len);
         const int k1 = (int)min((int64_t)(hi - first) * a.tile_len, (int64_t)L);
         const int slot = k > 1 ? (int)(sb + (uint32_t)w - sp.owner(first)) : -1;
-        process_item<D, FP8>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
+        process_item<D, FP8, PAGE>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
       }
       first_carry += ft;
       slot_carry += st;
@@ -820,7 +876,7 @@ __global__ __launch_bounds__(64) void hda_plan_kernel(const int32_t* __restrict_
   }
 }
 
-template <int D, bool FP8, bool DEVPLAN>
+template <int D, bool FP8, bool DEVPLAN, bool PAGE>
 hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_t stream,
                   void* split_event) {
   hipError_t e;
@@ -831,8 +887,8 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
     if (e != hipSuccess) return e;
     a.q = q_prime;   // attention reads the normalised, rotated q
   }
-  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, DEVPLAN>), dim3(grid), dim3(64 * kWaves), 0,
-                     stream, a, a.block_table, a.seq_lens, a.plan);
+  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, DEVPLAN, PAGE>), dim3(grid), dim3(64 * kWaves),
+                     0, stream, a, a.block_table, a.seq_lens, a.plan);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (split_event) {
@@ -847,11 +903,14 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
   return e;
 }
 
+// Per-page scales are built for the fp8 cache only (check_params refuses
+// them for bf16).
 template <int D, bool DEVPLAN>
 hipError_t launch_d(const Args& a, bool fp8, int grid, bool pro, uint16_t* qp, hipStream_t st,
                     void* ev) {
-  return fp8 ? launch<D, true, DEVPLAN>(a, grid, pro, qp, st, ev)
-             : launch<D, false, DEVPLAN>(a, grid, pro, qp, st, ev);
+  if (!fp8) return launch<D, false, DEVPLAN, false>(a, grid, pro, qp, st, ev);
+  return a.scale_mode == HDA_SCALE_PAGE ? launch<D, true, DEVPLAN, true>(a, grid, pro, qp, st, ev)
+                                        : launch<D, true, DEVPLAN, false>(a, grid, pro, qp, st, ev);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -878,6 +937,13 @@ int check_params(const hda_params* p, const void* q, const void* k_pages, const 
     if (!p->q_norm_w || !p->k_norm_w || !p->k_new || !p->v_new) return HDA_ERR_INVALID_ARG;
     if (!(p->rms_eps >= 0.f) || !(p->rope_theta > 0.f)) return HDA_ERR_INVALID_ARG;
   }
+  if (p->scale_mode != HDA_SCALE_TENSOR && p->scale_mode != HDA_SCALE_HEAD &&
+      p->scale_mode != HDA_SCALE_PAGE)
+    return HDA_ERR_INVALID_ARG;
+  if (p->scale_mode != HDA_SCALE_TENSOR && (!p->k_scales || !p->v_scales))
+    return HDA_ERR_INVALID_ARG;
+  if (p->scale_mode == HDA_SCALE_PAGE && p->kv_dtype != HDA_KV_FP8_E4M3) return HDA_ERR_UNSUPPORTED;
+  if (p->reserved0 != 0) return HDA_ERR_INVALID_ARG;
   return HDA_OK;
 }
 
@@ -906,6 +972,9 @@ Args make_args(const hda_params* p, const void* q, void* k_pages, void* v_pages,
   a.k_norm_w = static_cast<const uint16_t*>(p->k_norm_w);
   a.k_new = static_cast<const uint16_t*>(p->k_new);
   a.v_new = static_cast<const uint16_t*>(p->v_new);
+  a.scale_mode = p->scale_mode;
+  a.k_scales = p->scale_mode == HDA_SCALE_TENSOR ? nullptr : p->k_scales;
+  a.v_scales = p->scale_mode == HDA_SCALE_TENSOR ? nullptr : p->v_scales;
   a.head_stride = p->page_size * D * elem;
   a.page_stride = (int64_t)a.head_stride * p->n_kv_heads;
   a.num_pages = (int32_t)(p->num_pages < 0x7fffffffLL ? p->num_pages : 0x7fffffffLL);

@@ -28,6 +28,10 @@ HDA_ERR_BAD_PLAN = -7
 
 HDA_KV_BF16 = 0
 HDA_KV_FP8_E4M3 = 1
+HDA_SCALE_TENSOR = 0
+HDA_SCALE_HEAD = 1
+HDA_SCALE_PAGE = 2
+SCALE_MODES = {"tensor": HDA_SCALE_TENSOR, "head": HDA_SCALE_HEAD, "page": HDA_SCALE_PAGE}
 PLAN_HEADER_INTS = 8
 
 # every symbol include/hda.h declares
@@ -65,6 +69,10 @@ class hda_params(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_int64),
         ("split_event", ctypes.c_void_p),
+        ("scale_mode", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("k_scales", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
     ]
 
 
@@ -276,6 +284,11 @@ class DeviceBatch:
             for k in ("q_norm_w", "k_norm_w", "k_new", "v_new"):
                 t[k] = torch.from_numpy(inp[k].view(np.int16)).to(device)
             kw.update(prologue=1, rms_eps=float(inp["rms_eps"]), rope_theta=float(inp["rope_theta"]))
+        mode = inp.get("scale_mode", "tensor")
+        kw["scale_mode"] = SCALE_MODES[mode]
+        if mode != "tensor":
+            for k in ("k_scales", "v_scales"):
+                t[k] = torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.float32)).to(device)
         return cls(t, kw, device)
 
     def workspace(self, nbytes):
@@ -287,6 +300,9 @@ class DeviceBatch:
     def params(self, plan, workspace=None, need=None):
         p = hda_params(**self.kw)
         t = self.t
+        if "k_scales" in t:
+            p.k_scales = t["k_scales"].data_ptr()
+            p.v_scales = t["v_scales"].data_ptr()
         if self.kw.get("prologue"):
             p.q_norm_w = t["q_norm_w"].data_ptr()
             p.k_norm_w = t["k_norm_w"].data_ptr()

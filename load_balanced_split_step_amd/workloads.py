@@ -36,6 +36,8 @@ Recipe (the pages use no dataset; these stand in for a serving batch):
   * fp8: scale = amax / 448 in float32 over the drawn values of the whole
     pool ("tensor"), of one kv head ("head") or of one (page, kv head) slab
     ("page"); codes from torch's float8_e4m3fn cast of clip(x / scale, +-448);
+    a bf16 cache with "head" scales stores bf16(x / scale) with the same
+    per-head scales (no scale otherwise);
   * rows past len_b in a request's last page hold NaN (when poisoned), and
     for the prologue workload so does the new token's slot len_b - 1.
 """
@@ -155,12 +157,13 @@ def _draw_pool(ss, n_pages, w: Workload, head_scales, fp8_scale=None):
     children = [np.random.SeedSequence(ss.entropy, spawn_key=ss.spawn_key + (c,))
                 for c in range(n_chunks)]
     fp8 = w.kv_dtype == "fp8"
+    scaled = fp8 or w.kv_scale != "tensor"     # a bf16 cache may carry head scales
     page_mode = fp8 and w.kv_scale == "page"
-    amax_pass = fp8 and not page_mode and fp8_scale is None
+    amax_pass = scaled and not page_mode and fp8_scale is None
     if not amax_pass:
         out = np.empty((n_slabs, slab), dtype=np.uint8 if fp8 else np.uint16)
     slab_scale = np.empty(n_slabs, dtype=np.float32) if page_mode else None
-    if fp8 and not page_mode and not amax_pass:
+    if scaled and not page_mode and not amax_pass:
         fp8_scale = np.broadcast_to(np.asarray(fp8_scale, dtype=np.float32), (Hkv,))
 
     def work(c):
@@ -181,6 +184,8 @@ def _draw_pool(ss, n_pages, w: Workload, head_scales, fp8_scale=None):
             out[s0:s1] = _fp8_bits(x / sc[:, None])
         elif fp8:
             out[s0:s1] = _fp8_bits(x / fp8_scale[heads][:, None])
+        elif scaled:
+            out[s0:s1] = _bf16_bits(x / fp8_scale[heads][:, None])
         else:
             out[s0:s1] = _bf16_bits(x)
         return None
@@ -232,14 +237,16 @@ def make_inputs(w: Workload, seed: Optional[int] = None, poison: bool = True,
 
     k_scale = v_scale = np.float32(1.0)
     k_scales = v_scales = None
-    scale_mode = w.kv_scale if w.kv_dtype == "fp8" else "tensor"
+    scale_mode = w.kv_scale
     assert scale_mode in ("tensor", "head", "page")
+    if w.kv_dtype == "bf16" and scale_mode == "page":
+        raise ValueError("per-page scales are for an fp8 cache")
     k_ss, v_ss = ss[_S_K], ss[_S_V]
     if scale_mode == "page":
         k_pages, k_scales = _draw_pool(k_ss, n_pages, w, head_k)
         v_pages, v_scales = _draw_pool(v_ss, n_pages, w, head_v)
     else:
-        if w.kv_dtype == "fp8":
+        if w.kv_dtype == "fp8" or scale_mode == "head":
             ka = _draw_pool(k_ss, n_pages, w, head_k) / np.float32(448.0)
             va = _draw_pool(v_ss, n_pages, w, head_v) / np.float32(448.0)
             if scale_mode == "head":

@@ -203,8 +203,29 @@ def test_decode_argument_errors(lib):
     assert _decode_status(lib, _params(), bad) == E.HDA_ERR_BAD_PLAN
     assert _decode_status(lib, _params(workspace=None), plan) == E.HDA_ERR_WORKSPACE
     assert _decode_status(lib, _params(workspace_bytes=100), plan) == E.HDA_ERR_WORKSPACE
+    # scale granularity
+    assert _decode_status(lib, _params(scale_mode=3), plan) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(scale_mode=E.HDA_SCALE_HEAD), plan) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(scale_mode=E.HDA_SCALE_HEAD, k_scales=FAKE + 0x7000),
+                          plan) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(scale_mode=E.HDA_SCALE_PAGE, k_scales=FAKE + 0x7000,
+                                       v_scales=FAKE + 0x8000), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(reserved0=1), plan) == E.HDA_ERR_INVALID_ARG
     for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.hda_status_string(s)
+
+
+def test_header_constants_match_binding():
+    """Every #define of the header that the binding mirrors has the same value."""
+    import re
+    text = open(os.path.join(ROOT, "include", "hda.h")).read()
+    defs = {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define\s+(HDA_\w+)\s+\(?(-?\d+)\)?", text)}
+    mirrored = [k for k in dir(hda) if k.startswith("HDA_") and isinstance(getattr(hda, k), int)]
+    assert len(mirrored) >= 13
+    for k in mirrored:
+        assert defs[k] == getattr(hda, k), k
+    assert defs["HDA_PLAN_HEADER_INTS"] == hda.PLAN_HEADER_INTS
 
 
 def test_workspace_bound(lib):

@@ -30,6 +30,14 @@ SCALED = {
     "extreme_s": (CONFIGS["extreme"].with_(name="extreme_s", batch=8), [16384] + [1000] * 7),
     "longtail_s": (CONFIGS["longtail"].with_(name="longtail_s", batch=12, len_range=(256, 6000)), None),
     "fp8_s": (CONFIGS["fp8"].with_(name="fp8_s", batch=12, len_range=(100, 3000)), None),
+    "fp8_page_s": (CONFIGS["fp8_page"].with_(name="fp8_page_s", batch=10, len_range=(100, 3000)),
+                   None),
+    # per-head scales; and per-page scales on 16-token pages, where the two
+    # halves of a 32-token chunk sit on different pages with their own scales
+    "fp8_head_s": (CONFIGS["fp8"].with_(name="fp8_head_s", batch=8, len_range=(50, 2000),
+                                        kv_scale="head", head_scale=True), None),
+    "tiny_page": (CONFIGS["tiny"].with_(name="tiny_page", kv_dtype="fp8", kv_scale="page",
+                                        head_scale=True, placement="random"), None),
 }
 
 
@@ -137,9 +145,11 @@ def test_edge_shapes(name, w, lens):
         assert err <= tol, (name, pname, err)
 
 
-@pytest.mark.parametrize("kv", ["fp8", "bf16"])
-def test_prologue_writes_new_token(kv):
-    w = CONFIGS["fp8"].with_(name="pro", batch=9, len_range=(16, 900), kv_dtype=kv)
+@pytest.mark.parametrize("kv,mode", [("fp8", "tensor"), ("bf16", "tensor"), ("fp8", "head"),
+                                     ("fp8", "page"), ("bf16", "head")])
+def test_prologue_writes_new_token(kv, mode):
+    w = CONFIGS["fp8"].with_(name="pro", batch=9, len_range=(16, 900), kv_dtype=kv,
+                             kv_scale=mode, head_scale=mode != "tensor")
     inp = make_inputs(w)
     _, _, _, (kc, vc, kx, vx) = oracle_inputs(inp)
     dev = hda.DeviceBatch.from_inputs(inp)

@@ -12,7 +12,7 @@ import torch
 import load_balanced_split_step_amd.hda as hda
 import oracle
 from load_balanced_split_step_amd.workloads import CONFIGS, make_inputs
-from tests.gpu_util import TOL, need_gpu, oracle_inputs
+from tests.gpu_util import TOL, need_gpu, oracle_inputs, scale_kw
 
 pytestmark = pytest.mark.gpu
 
@@ -42,10 +42,13 @@ def v_range_check(out, inp, vpool, n_req=None):
     ps = w.page_size
     o = out.cpu().numpy()
     B = len(inp["seq_lens"])
+    kw = scale_kw(inp)
     for b in range(B if n_req is None else min(B, n_req)):
         L = int(inp["seq_lens"][b])
+        vs = oracle.row_scales(kw["v_scale"], kw["scale_mode"], kw["v_scales"],
+                               inp["block_table"][b], L, ps, w.n_kv_heads)   # [L, Hkv]
         v = oracle.decode_kv(oracle.gather_request(vpool, inp["block_table"][b], L, ps),
-                             w.kv_dtype, float(inp["v_scale"]))            # [L, Hkv, D]
+                             w.kv_dtype, vs[:, :, None])                      # [L, Hkv, D]
         lo, hi = v.min(axis=0), v.max(axis=0)                               # [Hkv, D]
         for h in range(w.n_q_heads):
             kvh = h // g
@@ -53,7 +56,7 @@ def v_range_check(out, inp, vpool, n_req=None):
             assert np.all(o[b, h] >= lo[kvh] - slack) and np.all(o[b, h] <= hi[kvh] + slack), (b, h)
 
 
-@pytest.mark.parametrize("name", ["uniform", "extreme", "longtail", "fp8"])
+@pytest.mark.parametrize("name", ["uniform", "extreme", "longtail", "fp8", "fp8_page"])
 def test_full_size_sampled(name):
     w = CONFIGS[name]
     inp = make_inputs(w)
@@ -67,8 +70,7 @@ def test_full_size_sampled(name):
     q, kp, vp, _ = oracle_inputs(inp)
     pairs = sample_pairs(lens, w.n_q_heads, w.group, seed=w.seed)
     ref = oracle.attention_selected(q, kp, vp, inp["block_table"], lens, w.kv_dtype,
-                                    float(inp["sm_scale"]), pairs, float(inp["k_scale"]),
-                                    float(inp["v_scale"]))
+                                    float(inp["sm_scale"]), pairs, **scale_kw(inp))
     o = out.cpu().numpy()
     err = max(float(np.abs(o[b, h] - ref[(b, h)]).max()) for b, h in pairs)
     print(f"{name}: {len(pairs)} sampled (b, h), max err {err:.3e}", flush=True)

@@ -55,6 +55,8 @@ AUTO = [
     ("many", Workload("many", 150, 16, 2, 128, 16, seed=61), None, [(32, 64), (16, 500), (256, 3)]),
     ("fp8_s", CONFIGS["fp8"].with_(name="fp8_s", batch=70, len_range=(20, 2000)), None,
      [(128, 64), (64, 13)]),
+    ("fp8_page_s", CONFIGS["fp8_page"].with_(name="fp8_page_s", batch=20, len_range=(20, 3000)),
+     None, [(128, 64), (32, 100)]),
 ]
 
 
