@@ -45,6 +45,8 @@ from .attention import (
 )
 from .prologue import (rms_norm, rope, prologue_step, bf16_encode, write_new_token,
                        slot_scales)
+from .fp8_math import (quantize_q_fp8, dequantized_q, attention_fp8q,
+                       weight_rounding_bounds)
 
 __all__ = [
     "bf16_to_f64", "fp8_decode", "fp8_encode", "FP8_MAX",
@@ -52,5 +54,6 @@ __all__ = [
     "gather_request", "attention_reference", "attention_selected",
     "attention_bruteforce", "split_merge_reference", "decode_kv", "row_scales",
     "SCALE_MODES", "rms_norm", "rope", "prologue_step", "bf16_encode", "write_new_token",
-    "slot_scales",
+    "slot_scales", "quantize_q_fp8", "dequantized_q", "attention_fp8q",
+    "weight_rounding_bounds",
 ]
