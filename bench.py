@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--workload", default="extreme")
     ap.add_argument("--kv-scale", choices=["tensor", "head", "page"], default=None,
                     help="override the workload's fp8 scale granularity")
+    ap.add_argument("--math", choices=["bf16", "fp8"], default="bf16",
+                    help="product arithmetic: bf16 (cache widened to bf16) or fp8 (native fp8 "
+                         "MFMA operands, V pages dim-major; fp8 cache only)")
     ap.add_argument("--tile-len", type=int, default=None)
     ap.add_argument("--workgroups", type=int, default=None)
     ap.add_argument("--copies", type=int, default=4, help="KV pool copies rotated over")
@@ -156,7 +159,7 @@ def main():
     inp = make_inputs(w)
     log(f"generated {args.workload} inputs in {time.time() - t:.1f}s")
     lens = inp["seq_lens"]
-    dev = hda.DeviceBatch.from_inputs(inp, device="cuda:0")
+    dev = hda.DeviceBatch.from_inputs(inp, device="cuda:0", math=args.math)
     copies = [(dev.t["k_pages"], dev.t["v_pages"])]
     for _ in range(max(0, args.copies - 1)):
         copies.append((dev.t["k_pages"].clone(), dev.t["v_pages"].clone()))
@@ -302,6 +305,7 @@ def main():
             "batch": int(len(lens)), "kv_tokens": int(lens.sum()),
             "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
             "page_size": w.page_size, "kv_dtype": w.kv_dtype, "kv_scale": inp["scale_mode"],
+            "math": args.math,
             "tile_len": tl,
             "n_workgroups": W, "kv_bytes": kv},
         "us_per_step": {"wall": round(ms_per_step * 1e3, 2),

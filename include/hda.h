@@ -72,6 +72,31 @@ extern "C" {
 #define HDA_SCALE_HEAD 1
 #define HDA_SCALE_PAGE 2   /* fp8 cache only */
 
+/* Product arithmetic (hda_params.math).
+ *   HDA_MATH_BF16  cache elements widened exactly to bf16, q in bf16,
+ *                  softmax weights rounded to bf16; fp32 accumulation
+ *   HDA_MATH_FP8   fp8 cache only: QK^T and PV on fp8 matrix-core operands.
+ *                  q is quantised per (request, q head) to E4M3 with scale
+ *                  amax/448 (codes round-to-nearest-even from q/scale in
+ *                  float32) and the softmax weights are rounded to E4M3
+ *                  (times 2^8) before PV, the normaliser summing the same
+ *                  rounded weights.  Needs v_layout HDA_V_DIM_MAJOR, D 128,
+ *                  page_size >= 64 and tensor or head scales.
+ * The pages report FP8 execution and name cache precision as a setting the
+ * results depend on (remio.ai page, section "Lo que la afirmación de un
+ * 48,8 % de TPOT no demuestra"); fp8 attention arithmetic is this library's
+ * own option. */
+#define HDA_MATH_BF16 0
+#define HDA_MATH_FP8 1
+
+/* V page layout (hda_params.v_layout); K pages are always token-major.
+ *   HDA_V_TOKEN_MAJOR  [num_pages][Hkv][page_size][D]
+ *   HDA_V_DIM_MAJOR    [num_pages][Hkv][D][page_size]: the tokens of one
+ *                      head dim are contiguous (the V layout of the original
+ *                      vLLM paged-attention cache); HDA_MATH_FP8 only */
+#define HDA_V_TOKEN_MAJOR 0
+#define HDA_V_DIM_MAJOR 1
+
 /*
  * Plan format (int32 array), produced by hda_plan / hda_plan_static:
  *   [0..7]   header: VERSION, B, tile_len (0 for a static plan), W, T, N, P, 0
@@ -181,9 +206,11 @@ typedef struct hda_params {
    * prologue stores the new token with the scale of its slot (it never
    * changes a scale: a caller that rescales a page does so itself). */
   int32_t scale_mode;
-  int32_t reserved0;          /* must be 0 */
+  int32_t math;               /* HDA_MATH_BF16 or HDA_MATH_FP8 */
   const float* k_scales;      /* [device] [Hkv] or [num_pages][Hkv]; NULL for TENSOR */
   const float* v_scales;      /* [device] likewise */
+  int32_t v_layout;           /* HDA_V_TOKEN_MAJOR or HDA_V_DIM_MAJOR */
+  int32_t reserved0;          /* must be 0 */
 } hda_params;
 
 /*

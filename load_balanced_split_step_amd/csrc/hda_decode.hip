@@ -74,6 +74,7 @@ struct Args {
   int32_t n_wg, n_items, n_parts;
   int32_t tile_len;      // device-planned launches only
   int32_t scale_mode;    // HDA_SCALE_*
+  int32_t v_dim_major;   // V pages [page][Hkv][D][page_size] instead of [..][page_size][D]
   float qk_scale_log2;   // sm_scale * k_scale * log2(e)
   float v_scale;
   float k_scale, rms_eps, rope_theta;
@@ -381,6 +382,62 @@ struct TileSmem {
   __attribute__((aligned(16))) uint16_t q[kMaxGroup][D];
 };
 
+// One wave's PV accumulators into LDS: lane (i, kg) holds q head 4*kg + r in
+// acc[nb][r], for head dim DPL*i + nb (BLOCKED false) or 16*nb + i (true).
+template <int D, bool BLOCKED = false>
+__device__ inline void store_wave_acc(TileSmem<D>& sm, int wave, int i, int kg, int g,
+                                      const f32x4 (&acc)[D / 16]) {
+  constexpr int DPL = D / 16;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int hh = 4 * kg + r;
+    if (hh < g) {
+      if constexpr (BLOCKED) {
+#pragma unroll
+        for (int nb = 0; nb < DPL; ++nb) sm.acc[wave][hh][16 * nb + i] = acc[nb][r];
+      } else {
+#pragma unroll
+        for (int v4 = 0; v4 < DPL / 4; ++v4) {
+          f32x4 o = {acc[4 * v4][r], acc[4 * v4 + 1][r], acc[4 * v4 + 2][r], acc[4 * v4 + 3][r]};
+          *reinterpret_cast<f32x4*>(&sm.acc[wave][hh][DPL * i + 4 * v4]) = o;
+        }
+      }
+    }
+  }
+}
+
+// Cross-wave combine of one item from LDS (per q head: running max m,
+// weight sum l in units of 2^lse_shift, unnormalised output), then the
+// output row (slot -1) or the partial and its natural-log log-sum-exp.
+template <int D>
+__device__ inline void finish_item(const Args& a, const TileSmem<D>& sm, int b, int h, int slot,
+                                   float vsc, float lse_shift, int tid) {
+  const int g = a.group;
+  for (int idx = tid; idx < g * D; idx += 64 * kWaves) {
+    const int hh = idx / D, d = idx - hh * D;
+    float M = sm.m[0][hh];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][hh]);
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float wt = __builtin_amdgcn_exp2f(sm.m[ww][hh] - M);
+      lsum += wt * sm.l[ww][hh];
+      o += wt * sm.acc[ww][hh][d];
+    }
+    o = o / lsum * vsc;
+    const int64_t hq = (int64_t)h * g + hh;
+    if (slot < 0) {
+      a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = o;
+    } else {
+      a.part_o[((int64_t)slot * a.n_q_heads + hq) * D + d] = o;
+      if (d == 0)
+        a.part_lse[(int64_t)slot * a.n_q_heads + hq] =
+            (M + log2f(lsum) - lse_shift) * 0.69314718055994531f;
+    }
+  }
+}
+
 // New-token prologue, one workgroup (4 waves) per (request b, kv head h):
 // q' = RoPE(RMSNorm(q)) for the group's q heads into the workspace (bf16,
 // the precision the QK product takes), k' = RoPE(RMSNorm(k_new)) and v_new,
@@ -449,8 +506,15 @@ __global__ __launch_bounds__(256) void hda_prologue_kernel(Args a,
   if constexpr (FP8) {
     a.k_pages[row + lane] = (uint8_t)fp8_encode(k0v / ksc);
     a.k_pages[row + lane + D / 2] = (uint8_t)fp8_encode(k1v / ksc);
-    a.v_pages[row + lane] = (uint8_t)fp8_encode(v0 / vsc);
-    a.v_pages[row + lane + D / 2] = (uint8_t)fp8_encode(v1 / vsc);
+    if (a.v_dim_major) {   // column pos % ps of the (page, head) slab [D][ps]
+      const int64_t col = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
+                          (pos & (a.page_size - 1));
+      a.v_pages[col + (int64_t)lane * a.page_size] = (uint8_t)fp8_encode(v0 / vsc);
+      a.v_pages[col + (int64_t)(lane + D / 2) * a.page_size] = (uint8_t)fp8_encode(v1 / vsc);
+    } else {
+      a.v_pages[row + lane] = (uint8_t)fp8_encode(v0 / vsc);
+      a.v_pages[row + lane + D / 2] = (uint8_t)fp8_encode(v1 / vsc);
+    }
   } else {
     uint16_t* kp = reinterpret_cast<uint16_t*>(a.k_pages + row);
     uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pages + row);
@@ -534,45 +598,273 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
     float l_tot = l_run;
     l_tot += __shfl_xor(l_tot, 16);
     l_tot += __shfl_xor(l_tot, 32);
+    // the previous item's combine has finished reading this LDS
+    __syncthreads();
     if (kg == 0) {
       sm.m[wave][i] = m_run;
       sm.l[wave][i] = l_tot;
     }
+    store_wave_acc<D>(sm, wave, i, kg, g, acc);
+    __syncthreads();
+    finish_item<D>(a, sm, b, h, slot, vsc, 0.f, tid);
+}
+
+// ---- native-fp8 products: fp8 cache, dim-major V pages, D = 128 ----
+//
+// QK^T and PV take the fp8 codes as MFMA operands directly.  A wave takes
+// 64-token chunks (one page of 64, or a 64-token run of a larger page).
+//   QK: four 16-token M blocks, each one v_mfma_scale_f32_16x16x128_f8f6f4
+//       (scales 2^0) of K rows against q quantised to E4M3 per q head
+//       (s_q = amax / 448).  Row m of block mb is token
+//       16*(m/4) + 4*mb + m%4, so lane (i, kg) ends up with the scores of
+//       q head i for its 16 consecutive tokens 16*kg .. 16*kg+15.
+//   PV: the softmax weights, shifted by 2^8 and rounded to E4M3, against V
+//       codes read from dim-major pages, where those 16 tokens of one head
+//       dim are 16 consecutive bytes: two v_mfma_f32_16x16x32_fp8_fp8 per
+//       16-dim block (lane i takes dim 16*nb + i), no transposes.  The weight sum comes from the same
+//       rounded weights through one more MFMA against a block of 1.0 codes.
+constexpr int kChunkN = 64;
+constexpr uint64_t kFp8Ones = 0x3838383838383838ull;   // eight E4M3 1.0 codes
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+struct ChunkN {
+  u32x4 k[4][2];   // K: 32 dims of one token row per lane, per 16-token block
+  u32x4 v[8];      // V: 16 tokens of head dim 16*nb + i per lane, nb = 0..7
+};
+
+// Buffer resources of chunk c of (request b, kv head h): the 64 K rows from
+// token t, and the V slab from token column t%ps of every head-dim row.
+// Returns the number of rows below len (0 for a chunk without a page).
+__device__ inline int chunk_rsrc_n(const Args& a, const int32_t* __restrict__ block_table, int b,
+                                   int L, int h, int c, bool live, __amdgpu_buffer_rsrc_t& kr,
+                                   __amdgpu_buffer_rsrc_t& vr) {
+  const int t = c * kChunkN;
+  int rows = L - t;
+  rows = rows > kChunkN ? kChunkN : rows;
+  int64_t koff = 0, voff = 0;
+  int kbytes = 0, vbytes = 0;
+  if (live && rows > 0) {
+    const int pidx = t >> a.log2_ps;
+    if (pidx < a.max_pages) {
+      const int page = block_table[(int64_t)b * a.max_pages + pidx];
+      if (page >= 0 && page < a.num_pages) {
+        const int64_t slab = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride;
+        const int tin = t & (a.page_size - 1);
+        koff = slab + (int64_t)tin * 128;
+        kbytes = kChunkN * 128;
+        voff = slab + tin;
+        vbytes = 127 * a.page_size + kChunkN;   // dims 0..127, 64 columns from tin
+      }
+    }
+  }
+  kr = make_rsrc(a.k_pages + koff, kbytes);
+  vr = make_rsrc(a.v_pages + voff, vbytes);
+  return kbytes > 0 ? rows : 0;
+}
+
+// One lane offset per tensor serves every load of a chunk; the per-block
+// parts are wave-uniform and go in the scalar offset, which the buffer range
+// check leaves out.  Both stay inside the (page, kv head) slab by
+// construction (a 64-token chunk lies within one page of >= 64 tokens).  K
+// rows past len may thus be read: they only feed the scores of tokens past
+// len, which are overwritten with -inf.  V columns past len are masked after
+// the load.  A chunk without a page reads zeros (empty resource).
+__device__ inline void issue_chunk_n(ChunkN& ch, const __amdgpu_buffer_rsrc_t& kr,
+                                     const __amdgpu_buffer_rsrc_t& vr, int koff, int voff,
+                                     int ps) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hh = 4 * kg + r;
-      if (hh < g) {
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int v4 = 0; v4 < G::DPL / 4; ++v4) {
-          f32x4 o = {acc[4 * v4][r], acc[4 * v4 + 1][r], acc[4 * v4 + 2][r], acc[4 * v4 + 3][r]};
-          *reinterpret_cast<f32x4*>(&sm.acc[wave][hh][G::DPL * i + 4 * v4]) = o;
+    for (int u = 0; u < 2; ++u)
+      ch.k[mb][u] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff, 4 * 128 * mb + 64 * u, kStreamAux));
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+    ch.v[nb] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, 16 * nb * ps, kStreamAux));
+}
+
+__device__ inline uint64_t pack64(uint32_t lo, uint32_t hi) {
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
+// One 64-token chunk: scores, online-softmax update, acc += P8 V8, and the
+// rounded weights' sum into lacc (both in units of 2^8).  qs = score scale of
+// lane i's q head in log2 units (sm_scale * k scale * s_q * log2 e).
+__device__ inline void compute_chunk_n(const ChunkN& ch, const i32x8& qop, int c, int k0, int k1,
+                                       int rows, float qs, int kg, float& m_run, f32x4 (&acc)[8],
+                                       f32x4& lacc) {
+  float sc[16];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const i32x8 kop = {(int)ch.k[mb][0][0], (int)ch.k[mb][0][1], (int)ch.k[mb][0][2],
+                       (int)ch.k[mb][0][3], (int)ch.k[mb][1][0], (int)ch.k[mb][1][1],
+                       (int)ch.k[mb][1][2], (int)ch.k[mb][1][3]};
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 sacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qop, z, 0, 0, 0, 127,
+                                                                       0, 127);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[4 * mb + r] = sacc[r] * qs;
+  }
+  const int t0 = c * kChunkN;
+  if (t0 < k0 || t0 + kChunkN > k1) {   // partial chunk: mask tokens outside [k0, k1)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int t = t0 + 16 * kg + x;
+      if (t < k0 || t >= k1) sc[x] = -INFINITY;
+    }
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sc[x]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  uint32_t pw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float e0 = __builtin_amdgcn_exp2f(sc[4 * q] - m_new) * 256.f;
+    const float e1 = __builtin_amdgcn_exp2f(sc[4 * q + 1] - m_new) * 256.f;
+    const float e2 = __builtin_amdgcn_exp2f(sc[4 * q + 2] - m_new) * 256.f;
+    const float e3 = __builtin_amdgcn_exp2f(sc[4 * q + 3] - m_new) * 256.f;
+    uint32_t x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+    pw[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, (int)x, true);
+  }
+  m_run = m_new;
+  if (__ballot(alpha != 1.0f) != 0) {
+    float ar[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * kg + r);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[nb][r] *= ar[r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lacc[r] *= ar[r];
+  }
+  // weights of tokens 16*kg + 8*ks + j, j = 0..7, for K steps ks = 0, 1
+  const long p0 = (long)pack64(pw[0], pw[1]);
+  const long p1 = (long)pack64(pw[2], pw[3]);
+  // V columns past len hold anything (a NaN code times a zero weight would
+  // still poison the sum): zero them in the last chunk of a request
+  uint32_t vm[4] = {~0u, ~0u, ~0u, ~0u};
+  if (rows < kChunkN) {
+    int nv = rows - 16 * kg;
+    nv = nv < 0 ? 0 : (nv > 16 ? 16 : nv);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int bq = nv - 4 * q;
+      vm[q] = bq >= 4 ? ~0u : (bq <= 0 ? 0u : ((1u << (8 * bq)) - 1u));
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const u32x4 v = ch.v[nb];
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+        p0, (long)pack64(v[0] & vm[0], v[1] & vm[1]), acc[nb], 0, 0, 0);
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+        p1, (long)pack64(v[2] & vm[2], v[3] & vm[3]), acc[nb], 0, 0, 0);
+  }
+  lacc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(p0, (long)kFp8Ones, lacc, 0, 0, 0);
+  lacc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(p1, (long)kFp8Ones, lacc, 0, 0, 0);
+}
+
+// One plan item in the native-fp8 mode (see process_item for the shape of
+// the loop and the combine).
+__device__ inline void process_item_fp8n(const Args& a, const int32_t* __restrict__ block_table,
+                                         TileSmem<128>& sm, int b, int k0, int k1, int slot,
+                                         int L, int h, int wave, int lane, int tid) {
+  const int i = lane & 15, kg = lane >> 4;
+  const int g = a.group;
+  float qk = a.qk_scale_log2, vsc = a.v_scale;
+  if (a.scale_mode == HDA_SCALE_HEAD) {
+    qk *= a.k_scales[h];
+    vsc *= a.v_scales[h];
+  }
+  // q head i in E4M3: lane (i, kg) holds dims 16*kg + 0..15 and 64 + 16*kg +
+  // 0..15, the order of the K rows' operand; s_q = amax / 448 (1 for a zero
+  // row), codes round-to-nearest-even from q / s_q in float32
+  const int64_t qrow = ((int64_t)b * a.n_q_heads + (int64_t)h * g + i) * 128;
+  float qv[32];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (i < g)
+      raw = *reinterpret_cast<const u32x4*>(a.q + qrow + 64 * (u >> 1) + 16 * kg + 8 * (u & 1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[8 * u + 2 * e] = __uint_as_float(raw[e] << 16);
+      qv[8 * u + 2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int x = 0; x < 32; ++x) amax = fmaxf(amax, fabsf(qv[x]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  const float s_q = amax > 0.f ? amax / 448.0f : 1.0f;
+  i32x8 qop;
+#pragma unroll
+  for (int dw = 0; dw < 8; ++dw) {
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = fminf(fmaxf(qv[4 * dw + e] / s_q, -448.f), 448.f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    qop[dw] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+  }
+  const float qs = qk * s_q;
+
+  const int c_last = (k1 - 1) / kChunkN;
+  int c = k0 / kChunkN + wave;
+  const bool has_chunks = c <= c_last;
+  ChunkN ring[2];
+  int rows_of[2];
+  __amdgpu_buffer_rsrc_t kr, vr;
+  // lane (i, kg): K row 16*(i/4) + i%4 of M block 0 (block mb adds 4*mb
+  // rows), bytes 16*kg of each 64-byte half; V row (head dim) i of each
+  // 16-dim block (block nb adds 16*nb rows: one load covers 16 whole rows),
+  // tokens 16*kg
+  const int koff = (16 * (i >> 2) + (i & 3)) * 128 + 16 * kg;
+  const int voff = i * a.page_size + 16 * kg;
+  float m_run = -INFINITY;
+  f32x4 acc[8], lacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (has_chunks) {
+    rows_of[0] = chunk_rsrc_n(a, block_table, b, L, h, c, true, kr, vr);
+    issue_chunk_n(ring[0], kr, vr, koff, voff, a.page_size);
+    bool done = false;
+    while (!done) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int cn = c + kWaves;
+        rows_of[1 - k] = chunk_rsrc_n(a, block_table, b, L, h, cn, cn <= c_last, kr, vr);
+        issue_chunk_n(ring[1 - k], kr, vr, koff, voff, a.page_size);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_chunk_n(ring[k], qop, c, k0, k1, rows_of[k], qs, kg, m_run, acc, lacc);
+        c += kWaves;
+        if (c > c_last) {
+          done = true;
+          break;
         }
       }
     }
-    __syncthreads();
-    for (int idx = tid; idx < g * D; idx += 64 * kWaves) {
-      const int hh = idx / D, d = idx - hh * D;
-      float M = sm.m[0][hh];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][hh]);
-      float lsum = 0.f, o = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float wt = __builtin_amdgcn_exp2f(sm.m[ww][hh] - M);
-        lsum += wt * sm.l[ww][hh];
-        o += wt * sm.acc[ww][hh][d];
-      }
-      o = o / lsum * vsc;
-      const int64_t hq = (int64_t)h * g + hh;
-      if (slot < 0) {
-        a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = o;
-      } else {
-        a.part_o[((int64_t)slot * a.n_q_heads + hq) * D + d] = o;
-        if (d == 0)
-          a.part_lse[(int64_t)slot * a.n_q_heads + hq] = (M + log2f(lsum)) * 0.69314718055994531f;
-      }
-    }
+  }
 
+  // the previous item's combine has finished reading this LDS
+  __syncthreads();
+  if (kg == 0) sm.m[wave][i] = m_run;
+  if (i == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * kg + r < g) sm.l[wave][4 * kg + r] = lacc[r];
+  }
+  store_wave_acc<128, true>(sm, wave, i, kg, g, acc);
+  __syncthreads();
+  finish_item<128>(a, sm, b, h, slot, vsc, 8.f, tid);
 }
 
 // ---- device-side planning: the host planner's arithmetic, per wave ----
@@ -642,10 +934,22 @@ __device__ inline uint32_t total_tiles(const int32_t* __restrict__ seq_lens, int
   return __builtin_amdgcn_readfirstlane(T);
 }
 
+// One item by the kernel variant's item routine.
+template <int D, bool FP8, bool PAGE, bool NATIVE>
+__device__ inline void run_item(const Args& a, const int32_t* __restrict__ block_table,
+                                TileSmem<D>& sm, int b, int k0, int k1, int slot, int L, int h,
+                                int wave, int lane, int tid) {
+  if constexpr (NATIVE)
+    process_item_fp8n(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
+  else
+    process_item<D, FP8, PAGE>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
+}
+
 // Workgroup (w, h): W * Hkv workgroups, kv head fastest.  Items come from the
 // host plan (DEVPLAN false) or are derived here from the device lengths with
-// the same rule (DEVPLAN true), in the same order.
-template <int D, bool FP8, bool DEVPLAN, bool PAGE>
+// the same rule (DEVPLAN true), in the same order.  NATIVE selects the
+// native-fp8 item routine (D = 128).
+template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE>
 __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
     Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ plan) {
@@ -667,8 +971,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
       const int b = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
                 slot = items[4 * it + 3];
       if ((unsigned)b >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
-      process_item<D, FP8, PAGE>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], h, wave, lane,
-                                 tid);
+      run_item<D, FP8, PAGE, NATIVE>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], h, wave,
+                                     lane, tid);
     }
   } else {
     // Every wave derives the same plan facts; they stay wave-uniform.
@@ -701,7 +1005,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
         const int k0 = (int)((int64_t)(lo - first) * a.tile_len);
         const int k1 = (int)min((int64_t)(hi - first) * a.tile_len, (int64_t)L);
         const int slot = k > 1 ? (int)(sb + (uint32_t)w - sp.owner(first)) : -1;
-        process_item<D, FP8, PAGE>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
+        run_item<D, FP8, PAGE, NATIVE>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane,
+                                       tid);
       }
       first_carry += ft;
       slot_carry += st;
@@ -876,7 +1181,7 @@ __global__ __launch_bounds__(64) void hda_plan_kernel(const int32_t* __restrict_
   }
 }
 
-template <int D, bool FP8, bool DEVPLAN, bool PAGE>
+template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE = false>
 hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_t stream,
                   void* split_event) {
   hipError_t e;
@@ -887,8 +1192,8 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
     if (e != hipSuccess) return e;
     a.q = q_prime;   // attention reads the normalised, rotated q
   }
-  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, DEVPLAN, PAGE>), dim3(grid), dim3(64 * kWaves),
-                     0, stream, a, a.block_table, a.seq_lens, a.plan);
+  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, DEVPLAN, PAGE, NATIVE>), dim3(grid),
+                     dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens, a.plan);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (split_event) {
@@ -906,8 +1211,10 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
 // Per-page scales are built for the fp8 cache only (check_params refuses
 // them for bf16).
 template <int D, bool DEVPLAN>
-hipError_t launch_d(const Args& a, bool fp8, int grid, bool pro, uint16_t* qp, hipStream_t st,
-                    void* ev) {
+hipError_t launch_d(const Args& a, bool fp8, bool native, int grid, bool pro, uint16_t* qp,
+                    hipStream_t st, void* ev) {
+  if constexpr (D == 128)
+    if (native) return launch<128, true, DEVPLAN, false, true>(a, grid, pro, qp, st, ev);
   if (!fp8) return launch<D, false, DEVPLAN, false>(a, grid, pro, qp, st, ev);
   return a.scale_mode == HDA_SCALE_PAGE ? launch<D, true, DEVPLAN, true>(a, grid, pro, qp, st, ev)
                                         : launch<D, true, DEVPLAN, false>(a, grid, pro, qp, st, ev);
@@ -943,7 +1250,16 @@ int check_params(const hda_params* p, const void* q, const void* k_pages, const 
   if (p->scale_mode != HDA_SCALE_TENSOR && (!p->k_scales || !p->v_scales))
     return HDA_ERR_INVALID_ARG;
   if (p->scale_mode == HDA_SCALE_PAGE && p->kv_dtype != HDA_KV_FP8_E4M3) return HDA_ERR_UNSUPPORTED;
+  if (p->math != HDA_MATH_BF16 && p->math != HDA_MATH_FP8) return HDA_ERR_INVALID_ARG;
+  if (p->v_layout != HDA_V_TOKEN_MAJOR && p->v_layout != HDA_V_DIM_MAJOR) return HDA_ERR_INVALID_ARG;
   if (p->reserved0 != 0) return HDA_ERR_INVALID_ARG;
+  // the native-fp8 kernel: fp8 cache, dim-major V, D 128, pages of >= 64
+  // tokens, tensor or head scales; dim-major V pages only with it
+  if (p->math == HDA_MATH_FP8 &&
+      (p->kv_dtype != HDA_KV_FP8_E4M3 || p->v_layout != HDA_V_DIM_MAJOR || p->head_dim != 128 ||
+       p->page_size < 64 || p->scale_mode == HDA_SCALE_PAGE))
+    return HDA_ERR_UNSUPPORTED;
+  if (p->v_layout == HDA_V_DIM_MAJOR && p->math != HDA_MATH_FP8) return HDA_ERR_UNSUPPORTED;
   return HDA_OK;
 }
 
@@ -973,6 +1289,7 @@ Args make_args(const hda_params* p, const void* q, void* k_pages, void* v_pages,
   a.k_new = static_cast<const uint16_t*>(p->k_new);
   a.v_new = static_cast<const uint16_t*>(p->v_new);
   a.scale_mode = p->scale_mode;
+  a.v_dim_major = p->v_layout == HDA_V_DIM_MAJOR;
   a.k_scales = p->scale_mode == HDA_SCALE_TENSOR ? nullptr : p->k_scales;
   a.v_scales = p->scale_mode == HDA_SCALE_TENSOR ? nullptr : p->v_scales;
   a.head_stride = p->page_size * D * elem;
@@ -1025,10 +1342,12 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
   a.tile_len = plan_host[2];
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
+  const bool native = p->math == HDA_MATH_FP8;
   const bool pro = p->prologue != 0;
-  hipError_t e = p->head_dim == 64
-                     ? launch_d<64, false>(a, fp8, (int)grid, pro, a.q_prime, hs, p->split_event)
-                     : launch_d<128, false>(a, fp8, (int)grid, pro, a.q_prime, hs, p->split_event);
+  hipError_t e =
+      p->head_dim == 64
+          ? launch_d<64, false>(a, fp8, native, (int)grid, pro, a.q_prime, hs, p->split_event)
+          : launch_d<128, false>(a, fp8, native, (int)grid, pro, a.q_prime, hs, p->split_event);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
 }
 
@@ -1059,10 +1378,12 @@ extern "C" int hda_decode_auto(const hda_params* p, const void* q, void* k_pages
   a.tile_len = tile_len;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
+  const bool native = p->math == HDA_MATH_FP8;
   const bool pro = p->prologue != 0;
-  hipError_t e = p->head_dim == 64
-                     ? launch_d<64, true>(a, fp8, (int)grid, pro, a.q_prime, hs, p->split_event)
-                     : launch_d<128, true>(a, fp8, (int)grid, pro, a.q_prime, hs, p->split_event);
+  hipError_t e =
+      p->head_dim == 64
+          ? launch_d<64, true>(a, fp8, native, (int)grid, pro, a.q_prime, hs, p->split_event)
+          : launch_d<128, true>(a, fp8, native, (int)grid, pro, a.q_prime, hs, p->split_event);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
 }
 

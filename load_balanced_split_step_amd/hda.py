@@ -32,6 +32,10 @@ HDA_SCALE_TENSOR = 0
 HDA_SCALE_HEAD = 1
 HDA_SCALE_PAGE = 2
 SCALE_MODES = {"tensor": HDA_SCALE_TENSOR, "head": HDA_SCALE_HEAD, "page": HDA_SCALE_PAGE}
+HDA_MATH_BF16 = 0
+HDA_MATH_FP8 = 1
+HDA_V_TOKEN_MAJOR = 0
+HDA_V_DIM_MAJOR = 1
 PLAN_HEADER_INTS = 8
 
 # every symbol include/hda.h declares
@@ -70,9 +74,11 @@ class hda_params(ctypes.Structure):
         ("workspace_bytes", ctypes.c_int64),
         ("split_event", ctypes.c_void_p),
         ("scale_mode", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("math", ctypes.c_int32),
         ("k_scales", ctypes.c_void_p),
         ("v_scales", ctypes.c_void_p),
+        ("v_layout", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
     ]
 
 
@@ -263,13 +269,18 @@ class DeviceBatch:
         self._ws = None
 
     @classmethod
-    def from_inputs(cls, inp, device="cuda:0"):
+    def from_inputs(cls, inp, device="cuda:0", math="bf16"):
+        """math "fp8": the native-fp8 product mode, with the V pages stored
+        dim-major ([page][Hkv][D][page_size]) on the device."""
         import torch
         w = inp["workload"]
+        vp = inp["v_pages"]
+        if math == "fp8":
+            vp = np.ascontiguousarray(np.swapaxes(vp, 2, 3))
         t = {
             "q": torch.from_numpy(inp["q"].view(np.int16)).to(device),
             "k_pages": torch.from_numpy(inp["k_pages"].view(np.uint8).reshape(-1)).to(device),
-            "v_pages": torch.from_numpy(inp["v_pages"].view(np.uint8).reshape(-1)).to(device),
+            "v_pages": torch.from_numpy(vp.view(np.uint8).reshape(-1)).to(device),
             "block_table": torch.from_numpy(inp["block_table"]).to(device),
             "seq_lens": torch.from_numpy(inp["seq_lens"]).to(device),
         }
@@ -279,7 +290,9 @@ class DeviceBatch:
                   num_pages=inp["k_pages"].shape[0],
                   kv_dtype=HDA_KV_FP8_E4M3 if w.kv_dtype == "fp8" else HDA_KV_BF16,
                   sm_scale=float(inp["sm_scale"]), k_scale=float(inp["k_scale"]),
-                  v_scale=float(inp["v_scale"]), prologue=0)
+                  v_scale=float(inp["v_scale"]), prologue=0,
+                  math=HDA_MATH_FP8 if math == "fp8" else HDA_MATH_BF16,
+                  v_layout=HDA_V_DIM_MAJOR if math == "fp8" else HDA_V_TOKEN_MAJOR)
         if w.prologue:
             for k in ("q_norm_w", "k_norm_w", "k_new", "v_new"):
                 t[k] = torch.from_numpy(inp[k].view(np.int16)).to(device)
@@ -290,6 +303,16 @@ class DeviceBatch:
             for k in ("k_scales", "v_scales"):
                 t[k] = torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.float32)).to(device)
         return cls(t, kw, device)
+
+    def v_pages_token_major(self, shape):
+        """The device V pool read back as numpy [NP, Hkv, ps, D] in the
+        token-major order, whatever the device layout (raw element bits)."""
+        dt = np.uint8 if self.kw["kv_dtype"] == HDA_KV_FP8_E4M3 else np.uint16
+        raw = self.t["v_pages"].cpu().numpy().view(dt)
+        if self.kw.get("v_layout") == HDA_V_DIM_MAJOR:
+            NP, Hkv, ps, D = shape
+            return np.swapaxes(raw.reshape(NP, Hkv, D, ps), 2, 3)
+        return raw.reshape(shape)
 
     def workspace(self, nbytes):
         import torch

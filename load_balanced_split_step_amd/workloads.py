@@ -28,7 +28,9 @@ Recipe (the pages use no dataset; these stand in for a serving batch):
     new-token k/v); large tensors are drawn in fixed-size chunks, each from
     its own spawned child stream, so the bytes do not depend on threading;
   * values ~ N(0, 1) in float32, then rounded to bf16 by torch's
-    round-to-nearest-even cast (a library conversion);
+    round-to-nearest-even cast (a library conversion); optionally the V
+    values of request b are multiplied by 2^-u_b, u_b ~ U(0, v_req_spread)
+    (a stress case for scale granularity, drawn from its own stream);
   * log-uniform lengths: floor(exp(U(ln lo, ln hi))) clamped to [lo, hi];
   * random placement: the pool holds exactly sum_b ceil(len_b / page) pages
     and logical page p of request b lives in physical page
@@ -56,7 +58,8 @@ BF16_NAN = np.uint16(0x7FC0)
 FP8_NAN = np.uint8(0x7F)
 
 # stream indices of SeedSequence(seed).spawn(...)
-_S_LENS, _S_PERM, _S_Q, _S_K, _S_V, _S_HEADSCALE, _S_NORMW, _S_NEW = range(8)
+_S_LENS, _S_PERM, _S_Q, _S_K, _S_V, _S_HEADSCALE, _S_NORMW, _S_NEW, _S_SLABSCALE = range(9)
+_N_STREAMS = 9
 
 
 @dataclass(frozen=True)
@@ -74,6 +77,7 @@ class Workload:
     head_scale: bool = False            # per-kv-head U(0.5, 2) on K and V
     prologue: bool = False              # new token written by the prologue
     kv_scale: str = "tensor"            # fp8 scale granularity: tensor, head, page
+    v_req_spread: float = 0.0           # per-request V magnitude 2^-U(0, spread)
     seed: int = 0
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
@@ -134,12 +138,12 @@ def draw_lengths(w: Workload, seed: int):
         assert len(lens) == w.batch
         return lens.astype(np.int32)
     lo, hi = w.len_range
-    r = _rng(np.random.SeedSequence(seed).spawn(8)[_S_LENS])
+    r = _rng(np.random.SeedSequence(seed).spawn(_N_STREAMS)[_S_LENS])
     u = r.uniform(math.log(lo), math.log(hi), size=w.batch)
     return np.clip(np.floor(np.exp(u)), lo, hi).astype(np.int32)
 
 
-def _draw_pool(ss, n_pages, w: Workload, head_scales, fp8_scale=None):
+def _draw_pool(ss, n_pages, w: Workload, head_scales, fp8_scale=None, slab_mult=None):
     """One page pool [n_pages, Hkv, ps, D], drawn in chunks of whole
     (page, head) slabs.
 
@@ -174,6 +178,8 @@ def _draw_pool(ss, n_pages, w: Workload, head_scales, fp8_scale=None):
         heads = np.arange(s0, s1) % Hkv
         if head_scales is not None:
             x *= head_scales[heads][:, None]
+        if slab_mult is not None:
+            x *= slab_mult[s0:s1][:, None]
         if amax_pass:
             am = np.abs(x).max(axis=1)
             return np.array([am[heads == h].max(initial=0.0) for h in range(Hkv)],
@@ -211,7 +217,7 @@ def make_inputs(w: Workload, seed: Optional[int] = None, poison: bool = True,
     k_norm_w [D] u16, k_new, v_new [B, Hkv, D] u16, rms_eps, rope_theta.
     """
     seed = w.seed if seed is None else seed
-    ss = np.random.SeedSequence(seed).spawn(8)
+    ss = np.random.SeedSequence(seed).spawn(_N_STREAMS)
     lens = (np.asarray(lengths, dtype=np.int32) if lengths is not None
             else draw_lengths(w, seed))
     B = len(lens)
@@ -235,6 +241,14 @@ def make_inputs(w: Workload, seed: Optional[int] = None, poison: bool = True,
         hs = _rng(ss[_S_HEADSCALE]).uniform(0.5, 2.0, size=(2, Hkv)).astype(np.float32)
         head_k, head_v = hs[0], hs[1]
 
+    mult_k = mult_v = None
+    if w.v_req_spread > 0:
+        # every page belongs to one request: its V slabs take that request's factor
+        u = _rng(ss[_S_SLABSCALE]).uniform(0.0, w.v_req_spread, size=B)
+        owner = np.empty(n_pages, dtype=np.int64)
+        for b in range(B):
+            owner[block_table[b, :pages_per[b]]] = b
+        mult_v = np.repeat(np.exp2(-u).astype(np.float32)[owner], Hkv)
     k_scale = v_scale = np.float32(1.0)
     k_scales = v_scales = None
     scale_mode = w.kv_scale
@@ -243,20 +257,22 @@ def make_inputs(w: Workload, seed: Optional[int] = None, poison: bool = True,
         raise ValueError("per-page scales are for an fp8 cache")
     k_ss, v_ss = ss[_S_K], ss[_S_V]
     if scale_mode == "page":
-        k_pages, k_scales = _draw_pool(k_ss, n_pages, w, head_k)
-        v_pages, v_scales = _draw_pool(v_ss, n_pages, w, head_v)
+        k_pages, k_scales = _draw_pool(k_ss, n_pages, w, head_k, slab_mult=mult_k)
+        v_pages, v_scales = _draw_pool(v_ss, n_pages, w, head_v, slab_mult=mult_v)
     else:
         if w.kv_dtype == "fp8" or scale_mode == "head":
-            ka = _draw_pool(k_ss, n_pages, w, head_k) / np.float32(448.0)
-            va = _draw_pool(v_ss, n_pages, w, head_v) / np.float32(448.0)
+            ka = _draw_pool(k_ss, n_pages, w, head_k, slab_mult=mult_k) / np.float32(448.0)
+            va = _draw_pool(v_ss, n_pages, w, head_v, slab_mult=mult_v) / np.float32(448.0)
             if scale_mode == "head":
                 k_scales, v_scales = ka.astype(np.float32), va.astype(np.float32)
             else:
                 k_scale, v_scale = np.float32(ka.max()), np.float32(va.max())
         k_pages = _draw_pool(k_ss, n_pages, w, head_k,
-                             fp8_scale=k_scales if scale_mode == "head" else k_scale)
+                             fp8_scale=k_scales if scale_mode == "head" else k_scale,
+                             slab_mult=mult_k)
         v_pages = _draw_pool(v_ss, n_pages, w, head_v,
-                             fp8_scale=v_scales if scale_mode == "head" else v_scale)
+                             fp8_scale=v_scales if scale_mode == "head" else v_scale,
+                             slab_mult=mult_v)
 
     q = _bf16_bits(_rng(ss[_S_Q]).standard_normal((B, Hq, D), dtype=np.float32))
 

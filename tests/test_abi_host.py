@@ -211,6 +211,18 @@ def test_decode_argument_errors(lib):
     assert _decode_status(lib, _params(scale_mode=E.HDA_SCALE_PAGE, k_scales=FAKE + 0x7000,
                                        v_scales=FAKE + 0x8000), plan) == E.HDA_ERR_UNSUPPORTED
     assert _decode_status(lib, _params(reserved0=1), plan) == E.HDA_ERR_INVALID_ARG
+    # native-fp8 products and dim-major V pages
+    fp8n = dict(kv_dtype=E.HDA_KV_FP8_E4M3, head_dim=128, page_size=64, math=E.HDA_MATH_FP8,
+                v_layout=E.HDA_V_DIM_MAJOR)
+    assert _decode_status(lib, _params(math=2), plan) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(v_layout=2), plan) == E.HDA_ERR_INVALID_ARG
+    assert _decode_status(lib, _params(**dict(fp8n, kv_dtype=E.HDA_KV_BF16)), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(**dict(fp8n, v_layout=0)), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(**dict(fp8n, head_dim=64)), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(**dict(fp8n, page_size=32)), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(**dict(fp8n, scale_mode=E.HDA_SCALE_PAGE, k_scales=FAKE + 0x7000,
+                                              v_scales=FAKE + 0x8000)), plan) == E.HDA_ERR_UNSUPPORTED
+    assert _decode_status(lib, _params(v_layout=E.HDA_V_DIM_MAJOR), plan) == E.HDA_ERR_UNSUPPORTED
     for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.hda_status_string(s)
 
