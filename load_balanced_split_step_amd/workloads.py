@@ -58,8 +58,8 @@ BF16_NAN = np.uint16(0x7FC0)
 FP8_NAN = np.uint8(0x7F)
 
 # stream indices of SeedSequence(seed).spawn(...)
-_S_LENS, _S_PERM, _S_Q, _S_K, _S_V, _S_HEADSCALE, _S_NORMW, _S_NEW, _S_SLABSCALE = range(9)
-_N_STREAMS = 9
+_S_LENS, _S_PERM, _S_Q, _S_K, _S_V, _S_HEADSCALE, _S_NORMW, _S_NEW, _S_SLABSCALE, _S_QLEN = range(10)
+_N_STREAMS = 10
 
 
 @dataclass(frozen=True)
@@ -78,6 +78,10 @@ class Workload:
     prologue: bool = False              # new token written by the prologue
     kv_scale: str = "tensor"            # fp8 scale granularity: tensor, head, page
     v_req_spread: float = 0.0           # per-request V magnitude 2^-U(0, spread)
+    # multi-token queries (prefill / chunked prefill): q_len per request, or
+    # drawn uniformly from q_len_range; the cache lengths include them
+    q_lens: Optional[Tuple[int, ...]] = None
+    q_len_range: Optional[Tuple[int, int]] = None
     seed: int = 0
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
@@ -85,6 +89,10 @@ class Workload:
     @property
     def group(self):
         return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def prefill(self):
+        return self.q_lens is not None or self.q_len_range is not None
 
     def with_(self, **kw):
         return replace(self, **kw)
@@ -206,12 +214,26 @@ def _draw_pool(ss, n_pages, w: Workload, head_scales, fp8_scale=None, slab_mult=
     return bits
 
 
+def draw_q_lens(w: Workload, seed: int, kv_lens):
+    """Query rows per request for a multi-token workload (<= the cache length)."""
+    if w.q_lens is not None:
+        q = np.array(w.q_lens, dtype=np.int64)
+        assert len(q) == len(kv_lens)
+    else:
+        lo, hi = w.q_len_range
+        r = _rng(np.random.SeedSequence(seed).spawn(_N_STREAMS)[_S_QLEN])
+        q = r.integers(lo, hi + 1, size=len(kv_lens))
+    return np.minimum(q, np.asarray(kv_lens, dtype=np.int64)).astype(np.int32)
+
+
 def make_inputs(w: Workload, seed: Optional[int] = None, poison: bool = True,
-                lengths: Optional[Sequence[int]] = None):
+                lengths: Optional[Sequence[int]] = None,
+                q_lens: Optional[Sequence[int]] = None):
     """Draw one decode batch.  Returns a dict of numpy arrays and scalars:
 
     q [B, Hq, D] u16 (bf16), k_pages / v_pages [NP, Hkv, ps, D] (u16 bf16 or
-    u8 fp8), block_table [B, max_pages] i32, seq_lens [B] i32, sm_scale,
+    u8 fp8), block_table [B, max_pages] i32, seq_lens [B] i32 (cache lengths),
+    for a multi-token workload q_lens [B] i32 and q packed [sum q_lens, Hq, D], sm_scale,
     k_scale, v_scale (float32), scale_mode with k_scales / v_scales (None,
     float32 [Hkv] or [NP, Hkv]), and for the prologue workload q_norm_w,
     k_norm_w [D] u16, k_new, v_new [B, Hkv, D] u16, rms_eps, rope_theta.
@@ -274,13 +296,22 @@ def make_inputs(w: Workload, seed: Optional[int] = None, poison: bool = True,
                              fp8_scale=v_scales if scale_mode == "head" else v_scale,
                              slab_mult=mult_v)
 
-    q = _bf16_bits(_rng(ss[_S_Q]).standard_normal((B, Hq, D), dtype=np.float32))
+    qlens = None
+    if w.prefill or q_lens is not None:
+        qlens = (np.minimum(np.asarray(q_lens, dtype=np.int32), lens) if q_lens is not None
+                 else draw_q_lens(w, seed, lens))
+        n_q = int(qlens.sum())
+    else:
+        n_q = B
+    q = _bf16_bits(_rng(ss[_S_Q]).standard_normal((n_q, Hq, D), dtype=np.float32))
 
     inp = dict(workload=w, seed=seed, q=q, k_pages=k_pages, v_pages=v_pages,
                block_table=block_table, seq_lens=lens.astype(np.int32),
                sm_scale=np.float32(1.0 / math.sqrt(D)),
                k_scale=k_scale, v_scale=v_scale, kv_dtype=w.kv_dtype,
                scale_mode=scale_mode, k_scales=k_scales, v_scales=v_scales)
+    if qlens is not None:
+        inp["q_lens"] = qlens
 
     if w.prologue:
         r = _rng(ss[_S_NORMW])

@@ -47,6 +47,7 @@ from .prologue import (rms_norm, rope, prologue_step, bf16_encode, write_new_tok
                        slot_scales)
 from .fp8_math import (quantize_q_fp8, dequantized_q, attention_fp8q,
                        weight_rounding_bounds)
+from .prefill import prefill_reference, prefill_rows, q_offsets
 
 __all__ = [
     "bf16_to_f64", "fp8_decode", "fp8_encode", "FP8_MAX",
@@ -55,5 +56,5 @@ __all__ = [
     "attention_bruteforce", "split_merge_reference", "decode_kv", "row_scales",
     "SCALE_MODES", "rms_norm", "rope", "prologue_step", "bf16_encode", "write_new_token",
     "slot_scales", "quantize_q_fp8", "dequantized_q", "attention_fp8q",
-    "weight_rounding_bounds",
+    "weight_rounding_bounds", "prefill_reference", "prefill_rows", "q_offsets",
 ]
