@@ -140,6 +140,150 @@ def cpu_baseline(inp, budget_s):
                       f"numpy fp64, BLAS threads {threads}"}
 
 
+def cpu_baseline_prefill(inp, budget_s):
+    """The fp64 prefill oracle, as it stands, on a bounded sample: whole
+    requests, shortest cache first, until the time budget is spent.  Rate =
+    KV bytes each query row reads (its causal prefix) per second."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    w = inp["workload"]
+    order = np.argsort(inp["seq_lens"], kind="stable")
+    off = oracle.q_offsets(inp["q_lens"])
+    elem = 1 if w.kv_dtype == "fp8" else 2
+    done, kvb, t0 = 0, 0, time.perf_counter()
+    for b in order.tolist() * 8:
+        sub = dict(block_table=inp["block_table"][[b]], seq_lens=inp["seq_lens"][[b]],
+                   q_lens=inp["q_lens"][[b]])
+        oracle.prefill_reference(oracle.bf16_to_f64(inp["q"][off[b]:off[b + 1]]), inp["k_pages"],
+                                 inp["v_pages"], sub["block_table"], sub["seq_lens"],
+                                 sub["q_lens"], w.kv_dtype, float(inp["sm_scale"]),
+                                 float(inp["k_scale"]), float(inp["v_scale"]))
+        L, n = int(inp["seq_lens"][b]), int(inp["q_lens"][b])
+        kvb += sum(L - n + r + 1 for r in range(n)) * w.n_kv_heads * w.head_dim * 2 * elem
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    secs = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(kvb / secs / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} request passes (shortest caches first) in {secs:.1f} s; "
+                      f"numpy fp64, BLAS threads {threads}"}
+
+
+def bench_prefill(args, w, inp):
+    """Multi-token step: row blocks and plan on the host from the current
+    lengths, async upload of both from pinned memory, hda_prefill."""
+    import numpy as np
+    import torch
+    import load_balanced_split_step_amd.hda as hda
+    lens, qlens = inp["seq_lens"], inp["q_lens"]
+    dev = hda.DeviceBatch.from_inputs(inp, device="cuda:0")
+    copies = [(dev.t["k_pages"], dev.t["v_pages"])]
+    for _ in range(max(0, args.copies - 1)):
+        copies.append((dev.t["k_pages"].clone(), dev.t["v_pages"].clone()))
+    qb = hda.hda_prefill_rows_per_block(w.n_q_heads, w.n_kv_heads)
+    rows, row_lens = hda.hda_prefill_rows(qlens, lens, qb)
+    tl, W = hda.launch_config(row_lens, w.n_kv_heads)
+    tl = args.tile_len or tl
+    W = args.workgroups or W
+    R = len(rows)
+    cap = hda.hda_plan_capacity(R, W)
+    NB = 3
+    pin_plan = [torch.empty(cap, dtype=torch.int32).pin_memory() for _ in range(NB)]
+    pin_rows = [torch.empty(4 * R, dtype=torch.int32).pin_memory() for _ in range(NB)]
+    d_plan = [torch.empty(cap, dtype=torch.int32, device="cuda:0") for _ in range(NB)]
+    d_rows = [torch.empty(4 * R, dtype=torch.int32, device="cuda:0") for _ in range(NB)]
+    n_q = int(qlens.sum())
+    out = torch.empty((n_q, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    done_ev = [torch.cuda.Event() for _ in range(NB)]
+    used = [False] * NB
+    params = dev.prefill_params(hda.hda_plan(row_lens, tl, W))
+
+    def step(s, events=None):
+        j = s % NB
+        if used[j]:
+            done_ev[j].synchronize()
+        r, rl = hda.hda_prefill_rows(qlens, lens, qb)                    # row blocks
+        pin_rows[j].numpy()[:] = r.reshape(-1)
+        n = hda.hda_plan_into(rl, tl, W, pin_plan[j].numpy())           # the decode planner
+        d_rows[j].copy_(pin_rows[j], non_blocking=True)
+        d_plan[j][:n].copy_(pin_plan[j][:n], non_blocking=True)
+        done_ev[j].record(stream)
+        used[j] = True
+        kp, vp = copies[s % len(copies)]
+        if events is not None:
+            events[0].record(stream)
+            params.split_event = events[1].cuda_event
+        else:
+            params.split_event = None
+        hda.hda_prefill(params, dev.t["q"], kp, vp, dev.t["block_table"], dev.t["seq_lens"], n_q,
+                        pin_rows[j].numpy().reshape(R, 4), d_rows[j], pin_plan[j].numpy()[:n],
+                        d_plan[j], out, stream)
+        if events is not None:
+            events[2].record(stream)
+        return n
+
+    for s in range(args.warmup):
+        plan_len = step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        plan_len = step(args.warmup + s)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    n_prof = max(10, min(args.steps, 50))
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(n_prof)]
+    for e in evs:
+        for x in e:
+            x.record(stream)
+    torch.cuda.synchronize()
+    for s in range(n_prof):
+        step(s, evs[s])
+    torch.cuda.synchronize()
+    kmean = sum(a.elapsed_time(b) for a, b, _ in evs) / n_prof
+    dmean = sum(a.elapsed_time(c) for a, _, c in evs) / n_prof
+    elem = 1 if w.kv_dtype == "fp8" else 2
+    per_tok = w.n_kv_heads * w.head_dim * 2 * elem
+    unique_kv = int(lens.astype(np.int64).sum()) * per_tok
+    # this design's minimum for the tile kernel: each row block reads its
+    # causal prefix once, plus q, out and the tables
+    reread_kv = int(np.asarray(row_lens, np.int64).sum()) * per_tok
+    algo = reread_kv + n_q * w.n_q_heads * w.head_dim * (2 + 4) + R * 16 + plan_len * 4
+    achieved = algo / (kmean * 1e-3) / 1e9
+    log(f"prefill step {ms_per_step * 1e3:.1f} us wall, kernels {dmean * 1e3:.1f} us, "
+        f"tile kernel {kmean * 1e3:.1f} us; {R} row blocks of <= {qb} rows, "
+        f"KV read {reread_kv / unique_kv:.2f}x the cache")
+    res = {
+        "metric": "multi-token attention: query rows/s (row blocks through the decode planner), 1 GPU",
+        "value": round(n_q / (ms_per_step * 1e-3), 1),
+        "unit": "query rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {len(lens)} requests, {n_q} query rows over "
+                               f"{int(lens.sum())} cached tokens",
+                   "batch": int(len(lens)), "query_rows": n_q, "kv_tokens": int(lens.sum()),
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "page_size": w.page_size, "kv_dtype": w.kv_dtype, "rows_per_block": qb,
+                   "row_blocks": R, "tile_len": tl, "n_workgroups": W},
+        "us_per_step": {"wall": round(ms_per_step * 1e3, 2), "kernels_mean": round(dmean * 1e3, 2),
+                        "tile_kernel_mean": round(kmean * 1e3, 2)},
+        "kv_gbs_unique": round(unique_kv / (dmean * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": algo,
+                     "kernel": "hda_decode_kernel, multi-token rows (HIP events on its stream)"},
+    }
+    if not args.no_cpu:
+        log("timing the fp64 prefill oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline_prefill(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -158,6 +302,9 @@ def main():
     t = time.time()
     inp = make_inputs(w)
     log(f"generated {args.workload} inputs in {time.time() - t:.1f}s")
+    if w.prefill:
+        bench_prefill(args, w, inp)
+        return
     lens = inp["seq_lens"]
     dev = hda.DeviceBatch.from_inputs(inp, device="cuda:0", math=args.math)
     copies = [(dev.t["k_pages"], dev.t["v_pages"])]

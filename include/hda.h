@@ -283,6 +283,76 @@ int64_t hda_workspace_bytes_bound(int32_t batch, int32_t n_workgroups,
 int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
                     int32_t n_workgroups, int32_t* plan, int64_t capacity, void* stream);
 
+/*
+ * ---- Multi-token queries (prefill, chunked prefill, speculative checks) ----
+ *
+ * The backend's attention also serves the prefill phase (the pages report
+ * lower time to first token: remio.ai page, section "Por qué Tencent HPC
+ * importa para el serving de modelos en línea") but describe no prefill
+ * algorithm.  Here: request b brings q_len_b new query rows whose K and V are
+ * already in the cache, which holds kv_len_b >= q_len_b tokens; row r sits at
+ * position kv_len_b - q_len_b + r and attends causally to tokens 0..pos.
+ * q and out are packed request after request: [sum q_len][Hq][D].
+ *
+ * The rows of each request are grouped into blocks of
+ * hda_prefill_rows_per_block() rows, whose (row, q head) pairs fill the 16
+ * matrix-core columns the decode kernel gives one kv head's q heads.  Each
+ * block enters the decode tile planner as one "request" whose length is its
+ * causal extent, so hda_plan is used unchanged (its batch = the number of
+ * blocks) and a block's partial results are merged as a request's are.
+ */
+
+/* Rows per block: 16 / (Hq / Hkv), or -1 for a group above 16. */
+int32_t hda_prefill_rows_per_block(int32_t n_q_heads, int32_t n_kv_heads);
+
+/*
+ * The row blocks of a batch.  q_lens, kv_lens [host] int32[batch] with
+ * 1 <= q_len <= kv_len.  Writes rows [host] int32[n][4] = (request, packed
+ * index of the first row, rows in the block, position of the first row) and
+ * row_lens [host] int32[n] (position of the last row + 1: the lengths to give
+ * hda_plan), blocks in request order.  *n_rows receives n (also when the
+ * buffers are NULL or smaller than capacity, which returns HDA_ERR_CAPACITY).
+ * Errors: HDA_ERR_INVALID_ARG, HDA_ERR_CAPACITY.
+ */
+int hda_prefill_rows(const int32_t* q_lens, const int32_t* kv_lens, int32_t batch,
+                     int32_t rows_per_block, int32_t* rows, int32_t* row_lens,
+                     int64_t capacity, int64_t* n_rows);
+
+/* Workspace bytes for hda_prefill with this plan: partial outputs float32
+ * [P][rows_per_block][Hq][D], then partial log-sum-exps float32
+ * [P][rows_per_block][Hq], each region aligned to 256 bytes.  -1 on a
+ * malformed header or sizes. */
+int64_t hda_prefill_workspace_bytes(const int32_t* plan, int64_t plan_len, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t head_dim);
+
+/*
+ * One multi-token attention step enqueued on `stream`: the tile kernel over
+ * the plan's items (each covering a row block's KV range), then the
+ * log-sum-exp merge of split blocks.  Asynchronous; allocates nothing.
+ *
+ *   p            as for hda_decode, with batch = B requests; prologue 0,
+ *                math HDA_MATH_BF16, v_layout HDA_V_TOKEN_MAJOR (other
+ *                settings: HDA_ERR_UNSUPPORTED); all scale modes
+ *   q            [device] bf16 [n_q][Hq][D], packed
+ *   block_table  [device] int32 [B][max_pages_per_req]
+ *   kv_lens      [device] int32 [B], cache lengths (new rows included)
+ *   n_q          total query rows (sum of q_len)
+ *   rows_host,
+ *   rows_dev     [host] and [device] copies of hda_prefill_rows' blocks,
+ *                n_rows = the plan's batch
+ *   plan_host,
+ *   plan_dev     hda_plan(row_lens, n_rows, tile_len, W), as for hda_decode
+ *   out          [device] float32 [n_q][Hq][D]
+ * Errors (host, before any launch): HDA_ERR_INVALID_ARG (incl. a block out
+ * of range or with more rows than hda_prefill_rows_per_block),
+ * HDA_ERR_UNSUPPORTED, HDA_ERR_BAD_PLAN, HDA_ERR_WORKSPACE; HDA_ERR_HIP if a
+ * launch fails.
+ */
+int hda_prefill(const hda_params* p, const void* q, const void* k_pages, const void* v_pages,
+                const int32_t* block_table, const int32_t* kv_lens, int32_t n_q,
+                const int32_t* rows_host, const int32_t* rows_dev, const int32_t* plan_host,
+                const int32_t* plan_dev, int64_t plan_len, float* out, void* stream);
+
 /* Static description of a status code. */
 const char* hda_status_string(int status);
 

@@ -60,6 +60,8 @@ struct Args {
   float* part_lse;
   uint16_t* q_prime;     // workspace copy of the prologue's q' (bf16 [B][Hq][D])
   int32_t* req_slots;    // device-planned launches: per request (first slot, slot count)
+  const int32_t* rows;   // multi-token launches: row blocks [n][4] (request, first packed
+                         // row, rows, position of the first row)
   const uint16_t* q_norm_w;
   const uint16_t* k_norm_w;
   const uint16_t* k_new;
@@ -73,6 +75,8 @@ struct Args {
   int32_t page_size, log2_ps, max_pages;
   int32_t n_wg, n_items, n_parts;
   int32_t tile_len;      // device-planned launches only
+  int32_t qb;            // query rows per block: partial slots hold qb x Hq rows (1 for decode)
+  int32_t n_req;         // requests (block-table rows); multi-token launches
   int32_t scale_mode;    // HDA_SCALE_*
   int32_t v_dim_major;   // V pages [page][Hkv][D][page_size] instead of [..][page_size][D]
   float qk_scale_log2;   // sm_scale * k_scale * log2(e)
@@ -282,10 +286,15 @@ __device__ inline void issue_chunk(Chunk<D, FP8>& ch, const __amdgpu_buffer_rsrc
 // weights its page's V factor: the MFMA gets bf16(p * vs), and the running
 // sum adds that rounded weight divided by vs, so the normaliser counts
 // exactly the weight each V row received.
-template <int D, bool FP8, bool PAGE>
+//
+// With PF (multi-token rows), column i also stops at its own causal limit
+// lim (lim_min: the smallest over the columns, wave-uniform), and a column
+// whose tokens are all masked so far keeps m = -inf without producing NaN.
+template <int D, bool FP8, bool PAGE, bool PF>
 __device__ inline void compute_chunk(const Chunk<D, FP8>& ch, const bf16x8 (&qop)[Geo<D, FP8>::STEPS],
-                                     int c, int k0, int k1, float qk_scale_log2, int kg,
-                                     float& m_run, float& l_run, f32x4 (&acc)[Geo<D, FP8>::DPL]) {
+                                     int c, int k0, int k1, int lim, int lim_min,
+                                     float qk_scale_log2, int kg, float& m_run, float& l_run,
+                                     f32x4 (&acc)[Geo<D, FP8>::DPL]) {
   using G = Geo<D, FP8>;
   f32x4 sacc[2];
 #pragma unroll
@@ -305,11 +314,12 @@ __device__ inline void compute_chunk(const Chunk<D, FP8>& ch, const bf16x8 (&qop
 #pragma unroll
   for (int j = 0; j < 8; ++j) sc[j] = sacc[j >> 2][j & 3] * qs[j >> 2];
   const int t0 = c * kChunk;
-  if (t0 < k0 || t0 + kChunk > k1) {  // partial chunk: mask tokens outside [k0, k1)
+  // partial chunk: mask tokens outside [k0, k1) (and, for PF, past lim)
+  if (t0 < k0 || t0 + kChunk > k1 || (PF && t0 + kChunk - 1 > lim_min)) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = t0 + 16 * (j >> 2) + 4 * kg + (j & 3);
-      if (t < k0 || t >= k1) sc[j] = -INFINITY;
+      if (t < k0 || t >= k1 || (PF && t > lim)) sc[j] = -INFINITY;
     }
   }
   float mx = sc[0];
@@ -317,7 +327,10 @@ __device__ inline void compute_chunk(const Chunk<D, FP8>& ch, const bf16x8 (&qop
   for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
+  const float m_max = fmaxf(m_run, mx);
+  // a column with every token masked so far: subtract 0, so that its weights
+  // and alpha come out 0 (not NaN) and its state stays empty
+  const float m_new = (PF && m_max == -INFINITY) ? 0.f : m_max;
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
   bf16x8 pop;
   float psum = 0.f;
@@ -338,7 +351,7 @@ __device__ inline void compute_chunk(const Chunk<D, FP8>& ch, const bf16x8 (&qop
     }
   }
   l_run = l_run * alpha + psum;
-  m_run = m_new;
+  m_run = m_max;
   if (__ballot(alpha != 1.0f) != 0) {
     float ar[4];
 #pragma unroll
@@ -382,16 +395,17 @@ struct TileSmem {
   __attribute__((aligned(16))) uint16_t q[kMaxGroup][D];
 };
 
-// One wave's PV accumulators into LDS: lane (i, kg) holds q head 4*kg + r in
-// acc[nb][r], for head dim DPL*i + nb (BLOCKED false) or 16*nb + i (true).
+// One wave's PV accumulators into LDS: lane (i, kg) holds column 4*kg + r
+// (a q head; for multi-token rows a (row, q head) pair) in acc[nb][r], for
+// head dim DPL*i + nb (BLOCKED false) or 16*nb + i (true).
 template <int D, bool BLOCKED = false>
-__device__ inline void store_wave_acc(TileSmem<D>& sm, int wave, int i, int kg, int g,
+__device__ inline void store_wave_acc(TileSmem<D>& sm, int wave, int i, int kg, int ncols,
                                       const f32x4 (&acc)[D / 16]) {
   constexpr int DPL = D / 16;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int hh = 4 * kg + r;
-    if (hh < g) {
+    if (hh < ncols) {
       if constexpr (BLOCKED) {
 #pragma unroll
         for (int nb = 0; nb < DPL; ++nb) sm.acc[wave][hh][16 * nb + i] = acc[nb][r];
@@ -406,34 +420,42 @@ __device__ inline void store_wave_acc(TileSmem<D>& sm, int wave, int i, int kg, 
   }
 }
 
-// Cross-wave combine of one item from LDS (per q head: running max m,
+// Cross-wave combine of one item from LDS (per column: running max m,
 // weight sum l in units of 2^lse_shift, unnormalised output), then the
 // output row (slot -1) or the partial and its natural-log log-sum-exp.
+// Column c is packed row qrow0 + c / g, q head h*g + c % g (decode: one row,
+// qrow0 = the request).  A column with no unmasked token in this item (only
+// possible for multi-token rows) gives o = 0 and lse = -inf, which the merge
+// weighs by zero.
 template <int D>
-__device__ inline void finish_item(const Args& a, const TileSmem<D>& sm, int b, int h, int slot,
-                                   float vsc, float lse_shift, int tid) {
+__device__ inline void finish_item(const Args& a, const TileSmem<D>& sm, int qrow0, int ncols,
+                                   int h, int slot, float vsc, float lse_shift, int tid) {
   const int g = a.group;
-  for (int idx = tid; idx < g * D; idx += 64 * kWaves) {
+  for (int idx = tid; idx < ncols * D; idx += 64 * kWaves) {
     const int hh = idx / D, d = idx - hh * D;
     float M = sm.m[0][hh];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][hh]);
     float lsum = 0.f, o = 0.f;
+    if (M != -INFINITY) {
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float wt = __builtin_amdgcn_exp2f(sm.m[ww][hh] - M);
-      lsum += wt * sm.l[ww][hh];
-      o += wt * sm.acc[ww][hh][d];
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float wt = __builtin_amdgcn_exp2f(sm.m[ww][hh] - M);
+        lsum += wt * sm.l[ww][hh];
+        o += wt * sm.acc[ww][hh][d];
+      }
     }
-    o = o / lsum * vsc;
-    const int64_t hq = (int64_t)h * g + hh;
+    o = lsum > 0.f ? o / lsum * vsc : 0.f;
+    const int qr = hh / g;
+    const int64_t hq = (int64_t)h * g + (hh - qr * g);
     if (slot < 0) {
-      a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = o;
+      a.out[((int64_t)(qrow0 + qr) * a.n_q_heads + hq) * D + d] = o;
     } else {
-      a.part_o[((int64_t)slot * a.n_q_heads + hq) * D + d] = o;
+      const int64_t prow = ((int64_t)slot * a.qb + qr) * a.n_q_heads + hq;
+      a.part_o[prow * D + d] = o;
       if (d == 0)
-        a.part_lse[(int64_t)slot * a.n_q_heads + hq] =
-            (M + log2f(lsum) - lse_shift) * 0.69314718055994531f;
+        a.part_lse[prow] = lsum > 0.f ? (M + log2f(lsum) - lse_shift) * 0.69314718055994531f
+                                      : -INFINITY;
     }
   }
 }
@@ -527,10 +549,15 @@ __global__ __launch_bounds__(256) void hda_prologue_kernel(Args a,
 
 // One plan item (b, [k0, k1), slot) for kv head h: the waves stream the
 // item's chunks, combine in LDS, and write the output (slot -1) or a partial.
-template <int D, bool FP8, bool PAGE>
+//
+// Multi-token rows (PF): the item covers nq query rows of request b starting
+// at packed row qrow0 and position pos0; column i is row i / g, q head
+// h*g + i % g, with causal limit pos0 + i / g.  Decode is nq = 1, qrow0 = b.
+template <int D, bool FP8, bool PAGE, bool PF>
 __device__ inline void process_item(const Args& a, const int32_t* __restrict__ block_table,
                                     TileSmem<D>& sm, int b, int k0, int k1, int slot, int L,
-                                    int h, int wave, int lane, int tid) {
+                                    int qrow0, int nq, int pos0, int h, int wave, int lane,
+                                    int tid) {
   using G = Geo<D, FP8>;
   const int i = lane & 15, kg = lane >> 4;
   const int g = a.group;
@@ -541,7 +568,11 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
     qk *= a.k_scales[h];
     vsc *= a.v_scales[h];
   }
-    const int64_t qrow0 = ((int64_t)b * a.n_q_heads + (int64_t)h * g) * D;
+    const int qr = PF ? i / g : 0;
+    const int hh = i - qr * g;
+    const bool col_live = PF ? qr < nq : i < g;
+    const int lim = col_live ? pos0 + qr : 0x7fffffff;   // causal limit of column i
+    const int64_t qbase = ((int64_t)(qrow0 + qr) * a.n_q_heads + (int64_t)h * g + hh) * D;
 
     // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
     const int c_last = (k1 - 1) / kChunk;
@@ -550,12 +581,12 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
     Chunk<D, FP8> ring[G::NBUF];
     __amdgpu_buffer_rsrc_t kr[2], vr[2];
 
-    // q operand (MFMA B): lane (i, kg) holds q head i, dims qk_dim(s, kg) + 0..7.
+    // q operand (MFMA B): lane (i, kg) holds column i, dims qk_dim(s, kg) + 0..7.
     bf16x8 qop[G::STEPS];
 #pragma unroll
     for (int s2 = 0; s2 < G::STEPS; ++s2) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (i < g) v = *reinterpret_cast<const u32x4*>(a.q + qrow0 + (int64_t)i * D + qk_dim<FP8>(s2, kg));
+      if (col_live) v = *reinterpret_cast<const u32x4*>(a.q + qbase + qk_dim<FP8>(s2, kg));
       qop[s2] = __builtin_bit_cast(bf16x8, v);
     }
 
@@ -583,7 +614,8 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
           chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr, ring[nx]);
           issue_chunk<D, FP8>(ring[nx], kr, vr, i, kg);
           __builtin_amdgcn_sched_barrier(0);
-          compute_chunk<D, FP8, PAGE>(ring[k], qop, c, k0, k1, qk, kg, m_run, l_run, acc);
+          compute_chunk<D, FP8, PAGE, PF>(ring[k], qop, c, k0, k1, lim, pos0, qk, kg, m_run,
+                                          l_run, acc);
           c += kWaves;
           if (c > c_last) {
             done = true;
@@ -604,9 +636,10 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
       sm.m[wave][i] = m_run;
       sm.l[wave][i] = l_tot;
     }
-    store_wave_acc<D>(sm, wave, i, kg, g, acc);
+    const int ncols = PF ? nq * g : g;
+    store_wave_acc<D>(sm, wave, i, kg, ncols, acc);
     __syncthreads();
-    finish_item<D>(a, sm, b, h, slot, vsc, 0.f, tid);
+    finish_item<D>(a, sm, qrow0, ncols, h, slot, vsc, 0.f, tid);
 }
 
 // ---- native-fp8 products: fp8 cache, dim-major V pages, D = 128 ----
@@ -864,7 +897,7 @@ __device__ inline void process_item_fp8n(const Args& a, const int32_t* __restric
   }
   store_wave_acc<128, true>(sm, wave, i, kg, g, acc);
   __syncthreads();
-  finish_item<128>(a, sm, b, h, slot, vsc, 8.f, tid);
+  finish_item<128>(a, sm, b, g, h, slot, vsc, 8.f, tid);
 }
 
 // ---- device-side planning: the host planner's arithmetic, per wave ----
@@ -942,14 +975,15 @@ __device__ inline void run_item(const Args& a, const int32_t* __restrict__ block
   if constexpr (NATIVE)
     process_item_fp8n(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
   else
-    process_item<D, FP8, PAGE>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
+    process_item<D, FP8, PAGE, false>(a, block_table, sm, b, k0, k1, slot, L, b, 1, L - 1, h,
+                                      wave, lane, tid);
 }
 
 // Workgroup (w, h): W * Hkv workgroups, kv head fastest.  Items come from the
 // host plan (DEVPLAN false) or are derived here from the device lengths with
 // the same rule (DEVPLAN true), in the same order.  NATIVE selects the
 // native-fp8 item routine (D = 128).
-template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE>
+template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE, bool PF = false>
 __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
     Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ plan) {
@@ -963,7 +997,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
   const int h = blockIdx.x % a.n_kv_heads;
   const int w = blockIdx.x / a.n_kv_heads;
 
-  if constexpr (!DEVPLAN) {
+  if constexpr (PF) {
+    // multi-token rows: a plan "request" is a row block
+    const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
+    const int32_t* items = wg_ptr + a.n_wg + 1;
+    const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
+    const int32_t* __restrict__ rows = a.rows;
+    for (int it = it_begin; it < it_end; ++it) {
+      const int rho = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
+                slot = items[4 * it + 3];
+      if ((unsigned)rho >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
+      const int b = rows[4 * rho], qrow0 = rows[4 * rho + 1], nq = rows[4 * rho + 2],
+                pos0 = rows[4 * rho + 3];
+      process_item<D, FP8, PAGE, true>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], qrow0,
+                                       nq, pos0, h, wave, lane, tid);
+    }
+  } else if constexpr (!DEVPLAN) {
     const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
     const int32_t* items = wg_ptr + a.n_wg + 1;
     const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
@@ -1026,14 +1075,26 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
 constexpr int kMergeEarly = 32;    // partial rows loaded before the weights
 constexpr int kMergeStage = 512;   // slot weights staged in LDS per pass
 
-template <int D, bool DEVPLAN>
+//
+// Multi-token launches (PF): workgroup (row block, row in block, q head);
+// slot s holds qb x Hq partial rows, and the output row is the block's
+// packed row.  A partial with lse = -inf (a column with no token in that
+// item) has weight zero and o = 0.
+template <int D, bool DEVPLAN, bool PF = false>
 __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __restrict__ plan,
                                                       const int32_t* __restrict__ seq_lens) {
   __shared__ float sm_w[kMergeStage];
   __shared__ float sm_red[2][D / 64];
   const int d = threadIdx.x, lane = d & 63, wave = d >> 6;
-  const int b = blockIdx.x / a.n_q_heads, hq = blockIdx.x % a.n_q_heads;
-  int s0, s1;
+  const int hq = blockIdx.x % a.n_q_heads;
+  const int rb = blockIdx.x / a.n_q_heads;          // request (decode) or block * qb + row
+  const int b = PF ? rb / a.qb : rb, qr = PF ? rb - b * a.qb : 0;
+  int s0, s1, orow = b;
+  if constexpr (PF) {
+    const int32_t* __restrict__ rows = a.rows;
+    if (qr >= rows[4 * b + 2]) return;               // past the block's rows
+    orow = rows[4 * b + 1] + qr;
+  }
   if constexpr (!DEVPLAN) {
     const int32_t* rpp = plan + HDA_PLAN_HEADER_INTS + a.n_wg + 1 + 4 * a.n_items;
     s0 = max(0, rpp[b]);
@@ -1045,17 +1106,18 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
   }
   if (s1 <= s0) return;
   const int n = s1 - s0;
-  const int64_t row_stride = (int64_t)a.n_q_heads * D;
-  const float* po = a.part_o + (int64_t)s0 * row_stride + (int64_t)hq * D + d;
-  const float* lse = a.part_lse + (int64_t)s0 * a.n_q_heads + hq;   // stride n_q_heads
+  const int64_t lstride = (int64_t)a.qb * a.n_q_heads;   // between slots, in rows
+  const int64_t row_stride = lstride * D;
+  const float* po = a.part_o + ((int64_t)s0 * lstride + (int64_t)qr * a.n_q_heads + hq) * D + d;
+  const float* lse = a.part_lse + (int64_t)s0 * lstride + (int64_t)qr * a.n_q_heads + hq;
 
   float early[kMergeEarly];
 #pragma unroll
   for (int u = 0; u < kMergeEarly; ++u) early[u] = u < n ? po[(int64_t)u * row_stride] : 0.f;
-  float my_lse = d < n ? lse[(int64_t)d * a.n_q_heads] : -INFINITY;
+  float my_lse = d < n ? lse[(int64_t)d * lstride] : -INFINITY;
 
   float m = my_lse;
-  for (int k = d + D; k < n; k += D) m = fmaxf(m, lse[(int64_t)k * a.n_q_heads]);
+  for (int k = d + D; k < n; k += D) m = fmaxf(m, lse[(int64_t)k * lstride]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if (lane == 0) sm_red[0][wave] = m;
@@ -1064,7 +1126,7 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
 #pragma unroll
   for (int w = 1; w < D / 64; ++w) M = fmaxf(M, sm_red[0][w]);
   float t = d < n ? expf(my_lse - M) : 0.f;
-  for (int k = d + D; k < n; k += D) t += expf(lse[(int64_t)k * a.n_q_heads] - M);
+  for (int k = d + D; k < n; k += D) t += expf(lse[(int64_t)k * lstride] - M);
   t = wave_sum(t);
   if (lane == 0) sm_red[1][wave] = t;
   __syncthreads();
@@ -1078,7 +1140,7 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
     const int cn = min(kMergeStage, n - c0);
     if (c0 > 0) __syncthreads();
     for (int k = d; k < cn; k += D) {
-      const float l = (c0 == 0 && k == d) ? my_lse : lse[(int64_t)(c0 + k) * a.n_q_heads];
+      const float l = (c0 == 0 && k == d) ? my_lse : lse[(int64_t)(c0 + k) * lstride];
       sm_w[k] = expf(l - M) * inv_total;
     }
     __syncthreads();
@@ -1098,7 +1160,7 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
     }
     for (; k < cn; ++k) acc += sm_w[k] * po[(int64_t)(c0 + k) * row_stride];
   }
-  a.out[((int64_t)b * a.n_q_heads + hq) * D + d] = acc;
+  a.out[((int64_t)orow * a.n_q_heads + hq) * D + d] = acc;
 }
 
 // The plan in the host format, built from device lengths by one wave with
@@ -1208,6 +1270,30 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
   return e;
 }
 
+template <int D, bool FP8, bool PAGE>
+hipError_t launch_prefill(Args a, int grid, int n_rows, hipStream_t stream, void* split_event) {
+  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, false, PAGE, false, true>), dim3(grid),
+                     dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens, a.plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (split_event) {
+    e = hipEventRecord(static_cast<hipEvent_t>(split_event), stream);
+    if (e != hipSuccess) return e;
+  }
+  if (a.n_parts == 0) return e;
+  hipLaunchKernelGGL((hda_merge_kernel<D, false, true>), dim3(n_rows * a.qb * a.n_q_heads),
+                     dim3(D), 0, stream, a, a.plan, a.seq_lens);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill_d(const Args& a, bool fp8, int grid, int n_rows, hipStream_t st,
+                            void* ev) {
+  if (!fp8) return launch_prefill<D, false, false>(a, grid, n_rows, st, ev);
+  return a.scale_mode == HDA_SCALE_PAGE ? launch_prefill<D, true, true>(a, grid, n_rows, st, ev)
+                                        : launch_prefill<D, true, false>(a, grid, n_rows, st, ev);
+}
+
 // Per-page scales are built for the fp8 cache only (check_params refuses
 // them for bf16).
 template <int D, bool DEVPLAN>
@@ -1304,6 +1390,8 @@ Args make_args(const hda_params* p, const void* q, void* k_pages, void* v_pages,
   a.max_pages = p->max_pages_per_req;
   a.n_wg = (int32_t)W;
   a.n_parts = (int32_t)P;
+  a.qb = 1;
+  a.n_req = p->batch;
   a.qk_scale_log2 = (float)((double)p->sm_scale * (double)p->k_scale * 1.4426950408889634);
   a.v_scale = p->v_scale;
   a.k_scale = p->k_scale;
@@ -1384,6 +1472,60 @@ extern "C" int hda_decode_auto(const hda_params* p, const void* q, void* k_pages
       p->head_dim == 64
           ? launch_d<64, true>(a, fp8, native, (int)grid, pro, a.q_prime, hs, p->split_event)
           : launch_d<128, true>(a, fp8, native, (int)grid, pro, a.q_prime, hs, p->split_event);
+  return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
+}
+
+extern "C" int hda_prefill(const hda_params* p, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* block_table,
+                           const int32_t* kv_lens, int32_t n_q, const int32_t* rows_host,
+                           const int32_t* rows_dev, const int32_t* plan_host,
+                           const int32_t* plan_dev, int64_t plan_len, float* out, void* stream) {
+  int st = check_params(p, q, k_pages, v_pages, block_table, kv_lens, out);
+  if (st != HDA_OK) return st;
+  if (p->prologue || p->math != HDA_MATH_BF16 || p->v_layout != HDA_V_TOKEN_MAJOR)
+    return HDA_ERR_UNSUPPORTED;
+  if (!rows_host || !rows_dev || !plan_host || !plan_dev || n_q < 1) return HDA_ERR_INVALID_ARG;
+  if (plan_len < HDA_PLAN_HEADER_INTS || plan_host[0] != HDA_PLAN_VERSION) return HDA_ERR_BAD_PLAN;
+  const int64_t R = plan_host[1], W = plan_host[3], N = plan_host[5], P = plan_host[6];
+  if (R < 1 || W < 1 || N < 1 || P < 0 || plan_len != HDA_PLAN_HEADER_INTS + (W + 1) + 4 * N + R + 1)
+    return HDA_ERR_BAD_PLAN;
+  const int32_t qb = hda_prefill_rows_per_block(p->n_q_heads, p->n_kv_heads);
+  if (qb < 1) return HDA_ERR_UNSUPPORTED;
+  // every block inside its request and the packed q (the kernel trusts them)
+  for (int64_t r = 0; r < R; ++r) {
+    const int32_t b = rows_host[4 * r], q0 = rows_host[4 * r + 1], nq = rows_host[4 * r + 2],
+                  pos0 = rows_host[4 * r + 3];
+    if (b < 0 || b >= p->batch || nq < 1 || nq > qb || q0 < 0 || (int64_t)q0 + nq > n_q ||
+        pos0 < 0)
+      return HDA_ERR_INVALID_ARG;
+  }
+  const int64_t grid = W * p->n_kv_heads;
+  if (grid > 0x7fffffffLL || R * qb * p->n_q_heads > 0x7fffffffLL) return HDA_ERR_UNSUPPORTED;
+  const int64_t ws_need = hda_prefill_workspace_bytes(plan_host, plan_len, p->n_q_heads,
+                                                      p->n_kv_heads, p->head_dim);
+  if (ws_need < 0) return HDA_ERR_BAD_PLAN;
+  if (P > 0 && (!p->workspace || p->workspace_bytes < ws_need)) return HDA_ERR_WORKSPACE;
+
+  Args a = make_args(p, q, const_cast<void*>(k_pages), const_cast<void*>(v_pages), block_table,
+                     kv_lens, out, W, 0);
+  const int64_t o_bytes = ((int64_t)P * qb * p->n_q_heads * p->head_dim * 4 + 255) / 256 * 256;
+  a.part_o = static_cast<float*>(p->workspace);
+  a.part_lse = p->workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(p->workspace) + o_bytes)
+                            : nullptr;
+  a.q_prime = nullptr;
+  a.req_slots = nullptr;
+  a.n_parts = (int32_t)P;
+  a.qb = qb;
+  a.batch = (int32_t)R;              // the plan's requests are the row blocks
+  a.rows = rows_dev;
+  a.plan = plan_dev;
+  a.n_items = (int32_t)N;
+  a.tile_len = plan_host[2];
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
+  hipError_t e = p->head_dim == 64
+                     ? launch_prefill_d<64>(a, fp8, (int)grid, (int)R, hs, p->split_event)
+                     : launch_prefill_d<128>(a, fp8, (int)grid, (int)R, hs, p->split_event);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
 }
 

@@ -282,6 +282,57 @@ int64_t hda_workspace_bytes(const int32_t* plan, int64_t plan_len,
          round_up(B * n_q_heads * head_dim * 2, 256) + round_up(B * 8, 256);
 }
 
+int32_t hda_prefill_rows_per_block(int32_t n_q_heads, int32_t n_kv_heads) {
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads) return -1;
+  const int32_t g = n_q_heads / n_kv_heads;
+  return g <= 16 ? 16 / g : -1;
+}
+
+// Row blocks of a multi-token batch: the query rows of each request, in
+// order, grouped into blocks of rows_per_block (the last shorter).  Row r of
+// request b sits at position kv_len - q_len + r; a block needs cache tokens
+// [0, position of its last row + 1), its length for hda_plan.
+int hda_prefill_rows(const int32_t* q_lens, const int32_t* kv_lens, int32_t batch,
+                     int32_t rows_per_block, int32_t* rows, int32_t* row_lens,
+                     int64_t capacity, int64_t* n_rows) {
+  if (!q_lens || !kv_lens || !n_rows || batch < 1 || rows_per_block < 1)
+    return HDA_ERR_INVALID_ARG;
+  int64_t R = 0, total_q = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (q_lens[b] < 1 || kv_lens[b] < 1 || q_lens[b] > kv_lens[b]) return HDA_ERR_INVALID_ARG;
+    R += ((int64_t)q_lens[b] + rows_per_block - 1) / rows_per_block;
+    total_q += q_lens[b];
+  }
+  if (R > kI32Max || total_q > kI32Max) return HDA_ERR_INVALID_ARG;
+  *n_rows = R;
+  if (!rows || !row_lens || capacity < R) return HDA_ERR_CAPACITY;
+  int64_t k = 0, q_start = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t n = q_lens[b], ctx = kv_lens[b] - q_lens[b];
+    for (int32_t q0 = 0; q0 < n; q0 += rows_per_block, ++k) {
+      const int32_t nq = std::min(rows_per_block, n - q0);
+      rows[4 * k] = b;
+      rows[4 * k + 1] = (int32_t)(q_start + q0);
+      rows[4 * k + 2] = nq;
+      rows[4 * k + 3] = ctx + q0;
+      row_lens[k] = ctx + q0 + nq;
+    }
+    q_start += n;
+  }
+  return HDA_OK;
+}
+
+int64_t hda_prefill_workspace_bytes(const int32_t* plan, int64_t plan_len, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t head_dim) {
+  if (!plan || plan_len < HDA_PLAN_HEADER_INTS || n_q_heads < 1 || n_kv_heads < 1 ||
+      head_dim < 1)
+    return -1;
+  const int32_t qb = hda_prefill_rows_per_block(n_q_heads, n_kv_heads);
+  if (qb < 1 || plan[0] != HDA_PLAN_VERSION || plan[1] < 1 || plan[6] < 0) return -1;
+  const int64_t P = plan[6];
+  return round_up(P * qb * n_q_heads * head_dim * 4, 256) + round_up(P * qb * n_q_heads * 4, 256);
+}
+
 const char* hda_status_string(int status) {
   switch (status) {
     case HDA_OK: return "ok";

@@ -41,7 +41,9 @@ PLAN_HEADER_INTS = 8
 # every symbol include/hda.h declares
 EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_plan_static", "hda_plan_validate",
            "hda_workspace_bytes", "hda_decode", "hda_decode_auto", "hda_workspace_bytes_bound",
-           "hda_plan_device", "hda_status_string", "hda_version", "hda_params_bytes")
+           "hda_plan_device", "hda_prefill_rows_per_block", "hda_prefill_rows",
+           "hda_prefill_workspace_bytes", "hda_prefill", "hda_status_string", "hda_version",
+           "hda_params_bytes")
 
 
 class HdaError(RuntimeError):
@@ -109,6 +111,11 @@ def load_library(path: Optional[str] = None):
                                            vp, vp]),
         "hda_workspace_bytes_bound": (i64, [i32, i32, i32, i32]),
         "hda_plan_device": (ctypes.c_int, [vp, i32, i32, i32, vp, i64, vp]),
+        "hda_prefill_rows_per_block": (i32, [i32, i32]),
+        "hda_prefill_rows": (ctypes.c_int, [pi32, pi32, i32, i32, pi32, pi32, i64, pi64]),
+        "hda_prefill_workspace_bytes": (i64, [pi32, i64, i32, i32, i32]),
+        "hda_prefill": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp, i32, pi32,
+                                       vp, pi32, vp, i64, vp, vp]),
         "hda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "hda_version": (ctypes.c_int, []),
         "hda_params_bytes": (i64, []),
@@ -250,6 +257,51 @@ def hda_plan_device(seq_lens, batch: int, tile_len: int, n_workgroups: int, plan
         raise HdaError(st, "hda_plan_device")
 
 
+def hda_prefill_rows_per_block(n_q_heads: int, n_kv_heads: int) -> int:
+    return load_library().hda_prefill_rows_per_block(int(n_q_heads), int(n_kv_heads))
+
+
+def hda_prefill_rows(q_lens, kv_lens, rows_per_block: int):
+    """Row blocks of a multi-token batch: (rows int32 [n, 4], row_lens int32 [n])."""
+    lib = load_library()
+    ql, kl = _lens(q_lens), _lens(kv_lens)
+    if len(ql) != len(kl):
+        raise ValueError("q_lens and kv_lens differ in length")
+    n = ctypes.c_int64(0)
+    st = lib.hda_prefill_rows(_i32p(ql), _i32p(kl), len(ql), int(rows_per_block), None, None, 0,
+                              ctypes.byref(n))
+    if st != HDA_ERR_CAPACITY:
+        raise HdaError(st, "hda_prefill_rows")
+    rows = np.empty((n.value, 4), dtype=np.int32)
+    row_lens = np.empty(n.value, dtype=np.int32)
+    st = lib.hda_prefill_rows(_i32p(ql), _i32p(kl), len(ql), int(rows_per_block), _i32p(rows),
+                              _i32p(row_lens), n.value, ctypes.byref(n))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_prefill_rows")
+    return rows, row_lens
+
+
+def hda_prefill_workspace_bytes(plan, n_q_heads: int, n_kv_heads: int, head_dim: int) -> int:
+    lib = load_library()
+    plan = np.ascontiguousarray(plan, dtype=np.int32)
+    return lib.hda_prefill_workspace_bytes(_i32p(plan), plan.size, int(n_q_heads),
+                                           int(n_kv_heads), int(head_dim))
+
+
+def hda_prefill(params: hda_params, q, k_pages, v_pages, block_table, kv_lens, n_q: int,
+                rows_host, rows_dev, plan_host, plan_dev, out, stream=None) -> None:
+    """Enqueue one multi-token attention step (see include/hda.h)."""
+    lib = load_library()
+    rows_host = np.ascontiguousarray(rows_host, dtype=np.int32)
+    plan_host = np.ascontiguousarray(plan_host, dtype=np.int32)
+    st = lib.hda_prefill(ctypes.byref(params), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                         _ptr(block_table), _ptr(kv_lens), int(n_q), _i32p(rows_host),
+                         _ptr(rows_dev), _i32p(plan_host), _ptr(plan_dev), plan_host.size,
+                         _ptr(out), _stream(stream))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_prefill")
+
+
 def _ptr(x):
     if x is None:
         return None
@@ -355,6 +407,46 @@ class DeviceBatch:
         hda_decode_auto(p, t["q"], t["k_pages"] if k_pages is None else k_pages,
                         t["v_pages"] if v_pages is None else v_pages, t["block_table"],
                         t["seq_lens"], tile_len, n_workgroups, out, stream)
+        return out
+
+    def prefill_plan(self, q_lens, tile_len=None, n_workgroups=None):
+        """(rows, plan) for this batch's query rows (row blocks through the
+        decode planner); default launch shape from launch_config."""
+        kv = self.t["seq_lens"].cpu().numpy()
+        qb = hda_prefill_rows_per_block(self.kw["n_q_heads"], self.kw["n_kv_heads"])
+        rows, row_lens = hda_prefill_rows(q_lens, kv, qb)
+        tl, W = launch_config(row_lens, self.kw["n_kv_heads"])
+        return rows, hda_plan(row_lens, tile_len or tl, n_workgroups or W)
+
+    def prefill_params(self, plan):
+        p = hda_params(**self.kw)
+        t = self.t
+        if "k_scales" in t:
+            p.k_scales = t["k_scales"].data_ptr()
+            p.v_scales = t["v_scales"].data_ptr()
+        need = hda_prefill_workspace_bytes(plan, self.kw["n_q_heads"], self.kw["n_kv_heads"],
+                                           self.kw["head_dim"])
+        ws = self.workspace(need)
+        p.workspace = ws.data_ptr()
+        p.workspace_bytes = ws.numel()
+        return p
+
+    def prefill(self, rows, plan, out=None, stream=None, rows_dev=None, plan_dev=None):
+        import torch
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        plan = np.ascontiguousarray(plan, dtype=np.int32)
+        t = self.t
+        n_q = t["q"].shape[0]
+        if out is None:
+            out = torch.empty((n_q, self.kw["n_q_heads"], self.kw["head_dim"]),
+                              dtype=torch.float32, device=self.device)
+        if rows_dev is None:
+            rows_dev = torch.from_numpy(rows.reshape(-1)).to(self.device)
+        if plan_dev is None:
+            plan_dev = torch.from_numpy(plan).to(self.device)
+        p = self.prefill_params(plan)
+        hda_prefill(p, t["q"], t["k_pages"], t["v_pages"], t["block_table"], t["seq_lens"], n_q,
+                    rows, rows_dev, plan, plan_dev, out, stream)
         return out
 
     def decode(self, plan, out=None, plan_dev=None, stream=None, k_pages=None, v_pages=None,

@@ -4,7 +4,8 @@ This module draws inputs and nothing else: it holds none of the attention,
 planning, normalisation or rotary arithmetic.  Both the HIP library's tests
 and the fp64 oracle consume the byte arrays it returns.
 
-Five workloads, all single-token grouped-query decode over a paged cache:
+Workloads, grouped-query attention over a paged cache (single-token decode
+unless they bring several query rows):
 
   tiny      4 requests, lengths {17, 64, 200, 513}, 8 q / 2 kv heads, D 64,
             page 16, bf16, pages laid out contiguously
@@ -21,6 +22,10 @@ Five workloads, all single-token grouped-query decode over a paged cache:
             RoPE with theta 1e6) must write before attention reads it
   fp8_page  the long-tail lengths and per-head magnitudes, fp8 E4M3FN cache
             with one fp32 scale per (page, kv head) slab, and the prologue
+  specdec   the extreme mix with 4 query rows per request (a speculative
+            check of 3 draft tokens plus one), causal over the cache
+  chunked   16 requests, cache lengths log-uniform in [2048, 32768], a
+            chunk of U{16..128} new query rows each (chunked prefill)
 
 Recipe (the pages use no dataset; these stand in for a serving batch):
   * numpy PCG64 streams spawned from SeedSequence(seed), one stream per
@@ -111,6 +116,11 @@ CONFIGS = {
     "fp8_page": Workload("fp8_page", 64, 64, 8, 128, 64, kv_dtype="fp8",
                          len_range=(256, 65536), head_scale=True, prologue=True,
                          kv_scale="page", seed=5),
+    # multi-token queries over the cache (lengths include the new rows)
+    "specdec": Workload("specdec", 32, 64, 8, 128, 64, lengths=(131072,) + (4096,) * 31,
+                        q_lens=(4,) * 32, seed=6),
+    "chunked": Workload("chunked", 16, 64, 8, 128, 64, len_range=(2048, 32768),
+                        q_len_range=(16, 128), seed=7),
 }
 
 _CHUNK_SLABS = 256

@@ -62,6 +62,34 @@ int main(int argc, char** argv) {
     st = hda_plan_validate(plan.data(), need - 1 - (int64_t)(rng() % need), lens.data(), B);
     if (st == HDA_OK) return fail("truncated accepted", it);
   }
+  // prefill row blocks: exact-size buffers, then one row short
+  for (int it = 0; it < iters / 4; ++it) {
+    const int B = 1 + (int)(rng() % 60);
+    std::vector<int32_t> kv(B), ql(B);
+    for (int b = 0; b < B; ++b) {
+      kv[b] = 1 + (int32_t)(rng() % (rng() % 2 ? 100 : 100000));
+      ql[b] = 1 + (int32_t)(rng() % kv[b]);
+    }
+    const int32_t qb = 1 + (int32_t)(rng() % 16);
+    int64_t n = 0;
+    if (hda_prefill_rows(ql.data(), kv.data(), B, qb, nullptr, nullptr, 0, &n) != HDA_ERR_CAPACITY)
+      return fail("prefill size query", it);
+    std::vector<int32_t> rows((size_t)n * 4), lens((size_t)n);
+    if (hda_prefill_rows(ql.data(), kv.data(), B, qb, rows.data(), lens.data(), n, &n) != HDA_OK)
+      return fail("prefill rows", it);
+    std::vector<int32_t> plan(1 << 16);
+    int64_t got = 0;
+    const int st = hda_plan(lens.data(), (int32_t)n, 1 + (int32_t)(rng() % 300),
+                            1 + (int32_t)(rng() % 300), plan.data(), (int64_t)plan.size(), &got);
+    if (st == HDA_OK && hda_plan_validate(plan.data(), got, lens.data(), (int32_t)n) != HDA_OK)
+      return fail("prefill plan validate", it);
+    if (n > 1) {
+      std::vector<int32_t> r2((size_t)(n - 1) * 4), l2((size_t)(n - 1));
+      if (hda_prefill_rows(ql.data(), kv.data(), B, qb, r2.data(), l2.data(), n - 1, &n) !=
+          HDA_ERR_CAPACITY)
+        return fail("prefill short buffer", it);
+    }
+  }
   printf("plan_fuzz: %d iterations clean\n", iters);
   return 0;
 }

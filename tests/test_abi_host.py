@@ -277,3 +277,100 @@ def test_decode_auto_and_plan_device_argument_errors(lib):
     assert lib.hda_plan_device(None, 4, 64, 4, vp(FAKE), 1000, None) == E.HDA_ERR_INVALID_ARG
     assert lib.hda_plan_device(vp(FAKE), 4, 0, 4, vp(FAKE), 1000, None) == E.HDA_ERR_INVALID_ARG
     assert lib.hda_plan_device(vp(FAKE), 4, 64, 4, vp(FAKE), 10, None) == E.HDA_ERR_CAPACITY
+
+
+# ---- multi-token (prefill) host entry points ----
+
+def test_prefill_rows_per_block(lib):
+    assert hda.hda_prefill_rows_per_block(64, 8) == 2
+    assert hda.hda_prefill_rows_per_block(8, 2) == 4
+    assert hda.hda_prefill_rows_per_block(16, 16) == 16
+    assert hda.hda_prefill_rows_per_block(16, 1) == 1
+    assert hda.hda_prefill_rows_per_block(34, 2) == -1
+    assert hda.hda_prefill_rows_per_block(7, 2) == -1
+
+
+def test_prefill_rows_bit_exact(lib):
+    import oracle
+    golden = os.path.join(ROOT, "tests", "golden", "prefill_rows.txt")
+    g = {}
+    for line in open(golden):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            g.setdefault(k, []).append([int(x) if x.lstrip("-").isdigit() else x for x in v])
+    rows, row_lens = hda.hda_prefill_rows(g["q_lens"][0], g["kv_lens"][0], g["rows_per_block"][0][0])
+    assert rows.tolist() == g["row"] and row_lens.tolist() == g["extents"][0]
+    plan = hda.hda_plan(row_lens, 4, 3)
+    assert plan[:8].tolist() == g["header"][0]
+    rng = np.random.default_rng(11)
+    for _ in range(500):
+        B = int(rng.integers(1, 40))
+        kv = rng.integers(1, int(rng.choice([10, 500, 50000])), size=B).astype(np.int32)
+        ql = np.minimum(rng.integers(1, int(rng.choice([3, 70, 2000])), size=B), kv).astype(np.int32)
+        qb = int(rng.choice([1, 2, 4, 8, 16]))
+        rows, row_lens = hda.hda_prefill_rows(ql, kv, qb)
+        want, ext = oracle.prefill_rows(ql, kv, qb)
+        assert [tuple(r) for r in rows.tolist()] == want and row_lens.tolist() == ext
+
+
+def test_prefill_rows_errors(lib):
+    import ctypes
+    n = ctypes.c_int64(0)
+    ql = np.array([3, 5], np.int32)
+    kv = np.array([10, 4], np.int32)           # q_len > kv_len for request 1
+    st = lib.hda_prefill_rows(hda._i32p(ql), hda._i32p(kv), 2, 2, None, None, 0, ctypes.byref(n))
+    assert st == hda.HDA_ERR_INVALID_ARG
+    kv = np.array([10, 5], np.int32)
+    st = lib.hda_prefill_rows(hda._i32p(ql), hda._i32p(kv), 2, 2, None, None, 0, ctypes.byref(n))
+    assert st == hda.HDA_ERR_CAPACITY and n.value == 2 + 3
+    rows = np.empty((4, 4), np.int32)
+    lens = np.empty(4, np.int32)
+    st = lib.hda_prefill_rows(hda._i32p(ql), hda._i32p(kv), 2, 2, hda._i32p(rows), hda._i32p(lens),
+                              4, ctypes.byref(n))
+    assert st == hda.HDA_ERR_CAPACITY and n.value == 5
+    st = lib.hda_prefill_rows(hda._i32p(ql), hda._i32p(kv), 2, 0, None, None, 0, ctypes.byref(n))
+    assert st == hda.HDA_ERR_INVALID_ARG
+
+
+def test_prefill_workspace_bytes(lib):
+    up = lambda x: (x + 255) // 256 * 256
+    rows, row_lens = hda.hda_prefill_rows([3, 1, 5], [10, 1, 5], 2)
+    plan = hda.hda_plan(row_lens, 4, 3)
+    P = int(plan[6])
+    assert P == 2
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128) == up(P * 2 * 64 * 128 * 4) + up(P * 2 * 64 * 4)
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 3, 128) == -1
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers are only used without a GPU")
+def test_prefill_argument_errors(lib):
+    import ctypes
+    E = hda
+    q_lens, kv_lens = np.array([3, 1, 5], np.int32), np.array([10, 1, 5], np.int32)
+    rows, row_lens = hda.hda_prefill_rows(q_lens, kv_lens, 2)
+    plan = hda.hda_plan(row_lens, 4, 3)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+
+    def call(p, rows=rows, plan=plan, n_q=9, **kw):
+        a = dict(q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, bt=FAKE + 0x3000, kv=FAKE + 0x4000,
+                 rd=FAKE + 0x5000, pd=FAKE + 0x6000, out=FAKE + 0x7000)
+        a.update(kw)
+        rows = np.ascontiguousarray(rows, np.int32)
+        return lib.hda_prefill(ctypes.byref(p), vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["bt"]),
+                               vp(a["kv"]), n_q, hda._i32p(rows), vp(a["rd"]), hda._i32p(plan),
+                               vp(a["pd"]), plan.size, vp(a["out"]), None)
+
+    base = dict(batch=3, n_q_heads=64, n_kv_heads=8, head_dim=128, page_size=16)
+    assert call(_params(**base), q=None) == E.HDA_ERR_INVALID_ARG
+    assert call(_params(**base, prologue=1, q_norm_w=FAKE, k_norm_w=FAKE, k_new=FAKE,
+                        v_new=FAKE, rope_theta=1e6)) == E.HDA_ERR_UNSUPPORTED
+    assert call(_params(**dict(base, kv_dtype=E.HDA_KV_FP8_E4M3, math=E.HDA_MATH_FP8,
+                               v_layout=E.HDA_V_DIM_MAJOR, page_size=64))) == E.HDA_ERR_UNSUPPORTED
+    assert call(_params(**base), n_q=8) == E.HDA_ERR_INVALID_ARG        # last block past n_q
+    bad = rows.copy(); bad[0, 2] = 3                                     # 3 rows > 2 per block
+    assert call(_params(**base), rows=bad) == E.HDA_ERR_INVALID_ARG
+    bad = rows.copy(); bad[1, 0] = 3                                     # request out of range
+    assert call(_params(**base), rows=bad) == E.HDA_ERR_INVALID_ARG
+    assert call(_params(**base), plan=plan[:-1]) == E.HDA_ERR_BAD_PLAN
+    assert call(_params(**base, workspace=None)) == E.HDA_ERR_WORKSPACE
+    assert call(_params(**base, workspace_bytes=64)) == E.HDA_ERR_WORKSPACE

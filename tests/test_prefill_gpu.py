@@ -1,0 +1,101 @@
+"""GPU parity of multi-token attention (hda_prefill) against the fp64 oracle.
+
+Row blocks of 16 / group query rows go through the decode tile planner;
+checked element by element at sizes the oracle finishes in seconds (ragged
+q lengths, blocks split over workgroups, tiles not aligned to chunks, every
+group size the kernel takes), one query per request bitwise equal to the
+decode path, and the full-size speculative-check workload on sampled rows.
+Bar: 2e-2 (bf16 cache), 6e-2 (fp8 cache) max-abs error.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import load_balanced_split_step_amd.hda as hda
+import oracle
+from load_balanced_split_step_amd.workloads import CONFIGS, Workload, make_inputs
+from tests.gpu_util import TOL, need_gpu, scale_kw, max_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def ref_prefill(inp):
+    return oracle.prefill_reference(oracle.bf16_to_f64(inp["q"]), inp["k_pages"], inp["v_pages"],
+                                    inp["block_table"], inp["seq_lens"], inp["q_lens"],
+                                    inp["kv_dtype"], float(inp["sm_scale"]), **scale_kw(inp))
+
+
+CASES = {
+    "tiny_pf": (CONFIGS["tiny"].with_(name="tiny_pf", q_len_range=(1, 20)), None, None),
+    "spec_s": (CONFIGS["specdec"].with_(name="spec_s", batch=8, lengths=None,
+                                        q_lens=(4,) * 8), [16384] + [1000] * 7, None),
+    "chunk_s": (CONFIGS["chunked"].with_(name="chunk_s", batch=6, len_range=(200, 3000),
+                                         q_len_range=(1, 70)), None, None),
+    "full_s": (Workload("full_s", 4, 16, 4, 128, 16, seed=80), [1, 33, 130, 257], [1, 33, 130, 257]),
+    "fp8_page_pf": (CONFIGS["fp8_page"].with_(name="fp8_page_pf", batch=6, len_range=(100, 2500),
+                                              prologue=False, q_len_range=(1, 40)), None, None),
+    "g16": (Workload("g16", 3, 32, 2, 128, 64, seed=81), [700, 90, 2000], [20, 3, 33]),
+    "g1": (Workload("g1", 3, 4, 4, 64, 32, seed=82), [300, 64, 65], [40, 64, 1]),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prefill_parity(name):
+    w, lens, qlens = CASES[name]
+    inp = make_inputs(w, lengths=lens, q_lens=qlens)
+    ref = ref_prefill(inp)
+    dev = hda.DeviceBatch.from_inputs(inp)
+    qb = hda.hda_prefill_rows_per_block(w.n_q_heads, w.n_kv_heads)
+    rows, row_lens = hda.hda_prefill_rows(inp["q_lens"], inp["seq_lens"], qb)
+    plans = [("default", dev.prefill_plan(inp["q_lens"])[1])]
+    for tl, W in [(64, 7), (100, 13), (16, 300), (512, 2)]:
+        plans.append((f"dyn-{tl}-{W}", hda.hda_plan(row_lens, tl, W)))
+    plans.append(("static-3", hda.hda_plan_static(row_lens, 3)))
+    tol = TOL[w.kv_dtype]
+    for pname, plan in plans:
+        out = dev.prefill(rows, plan)
+        torch.cuda.synchronize()
+        err = max_err(out, ref)
+        print(f"{name} {pname}: {len(rows)} blocks, P={int(plan[6])}, max err {err:.3e}", flush=True)
+        assert err <= tol, (name, pname, err)
+
+
+def test_single_query_rows_bitwise_equal_decode():
+    w = CONFIGS["extreme"].with_(name="pf1", batch=8)
+    lens = [9000] + [700] * 7
+    inp = make_inputs(w, lengths=lens, q_lens=[1] * 8)
+    dev = hda.DeviceBatch.from_inputs(inp)
+    rows, row_lens = hda.hda_prefill_rows(inp["q_lens"], inp["seq_lens"], 2)
+    assert np.array_equal(row_lens, inp["seq_lens"])
+    for tl, W in [(128, 24), (64, 5)]:
+        plan = hda.hda_plan(row_lens, tl, W)
+        a = dev.prefill(rows, plan)
+        b = dev.decode(plan)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (tl, W)
+
+
+def test_specdec_full_size_sampled():
+    w = CONFIGS["specdec"]
+    inp = make_inputs(w)
+    dev = hda.DeviceBatch.from_inputs(inp)
+    rows, plan = dev.prefill_plan(inp["q_lens"])
+    out = dev.prefill(rows, plan)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.isfinite(o).all()
+    off = oracle.q_offsets(inp["q_lens"])
+    worst = 0.0
+    for b in (0, 1, 31):                      # the 128K request and two 4K ones
+        sub = dict(inp, block_table=inp["block_table"][[b]], seq_lens=inp["seq_lens"][[b]],
+                   q_lens=inp["q_lens"][[b]], q=inp["q"][off[b]:off[b + 1]])
+        ref = ref_prefill(sub)
+        worst = max(worst, float(np.abs(o[off[b]:off[b + 1]] - ref).max()))
+    print(f"specdec full size: {len(rows)} blocks, sampled max err {worst:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
