@@ -352,3 +352,37 @@ def kv_bytes(inp):
     w = inp["workload"]
     elem = 1 if w.kv_dtype == "fp8" else 2
     return int(np.asarray(inp["seq_lens"], dtype=np.int64).sum()) * w.n_kv_heads * w.head_dim * 2 * elem
+
+
+# ---- Router GEMM inputs ----
+
+@dataclass(frozen=True)
+class RouterWorkload:
+    """Router logits x w^T: bf16 activations [tokens][hidden], fp32 weights
+    [experts][hidden] ~ N(0, 1/hidden) so that logits are ~ N(0, 1)."""
+    name: str
+    tokens: int
+    hidden: int
+    experts: int
+    seed: int = 0
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+ROUTER_CONFIGS = {
+    "router_small": RouterWorkload("router_small", 5, 96, 24, seed=20),
+    # DeepSeek-V3-like router shape (hidden 7168, 256 experts); the pages do
+    # not give Hy3's router shape; token counts span decode to prefill
+    "router": RouterWorkload("router", 64, 7168, 256, seed=21),
+}
+
+
+def make_router_inputs(w: RouterWorkload, tokens: Optional[int] = None):
+    """x bf16 bits [T][H] ~ N(0, 1), weights fp32 [E][H] ~ N(0, 1/H)."""
+    T = w.tokens if tokens is None else tokens
+    ss = np.random.SeedSequence(w.seed).spawn(2)
+    x = _bf16_bits(_rng(ss[0]).standard_normal((T, w.hidden), dtype=np.float32))
+    wt = (_rng(ss[1]).standard_normal((w.experts, w.hidden), dtype=np.float32)
+          * np.float32(1.0 / math.sqrt(w.hidden))).astype(np.float32)
+    return dict(workload=w, x=x, w=wt)

@@ -48,6 +48,8 @@ from .prologue import (rms_norm, rope, prologue_step, bf16_encode, write_new_tok
 from .fp8_math import (quantize_q_fp8, dequantized_q, attention_fp8q,
                        weight_rounding_bounds)
 from .prefill import prefill_reference, prefill_rows, q_offsets
+from .router import (split_router_weights, split_value, router_reference,
+                     router_split_reference, accumulation_bound)
 
 __all__ = [
     "bf16_to_f64", "fp8_decode", "fp8_encode", "FP8_MAX",
@@ -57,4 +59,6 @@ __all__ = [
     "SCALE_MODES", "rms_norm", "rope", "prologue_step", "bf16_encode", "write_new_token",
     "slot_scales", "quantize_q_fp8", "dequantized_q", "attention_fp8q",
     "weight_rounding_bounds", "prefill_reference", "prefill_rows", "q_offsets",
+    "split_router_weights", "split_value", "router_reference", "router_split_reference",
+    "accumulation_bound",
 ]
