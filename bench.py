@@ -284,6 +284,85 @@ def bench_prefill(args, w, inp):
     print(json.dumps(res), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+
+
+def bench_router(args):
+    """Router GEMM sweep over token counts (decode batch to prefill): the
+    fused split kernel (two bf16 MFMA products per K step, fp32 accumulate)
+    timed with HIP events on the launch stream, its roofline position, and
+    torch's fp32 GEMM on the same data as context."""
+    import numpy as np
+    import torch
+    import load_balanced_split_step_amd.hda as hda
+    from load_balanced_split_step_amd.workloads import ROUTER_CONFIGS, make_router_inputs
+    w = ROUTER_CONFIGS["router"]
+    E, H = w.experts, w.hidden
+    Ts = [1, 16, 64, 256, 1024, 4096, 16384]
+    big = make_router_inputs(w, tokens=max(Ts))
+    rw = hda.RouterWeights(big["w"])
+    wf = torch.from_numpy(big["w"]).cuda()
+    x_all = torch.from_numpy(big["x"].view(np.int16)).cuda()
+    stream = torch.cuda.current_stream()
+    sweep = []
+    for T in Ts:
+        x = x_all[:T].contiguous()
+        xf = x.view(torch.bfloat16).float()
+        out = torch.empty((T, E), dtype=torch.float32, device="cuda:0")
+
+        def run_ours():
+            rw.logits(x, out=out, stream=stream)
+
+        def run_f32():
+            torch.matmul(xf, wf.T)
+
+        res = {}
+        for name, fn in (("ours", run_ours), ("torch_fp32", run_f32)):
+            for _ in range(args.warmup):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) * 1e3 / args.steps          # us per call
+        flops = 4.0 * T * H * E                                          # two products
+        ws = hda.hda_router_workspace_bytes(T, E, H)
+        nbytes = T * H * 2 + E * H * 4 + T * E * 4 + 2 * ws
+        inten = flops / nbytes
+        bound = "mfma" if inten > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+        if bound == "mfma":
+            ach, peak, unit = flops / (res["ours"] * 1e-6) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = nbytes / (res["ours"] * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+        row = {"tokens": T, "us": round(res["ours"], 2), "torch_fp32_us": round(res["torch_fp32"], 2),
+               "speedup_vs_fp32": round(res["torch_fp32"] / res["ours"], 2),
+               "tflops": round(flops / (res["ours"] * 1e-6) / 1e12, 1), "bound": bound,
+               "achieved": round(ach, 1), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+               "hidden_splits": ws // (4 * T * E) if ws else 1}
+        sweep.append(row)
+        log(f"router T={T}: {res['ours']:.1f} us ({row['tflops']} TFLOP/s, {bound} {row['frac']:.3f}), "
+            f"torch fp32 {res['torch_fp32']:.1f} us")
+    head = sweep[-1]
+    res = {
+        "metric": "router GEMM (fp32 weights as bf16 hi + residual/256, fused): TFLOP/s at 16384 tokens, 1 GPU",
+        "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(head["us"] * 1e-3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"router logits: hidden {H}, {E} experts, tokens {Ts}",
+                   "hidden": H, "experts": E},
+        "roofline": {"bound": head["bound"], "achieved": head["achieved"], "peak": head["peak"],
+                     "unit": head["unit"], "frac": head["frac"], "traffic": None,
+                     "kernel": "hda_router_gemm_kernel (HIP events on the launch stream)"},
+        "sweep": sweep,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -296,6 +375,9 @@ def main():
     import load_balanced_split_step_amd.hda as hda
     from load_balanced_split_step_amd.workloads import CONFIGS, make_inputs, kv_bytes
 
+    if args.workload == "router":
+        bench_router(args)
+        return
     w = CONFIGS[args.workload]
     if args.kv_scale:
         w = w.with_(kv_scale=args.kv_scale)

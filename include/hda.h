@@ -353,6 +353,46 @@ int hda_prefill(const hda_params* p, const void* q, const void* k_pages, const v
                 const int32_t* rows_host, const int32_t* rows_dev, const int32_t* plan_host,
                 const int32_t* plan_dev, int64_t plan_len, float* out, void* stream);
 
+/*
+ * ---- Router GEMM (MoE expert-selection logits) ----
+ *
+ * The router multiplies bf16 activations by fp32 weights whose small
+ * differences can change the selected experts.  The pages describe keeping
+ * each fp32 weight as two bf16 parts -- the high part and a residual stored
+ * with a scale of 1/256 -- and running the two bf16 products in one kernel
+ * that shares the input loads, keeps both accumulators in registers and
+ * writes the combined result once (remio.ai page, Router GEMM section;
+ * arex-research page, Router GEMM paragraph).  Here hi = bf16(w),
+ * lo = bf16(256 (w - hi)), both round-to-nearest-even, and
+ *   out[t][e] = sum_h x[t][h] hi[e][h] + (sum_h x[t][h] lo[e][h]) / 256
+ * with fp32 accumulation.
+ */
+
+/* Splits fp32 weights [device] w[n] into hi and lo [device] bf16[n] on
+ * `stream` (a one-time weight preparation).  Errors: HDA_ERR_INVALID_ARG,
+ * HDA_ERR_UNSUPPORTED, HDA_ERR_HIP. */
+int hda_router_split_weights(const float* w, int64_t n, void* w_hi, void* w_lo, void* stream);
+
+/* Workspace bytes hda_router_gemm needs for this shape (0 when none), or -1
+ * for a shape it does not take (hidden not a positive multiple of 32). */
+int64_t hda_router_workspace_bytes(int32_t tokens, int32_t experts, int32_t hidden);
+
+/*
+ * Logits out[tokens][experts] (fp32, [device]) = x w^T from
+ *   x      [device] bf16 [tokens][hidden], 16-byte aligned
+ *   w_hi,
+ *   w_lo   [device] bf16 [experts][hidden] from hda_router_split_weights
+ * hidden must be a multiple of 32; tokens x hidden and experts x hidden
+ * below 2^30.  The workspace (hda_router_workspace_bytes) holds partial
+ * tiles when the hidden dimension is split across workgroups; partials are
+ * added in a fixed order, so results do not vary between runs.
+ * Asynchronous on `stream`.  Errors: HDA_ERR_INVALID_ARG,
+ * HDA_ERR_UNSUPPORTED, HDA_ERR_WORKSPACE, HDA_ERR_HIP.
+ */
+int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo, int32_t tokens,
+                    int32_t experts, int32_t hidden, float* out, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* hda_status_string(int status);
 

@@ -1,0 +1,230 @@
+// Router GEMM for MI355X (gfx950): MoE routing logits from bf16 activations
+// and fp32 weights kept as two bf16 parts.
+//
+// The pages describe the operator: fp32 router weights become a bf16 high
+// part and a bf16 residual stored with a scale of 1/256; two bf16 matrix
+// products run in one kernel, sharing the input movement and keeping their
+// accumulators in registers, and are combined once ("Tencent HPC llega a
+// SGLang ...", remio.ai, Router GEMM section; arex-research page, Router
+// GEMM paragraph).  Here: hi = bf16(w), lo = bf16(256 (w - hi)), and
+//   out[t][e] = sum_h x[t][h] hi[e][h] + (sum_h x[t][h] lo[e][h]) / 256
+// with fp32 accumulation on v_mfma_f32_16x16x32_bf16.
+//
+// Tiling.  A workgroup owns TM tokens (32 or 64) x 64 experts and a range of
+// the hidden dimension; its 4 waves take interleaved 32-wide K steps of that
+// range, each holding the full TM x 64 tile for both products (2 x TM/16 x 4
+// MFMA blocks), and combine through LDS at the end.  The activation fragment
+// of a K step is loaded once and feeds both products.  When the token and
+// expert tiles alone give too few workgroups for 256 compute units (decode
+// batches), the hidden dimension is also split S ways across workgroups;
+// their partial tiles go to the workspace and a second kernel adds them in a
+// fixed order (deterministic).  Rows past T or E read as zero through the
+// buffer range checks.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hda.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kWaves = 4;
+constexpr int kTileE = 64;        // experts per workgroup tile
+constexpr int kStepK = 32;        // K per MFMA
+constexpr float kResidualScale = 1.0f / 256.0f;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7fffffffLL ? 0x7fffffff : (int32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
+}
+
+__device__ inline bf16x8 load8(const __amdgpu_buffer_rsrc_t& r, int64_t off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+struct RouterArgs {
+  const uint16_t* x;     // bf16 [T][H]
+  const uint16_t* w_hi;  // bf16 [E][H]
+  const uint16_t* w_lo;  // bf16 [E][H], residual x 256
+  float* out;            // fp32 [T][E]
+  float* part;           // fp32 [S][T][E] when S > 1
+  int32_t T, E, H;
+  int32_t k_per_wg;      // hidden range per workgroup (multiple of 4 x 32)
+};
+
+// TM = 16 * MB tokens per tile.  Lane (i, kg) of a 16x16x32 MFMA block holds
+// row i, k = 8 kg .. 8 kg + 7 of both operands; the C layout is
+// C[4 kg + r][i].
+template <int MB>
+__global__ __launch_bounds__(64 * kWaves) void hda_router_gemm_kernel(RouterArgs a) {
+  constexpr int TM = 16 * MB;
+  __shared__ float red[kWaves][TM][kTileE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, kg = lane >> 4;
+  const int t0 = blockIdx.x * TM, e0 = blockIdx.y * kTileE, s = blockIdx.z;
+  const int kb = s * a.k_per_wg;
+  const int ke = min(a.H, kb + a.k_per_wg);
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (int64_t)a.T * a.H * 2);
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.w_hi, (int64_t)a.E * a.H * 2);
+  const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.w_lo, (int64_t)a.E * a.H * 2);
+
+  f32x4 acc_hi[MB][4], acc_lo[MB][4];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      acc_hi[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_lo[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  // byte offsets of this lane's rows at k = 0
+  int64_t xoff[MB], woff[4];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) xoff[m] = ((int64_t)(t0 + 16 * m + i) * a.H + 8 * kg) * 2;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) woff[n] = ((int64_t)(e0 + 16 * n + i) * a.H + 8 * kg) * 2;
+
+  for (int k = kb + kStepK * wave; k < ke; k += kStepK * kWaves) {
+    bf16x8 xa[MB], wh[4], wl[4];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) xa[m] = load8(xr, xoff[m] + 2 * k);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      wh[n] = load8(hr, woff[n] + 2 * k);
+      wl[n] = load8(lr, woff[n] + 2 * k);
+    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        acc_hi[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[m], wh[n], acc_hi[m][n], 0, 0, 0);
+        acc_lo[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[m], wl[n], acc_lo[m][n], 0, 0, 0);
+      }
+  }
+  // combine the two products, then the four waves
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[wave][16 * m + 4 * kg + r][16 * n + i] = acc_hi[m][n][r] + acc_lo[m][n][r] * kResidualScale;
+  __syncthreads();
+  float* dst = gridDim.z > 1 ? a.part + (int64_t)s * a.T * a.E : a.out;
+  for (int idx = tid; idx < TM * kTileE; idx += 64 * kWaves) {
+    const int tt = idx / kTileE, ee = idx - tt * kTileE;
+    const int t = t0 + tt, e = e0 + ee;
+    if (t < a.T && e < a.E)
+      dst[(int64_t)t * a.E + e] = (red[0][tt][ee] + red[1][tt][ee]) + (red[2][tt][ee] + red[3][tt][ee]);
+  }
+}
+
+// Sum of the S partial tiles, in slot order.
+__global__ __launch_bounds__(256) void hda_router_reduce_kernel(const float* __restrict__ part,
+                                                                float* __restrict__ out,
+                                                                int64_t n, int S) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= n) return;
+  float acc = part[j];
+  for (int s = 1; s < S; ++s) acc += part[(int64_t)s * n + j];
+  out[j] = acc;
+}
+
+// w -> (hi, lo): hi = bf16(w), lo = bf16(256 (w - hi)), both rounded to
+// nearest even (w - hi is exact in float32, and so is the scaling).
+__global__ __launch_bounds__(256) void hda_router_split_kernel(const float* __restrict__ w,
+                                                               uint16_t* __restrict__ hi,
+                                                               uint16_t* __restrict__ lo,
+                                                               int64_t n) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= n) return;
+  const float v = w[j];
+  const __bf16 h = (__bf16)v;
+  hi[j] = __builtin_bit_cast(uint16_t, h);
+  lo[j] = __builtin_bit_cast(uint16_t, (__bf16)((v - (float)h) * 256.0f));
+}
+
+// Launch shape: token tile, expert tiles, and the hidden split S.
+struct RouterShape {
+  int mb, tiles_t, tiles_e, S, k_per_wg;
+};
+
+RouterShape router_shape(int32_t T, int32_t E, int32_t H) {
+  RouterShape r;
+  r.mb = T <= 32 ? 2 : 4;
+  r.tiles_t = (T + 16 * r.mb - 1) / (16 * r.mb);
+  r.tiles_e = (E + kTileE - 1) / kTileE;
+  const int64_t base = (int64_t)r.tiles_t * r.tiles_e;
+  constexpr int kRound = kStepK * kWaves;                 // one K step per wave
+  const int rounds_total = (H + kRound - 1) / kRound;     // >= 1 for H >= 1; last may be partial
+  int64_t S = (512 + base - 1) / base;
+  S = S < 1 ? 1 : (S > rounds_total ? rounds_total : S);
+  const int rounds = (int)((rounds_total + S - 1) / S);   // per workgroup, >= 1
+  r.k_per_wg = rounds * kRound;
+  r.S = (H + r.k_per_wg - 1) / r.k_per_wg;
+  return r;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int64_t hda_router_workspace_bytes(int32_t tokens, int32_t experts, int32_t hidden) {
+  if (tokens < 1 || experts < 1 || hidden < kStepK || hidden % kStepK) return -1;
+  const RouterShape r = router_shape(tokens, experts, hidden);
+  return r.S > 1 ? (int64_t)r.S * tokens * experts * 4 : 0;
+}
+
+extern "C" int hda_router_split_weights(const float* w, int64_t n, void* w_hi, void* w_lo,
+                                        void* stream) {
+  if (!w || !w_hi || !w_lo || n < 1) return HDA_ERR_INVALID_ARG;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return HDA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(hda_router_split_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), w, static_cast<uint16_t*>(w_hi),
+                     static_cast<uint16_t*>(w_lo), n);
+  return hipGetLastError() == hipSuccess ? HDA_OK : HDA_ERR_HIP;
+}
+
+extern "C" int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo, int32_t tokens,
+                               int32_t experts, int32_t hidden, float* out, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
+  if (!x || !w_hi || !w_lo || !out || tokens < 1 || experts < 1 || hidden < 1)
+    return HDA_ERR_INVALID_ARG;
+  if (hidden % kStepK) return HDA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w_hi) || !aligned16(w_lo)) return HDA_ERR_INVALID_ARG;
+  if ((int64_t)tokens * hidden * 2 > 0x7fffffffLL || (int64_t)experts * hidden * 2 > 0x7fffffffLL)
+    return HDA_ERR_UNSUPPORTED;                 // 32-bit buffer offsets
+  const RouterShape r = router_shape(tokens, experts, hidden);
+  const int64_t need = hda_router_workspace_bytes(tokens, experts, hidden);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return HDA_ERR_WORKSPACE;
+  RouterArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w_hi = static_cast<const uint16_t*>(w_hi);
+  a.w_lo = static_cast<const uint16_t*>(w_lo);
+  a.out = out;
+  a.part = static_cast<float*>(workspace);
+  a.T = tokens;
+  a.E = experts;
+  a.H = hidden;
+  a.k_per_wg = r.k_per_wg;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const dim3 grid(r.tiles_t, r.tiles_e, r.S);
+  if (r.mb == 2)
+    hipLaunchKernelGGL(hda_router_gemm_kernel<2>, grid, dim3(64 * kWaves), 0, hs, a);
+  else
+    hipLaunchKernelGGL(hda_router_gemm_kernel<4>, grid, dim3(64 * kWaves), 0, hs, a);
+  if (hipGetLastError() != hipSuccess) return HDA_ERR_HIP;
+  if (r.S > 1) {
+    const int64_t n = (int64_t)tokens * experts;
+    hipLaunchKernelGGL(hda_router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       hs, a.part, out, n, r.S);
+    if (hipGetLastError() != hipSuccess) return HDA_ERR_HIP;
+  }
+  return HDA_OK;
+}

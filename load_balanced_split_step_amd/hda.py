@@ -42,7 +42,8 @@ PLAN_HEADER_INTS = 8
 EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_plan_static", "hda_plan_validate",
            "hda_workspace_bytes", "hda_decode", "hda_decode_auto", "hda_workspace_bytes_bound",
            "hda_plan_device", "hda_prefill_rows_per_block", "hda_prefill_rows",
-           "hda_prefill_workspace_bytes", "hda_prefill", "hda_status_string", "hda_version",
+           "hda_prefill_workspace_bytes", "hda_prefill", "hda_router_split_weights",
+           "hda_router_workspace_bytes", "hda_router_gemm", "hda_status_string", "hda_version",
            "hda_params_bytes")
 
 
@@ -116,6 +117,9 @@ def load_library(path: Optional[str] = None):
         "hda_prefill_workspace_bytes": (i64, [pi32, i64, i32, i32, i32]),
         "hda_prefill": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp, i32, pi32,
                                        vp, pi32, vp, i64, vp, vp]),
+        "hda_router_split_weights": (ctypes.c_int, [vp, i64, vp, vp, vp]),
+        "hda_router_workspace_bytes": (i64, [i32, i32, i32]),
+        "hda_router_gemm": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
         "hda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "hda_version": (ctypes.c_int, []),
         "hda_params_bytes": (i64, []),
@@ -300,6 +304,60 @@ def hda_prefill(params: hda_params, q, k_pages, v_pages, block_table, kv_lens, n
                          _ptr(out), _stream(stream))
     if st != HDA_OK:
         raise HdaError(st, "hda_prefill")
+
+
+def hda_router_split_weights(w, w_hi, w_lo, stream=None) -> None:
+    """Enqueue the split of fp32 weights w (device) into bf16 hi / lo."""
+    n = w.numel() if hasattr(w, "numel") else int(w)
+    st = load_library().hda_router_split_weights(_ptr(w), n, _ptr(w_hi), _ptr(w_lo),
+                                                 _stream(stream))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_router_split_weights")
+
+
+def hda_router_workspace_bytes(tokens: int, experts: int, hidden: int) -> int:
+    return load_library().hda_router_workspace_bytes(int(tokens), int(experts), int(hidden))
+
+
+def hda_router_gemm(x, w_hi, w_lo, tokens: int, experts: int, hidden: int, out, workspace=None,
+                    workspace_bytes: int = 0, stream=None) -> None:
+    """Enqueue out = x hi^T + (x lo^T)/256 (see include/hda.h)."""
+    if workspace is not None and hasattr(workspace, "numel"):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = load_library().hda_router_gemm(_ptr(x), _ptr(w_hi), _ptr(w_lo), int(tokens),
+                                        int(experts), int(hidden), _ptr(out), _ptr(workspace),
+                                        int(workspace_bytes), _stream(stream))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_router_gemm")
+
+
+class RouterWeights:
+    """Device-resident split router weights plus a workspace; convenience for
+    tests and the bench."""
+
+    def __init__(self, w, device="cuda:0"):
+        import torch
+        self.w = torch.as_tensor(w, dtype=torch.float32).to(device).contiguous()
+        self.E, self.H = self.w.shape
+        self.hi = torch.empty((self.E, self.H), dtype=torch.int16, device=device)
+        self.lo = torch.empty_like(self.hi)
+        self.device = device
+        self._ws = None
+        hda_router_split_weights(self.w, self.hi, self.lo)
+
+    def logits(self, x, out=None, stream=None):
+        import torch
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, self.E), dtype=torch.float32, device=self.device)
+        need = hda_router_workspace_bytes(T, self.E, self.H)
+        if need < 0:
+            raise HdaError(HDA_ERR_UNSUPPORTED, "hda_router_workspace_bytes")
+        if need and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        hda_router_gemm(x, self.hi, self.lo, T, self.E, self.H, out,
+                        self._ws if need else None, need, stream)
+        return out
 
 
 def _ptr(x):

@@ -374,3 +374,45 @@ def test_prefill_argument_errors(lib):
     assert call(_params(**base), plan=plan[:-1]) == E.HDA_ERR_BAD_PLAN
     assert call(_params(**base, workspace=None)) == E.HDA_ERR_WORKSPACE
     assert call(_params(**base, workspace_bytes=64)) == E.HDA_ERR_WORKSPACE
+
+
+def test_router_workspace_bytes_shapes(lib):
+    """The launch-shape arithmetic on the host: every accepted shape gives a
+    whole number of partial tiles (S x T x E x 4 bytes, or none), small and
+    odd hidden sizes included; rejected shapes give -1."""
+    for T in (1, 5, 16, 33, 64, 100, 1000, 20000):
+        for E in (1, 24, 64, 256):
+            for H in (32, 64, 96, 128, 160, 1024, 7168):
+                n = hda.hda_router_workspace_bytes(T, E, H)
+                assert n >= 0 and n % (4 * T * E) == 0
+                S = n // (4 * T * E)
+                assert S == 0 or 2 <= S <= -(-H // 128)
+    assert hda.hda_router_workspace_bytes(4, 8, 48) == -1
+    assert hda.hda_router_workspace_bytes(0, 8, 64) == -1
+    assert hda.hda_router_workspace_bytes(4, 8, 0) == -1
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers are only used without a GPU")
+def test_router_argument_errors(lib):
+    import ctypes
+    E = hda
+    vp = ctypes.c_void_p
+
+    def call(x=FAKE, hi=FAKE + 0x1000, lo=FAKE + 0x2000, T=8, Ex=16, H=64, out=FAKE + 0x3000,
+             ws=None, wsb=0):
+        return lib.hda_router_gemm(vp(x) if x else None, vp(hi) if hi else None,
+                                   vp(lo) if lo else None, T, Ex, H, vp(out) if out else None,
+                                   vp(ws) if ws else None, wsb, None)
+
+    assert call(x=None) == E.HDA_ERR_INVALID_ARG
+    assert call(out=None) == E.HDA_ERR_INVALID_ARG
+    assert call(T=0) == E.HDA_ERR_INVALID_ARG
+    assert call(H=48) == E.HDA_ERR_UNSUPPORTED
+    assert call(x=FAKE + 8) == E.HDA_ERR_INVALID_ARG                 # not 16-byte aligned
+    assert call(T=1 << 20, H=1024) == E.HDA_ERR_UNSUPPORTED          # beyond 32-bit offsets
+    need = hda.hda_router_workspace_bytes(8, 16, 64)
+    if need > 0:
+        assert call() == E.HDA_ERR_WORKSPACE
+        assert call(ws=FAKE + 0x4000, wsb=need - 4) == E.HDA_ERR_WORKSPACE
+    assert lib.hda_router_split_weights(None, 10, vp(FAKE), vp(FAKE), None) == E.HDA_ERR_INVALID_ARG
+    assert lib.hda_router_split_weights(vp(FAKE), 0, vp(FAKE), vp(FAKE), None) == E.HDA_ERR_INVALID_ARG
