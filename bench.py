@@ -289,9 +289,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 
 def bench_router(args):
     """Router GEMM sweep over token counts (decode batch to prefill): the
-    fused split kernel (two bf16 MFMA products per K step, fp32 accumulate)
-    timed with HIP events on the launch stream, its roofline position, and
-    torch's fp32 GEMM on the same data as context."""
+    fused split kernel (two bf16 MFMA products per K step, fp32 accumulate),
+    device time per call from a replayed HIP graph of 10 calls (HIP events
+    on the replay stream), its roofline position, and torch's fp32 GEMM on
+    the same data, timed the same way, as context."""
     import numpy as np
     import torch
     import load_balanced_split_step_amd.hda as hda
@@ -311,7 +312,7 @@ def bench_router(args):
         out = torch.empty((T, E), dtype=torch.float32, device="cuda:0")
 
         def run_ours():
-            rw.logits(x, out=out, stream=stream)
+            rw.logits(x, out=out, stream=torch.cuda.current_stream())
 
         def run_f32():
             torch.matmul(xf, wf.T)
@@ -320,15 +321,25 @@ def bench_router(args):
         for name, fn in (("ours", run_ours), ("torch_fp32", run_f32)):
             for _ in range(args.warmup):
                 fn()
+            torch.cuda.synchronize()
+            # device time per call: a HIP graph of `calls` back-to-back calls,
+            # replayed, so that host launch costs do not enter
+            calls = 10
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(calls):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(max(1, args.steps // 2)):
+                g.replay()
+            e1.record()
             torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(args.steps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            res[name] = e0.elapsed_time(e1) * 1e3 / args.steps          # us per call
+            res[name] = e0.elapsed_time(e1) * 1e3 / (calls * max(1, args.steps // 2))
+            del g
         flops = 4.0 * T * H * E                                          # two products
         ws = hda.hda_router_workspace_bytes(T, E, H)
         nbytes = T * H * 2 + E * H * 4 + T * E * 4 + 2 * ws
@@ -357,7 +368,7 @@ def bench_router(args):
                    "hidden": H, "experts": E},
         "roofline": {"bound": head["bound"], "achieved": head["achieved"], "peak": head["peak"],
                      "unit": head["unit"], "frac": head["frac"], "traffic": None,
-                     "kernel": "hda_router_gemm_kernel (HIP events on the launch stream)"},
+                     "kernel": "hda_router_gemm_lds_kernel at 16384 tokens (graph replay, HIP events)"},
         "sweep": sweep,
     }
     print(json.dumps(res), flush=True)

@@ -10,7 +10,7 @@
 //   out[t][e] = sum_h x[t][h] hi[e][h] + (sum_h x[t][h] lo[e][h]) / 256
 // with fp32 accumulation on v_mfma_f32_16x16x32_bf16.
 //
-// Tiling.  A workgroup owns TM tokens (32 or 64) x 64 experts and a range of
+// Tiling (small batches).  A workgroup owns TM tokens (32 or 64) x 64 experts and a range of
 // the hidden dimension; its 4 waves take interleaved 32-wide K steps of that
 // range, each holding the full TM x 64 tile for both products (2 x TM/16 x 4
 // MFMA blocks), and combine through LDS at the end.  The activation fragment
@@ -89,22 +89,42 @@ __global__ __launch_bounds__(64 * kWaves) void hda_router_gemm_kernel(RouterArgs
 #pragma unroll
   for (int n = 0; n < 4; ++n) woff[n] = ((int64_t)(e0 + 16 * n + i) * a.H + 8 * kg) * 2;
 
-  for (int k = kb + kStepK * wave; k < ke; k += kStepK * kWaves) {
+  // two fragment sets: the loads of the wave's next K step are in flight
+  // while the current step multiplies
+  struct Frags {
     bf16x8 xa[MB], wh[4], wl[4];
+  };
+  auto load = [&](Frags& f, int k) {
 #pragma unroll
-    for (int m = 0; m < MB; ++m) xa[m] = load8(xr, xoff[m] + 2 * k);
+    for (int m = 0; m < MB; ++m) f.xa[m] = load8(xr, xoff[m] + 2 * k);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      wh[n] = load8(hr, woff[n] + 2 * k);
-      wl[n] = load8(lr, woff[n] + 2 * k);
+      f.wh[n] = load8(hr, woff[n] + 2 * k);
+      f.wl[n] = load8(lr, woff[n] + 2 * k);
     }
+  };
+  auto mma = [&](const Frags& f) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        acc_hi[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[m], wh[n], acc_hi[m][n], 0, 0, 0);
-        acc_lo[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[m], wl[n], acc_lo[m][n], 0, 0, 0);
+        acc_hi[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.xa[m], f.wh[n], acc_hi[m][n], 0, 0, 0);
+        acc_lo[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.xa[m], f.wl[n], acc_lo[m][n], 0, 0, 0);
       }
+  };
+  constexpr int kStride = kStepK * kWaves;
+  Frags f0, f1;
+  int k = kb + kStepK * wave;
+  if (k < ke) load(f0, k);
+  while (k < ke) {
+    const int k1 = k + kStride;
+    if (k1 < ke) load(f1, k1);
+    mma(f0);
+    if (k1 >= ke) break;
+    const int k2 = k1 + kStride;
+    if (k2 < ke) load(f0, k2);
+    mma(f1);
+    k = k2;
   }
   // combine the two products, then the four waves
 #pragma unroll
@@ -124,14 +144,128 @@ __global__ __launch_bounds__(64 * kWaves) void hda_router_gemm_kernel(RouterArgs
   }
 }
 
-// Sum of the S partial tiles, in slot order.
+// Large batches: 128 tokens x 128 experts per workgroup, K sliced by 32 and
+// staged through LDS (double-buffered: the next slice is loaded into
+// registers while the current one is multiplied).  Wave (wm, wn) owns the
+// 64 x 64 sub-tile at (64 wm, 64 wn): 4 x 4 blocks for each product.  LDS
+// rows are 64 bytes (32 bf16), so the 64 lanes of a fragment read cover one
+// contiguous KiB and do not conflict.
+constexpr int kBigM = 128, kBigN = 128;
+
+struct BigStage {
+  uint16_t a[kBigM][kStepK];
+  uint16_t bh[kBigN][kStepK];
+  uint16_t bl[kBigN][kStepK];
+};
+
+__global__ __launch_bounds__(64 * kWaves, 2) void hda_router_gemm_lds_kernel(RouterArgs a) {
+  __shared__ BigStage st[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, kg = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.x * kBigM, e0 = blockIdx.y * kBigN;
+  const int kb = blockIdx.z * a.k_per_wg;
+  const int ke = min(a.H, kb + a.k_per_wg);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (int64_t)a.T * a.H * 2);
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.w_hi, (int64_t)a.E * a.H * 2);
+  const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.w_lo, (int64_t)a.E * a.H * 2);
+
+  // global -> LDS copy: 512 16-byte chunks per tile, two per thread; chunk c
+  // is row c / 4, k offset 8 (c % 4)
+  int64_t ga[2], gb[2];
+  int lrow[2], lcol[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = tid + 256 * u;
+    lrow[u] = c >> 2;
+    lcol[u] = 8 * (c & 3);
+    ga[u] = ((int64_t)(t0 + lrow[u]) * a.H + lcol[u]) * 2;
+    gb[u] = ((int64_t)(e0 + lrow[u]) * a.H + lcol[u]) * 2;
+  }
+  u32x4 ra[2], rh[2], rl[2];
+  auto load = [&](int k) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      ra[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(ga[u] + 2 * k), 0, 0));
+      rh[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hr, (int)(gb[u] + 2 * k), 0, 0));
+      rl[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(lr, (int)(gb[u] + 2 * k), 0, 0));
+    }
+  };
+  auto store = [&](BigStage& s) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      *reinterpret_cast<u32x4*>(&s.a[lrow[u]][lcol[u]]) = ra[u];
+      *reinterpret_cast<u32x4*>(&s.bh[lrow[u]][lcol[u]]) = rh[u];
+      *reinterpret_cast<u32x4*>(&s.bl[lrow[u]][lcol[u]]) = rl[u];
+    }
+  };
+
+  f32x4 acc_hi[4][4], acc_lo[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      acc_hi[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_lo[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  const int nk = (ke - kb) / kStepK;
+  load(kb);
+  store(st[0]);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + 1 < nk) load(kb + kStepK * (ks + 1));
+    const BigStage& s = st[ks & 1];
+    bf16x8 fa[4], fh[4], fl[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      fa[m] = *reinterpret_cast<const bf16x8*>(&s.a[64 * wm + 16 * m + i][8 * kg]);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      fh[n] = *reinterpret_cast<const bf16x8*>(&s.bh[64 * wn + 16 * n + i][8 * kg]);
+      fl[n] = *reinterpret_cast<const bf16x8*>(&s.bl[64 * wn + 16 * n + i][8 * kg]);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        acc_hi[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fh[n], acc_hi[m][n], 0, 0, 0);
+        acc_lo[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fl[n], acc_lo[m][n], 0, 0, 0);
+      }
+    if (ks + 1 < nk) store(st[(ks + 1) & 1]);
+    __syncthreads();
+  }
+  float* dst = gridDim.z > 1 ? a.part + (int64_t)blockIdx.z * a.T * a.E : a.out;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 64 * wm + 16 * m + 4 * kg + r, e = e0 + 64 * wn + 16 * n + i;
+        if (t < a.T && e < a.E)
+          dst[(int64_t)t * a.E + e] = acc_hi[m][n][r] + acc_lo[m][n][r] * kResidualScale;
+      }
+}
+
+// Sum of the S partial tiles, in slot order.  The loads of a batch of 16
+// partials are all issued before any is added (one memory round trip per
+// batch instead of one per partial); the additions keep slot order.
 __global__ __launch_bounds__(256) void hda_router_reduce_kernel(const float* __restrict__ part,
                                                                 float* __restrict__ out,
                                                                 int64_t n, int S) {
+  constexpr int kBatch = 16;
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (j >= n) return;
-  float acc = part[j];
-  for (int s = 1; s < S; ++s) acc += part[(int64_t)s * n + j];
+  float acc = 0.f;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = s0 + u < S ? part[(int64_t)(s0 + u) * n + j] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (s0 + u < S) acc = (s0 + u == 0) ? v[u] : acc + v[u];
+  }
   out[j] = acc;
 }
 
@@ -152,10 +286,34 @@ __global__ __launch_bounds__(256) void hda_router_split_kernel(const float* __re
 // Launch shape: token tile, expert tiles, and the hidden split S.
 struct RouterShape {
   int mb, tiles_t, tiles_e, S, k_per_wg;
+  bool big;   // the LDS-staged 128 x 128 kernel
 };
+
+// The LDS-staged 128 x 128 kernel takes a batch when its tiles, split along
+// the hidden dimension into ranges of at least 16 K steps, reach 256
+// workgroups (one per compute unit); smaller batches take the split-K
+// register kernel (measured: 64 large tiles alone leave three quarters of
+// the compute units idle).
+constexpr int64_t kBigMinGroups = 256;
+constexpr int kBigMinSteps = 16;
 
 RouterShape router_shape(int32_t T, int32_t E, int32_t H) {
   RouterShape r;
+  const int64_t big_tiles = (int64_t)((T + kBigM - 1) / kBigM) * ((E + kBigN - 1) / kBigN);
+  const int64_t max_split = H / (kStepK * kBigMinSteps);
+  if (max_split >= 1 && big_tiles * max_split >= kBigMinGroups) {
+    r.big = true;
+    r.mb = 8;
+    r.tiles_t = (T + kBigM - 1) / kBigM;
+    r.tiles_e = (E + kBigN - 1) / kBigN;
+    int64_t S = (kBigMinGroups + big_tiles - 1) / big_tiles;
+    S = S < 1 ? 1 : (S > max_split ? max_split : S);
+    const int steps = H / kStepK;
+    r.k_per_wg = (int)((steps + S - 1) / S) * kStepK;
+    r.S = (H + r.k_per_wg - 1) / r.k_per_wg;
+    return r;
+  }
+  r.big = false;
   r.mb = T <= 32 ? 2 : 4;
   r.tiles_t = (T + 16 * r.mb - 1) / (16 * r.mb);
   r.tiles_e = (E + kTileE - 1) / kTileE;
@@ -215,7 +373,9 @@ extern "C" int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo
   a.k_per_wg = r.k_per_wg;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const dim3 grid(r.tiles_t, r.tiles_e, r.S);
-  if (r.mb == 2)
+  if (r.big)
+    hipLaunchKernelGGL(hda_router_gemm_lds_kernel, grid, dim3(64 * kWaves), 0, hs, a);
+  else if (r.mb == 2)
     hipLaunchKernelGGL(hda_router_gemm_kernel<2>, grid, dim3(64 * kWaves), 0, hs, a);
   else
     hipLaunchKernelGGL(hda_router_gemm_kernel<4>, grid, dim3(64 * kWaves), 0, hs, a);

@@ -39,8 +39,11 @@ def test_split_bit_exact():
     assert np.array_equal(rw.lo.cpu().numpy().view(np.uint16), lo)
 
 
+# the last four take the LDS-staged 128 x 128 kernel (with 13, 4 and 1
+# hidden splits; the last with ragged token and expert edges)
 SHAPES = [(1, 256, 7168), (5, 24, 96), (16, 256, 7168), (33, 100, 7168), (64, 256, 7168),
-          (100, 256, 7168), (257, 72, 1024), (600, 256, 7168)]
+          (100, 256, 7168), (257, 72, 1024), (600, 256, 7168), (1280, 256, 7168),
+          (4096, 256, 7168), (16384, 256, 7168), (16300, 300, 1024)]
 
 
 @pytest.mark.parametrize("T,E,H", SHAPES)
