@@ -371,6 +371,24 @@ def bench_router(args):
                      "kernel": "hda_router_gemm_lds_kernel at 16384 tokens (graph replay, HIP events)"},
         "sweep": sweep,
     }
+    if not args.no_cpu:
+        # the fp64 oracle on a bounded sample: exact split products of
+        # 1024-token batches, repeated until the time budget is spent
+        import oracle
+        from threadpoolctl import threadpool_info
+        log("timing the fp64 router oracle on a bounded sample")
+        x = big["x"][:1024]
+        hi, lo = oracle.split_router_weights(big["w"])
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.router_split_reference(x, hi, lo)
+            n += 1
+        secs = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        res["cpu_baseline"] = {"value": round(n * 4.0 * 1024 * H * E / secs / 1e12, 4),
+                               "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"{n} exact split products of 1024 tokens in {secs:.1f} s; "
+                                         f"numpy fp64, BLAS threads {threads}"}
     print(json.dumps(res), flush=True)
 
 
