@@ -294,15 +294,21 @@ int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
  * position kv_len_b - q_len_b + r and attends causally to tokens 0..pos.
  * q and out are packed request after request: [sum q_len][Hq][D].
  *
- * The rows of each request are grouped into blocks of
- * hda_prefill_rows_per_block() rows, whose (row, q head) pairs fill the 16
- * matrix-core columns the decode kernel gives one kv head's q heads.  Each
- * block enters the decode tile planner as one "request" whose length is its
- * causal extent, so hda_plan is used unchanged (its batch = the number of
- * blocks) and a block's partial results are merged as a request's are.
+ * The rows of each request are grouped into blocks; the (row, q head) pairs
+ * of hda_prefill_rows_per_block() rows fill the 16 matrix-core columns the
+ * decode kernel gives one kv head's q heads.  Each block enters the decode
+ * tile planner as one "request" whose length is its causal extent, so
+ * hda_plan is used unchanged (its batch = the number of blocks) and a
+ * block's partial results are merged as a request's are.  Blocks of up to
+ * that many rows run on the decode kernel's column shape, the chunks of an
+ * item split over the 4 waves; blocks of up to 4x that many rows (for long
+ * query runs) run with each K/V chunk loaded once into LDS and shared by
+ * the 4 waves, wave w taking the block's w-th group of rows -- a quarter of
+ * the bytes requested per query row.
  */
 
-/* Rows per block: 16 / (Hq / Hkv), or -1 for a group above 16. */
+/* Rows per block that fill the 16 columns: 16 / (Hq / Hkv), or -1 for a
+ * group above 16.  hda_prefill accepts blocks of up to 4x this many rows. */
 int32_t hda_prefill_rows_per_block(int32_t n_q_heads, int32_t n_kv_heads);
 
 /*
@@ -318,12 +324,15 @@ int hda_prefill_rows(const int32_t* q_lens, const int32_t* kv_lens, int32_t batc
                      int32_t rows_per_block, int32_t* rows, int32_t* row_lens,
                      int64_t capacity, int64_t* n_rows);
 
-/* Workspace bytes for hda_prefill with this plan: partial outputs float32
- * [P][rows_per_block][Hq][D], then partial log-sum-exps float32
- * [P][rows_per_block][Hq], each region aligned to 256 bytes.  -1 on a
- * malformed header or sizes. */
+/* Workspace bytes for hda_prefill with this plan and blocks of at most
+ * rows_per_block rows (1 .. 4 x hda_prefill_rows_per_block): partial outputs
+ * float32 [P][rows_per_block][Hq][D], then partial log-sum-exps float32
+ * [P][rows_per_block][Hq], each region aligned to 256 bytes (hda_prefill
+ * lays them out with the largest block's row count).  -1 on a malformed
+ * header or sizes. */
 int64_t hda_prefill_workspace_bytes(const int32_t* plan, int64_t plan_len, int32_t n_q_heads,
-                                    int32_t n_kv_heads, int32_t head_dim);
+                                    int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t rows_per_block);
 
 /*
  * One multi-token attention step enqueued on `stream`: the tile kernel over
@@ -344,7 +353,7 @@ int64_t hda_prefill_workspace_bytes(const int32_t* plan, int64_t plan_len, int32
  *   plan_dev     hda_plan(row_lens, n_rows, tile_len, W), as for hda_decode
  *   out          [device] float32 [n_q][Hq][D]
  * Errors (host, before any launch): HDA_ERR_INVALID_ARG (incl. a block out
- * of range or with more rows than hda_prefill_rows_per_block),
+ * of range or with more than 4 x hda_prefill_rows_per_block rows),
  * HDA_ERR_UNSUPPORTED, HDA_ERR_BAD_PLAN, HDA_ERR_WORKSPACE; HDA_ERR_HIP if a
  * launch fails.
  */

@@ -900,6 +900,213 @@ __device__ inline void process_item_fp8n(const Args& a, const int32_t* __restric
   finish_item<128>(a, sm, b, g, h, slot, vsc, 8.f, tid);
 }
 
+// ---- multi-token rows with the K/V chunk shared through LDS ----
+//
+// For blocks of more than 16/g query rows: the workgroup loads each 32-token
+// K/V chunk of the item once into LDS (256 threads, 16-byte pieces,
+// double-buffered: the next chunk's pieces are in registers while the
+// current one is multiplied), and all four waves use it, wave w for the
+// block's rows [w*16/g, (w+1)*16/g) -- 16 columns each, the decode kernel's
+// column shape.  The bytes requested from memory per item drop by the
+// number of busy waves.  Each wave runs the same per-chunk arithmetic
+// (compute_chunk) on registers filled from LDS and finishes its own columns
+// (no cross-wave combine).  LDS rows are padded by 16 bytes so the
+// fragment reads of 16 rows do not share banks.
+template <int D, bool FP8>
+struct SharedChunk {
+  static constexpr int RB = Geo<D, FP8>::RB;
+  static constexpr int RS = RB + 16;                 // padded row stride
+  uint8_t k[kChunk * RS];
+  uint8_t v[kChunk * RS];
+};
+
+template <int D, bool FP8, bool PAGE>
+__device__ inline void process_item_shared(const Args& a, const int32_t* __restrict__ block_table,
+                                           SharedChunk<D, FP8> (&buf)[2], int b, int k0,
+                                           int k1, int slot, int L, int qrow0, int nq, int pos0,
+                                           int h, int wave, int lane, int tid) {
+  using G = Geo<D, FP8>;
+  using SC = SharedChunk<D, FP8>;
+  constexpr int PPR = G::RB / 16;                    // 16-byte pieces per row
+  constexpr int PIECES = 2 * kChunk * PPR;           // K and V of one chunk
+  constexpr int PER_T = (PIECES + 64 * kWaves - 1) / (64 * kWaves);
+  const int i = lane & 15, kg = lane >> 4;
+  const int g = a.group;
+  const int qbw = kMaxGroup / g;                     // rows per wave
+  const int r0 = wave * qbw;                         // wave's first row in the block
+  const int nqw = max(0, min(qbw, nq - r0));         // rows this wave owns
+  float qk = a.qk_scale_log2, vsc = a.v_scale;
+  if (!PAGE && a.scale_mode == HDA_SCALE_HEAD) {
+    qk *= a.k_scales[h];
+    vsc *= a.v_scales[h];
+  }
+  const int qr = i / g, hh = i - qr * g;
+  const bool col_live = qr < nqw;
+  const int lim = col_live ? pos0 + r0 + qr : 0x7fffffff;
+  const int lim_min = pos0 + r0;                     // the wave's first row
+  const int lim_max = pos0 + r0 + nqw - 1;           // its last row (uniform)
+  const int64_t qbase = ((int64_t)(qrow0 + r0 + qr) * a.n_q_heads + (int64_t)h * g + hh) * D;
+  bf16x8 qop[G::STEPS];
+#pragma unroll
+  for (int s2 = 0; s2 < G::STEPS; ++s2) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (col_live) v = *reinterpret_cast<const u32x4*>(a.q + qbase + qk_dim<FP8>(s2, kg));
+    qop[s2] = __builtin_bit_cast(bf16x8, v);
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[G::DPL];
+#pragma unroll
+  for (int nb = 0; nb < G::DPL; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // cooperative copy of chunk c into registers: piece p = tid + 256 u is
+  // tensor p / (32 PPR), row (p % (32 PPR)) / PPR, 16-byte column p % PPR
+  u32x4 stage[PER_T];
+  float sks[2] = {1.f, 1.f}, svs[2] = {1.f, 1.f};    // page factors of the two halves
+  auto fetch = [&](int c) {
+    const int t0 = c * kChunk;
+    int pg[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int t = t0 + 16 * hf;
+      const int pidx = t >> a.log2_ps;
+      pg[hf] = (t < L && pidx < a.max_pages) ? block_table[(int64_t)b * a.max_pages + pidx] : -1;
+      if constexpr (PAGE) {
+        if (pg[hf] >= 0 && pg[hf] < a.num_pages) {
+          sks[hf] = a.k_scales[(int64_t)pg[hf] * a.n_kv_heads + h];
+          svs[hf] = a.v_scales[(int64_t)pg[hf] * a.n_kv_heads + h];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int pc = tid + 64 * kWaves * u;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (pc < PIECES) {
+        const int tensor = pc / (kChunk * PPR), rem = pc - tensor * (kChunk * PPR);
+        const int row = rem / PPR, col = rem - row * PPR;
+        const int t = t0 + row, page = pg[row >> 4];
+        if (t < L && page >= 0 && page < a.num_pages) {
+          const uint8_t* base = tensor ? a.v_pages : a.k_pages;
+          const int64_t off = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
+                              (int64_t)(t & (a.page_size - 1)) * G::RB + 16 * col;
+          x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+        }
+      }
+      stage[u] = x;
+    }
+  };
+  auto put = [&](SC& sc) {
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int pc = tid + 64 * kWaves * u;
+      if (pc < PIECES) {
+        const int tensor = pc / (kChunk * PPR), rem = pc - tensor * (kChunk * PPR);
+        const int row = rem / PPR, col = rem - row * PPR;
+        uint8_t* dst = (tensor ? sc.v : sc.k) + row * SC::RS + 16 * col;
+        *reinterpret_cast<u32x4*>(dst) = stage[u];
+      }
+    }
+  };
+
+  const int c_first = k0 / kChunk, c_last = (k1 - 1) / kChunk;
+  float cks[2], cvs[2];
+  fetch(c_first);
+  __syncthreads();                  // the previous item's readers are done with buf
+  put(buf[0]);
+  cks[0] = sks[0]; cks[1] = sks[1]; cvs[0] = svs[0]; cvs[1] = svs[1];
+  __syncthreads();
+  for (int c = c_first; c <= c_last; ++c) {
+    const int cur = (c - c_first) & 1;
+    if (c < c_last) fetch(c + 1);
+    // the wave's columns see no token of this chunk: skip its arithmetic
+    if (nqw > 0 && c * kChunk <= lim_max) {
+      const SC& sc = buf[cur];
+      Chunk<D, FP8> ch;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int u = 0; u < G::KL; ++u)
+          ch.k[hf][u] = *reinterpret_cast<const u32x4*>(sc.k + (16 * hf + i) * SC::RS + 64 * u + 16 * kg);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint8_t* row = sc.v + (16 * (j >> 2) + 4 * kg + (j & 3)) * SC::RS + i * G::VW * 4;
+        if constexpr (G::VW == 4) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(row);
+          ch.v[j][0] = x[0]; ch.v[j][1] = x[1]; ch.v[j][2] = x[2]; ch.v[j][3] = x[3];
+        } else if constexpr (G::VW == 2) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(row);
+          ch.v[j][0] = x[0]; ch.v[j][1] = x[1];
+        } else {
+          ch.v[j][0] = *reinterpret_cast<const uint32_t*>(row);
+        }
+      }
+      if constexpr (PAGE) {
+        ch.ks[0] = cks[0]; ch.ks[1] = cks[1]; ch.vs[0] = cvs[0]; ch.vs[1] = cvs[1];
+      }
+      compute_chunk<D, FP8, PAGE, true>(ch, qop, c, k0, k1, lim, lim_min, qk, kg, m_run, l_run,
+                                        acc);
+    }
+    if (c < c_last) {
+      put(buf[cur ^ 1]);
+      cks[0] = sks[0]; cks[1] = sks[1]; cvs[0] = svs[0]; cvs[1] = svs[1];
+    }
+    __syncthreads();
+  }
+
+  // finish the wave's own columns: l per column from the score layout
+  // (lane i holds column i), o = acc / l in the accumulator layout
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (nqw == 0) return;
+  const int ncols = nqw * g;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int col = 4 * kg + r;
+    const float lc = __shfl(l_tot, col);
+    if (col >= ncols) continue;
+    const int cq = col / g;
+    const int64_t hq = (int64_t)h * g + (col - cq * g);
+    const float inv = lc > 0.f ? vsc / lc : 0.f;
+    float* dst;
+    if (slot < 0)
+      dst = a.out + ((int64_t)(qrow0 + r0 + cq) * a.n_q_heads + hq) * D;
+    else
+      dst = a.part_o + (((int64_t)slot * a.qb + r0 + cq) * a.n_q_heads + hq) * D;
+#pragma unroll
+    for (int nb = 0; nb < G::DPL; ++nb) dst[G::DPL * i + nb] = acc[nb][r] * inv;
+  }
+  if (slot >= 0 && kg == 0 && i < ncols) {
+    const int cq = i / g;
+    const int64_t prow = ((int64_t)slot * a.qb + r0 + cq) * a.n_q_heads + (int64_t)h * g + (i - cq * g);
+    a.part_lse[prow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+template <int D, bool FP8, bool PAGE>
+__global__ __launch_bounds__(64 * kWaves, 2) void hda_prefill_shared_kernel(
+    Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ plan) {
+  __shared__ SharedChunk<D, FP8> buf[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x % a.n_kv_heads;
+  const int w = blockIdx.x / a.n_kv_heads;
+  const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
+  const int32_t* items = wg_ptr + a.n_wg + 1;
+  const int32_t* __restrict__ rows = a.rows;
+  const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
+  for (int it = it_begin; it < it_end; ++it) {
+    const int rho = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
+              slot = items[4 * it + 3];
+    if ((unsigned)rho >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
+    const int b = rows[4 * rho], qrow0 = rows[4 * rho + 1], nq = rows[4 * rho + 2],
+              pos0 = rows[4 * rho + 3];
+    process_item_shared<D, FP8, PAGE>(a, block_table, buf, b, k0, k1, slot, seq_lens[b], qrow0,
+                                      nq, pos0, h, wave, lane, tid);
+  }
+}
+
 // ---- device-side planning: the host planner's arithmetic, per wave ----
 // T tiles over W workgroups, the first r = T mod W taking q + 1 tiles.
 struct SplitDev {
@@ -1272,8 +1479,12 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
 
 template <int D, bool FP8, bool PAGE>
 hipError_t launch_prefill(Args a, int grid, int n_rows, hipStream_t stream, void* split_event) {
-  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, false, PAGE, false, true>), dim3(grid),
-                     dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens, a.plan);
+  if (a.qb > kMaxGroup / a.group)      // blocks larger than one wave's columns: shared chunks
+    hipLaunchKernelGGL((hda_prefill_shared_kernel<D, FP8, PAGE>), dim3(grid), dim3(64 * kWaves),
+                       0, stream, a, a.block_table, a.seq_lens, a.plan);
+  else
+    hipLaunchKernelGGL((hda_decode_kernel<D, FP8, false, PAGE, false, true>), dim3(grid),
+                       dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens, a.plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (split_event) {
@@ -1489,20 +1700,23 @@ extern "C" int hda_prefill(const hda_params* p, const void* q, const void* k_pag
   const int64_t R = plan_host[1], W = plan_host[3], N = plan_host[5], P = plan_host[6];
   if (R < 1 || W < 1 || N < 1 || P < 0 || plan_len != HDA_PLAN_HEADER_INTS + (W + 1) + 4 * N + R + 1)
     return HDA_ERR_BAD_PLAN;
-  const int32_t qb = hda_prefill_rows_per_block(p->n_q_heads, p->n_kv_heads);
-  if (qb < 1) return HDA_ERR_UNSUPPORTED;
-  // every block inside its request and the packed q (the kernel trusts them)
+  const int32_t unit = hda_prefill_rows_per_block(p->n_q_heads, p->n_kv_heads);
+  if (unit < 1) return HDA_ERR_UNSUPPORTED;
+  // every block inside its request and the packed q (the kernel trusts
+  // them); the largest block sets the partial-slot stride and the kernel
+  int32_t qb = 1;
   for (int64_t r = 0; r < R; ++r) {
     const int32_t b = rows_host[4 * r], q0 = rows_host[4 * r + 1], nq = rows_host[4 * r + 2],
                   pos0 = rows_host[4 * r + 3];
-    if (b < 0 || b >= p->batch || nq < 1 || nq > qb || q0 < 0 || (int64_t)q0 + nq > n_q ||
-        pos0 < 0)
+    if (b < 0 || b >= p->batch || nq < 1 || nq > kWaves * unit || q0 < 0 ||
+        (int64_t)q0 + nq > n_q || pos0 < 0)
       return HDA_ERR_INVALID_ARG;
+    qb = nq > qb ? nq : qb;
   }
   const int64_t grid = W * p->n_kv_heads;
   if (grid > 0x7fffffffLL || R * qb * p->n_q_heads > 0x7fffffffLL) return HDA_ERR_UNSUPPORTED;
   const int64_t ws_need = hda_prefill_workspace_bytes(plan_host, plan_len, p->n_q_heads,
-                                                      p->n_kv_heads, p->head_dim);
+                                                      p->n_kv_heads, p->head_dim, qb);
   if (ws_need < 0) return HDA_ERR_BAD_PLAN;
   if (P > 0 && (!p->workspace || p->workspace_bytes < ws_need)) return HDA_ERR_WORKSPACE;
 

@@ -323,12 +323,16 @@ int hda_prefill_rows(const int32_t* q_lens, const int32_t* kv_lens, int32_t batc
 }
 
 int64_t hda_prefill_workspace_bytes(const int32_t* plan, int64_t plan_len, int32_t n_q_heads,
-                                    int32_t n_kv_heads, int32_t head_dim) {
+                                    int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t rows_per_block) {
   if (!plan || plan_len < HDA_PLAN_HEADER_INTS || n_q_heads < 1 || n_kv_heads < 1 ||
       head_dim < 1)
     return -1;
-  const int32_t qb = hda_prefill_rows_per_block(n_q_heads, n_kv_heads);
-  if (qb < 1 || plan[0] != HDA_PLAN_VERSION || plan[1] < 1 || plan[6] < 0) return -1;
+  const int32_t unit = hda_prefill_rows_per_block(n_q_heads, n_kv_heads);
+  const int32_t qb = rows_per_block;
+  if (unit < 1 || qb < 1 || qb > 4 * unit || plan[0] != HDA_PLAN_VERSION || plan[1] < 1 ||
+      plan[6] < 0)
+    return -1;
   const int64_t P = plan[6];
   return round_up(P * qb * n_q_heads * head_dim * 4, 256) + round_up(P * qb * n_q_heads * 4, 256);
 }

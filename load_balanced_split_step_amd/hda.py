@@ -114,7 +114,7 @@ def load_library(path: Optional[str] = None):
         "hda_plan_device": (ctypes.c_int, [vp, i32, i32, i32, vp, i64, vp]),
         "hda_prefill_rows_per_block": (i32, [i32, i32]),
         "hda_prefill_rows": (ctypes.c_int, [pi32, pi32, i32, i32, pi32, pi32, i64, pi64]),
-        "hda_prefill_workspace_bytes": (i64, [pi32, i64, i32, i32, i32]),
+        "hda_prefill_workspace_bytes": (i64, [pi32, i64, i32, i32, i32, i32]),
         "hda_prefill": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp, i32, pi32,
                                        vp, pi32, vp, i64, vp, vp]),
         "hda_router_split_weights": (ctypes.c_int, [vp, i64, vp, vp, vp]),
@@ -285,11 +285,12 @@ def hda_prefill_rows(q_lens, kv_lens, rows_per_block: int):
     return rows, row_lens
 
 
-def hda_prefill_workspace_bytes(plan, n_q_heads: int, n_kv_heads: int, head_dim: int) -> int:
+def hda_prefill_workspace_bytes(plan, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                                rows_per_block: int) -> int:
     lib = load_library()
     plan = np.ascontiguousarray(plan, dtype=np.int32)
     return lib.hda_prefill_workspace_bytes(_i32p(plan), plan.size, int(n_q_heads),
-                                           int(n_kv_heads), int(head_dim))
+                                           int(n_kv_heads), int(head_dim), int(rows_per_block))
 
 
 def hda_prefill(params: hda_params, q, k_pages, v_pages, block_table, kv_lens, n_q: int,
@@ -467,23 +468,27 @@ class DeviceBatch:
                         t["seq_lens"], tile_len, n_workgroups, out, stream)
         return out
 
-    def prefill_plan(self, q_lens, tile_len=None, n_workgroups=None):
+    def prefill_plan(self, q_lens, tile_len=None, n_workgroups=None, shared=False):
         """(rows, plan) for this batch's query rows (row blocks through the
-        decode planner); default launch shape from launch_config."""
+        decode planner); shared: blocks of 4x the column-filling size (K/V
+        chunks shared through LDS); default launch shape from launch_config."""
         kv = self.t["seq_lens"].cpu().numpy()
         qb = hda_prefill_rows_per_block(self.kw["n_q_heads"], self.kw["n_kv_heads"])
-        rows, row_lens = hda_prefill_rows(q_lens, kv, qb)
+        rows, row_lens = hda_prefill_rows(q_lens, kv, 4 * qb if shared else qb)
         tl, W = launch_config(row_lens, self.kw["n_kv_heads"])
         return rows, hda_plan(row_lens, tile_len or tl, n_workgroups or W)
 
-    def prefill_params(self, plan):
+    def prefill_params(self, plan, rows_per_block=None):
         p = hda_params(**self.kw)
         t = self.t
         if "k_scales" in t:
             p.k_scales = t["k_scales"].data_ptr()
             p.v_scales = t["v_scales"].data_ptr()
+        if rows_per_block is None:      # enough for either kernel
+            rows_per_block = 4 * hda_prefill_rows_per_block(self.kw["n_q_heads"],
+                                                            self.kw["n_kv_heads"])
         need = hda_prefill_workspace_bytes(plan, self.kw["n_q_heads"], self.kw["n_kv_heads"],
-                                           self.kw["head_dim"])
+                                           self.kw["head_dim"], rows_per_block)
         ws = self.workspace(need)
         p.workspace = ws.data_ptr()
         p.workspace_bytes = ws.numel()

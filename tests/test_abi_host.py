@@ -338,8 +338,10 @@ def test_prefill_workspace_bytes(lib):
     plan = hda.hda_plan(row_lens, 4, 3)
     P = int(plan[6])
     assert P == 2
-    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128) == up(P * 2 * 64 * 128 * 4) + up(P * 2 * 64 * 4)
-    assert hda.hda_prefill_workspace_bytes(plan, 64, 3, 128) == -1
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 2) == up(P * 2 * 64 * 128 * 4) + up(P * 2 * 64 * 4)
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 8) == up(P * 8 * 64 * 128 * 4) + up(P * 8 * 64 * 4)
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 9) == -1      # above 4 x 16/g
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 3, 128, 2) == -1
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="fake device pointers are only used without a GPU")
@@ -367,8 +369,8 @@ def test_prefill_argument_errors(lib):
     assert call(_params(**dict(base, kv_dtype=E.HDA_KV_FP8_E4M3, math=E.HDA_MATH_FP8,
                                v_layout=E.HDA_V_DIM_MAJOR, page_size=64))) == E.HDA_ERR_UNSUPPORTED
     assert call(_params(**base), n_q=8) == E.HDA_ERR_INVALID_ARG        # last block past n_q
-    bad = rows.copy(); bad[0, 2] = 3                                     # 3 rows > 2 per block
-    assert call(_params(**base), rows=bad) == E.HDA_ERR_INVALID_ARG
+    bad = rows.copy(); bad[0, 2] = 9                                     # 9 rows > 4 x 2 per block
+    assert call(_params(**base), rows=bad, n_q=20) == E.HDA_ERR_INVALID_ARG
     bad = rows.copy(); bad[1, 0] = 3                                     # request out of range
     assert call(_params(**base), rows=bad) == E.HDA_ERR_INVALID_ARG
     assert call(_params(**base), plan=plan[:-1]) == E.HDA_ERR_BAD_PLAN

@@ -45,15 +45,18 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("shared", [False, True], ids=["column-blocks", "shared-chunks"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_prefill_parity(name):
+def test_prefill_parity(name, shared):
+    """Blocks of 16/g rows (decode column shape), or of 4x that with each
+    K/V chunk loaded once into LDS for the 4 waves."""
     w, lens, qlens = CASES[name]
     inp = make_inputs(w, lengths=lens, q_lens=qlens)
     ref = ref_prefill(inp)
     dev = hda.DeviceBatch.from_inputs(inp)
-    qb = hda.hda_prefill_rows_per_block(w.n_q_heads, w.n_kv_heads)
+    qb = hda.hda_prefill_rows_per_block(w.n_q_heads, w.n_kv_heads) * (4 if shared else 1)
     rows, row_lens = hda.hda_prefill_rows(inp["q_lens"], inp["seq_lens"], qb)
-    plans = [("default", dev.prefill_plan(inp["q_lens"])[1])]
+    plans = [("default", dev.prefill_plan(inp["q_lens"], shared=shared)[1])]
     for tl, W in [(64, 7), (100, 13), (16, 300), (512, 2)]:
         plans.append((f"dyn-{tl}-{W}", hda.hda_plan(row_lens, tl, W)))
     plans.append(("static-3", hda.hda_plan_static(row_lens, 3)))
@@ -62,7 +65,8 @@ def test_prefill_parity(name):
         out = dev.prefill(rows, plan)
         torch.cuda.synchronize()
         err = max_err(out, ref)
-        print(f"{name} {pname}: {len(rows)} blocks, P={int(plan[6])}, max err {err:.3e}", flush=True)
+        print(f"{name} {pname} {'shared' if shared else 'columns'}: {len(rows)} blocks, "
+              f"P={int(plan[6])}, max err {err:.3e}", flush=True)
         assert err <= tol, (name, pname, err)
 
 
