@@ -50,9 +50,9 @@ def parse():
     ap.add_argument("--math", choices=["bf16", "fp8"], default="bf16",
                     help="product arithmetic: bf16 (cache widened to bf16) or fp8 (native fp8 "
                          "MFMA operands, V pages dim-major; fp8 cache only)")
-    ap.add_argument("--shared", choices=["auto", "yes", "no"], default="auto",
-                    help="multi-token workloads: row blocks of 4x16/group rows with K/V chunks "
-                         "shared through LDS (yes), of 16/group rows (no), or by mean query run")
+    ap.add_argument("--tiles", choices=["auto", "1", "2", "4", "8", "16"], default="auto",
+                    help="multi-token workloads: row blocks of this many tiles of 16/group rows "
+                         "(4 and 8: K/V chunks shared through LDS); auto: by the mean query run")
     ap.add_argument("--tile-len", type=int, default=None)
     ap.add_argument("--workgroups", type=int, default=None)
     ap.add_argument("--copies", type=int, default=4, help="KV pool copies rotated over")
@@ -187,9 +187,13 @@ def bench_prefill(args, w, inp):
     for _ in range(max(0, args.copies - 1)):
         copies.append((dev.t["k_pages"].clone(), dev.t["v_pages"].clone()))
     unit = hda.hda_prefill_rows_per_block(w.n_q_heads, w.n_kv_heads)
-    shared = (args.shared == "yes" or
-              (args.shared == "auto" and float(np.mean(qlens)) > unit))
-    qb = 4 * unit if shared else unit
+    def block_rows():
+        if args.tiles == "auto":
+            return hda.hda_prefill_block_rows(qlens, w.n_q_heads, w.n_kv_heads)
+        return int(args.tiles) * unit
+
+    qb = block_rows()
+    tiles = qb // unit
     rows, row_lens = hda.hda_prefill_rows(qlens, lens, qb)
     tl, W = hda.launch_config(row_lens, w.n_kv_heads)
     tl = args.tile_len or tl
@@ -212,7 +216,7 @@ def bench_prefill(args, w, inp):
         j = s % NB
         if used[j]:
             done_ev[j].synchronize()
-        r, rl = hda.hda_prefill_rows(qlens, lens, qb)                    # row blocks
+        r, rl = hda.hda_prefill_rows(qlens, lens, block_rows())          # row blocks
         pin_rows[j].numpy()[:] = r.reshape(-1)
         n = hda.hda_plan_into(rl, tl, W, pin_plan[j].numpy())           # the decode planner
         d_rows[j].copy_(pin_rows[j], non_blocking=True)
@@ -261,7 +265,8 @@ def bench_prefill(args, w, inp):
     achieved = algo / (kmean * 1e-3) / 1e9
     log(f"prefill step {ms_per_step * 1e3:.1f} us wall, kernels {dmean * 1e3:.1f} us, "
         f"tile kernel {kmean * 1e3:.1f} us; {R} row blocks of <= {qb} rows "
-        f"({'K/V chunks shared through LDS' if shared else 'column blocks'}), "
+        f"({tiles} tile{'s' if tiles > 1 else ''} of {unit}"
+        f"{', K/V chunks shared through LDS' if tiles > 2 else ''}), "
         f"KV read {reread_kv / unique_kv:.2f}x the cache")
     res = {
         "metric": "multi-token attention: query rows/s (row blocks through the decode planner), 1 GPU",
@@ -276,7 +281,7 @@ def bench_prefill(args, w, inp):
                    "batch": int(len(lens)), "query_rows": n_q, "kv_tokens": int(lens.sum()),
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "kv_dtype": w.kv_dtype, "rows_per_block": qb,
-                   "shared_chunks": bool(shared),
+                   "tiles_per_block": tiles, "shared_chunks": tiles > 2,
                    "row_blocks": R, "tile_len": tl, "n_workgroups": W},
         "us_per_step": {"wall": round(ms_per_step * 1e3, 2), "kernels_mean": round(dmean * 1e3, 2),
                         "tile_kernel_mean": round(kmean * 1e3, 2)},

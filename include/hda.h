@@ -283,6 +283,9 @@ int64_t hda_workspace_bytes_bound(int32_t batch, int32_t n_workgroups,
 int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
                     int32_t n_workgroups, int32_t* plan, int64_t capacity, void* stream);
 
+/* Largest row block of hda_prefill, in units of hda_prefill_rows_per_block(). */
+#define HDA_PREFILL_MAX_TILES 16
+
 /*
  * ---- Multi-token queries (prefill, chunked prefill, speculative checks) ----
  *
@@ -295,21 +298,33 @@ int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
  * q and out are packed request after request: [sum q_len][Hq][D].
  *
  * The rows of each request are grouped into blocks; the (row, q head) pairs
- * of hda_prefill_rows_per_block() rows fill the 16 matrix-core columns the
- * decode kernel gives one kv head's q heads.  Each block enters the decode
- * tile planner as one "request" whose length is its causal extent, so
- * hda_plan is used unchanged (its batch = the number of blocks) and a
- * block's partial results are merged as a request's are.  Blocks of up to
- * that many rows run on the decode kernel's column shape, the chunks of an
- * item split over the 4 waves; blocks of up to 4x that many rows (for long
- * query runs) run with each K/V chunk loaded once into LDS and shared by
- * the 4 waves, wave w taking the block's w-th group of rows -- a quarter of
- * the bytes requested per query row.
+ * of hda_prefill_rows_per_block() rows -- a tile -- fill the 16 matrix-core
+ * columns the decode kernel gives one kv head's q heads.  Each block enters
+ * the decode tile planner as one "request" whose length is its causal
+ * extent, so hda_plan is used unchanged (its batch = the number of blocks)
+ * and a block's partial results are merged as a request's are.  The largest
+ * block picks the kernel shape:
+ *   1 tile    the decode kernel's column shape, an item's chunks split over
+ *             the 4 waves;
+ *   2 tiles   the same, each wave multiplying its chunks by both tiles;
+ *   4 tiles   each K/V chunk loaded once into LDS and shared by the 4 waves,
+ *             wave w taking tile w;
+ *   8 tiles   the same, wave w taking tiles w and w + 4.
+ * K/V bytes requested per query row fall with the block size; a block longer
+ * than a request's run leaves tiles idle (hda_prefill_block_rows picks one).
  */
 
-/* Rows per block that fill the 16 columns: 16 / (Hq / Hkv), or -1 for a
- * group above 16.  hda_prefill accepts blocks of up to 4x this many rows. */
+/* Rows per block that fill the 16 columns (one tile): 16 / (Hq / Hkv), or
+ * -1 for a group above 16.  hda_prefill accepts blocks of up to
+ * HDA_PREFILL_MAX_TILES times this many rows. */
 int32_t hda_prefill_rows_per_block(int32_t n_q_heads, int32_t n_kv_heads);
+
+/* A block size for a batch: 1, 2, 4 or 8 tiles of hda_prefill_rows_per_block
+ * rows, the smallest power of two at least the mean query run
+ * (q_lens [host] int32[batch], each >= 1) in tiles, at most
+ * HDA_PREFILL_MAX_TILES.  -1 on a bad argument or group. */
+int32_t hda_prefill_block_rows(const int32_t* q_lens, int32_t batch, int32_t n_q_heads,
+                               int32_t n_kv_heads);
 
 /*
  * The row blocks of a batch.  q_lens, kv_lens [host] int32[batch] with
@@ -325,7 +340,8 @@ int hda_prefill_rows(const int32_t* q_lens, const int32_t* kv_lens, int32_t batc
                      int64_t capacity, int64_t* n_rows);
 
 /* Workspace bytes for hda_prefill with this plan and blocks of at most
- * rows_per_block rows (1 .. 4 x hda_prefill_rows_per_block): partial outputs
+ * rows_per_block rows (1 .. HDA_PREFILL_MAX_TILES x
+ * hda_prefill_rows_per_block): partial outputs
  * float32 [P][rows_per_block][Hq][D], then partial log-sum-exps float32
  * [P][rows_per_block][Hq], each region aligned to 256 bytes (hda_prefill
  * lays them out with the largest block's row count).  -1 on a malformed
@@ -353,7 +369,8 @@ int64_t hda_prefill_workspace_bytes(const int32_t* plan, int64_t plan_len, int32
  *   plan_dev     hda_plan(row_lens, n_rows, tile_len, W), as for hda_decode
  *   out          [device] float32 [n_q][Hq][D]
  * Errors (host, before any launch): HDA_ERR_INVALID_ARG (incl. a block out
- * of range or with more than 4 x hda_prefill_rows_per_block rows),
+ * of range or with more than HDA_PREFILL_MAX_TILES x
+ * hda_prefill_rows_per_block rows),
  * HDA_ERR_UNSUPPORTED, HDA_ERR_BAD_PLAN, HDA_ERR_WORKSPACE; HDA_ERR_HIP if a
  * launch fails.
  */

@@ -423,13 +423,14 @@ __device__ inline void store_wave_acc(TileSmem<D>& sm, int wave, int i, int kg, 
 // Cross-wave combine of one item from LDS (per column: running max m,
 // weight sum l in units of 2^lse_shift, unnormalised output), then the
 // output row (slot -1) or the partial and its natural-log log-sum-exp.
-// Column c is packed row qrow0 + c / g, q head h*g + c % g (decode: one row,
-// qrow0 = the request).  A column with no unmasked token in this item (only
-// possible for multi-token rows) gives o = 0 and lse = -inf, which the merge
-// weighs by zero.
+// Column c is packed row qrow0 + r0 + c / g, q head h*g + c % g, partial row
+// r0 + c / g of the slot (decode: one row, qrow0 = the request, r0 = 0).  A
+// column with no unmasked token in this item (only possible for multi-token
+// rows) gives o = 0 and lse = -inf, which the merge weighs by zero.
 template <int D>
 __device__ inline void finish_item(const Args& a, const TileSmem<D>& sm, int qrow0, int ncols,
-                                   int h, int slot, float vsc, float lse_shift, int tid) {
+                                   int h, int slot, float vsc, float lse_shift, int tid,
+                                   int r0 = 0) {
   const int g = a.group;
   for (int idx = tid; idx < ncols * D; idx += 64 * kWaves) {
     const int hh = idx / D, d = idx - hh * D;
@@ -449,9 +450,9 @@ __device__ inline void finish_item(const Args& a, const TileSmem<D>& sm, int qro
     const int qr = hh / g;
     const int64_t hq = (int64_t)h * g + (hh - qr * g);
     if (slot < 0) {
-      a.out[((int64_t)(qrow0 + qr) * a.n_q_heads + hq) * D + d] = o;
+      a.out[((int64_t)(qrow0 + r0 + qr) * a.n_q_heads + hq) * D + d] = o;
     } else {
-      const int64_t prow = ((int64_t)slot * a.qb + qr) * a.n_q_heads + hq;
+      const int64_t prow = ((int64_t)slot * a.qb + r0 + qr) * a.n_q_heads + hq;
       a.part_o[prow * D + d] = o;
       if (d == 0)
         a.part_lse[prow] = lsum > 0.f ? (M + log2f(lsum) - lse_shift) * 0.69314718055994531f
@@ -551,16 +552,22 @@ __global__ __launch_bounds__(256) void hda_prologue_kernel(Args a,
 // item's chunks, combine in LDS, and write the output (slot -1) or a partial.
 //
 // Multi-token rows (PF): the item covers nq query rows of request b starting
-// at packed row qrow0 and position pos0; column i is row i / g, q head
-// h*g + i % g, with causal limit pos0 + i / g.  Decode is nq = 1, qrow0 = b.
-template <int D, bool FP8, bool PAGE, bool PF>
+// at packed row qrow0 and position pos0.  The rows come in tiles of
+// unit = 16 / g rows (the MFMA's 16 columns); a wave multiplies each chunk it
+// loads by all TPW tiles, so a block of up to TPW * unit rows reads the
+// item's K/V once.  Column i of tile t is row t*unit + i / g, q head
+// h*g + i % g, with causal limit pos0 + t*unit + i / g.  Decode is TPW = 1,
+// nq = 1, qrow0 = b.
+template <int D, bool FP8, bool PAGE, bool PF, int TPW = 1>
 __device__ inline void process_item(const Args& a, const int32_t* __restrict__ block_table,
                                     TileSmem<D>& sm, int b, int k0, int k1, int slot, int L,
                                     int qrow0, int nq, int pos0, int h, int wave, int lane,
                                     int tid) {
+  static_assert(PF || TPW == 1, "several tiles are for multi-token rows");
   using G = Geo<D, FP8>;
   const int i = lane & 15, kg = lane >> 4;
   const int g = a.group;
+  const int unit = kMaxGroup / g;
   // score and output scales of this kv head (per-page factors are applied
   // per half-chunk instead)
   float qk = a.qk_scale_log2, vsc = a.v_scale;
@@ -568,78 +575,97 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
     qk *= a.k_scales[h];
     vsc *= a.v_scales[h];
   }
-    const int qr = PF ? i / g : 0;
-    const int hh = i - qr * g;
-    const bool col_live = PF ? qr < nq : i < g;
-    const int lim = col_live ? pos0 + qr : 0x7fffffff;   // causal limit of column i
-    const int64_t qbase = ((int64_t)(qrow0 + qr) * a.n_q_heads + (int64_t)h * g + hh) * D;
+  const int qr = PF ? i / g : 0;
+  const int hh = i - qr * g;
 
-    // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
-    const int c_last = (k1 - 1) / kChunk;
-    int c = k0 / kChunk + wave;
-    const bool has_chunks = c <= c_last;   // uniform per wave
-    Chunk<D, FP8> ring[G::NBUF];
-    __amdgpu_buffer_rsrc_t kr[2], vr[2];
+  // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
+  const int c_last = (k1 - 1) / kChunk;
+  int c = k0 / kChunk + wave;
+  const bool has_chunks = c <= c_last;   // uniform per wave
+  // (several tiles run at one wave per SIMD: registers for a third set)
+  constexpr int NB = TPW > 1 ? 3 : G::NBUF;
+  Chunk<D, FP8> ring[NB];
+  __amdgpu_buffer_rsrc_t kr[2], vr[2];
 
-    // q operand (MFMA B): lane (i, kg) holds column i, dims qk_dim(s, kg) + 0..7.
-    bf16x8 qop[G::STEPS];
+  // q operand (MFMA B) of tile t: lane (i, kg) holds column i, dims
+  // qk_dim(s, kg) + 0..7.
+  bf16x8 qop[TPW][G::STEPS];
+  int lim[TPW];
+  float m_run[TPW], l_run[TPW];
+  f32x4 acc[TPW][G::DPL];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int row = t * unit + qr;
+    const bool col_live = PF ? (qr < unit && row < nq) : i < g;
+    lim[t] = col_live ? pos0 + row : 0x7fffffff;   // causal limit of column i
+    const int64_t qbase = ((int64_t)(qrow0 + row) * a.n_q_heads + (int64_t)h * g + hh) * D;
 #pragma unroll
     for (int s2 = 0; s2 < G::STEPS; ++s2) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (col_live) v = *reinterpret_cast<const u32x4*>(a.q + qbase + qk_dim<FP8>(s2, kg));
-      qop[s2] = __builtin_bit_cast(bf16x8, v);
+      qop[t][s2] = __builtin_bit_cast(bf16x8, v);
     }
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < G::DPL; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 acc[G::DPL];
+  if (has_chunks) {
+    // A ring of NB register sets: the loads of the chunk NB-1 steps
+    // ahead are issued before this chunk's math (the scheduling barrier
+    // keeps the compiler from sinking them below it).
 #pragma unroll
-    for (int nb = 0; nb < G::DPL; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (has_chunks) {
-      // A ring of G::NBUF register sets: the loads of the chunk NBUF-1 steps
-      // ahead are issued before this chunk's math (the scheduling barrier
-      // keeps the compiler from sinking them below it).
+    for (int k = 0; k < NB - 1; ++k) {
+      const int ck = c + k * kWaves;
+      chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, ck, ck <= c_last, kr, vr, ring[k]);
+      issue_chunk<D, FP8>(ring[k], kr, vr, i, kg);
+    }
+    bool done = false;
+    while (!done) {
 #pragma unroll
-      for (int k = 0; k < G::NBUF - 1; ++k) {
-        const int ck = c + k * kWaves;
-        chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, ck, ck <= c_last, kr, vr, ring[k]);
-        issue_chunk<D, FP8>(ring[k], kr, vr, i, kg);
-      }
-      bool done = false;
-      while (!done) {
+      for (int k = 0; k < NB; ++k) {
+        const int cn = c + (NB - 1) * kWaves;
+        const int nx = (k + NB - 1) % NB;
+        chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr, ring[nx]);
+        issue_chunk<D, FP8>(ring[nx], kr, vr, i, kg);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_chunk<D, FP8, PAGE, PF>(ring[k], qop[0], c, k0, k1, lim[0], pos0, qk, kg,
+                                        m_run[0], l_run[0], acc[0]);
+        // (tile 0 outside the loop: a one-trip loop here changes the decode
+        // kernel's register allocation)
 #pragma unroll
-        for (int k = 0; k < G::NBUF; ++k) {
-          const int cn = c + (G::NBUF - 1) * kWaves;
-          const int nx = (k + G::NBUF - 1) % G::NBUF;
-          chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr, ring[nx]);
-          issue_chunk<D, FP8>(ring[nx], kr, vr, i, kg);
-          __builtin_amdgcn_sched_barrier(0);
-          compute_chunk<D, FP8, PAGE, PF>(ring[k], qop, c, k0, k1, lim, pos0, qk, kg, m_run,
-                                          l_run, acc);
-          c += kWaves;
-          if (c > c_last) {
-            done = true;
-            break;
-          }
+        for (int t = 1; t < TPW; ++t)
+          if (t * unit < nq)   // uniform: tiles past the block's rows idle
+            compute_chunk<D, FP8, PAGE, PF>(ring[k], qop[t], c, k0, k1, lim[t], pos0 + t * unit,
+                                            qk, kg, m_run[t], l_run[t], acc[t]);
+        c += kWaves;
+        if (c > c_last) {
+          done = true;
+          break;
         }
       }
     }
+  }
 
-
-    // Combine the waves of this workgroup.
-    float l_tot = l_run;
+  // Combine the waves of this workgroup, one tile at a time.
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int ncols = PF ? min(unit, nq - t * unit) * g : g;
+    if (t > 0 && ncols <= 0) break;   // uniform across the workgroup
+    float l_tot = l_run[t];
     l_tot += __shfl_xor(l_tot, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    // the previous item's combine has finished reading this LDS
+    // the previous combine (item or tile) has finished reading this LDS
     __syncthreads();
     if (kg == 0) {
-      sm.m[wave][i] = m_run;
+      sm.m[wave][i] = m_run[t];
       sm.l[wave][i] = l_tot;
     }
-    const int ncols = PF ? nq * g : g;
-    store_wave_acc<D>(sm, wave, i, kg, ncols, acc);
+    store_wave_acc<D>(sm, wave, i, kg, ncols, acc[t]);
     __syncthreads();
-    finish_item<D>(a, sm, qrow0, ncols, h, slot, vsc, 0.f, tid);
+    finish_item<D>(a, sm, qrow0, ncols, h, slot, vsc, 0.f, tid, t * unit);
+  }
 }
 
 // ---- native-fp8 products: fp8 cache, dim-major V pages, D = 128 ----
@@ -902,16 +928,18 @@ __device__ inline void process_item_fp8n(const Args& a, const int32_t* __restric
 
 // ---- multi-token rows with the K/V chunk shared through LDS ----
 //
-// For blocks of more than 16/g query rows: the workgroup loads each 32-token
-// K/V chunk of the item once into LDS (256 threads, 16-byte pieces,
+// For blocks of more than 2 * 16/g query rows: the workgroup loads each
+// 32-token K/V chunk of the item once into LDS (256 threads, 16-byte pieces,
 // double-buffered: the next chunk's pieces are in registers while the
-// current one is multiplied), and all four waves use it, wave w for the
-// block's rows [w*16/g, (w+1)*16/g) -- 16 columns each, the decode kernel's
-// column shape.  The bytes requested from memory per item drop by the
-// number of busy waves.  Each wave runs the same per-chunk arithmetic
-// (compute_chunk) on registers filled from LDS and finishes its own columns
-// (no cross-wave combine).  LDS rows are padded by 16 bytes so the
-// fragment reads of 16 rows do not share banks.
+// current one is multiplied), and all four waves use it.  The block's rows
+// come in tiles of unit = 16/g rows (16 columns, the decode kernel's column
+// shape); wave w owns tiles w, w + 4, ... (TPW of them), reads the chunk
+// from LDS into registers once and multiplies it by each of its tiles.  The
+// bytes requested from memory per item drop by the number of busy tiles, the
+// LDS bytes read per MFMA by TPW.  Each wave runs the same per-chunk
+// arithmetic (compute_chunk) and finishes its own columns (no cross-wave
+// combine).  LDS rows are padded by 16 bytes so the fragment reads of 16 rows
+// do not share banks.
 template <int D, bool FP8>
 struct SharedChunk {
   static constexpr int RB = Geo<D, FP8>::RB;
@@ -920,7 +948,7 @@ struct SharedChunk {
   uint8_t v[kChunk * RS];
 };
 
-template <int D, bool FP8, bool PAGE>
+template <int D, bool FP8, bool PAGE, int NW, int TPW>
 __device__ inline void process_item_shared(const Args& a, const int32_t* __restrict__ block_table,
                                            SharedChunk<D, FP8> (&buf)[2], int b, int k0,
                                            int k1, int slot, int L, int qrow0, int nq, int pos0,
@@ -929,34 +957,40 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
   using SC = SharedChunk<D, FP8>;
   constexpr int PPR = G::RB / 16;                    // 16-byte pieces per row
   constexpr int PIECES = 2 * kChunk * PPR;           // K and V of one chunk
-  constexpr int PER_T = (PIECES + 64 * kWaves - 1) / (64 * kWaves);
+  constexpr int PER_T = (PIECES + 64 * NW - 1) / (64 * NW);
   const int i = lane & 15, kg = lane >> 4;
   const int g = a.group;
-  const int qbw = kMaxGroup / g;                     // rows per wave
-  const int r0 = wave * qbw;                         // wave's first row in the block
-  const int nqw = max(0, min(qbw, nq - r0));         // rows this wave owns
+  const int unit = kMaxGroup / g;                    // rows per tile
   float qk = a.qk_scale_log2, vsc = a.v_scale;
   if (!PAGE && a.scale_mode == HDA_SCALE_HEAD) {
     qk *= a.k_scales[h];
     vsc *= a.v_scales[h];
   }
   const int qr = i / g, hh = i - qr * g;
-  const bool col_live = qr < nqw;
-  const int lim = col_live ? pos0 + r0 + qr : 0x7fffffff;
-  const int lim_min = pos0 + r0;                     // the wave's first row
-  const int lim_max = pos0 + r0 + nqw - 1;           // its last row (uniform)
-  const int64_t qbase = ((int64_t)(qrow0 + r0 + qr) * a.n_q_heads + (int64_t)h * g + hh) * D;
-  bf16x8 qop[G::STEPS];
+  int r0[TPW], nqw[TPW], lim[TPW], lim_min[TPW], lim_max[TPW];
+  bf16x8 qop[TPW][G::STEPS];
+  float m_run[TPW], l_run[TPW];
+  f32x4 acc[TPW][G::DPL];
 #pragma unroll
-  for (int s2 = 0; s2 < G::STEPS; ++s2) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (col_live) v = *reinterpret_cast<const u32x4*>(a.q + qbase + qk_dim<FP8>(s2, kg));
-    qop[s2] = __builtin_bit_cast(bf16x8, v);
+  for (int t = 0; t < TPW; ++t) {
+    r0[t] = (wave + NW * t) * unit;                  // the tile's first row in the block
+    nqw[t] = max(0, min(unit, nq - r0[t]));          // its rows (uniform)
+    const bool col_live = qr < nqw[t];
+    lim[t] = col_live ? pos0 + r0[t] + qr : 0x7fffffff;
+    lim_min[t] = pos0 + r0[t];
+    lim_max[t] = pos0 + r0[t] + nqw[t] - 1;
+    const int64_t qbase = ((int64_t)(qrow0 + r0[t] + qr) * a.n_q_heads + (int64_t)h * g + hh) * D;
+#pragma unroll
+    for (int s2 = 0; s2 < G::STEPS; ++s2) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (col_live) v = *reinterpret_cast<const u32x4*>(a.q + qbase + qk_dim<FP8>(s2, kg));
+      qop[t][s2] = __builtin_bit_cast(bf16x8, v);
+    }
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < G::DPL; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[G::DPL];
-#pragma unroll
-  for (int nb = 0; nb < G::DPL; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // cooperative copy of chunk c into registers: piece p = tid + 256 u is
   // tensor p / (32 PPR), row (p % (32 PPR)) / PPR, 16-byte column p % PPR
@@ -979,7 +1013,7 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
     }
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      const int pc = tid + 64 * kWaves * u;
+      const int pc = tid + 64 * NW * u;
       u32x4 x = {0u, 0u, 0u, 0u};
       if (pc < PIECES) {
         const int tensor = pc / (kChunk * PPR), rem = pc - tensor * (kChunk * PPR);
@@ -998,7 +1032,7 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
   auto put = [&](SC& sc) {
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      const int pc = tid + 64 * kWaves * u;
+      const int pc = tid + 64 * NW * u;
       if (pc < PIECES) {
         const int tensor = pc / (kChunk * PPR), rem = pc - tensor * (kChunk * PPR);
         const int row = rem / PPR, col = rem - row * PPR;
@@ -1018,8 +1052,15 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
   for (int c = c_first; c <= c_last; ++c) {
     const int cur = (c - c_first) & 1;
     if (c < c_last) fetch(c + 1);
-    // the wave's columns see no token of this chunk: skip its arithmetic
-    if (nqw > 0 && c * kChunk <= lim_max) {
+    // a tile whose columns see no token of this chunk skips its arithmetic
+    // (and the wave its LDS reads when no tile needs them)
+    bool need[TPW], any = false;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      need[t] = nqw[t] > 0 && c * kChunk <= lim_max[t];
+      any = any || need[t];
+    }
+    if (any) {
       const SC& sc = buf[cur];
       Chunk<D, FP8> ch;
 #pragma unroll
@@ -1043,8 +1084,11 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
       if constexpr (PAGE) {
         ch.ks[0] = cks[0]; ch.ks[1] = cks[1]; ch.vs[0] = cvs[0]; ch.vs[1] = cvs[1];
       }
-      compute_chunk<D, FP8, PAGE, true>(ch, qop, c, k0, k1, lim, lim_min, qk, kg, m_run, l_run,
-                                        acc);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+        if (need[t])
+          compute_chunk<D, FP8, PAGE, true>(ch, qop[t], c, k0, k1, lim[t], lim_min[t], qk, kg,
+                                            m_run[t], l_run[t], acc[t]);
     }
     if (c < c_last) {
       put(buf[cur ^ 1]);
@@ -1055,36 +1099,40 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
 
   // finish the wave's own columns: l per column from the score layout
   // (lane i holds column i), o = acc / l in the accumulator layout
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (nqw == 0) return;
-  const int ncols = nqw * g;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int col = 4 * kg + r;
-    const float lc = __shfl(l_tot, col);
-    if (col >= ncols) continue;
-    const int cq = col / g;
-    const int64_t hq = (int64_t)h * g + (col - cq * g);
-    const float inv = lc > 0.f ? vsc / lc : 0.f;
-    float* dst;
-    if (slot < 0)
-      dst = a.out + ((int64_t)(qrow0 + r0 + cq) * a.n_q_heads + hq) * D;
-    else
-      dst = a.part_o + (((int64_t)slot * a.qb + r0 + cq) * a.n_q_heads + hq) * D;
+  for (int t = 0; t < TPW; ++t) {
+    float l_tot = l_run[t];
+    l_tot += __shfl_xor(l_tot, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (nqw[t] == 0) break;
+    const int ncols = nqw[t] * g;
 #pragma unroll
-    for (int nb = 0; nb < G::DPL; ++nb) dst[G::DPL * i + nb] = acc[nb][r] * inv;
-  }
-  if (slot >= 0 && kg == 0 && i < ncols) {
-    const int cq = i / g;
-    const int64_t prow = ((int64_t)slot * a.qb + r0 + cq) * a.n_q_heads + (int64_t)h * g + (i - cq * g);
-    a.part_lse[prow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    for (int r = 0; r < 4; ++r) {
+      const int col = 4 * kg + r;
+      const float lc = __shfl(l_tot, col);
+      if (col >= ncols) continue;
+      const int cq = col / g;
+      const int64_t hq = (int64_t)h * g + (col - cq * g);
+      const float inv = lc > 0.f ? vsc / lc : 0.f;
+      float* dst;
+      if (slot < 0)
+        dst = a.out + ((int64_t)(qrow0 + r0[t] + cq) * a.n_q_heads + hq) * D;
+      else
+        dst = a.part_o + (((int64_t)slot * a.qb + r0[t] + cq) * a.n_q_heads + hq) * D;
+#pragma unroll
+      for (int nb = 0; nb < G::DPL; ++nb) dst[G::DPL * i + nb] = acc[t][nb][r] * inv;
+    }
+    if (slot >= 0 && kg == 0 && i < ncols) {
+      const int cq = i / g;
+      const int64_t prow =
+          ((int64_t)slot * a.qb + r0[t] + cq) * a.n_q_heads + (int64_t)h * g + (i - cq * g);
+      a.part_lse[prow] = l_tot > 0.f ? (m_run[t] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
   }
 }
 
-template <int D, bool FP8, bool PAGE>
-__global__ __launch_bounds__(64 * kWaves, 2) void hda_prefill_shared_kernel(
+template <int D, bool FP8, bool PAGE, int NW, int TPW>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && TPW == 1) ? 2 : 1) void hda_prefill_shared_kernel(
     Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ plan) {
   __shared__ SharedChunk<D, FP8> buf[2];
@@ -1102,8 +1150,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_prefill_shared_kernel(
     if ((unsigned)rho >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
     const int b = rows[4 * rho], qrow0 = rows[4 * rho + 1], nq = rows[4 * rho + 2],
               pos0 = rows[4 * rho + 3];
-    process_item_shared<D, FP8, PAGE>(a, block_table, buf, b, k0, k1, slot, seq_lens[b], qrow0,
-                                      nq, pos0, h, wave, lane, tid);
+    process_item_shared<D, FP8, PAGE, NW, TPW>(a, block_table, buf, b, k0, k1, slot, seq_lens[b],
+                                               qrow0, nq, pos0, h, wave, lane, tid);
   }
 }
 
@@ -1190,8 +1238,8 @@ __device__ inline void run_item(const Args& a, const int32_t* __restrict__ block
 // host plan (DEVPLAN false) or are derived here from the device lengths with
 // the same rule (DEVPLAN true), in the same order.  NATIVE selects the
 // native-fp8 item routine (D = 128).
-template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE, bool PF = false>
-__global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
+template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE, bool PF = false, int TPW = 1>
+__global__ __launch_bounds__(64 * kWaves, TPW == 1 ? 2 : 1) void hda_decode_kernel(
     Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ plan) {
   // The plan, lengths and block table are read-only here and reached by
@@ -1216,8 +1264,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
       if ((unsigned)rho >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
       const int b = rows[4 * rho], qrow0 = rows[4 * rho + 1], nq = rows[4 * rho + 2],
                 pos0 = rows[4 * rho + 3];
-      process_item<D, FP8, PAGE, true>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], qrow0,
-                                       nq, pos0, h, wave, lane, tid);
+      process_item<D, FP8, PAGE, true, TPW>(a, block_table, sm, b, k0, k1, slot, seq_lens[b],
+                                            qrow0, nq, pos0, h, wave, lane, tid);
     }
   } else if constexpr (!DEVPLAN) {
     const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
@@ -1477,14 +1525,30 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
   return e;
 }
 
+static_assert(HDA_PREFILL_MAX_TILES == 16, "largest block: 8 waves of two tiles");
+
 template <int D, bool FP8, bool PAGE>
 hipError_t launch_prefill(Args a, int grid, int n_rows, hipStream_t stream, void* split_event) {
-  if (a.qb > kMaxGroup / a.group)      // blocks larger than one wave's columns: shared chunks
-    hipLaunchKernelGGL((hda_prefill_shared_kernel<D, FP8, PAGE>), dim3(grid), dim3(64 * kWaves),
+  // by the largest block, in tiles of 16/g rows: one or two tiles per wave
+  // on the wave's own chunks, else chunks shared through LDS by four waves
+  // holding one or two tiles each
+  const int unit = kMaxGroup / a.group;
+  const dim3 blk(64 * kWaves);
+  if (a.qb <= unit)
+    hipLaunchKernelGGL((hda_decode_kernel<D, FP8, false, PAGE, false, true, 1>), dim3(grid), blk,
                        0, stream, a, a.block_table, a.seq_lens, a.plan);
+  else if (a.qb <= 2 * unit)
+    hipLaunchKernelGGL((hda_decode_kernel<D, FP8, false, PAGE, false, true, 2>), dim3(grid), blk,
+                       0, stream, a, a.block_table, a.seq_lens, a.plan);
+  else if (a.qb <= 4 * unit)
+    hipLaunchKernelGGL((hda_prefill_shared_kernel<D, FP8, PAGE, 4, 1>), dim3(grid), blk, 0, stream,
+                       a, a.block_table, a.seq_lens, a.plan);
+  else if (a.qb <= 8 * unit)
+    hipLaunchKernelGGL((hda_prefill_shared_kernel<D, FP8, PAGE, 8, 1>), dim3(grid), dim3(512), 0,
+                       stream, a, a.block_table, a.seq_lens, a.plan);
   else
-    hipLaunchKernelGGL((hda_decode_kernel<D, FP8, false, PAGE, false, true>), dim3(grid),
-                       dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens, a.plan);
+    hipLaunchKernelGGL((hda_prefill_shared_kernel<D, FP8, PAGE, 8, 2>), dim3(grid), dim3(512), 0,
+                       stream, a, a.block_table, a.seq_lens, a.plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (split_event) {
@@ -1708,7 +1772,7 @@ extern "C" int hda_prefill(const hda_params* p, const void* q, const void* k_pag
   for (int64_t r = 0; r < R; ++r) {
     const int32_t b = rows_host[4 * r], q0 = rows_host[4 * r + 1], nq = rows_host[4 * r + 2],
                   pos0 = rows_host[4 * r + 3];
-    if (b < 0 || b >= p->batch || nq < 1 || nq > kWaves * unit || q0 < 0 ||
+    if (b < 0 || b >= p->batch || nq < 1 || nq > HDA_PREFILL_MAX_TILES * unit || q0 < 0 ||
         (int64_t)q0 + nq > n_q || pos0 < 0)
       return HDA_ERR_INVALID_ARG;
     qb = nq > qb ? nq : qb;

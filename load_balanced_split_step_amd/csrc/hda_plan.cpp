@@ -288,6 +288,26 @@ int32_t hda_prefill_rows_per_block(int32_t n_q_heads, int32_t n_kv_heads) {
   return g <= 16 ? 16 / g : -1;
 }
 
+// Block size for a batch: tiles of 16/g rows, as many as the mean query run
+// fills, rounded up to a power of two (1, 2, 4 or 8 tiles: the four kernel
+// shapes).  A longer block lets more query rows share each K/V load; one
+// longer than most requests' runs leaves tiles idle.
+int32_t hda_prefill_block_rows(const int32_t* q_lens, int32_t batch, int32_t n_q_heads,
+                               int32_t n_kv_heads) {
+  const int32_t unit = hda_prefill_rows_per_block(n_q_heads, n_kv_heads);
+  if (!q_lens || batch < 1 || unit < 1) return -1;
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (q_lens[b] < 1) return -1;
+    total += q_lens[b];
+  }
+  const int64_t per_tile = (int64_t)unit * batch;              // mean / unit, rounded up
+  const int64_t need = (total + per_tile - 1) / per_tile;
+  int32_t tiles = 1;
+  while (tiles < HDA_PREFILL_MAX_TILES && tiles < need) tiles *= 2;
+  return tiles * unit;
+}
+
 // Row blocks of a multi-token batch: the query rows of each request, in
 // order, grouped into blocks of rows_per_block (the last shorter).  Row r of
 // request b sits at position kv_len - q_len + r; a block needs cache tokens
@@ -330,7 +350,7 @@ int64_t hda_prefill_workspace_bytes(const int32_t* plan, int64_t plan_len, int32
     return -1;
   const int32_t unit = hda_prefill_rows_per_block(n_q_heads, n_kv_heads);
   const int32_t qb = rows_per_block;
-  if (unit < 1 || qb < 1 || qb > 4 * unit || plan[0] != HDA_PLAN_VERSION || plan[1] < 1 ||
+  if (unit < 1 || qb < 1 || qb > HDA_PREFILL_MAX_TILES * unit || plan[0] != HDA_PLAN_VERSION || plan[1] < 1 ||
       plan[6] < 0)
     return -1;
   const int64_t P = plan[6];

@@ -36,12 +36,14 @@ HDA_MATH_BF16 = 0
 HDA_MATH_FP8 = 1
 HDA_V_TOKEN_MAJOR = 0
 HDA_V_DIM_MAJOR = 1
+HDA_PREFILL_MAX_TILES = 16
 PLAN_HEADER_INTS = 8
 
 # every symbol include/hda.h declares
 EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_plan_static", "hda_plan_validate",
            "hda_workspace_bytes", "hda_decode", "hda_decode_auto", "hda_workspace_bytes_bound",
-           "hda_plan_device", "hda_prefill_rows_per_block", "hda_prefill_rows",
+           "hda_plan_device", "hda_prefill_rows_per_block", "hda_prefill_block_rows",
+           "hda_prefill_rows",
            "hda_prefill_workspace_bytes", "hda_prefill", "hda_router_split_weights",
            "hda_router_workspace_bytes", "hda_router_gemm", "hda_status_string", "hda_version",
            "hda_params_bytes")
@@ -113,6 +115,7 @@ def load_library(path: Optional[str] = None):
         "hda_workspace_bytes_bound": (i64, [i32, i32, i32, i32]),
         "hda_plan_device": (ctypes.c_int, [vp, i32, i32, i32, vp, i64, vp]),
         "hda_prefill_rows_per_block": (i32, [i32, i32]),
+        "hda_prefill_block_rows": (i32, [pi32, i32, i32, i32]),
         "hda_prefill_rows": (ctypes.c_int, [pi32, pi32, i32, i32, pi32, pi32, i64, pi64]),
         "hda_prefill_workspace_bytes": (i64, [pi32, i64, i32, i32, i32, i32]),
         "hda_prefill": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp, i32, pi32,
@@ -263,6 +266,13 @@ def hda_plan_device(seq_lens, batch: int, tile_len: int, n_workgroups: int, plan
 
 def hda_prefill_rows_per_block(n_q_heads: int, n_kv_heads: int) -> int:
     return load_library().hda_prefill_rows_per_block(int(n_q_heads), int(n_kv_heads))
+
+
+def hda_prefill_block_rows(q_lens, n_q_heads: int, n_kv_heads: int) -> int:
+    """Block size (rows) for a batch: 1, 2, 4 or 8 tiles by the mean query run."""
+    ql = _lens(q_lens)
+    return load_library().hda_prefill_block_rows(_i32p(ql), len(ql), int(n_q_heads),
+                                                 int(n_kv_heads))
 
 
 def hda_prefill_rows(q_lens, kv_lens, rows_per_block: int):
@@ -468,13 +478,15 @@ class DeviceBatch:
                         t["seq_lens"], tile_len, n_workgroups, out, stream)
         return out
 
-    def prefill_plan(self, q_lens, tile_len=None, n_workgroups=None, shared=False):
+    def prefill_plan(self, q_lens, tile_len=None, n_workgroups=None, tiles=None):
         """(rows, plan) for this batch's query rows (row blocks through the
-        decode planner); shared: blocks of 4x the column-filling size (K/V
-        chunks shared through LDS); default launch shape from launch_config."""
+        decode planner); blocks of `tiles` x the column-filling size (default:
+        hda_prefill_block_rows); default launch shape from launch_config."""
         kv = self.t["seq_lens"].cpu().numpy()
-        qb = hda_prefill_rows_per_block(self.kw["n_q_heads"], self.kw["n_kv_heads"])
-        rows, row_lens = hda_prefill_rows(q_lens, kv, 4 * qb if shared else qb)
+        hq, hk = self.kw["n_q_heads"], self.kw["n_kv_heads"]
+        qb = (hda_prefill_block_rows(q_lens, hq, hk) if tiles is None
+              else tiles * hda_prefill_rows_per_block(hq, hk))
+        rows, row_lens = hda_prefill_rows(q_lens, kv, qb)
         tl, W = launch_config(row_lens, self.kw["n_kv_heads"])
         return rows, hda_plan(row_lens, tile_len or tl, n_workgroups or W)
 
@@ -484,9 +496,9 @@ class DeviceBatch:
         if "k_scales" in t:
             p.k_scales = t["k_scales"].data_ptr()
             p.v_scales = t["v_scales"].data_ptr()
-        if rows_per_block is None:      # enough for either kernel
-            rows_per_block = 4 * hda_prefill_rows_per_block(self.kw["n_q_heads"],
-                                                            self.kw["n_kv_heads"])
+        if rows_per_block is None:      # enough for any block
+            rows_per_block = HDA_PREFILL_MAX_TILES * hda_prefill_rows_per_block(
+                self.kw["n_q_heads"], self.kw["n_kv_heads"])
         need = hda_prefill_workspace_bytes(plan, self.kw["n_q_heads"], self.kw["n_kv_heads"],
                                            self.kw["head_dim"], rows_per_block)
         ws = self.workspace(need)

@@ -332,6 +332,28 @@ def test_prefill_rows_errors(lib):
     assert st == hda.HDA_ERR_INVALID_ARG
 
 
+def test_prefill_block_rows(lib):
+    """Tiles of 16/g rows: the smallest power of two (at most 16) covering the
+    mean query run."""
+    f = hda.hda_prefill_block_rows
+    assert f([1, 1, 1], 64, 8) == 2                    # decode rows: one tile
+    assert f([2, 2], 64, 8) == 2
+    assert f([3, 2], 64, 8) == 4                       # mean 2.5 rows: 2 tiles
+    assert f([4] * 32, 64, 8) == 4                     # speculative checks of 4
+    assert f([5, 4], 64, 8) == 8                       # mean 4.5 rows: 3 tiles -> 4
+    assert f([16, 16], 64, 8) == 16                    # 8 tiles
+    assert f([20, 12], 64, 8) == 16                    # mean 16 rows: 8 tiles
+    assert f([21, 12], 64, 8) == 32                    # mean 16.5 rows: 9 tiles -> 16
+    assert f([128, 100], 64, 8) == 32                  # capped at 16 tiles
+    assert f([20, 3, 33], 32, 2) == 16                 # group 16: 1-row tiles, mean 18.7 -> 16
+    assert f([1], 32, 2) == 1
+    assert f([16], 16, 16) == 16                       # group 1: 16-row tiles
+    assert f([17], 16, 16) == 32
+    assert f([0, 4], 64, 8) == -1
+    assert f([4], 7, 2) == -1
+    assert f([], 64, 8) == -1
+
+
 def test_prefill_workspace_bytes(lib):
     up = lambda x: (x + 255) // 256 * 256
     rows, row_lens = hda.hda_prefill_rows([3, 1, 5], [10, 1, 5], 2)
@@ -340,7 +362,8 @@ def test_prefill_workspace_bytes(lib):
     assert P == 2
     assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 2) == up(P * 2 * 64 * 128 * 4) + up(P * 2 * 64 * 4)
     assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 8) == up(P * 8 * 64 * 128 * 4) + up(P * 8 * 64 * 4)
-    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 9) == -1      # above 4 x 16/g
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 32) == up(P * 32 * 64 * 128 * 4) + up(P * 32 * 64 * 4)
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 33) == -1     # above 16 x 16/g
     assert hda.hda_prefill_workspace_bytes(plan, 64, 3, 128, 2) == -1
 
 
@@ -369,8 +392,8 @@ def test_prefill_argument_errors(lib):
     assert call(_params(**dict(base, kv_dtype=E.HDA_KV_FP8_E4M3, math=E.HDA_MATH_FP8,
                                v_layout=E.HDA_V_DIM_MAJOR, page_size=64))) == E.HDA_ERR_UNSUPPORTED
     assert call(_params(**base), n_q=8) == E.HDA_ERR_INVALID_ARG        # last block past n_q
-    bad = rows.copy(); bad[0, 2] = 9                                     # 9 rows > 4 x 2 per block
-    assert call(_params(**base), rows=bad, n_q=20) == E.HDA_ERR_INVALID_ARG
+    bad = rows.copy(); bad[0, 2] = 33                                    # 33 rows > 16 x 2 per block
+    assert call(_params(**base), rows=bad, n_q=40) == E.HDA_ERR_INVALID_ARG
     bad = rows.copy(); bad[1, 0] = 3                                     # request out of range
     assert call(_params(**base), rows=bad) == E.HDA_ERR_INVALID_ARG
     assert call(_params(**base), plan=plan[:-1]) == E.HDA_ERR_BAD_PLAN

@@ -1,10 +1,12 @@
 """GPU parity of multi-token attention (hda_prefill) against the fp64 oracle.
 
-Row blocks of 16 / group query rows go through the decode tile planner;
-checked element by element at sizes the oracle finishes in seconds (ragged
-q lengths, blocks split over workgroups, tiles not aligned to chunks, every
-group size the kernel takes), one query per request bitwise equal to the
-decode path, and the full-size speculative-check workload on sampled rows.
+Row blocks of 1, 2, 4 or 8 tiles of 16 / group query rows (the four kernel
+shapes) go through the decode tile planner; checked element by element at
+sizes the oracle finishes in seconds (ragged q lengths, partial blocks whose
+last tiles are idle, blocks split over workgroups, plan tiles not aligned to
+chunks, every group size the kernel takes), one query per request bitwise
+equal to the decode path, and the full-size speculative-check and chunked
+workloads on sampled rows.
 Bar: 2e-2 (bf16 cache), 6e-2 (fp8 cache) max-abs error.
 """
 
@@ -45,18 +47,19 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("shared", [False, True], ids=["column-blocks", "shared-chunks"])
+@pytest.mark.parametrize("tiles", [1, 2, 4, 8, 16], ids=["1tile", "2tiles", "4tiles-lds", "8tiles-lds", "16tiles-lds"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_prefill_parity(name, shared):
-    """Blocks of 16/g rows (decode column shape), or of 4x that with each
-    K/V chunk loaded once into LDS for the 4 waves."""
+def test_prefill_parity(name, tiles):
+    """Blocks of 1 or 2 tiles of 16/g rows (decode column shape, each wave
+    multiplying its chunks by every tile), or of 4 or 8 tiles with each K/V
+    chunk loaded once into LDS for the 4 waves."""
     w, lens, qlens = CASES[name]
     inp = make_inputs(w, lengths=lens, q_lens=qlens)
     ref = ref_prefill(inp)
     dev = hda.DeviceBatch.from_inputs(inp)
-    qb = hda.hda_prefill_rows_per_block(w.n_q_heads, w.n_kv_heads) * (4 if shared else 1)
+    qb = hda.hda_prefill_rows_per_block(w.n_q_heads, w.n_kv_heads) * tiles
     rows, row_lens = hda.hda_prefill_rows(inp["q_lens"], inp["seq_lens"], qb)
-    plans = [("default", dev.prefill_plan(inp["q_lens"], shared=shared)[1])]
+    plans = [("default", dev.prefill_plan(inp["q_lens"], tiles=tiles)[1])]
     for tl, W in [(64, 7), (100, 13), (16, 300), (512, 2)]:
         plans.append((f"dyn-{tl}-{W}", hda.hda_plan(row_lens, tl, W)))
     plans.append(("static-3", hda.hda_plan_static(row_lens, 3)))
@@ -65,7 +68,7 @@ def test_prefill_parity(name, shared):
         out = dev.prefill(rows, plan)
         torch.cuda.synchronize()
         err = max_err(out, ref)
-        print(f"{name} {pname} {'shared' if shared else 'columns'}: {len(rows)} blocks, "
+        print(f"{name} {pname} {tiles} tiles: {len(rows)} blocks, "
               f"P={int(plan[6])}, max err {err:.3e}", flush=True)
         assert err <= tol, (name, pname, err)
 
@@ -102,4 +105,39 @@ def test_specdec_full_size_sampled():
         ref = ref_prefill(sub)
         worst = max(worst, float(np.abs(o[off[b]:off[b + 1]] - ref).max()))
     print(f"specdec full size: {len(rows)} blocks, sampled max err {worst:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
+
+
+def _rows_ref(inp, b, j0, j1):
+    """Oracle output of rows [j0, j1) of request b: a request of its own whose
+    cache ends at the last of those rows (same block-table row)."""
+    off = oracle.q_offsets(inp["q_lens"])
+    n, L = int(inp["q_lens"][b]), int(inp["seq_lens"][b])
+    sub = dict(inp, block_table=inp["block_table"][[b]],
+               seq_lens=np.array([L - n + j1], np.int32), q_lens=np.array([j1 - j0], np.int32),
+               q=inp["q"][off[b] + j0:off[b] + j1])
+    return ref_prefill(sub), off[b] + j0
+
+
+def test_chunked_full_size_sampled():
+    """The chunked-prefill workload at full size in the launch configuration
+    the benchmark times (default block size and plan): the shortest request
+    whole, and the first and last rows of the longest."""
+    w = CONFIGS["chunked"]
+    inp = make_inputs(w)
+    dev = hda.DeviceBatch.from_inputs(inp)
+    rows, plan = dev.prefill_plan(inp["q_lens"])
+    out = dev.prefill(rows, plan)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.isfinite(o).all()
+    kv, ql = inp["seq_lens"], inp["q_lens"]
+    short, long_ = int(np.argmin(kv)), int(np.argmax(kv))
+    cases = [(short, 0, int(ql[short])), (long_, 0, 3), (long_, int(ql[long_]) - 5, int(ql[long_]))]
+    worst = 0.0
+    for b, j0, j1 in cases:
+        ref, r0 = _rows_ref(inp, b, j0, j1)
+        worst = max(worst, float(np.abs(o[r0:r0 + (j1 - j0)] - ref).max()))
+    print(f"chunked full size: {len(rows)} blocks of <= {int(rows[:, 2].max())} rows, "
+          f"sampled max err {worst:.3e}", flush=True)
     assert worst <= TOL["bf16"]
