@@ -52,7 +52,7 @@ def parse():
                          "MFMA operands, V pages dim-major; fp8 cache only)")
     ap.add_argument("--tiles", choices=["auto", "1", "2", "4", "8", "16"], default="auto",
                     help="multi-token workloads: row blocks of this many tiles of 16/group rows "
-                         "(4 and 8: K/V chunks shared through LDS); auto: by the mean query run")
+                         "(above 1: K/V chunks shared through LDS); auto: by the mean query run")
     ap.add_argument("--tile-len", type=int, default=None)
     ap.add_argument("--workgroups", type=int, default=None)
     ap.add_argument("--copies", type=int, default=4, help="KV pool copies rotated over")
@@ -266,7 +266,7 @@ def bench_prefill(args, w, inp):
     log(f"prefill step {ms_per_step * 1e3:.1f} us wall, kernels {dmean * 1e3:.1f} us, "
         f"tile kernel {kmean * 1e3:.1f} us; {R} row blocks of <= {qb} rows "
         f"({tiles} tile{'s' if tiles > 1 else ''} of {unit}"
-        f"{', K/V chunks shared through LDS' if tiles > 2 else ''}), "
+        f"{', K/V chunks shared through LDS' if tiles > 1 else ''}), "
         f"KV read {reread_kv / unique_kv:.2f}x the cache")
     res = {
         "metric": "multi-token attention: query rows/s (row blocks through the decode planner), 1 GPU",
@@ -281,7 +281,7 @@ def bench_prefill(args, w, inp):
                    "batch": int(len(lens)), "query_rows": n_q, "kv_tokens": int(lens.sum()),
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "kv_dtype": w.kv_dtype, "rows_per_block": qb,
-                   "tiles_per_block": tiles, "shared_chunks": tiles > 2,
+                   "tiles_per_block": tiles, "shared_chunks": tiles > 1,
                    "row_blocks": R, "tile_len": tl, "n_workgroups": W},
         "us_per_step": {"wall": round(ms_per_step * 1e3, 2), "kernels_mean": round(dmean * 1e3, 2),
                         "tile_kernel_mean": round(kmean * 1e3, 2)},

@@ -304,12 +304,12 @@ int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
  * extent, so hda_plan is used unchanged (its batch = the number of blocks)
  * and a block's partial results are merged as a request's are.  The largest
  * block picks the kernel shape:
- *   1 tile    the decode kernel's column shape, an item's chunks split over
- *             the 4 waves;
- *   2 tiles   the same, each wave multiplying its chunks by both tiles;
- *   4 tiles   each K/V chunk loaded once into LDS and shared by the 4 waves,
- *             wave w taking tile w;
- *   8 tiles   the same, wave w taking tiles w and w + 4.
+ *   1 tile        the decode kernel's column shape, an item's chunks split
+ *                 over the 4 waves;
+ *   2 to 4 tiles  each K/V chunk loaded once into LDS and shared by 4 waves,
+ *                 wave w taking tile w;
+ *   5 to 8 tiles  the same with 8 waves;
+ *   9 to 16       8 waves, wave w taking tiles w and w + 8.
  * K/V bytes requested per query row fall with the block size; a block longer
  * than a request's run leaves tiles idle (hda_prefill_block_rows picks one).
  */
@@ -319,7 +319,7 @@ int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
  * HDA_PREFILL_MAX_TILES times this many rows. */
 int32_t hda_prefill_rows_per_block(int32_t n_q_heads, int32_t n_kv_heads);
 
-/* A block size for a batch: 1, 2, 4 or 8 tiles of hda_prefill_rows_per_block
+/* A block size for a batch: 1, 2, 4, 8 or 16 tiles of hda_prefill_rows_per_block
  * rows, the smallest power of two at least the mean query run
  * (q_lens [host] int32[batch], each >= 1) in tiles, at most
  * HDA_PREFILL_MAX_TILES.  -1 on a bad argument or group. */

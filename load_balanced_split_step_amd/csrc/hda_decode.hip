@@ -278,6 +278,101 @@ __device__ inline void issue_chunk(Chunk<D, FP8>& ch, const __amdgpu_buffer_rsrc
   }
 }
 
+// Max and sum over the four lanes (i, kg = 0..3) that share a column i:
+// gfx950's lane swaps exchange the 16-lane rows 0<->1, 2<->3 (xor 16) and
+// the 32-lane halves (xor 32) without going through LDS.
+__device__ inline float kg_reduce_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float kg_reduce_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Online-softmax update for one 32-token chunk of scores sacc (MFMA C
+// layout: lane (i = lane % 16, kg = lane / 16) holds the scores of column i
+// for tokens 16*hf + 4*kg + r in sacc[hf][r]): scale, mask, new running max,
+// rescale of l and of the PV accumulators, and the bf16 weights for the PV
+// product (k index 8*kg + j <-> token 16*(j/4) + 4*kg + j%4).
+//
+// With PAGE, the scores of each half take its page's K factor ks[hf], and
+// the PV weights its page's V factor vs[hf]: the MFMA gets bf16(p * vs), and
+// the running sum adds that rounded weight divided by vs, so the normaliser
+// counts exactly the weight each V row received.
+//
+// With PF (multi-token rows), column i also stops at its own causal limit
+// lim (lim_min: the smallest over the columns, wave-uniform), and a column
+// whose tokens are all masked so far keeps m = -inf without producing NaN.
+//
+// The PV accumulators hold column i in lane (i, kg) (the score layout), so
+// the rescale by alpha needs no exchange between lanes.  (The decode path,
+// compute_chunk, keeps its own copy of these steps for its accumulator
+// layout, column 4*kg + r in acc[nb][r].)
+template <int DPL, bool PAGE, bool PF>
+__device__ __attribute__((always_inline)) inline bf16x8 softmax_update(const f32x4 (&sacc)[2], const float (&ks)[2],
+                                        const float (&vs)[2], int c, int k0, int k1, int lim,
+                                        int lim_min, float qk_scale_log2, int kg, float& m_run,
+                                        float& l_run, f32x4 (&acc)[DPL]) {
+  float qs[2] = {qk_scale_log2, qk_scale_log2};
+  if constexpr (PAGE) {
+    qs[0] *= ks[0];
+    qs[1] *= ks[1];
+  }
+  float sc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sc[j] = sacc[j >> 2][j & 3] * qs[j >> 2];
+  const int t0 = c * kChunk;
+  // partial chunk: mask tokens outside [k0, k1) (and, for PF, past lim)
+  if (t0 < k0 || t0 + kChunk > k1 || (PF && t0 + kChunk - 1 > lim_min)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = t0 + 16 * (j >> 2) + 4 * kg + (j & 3);
+      if (t < k0 || t >= k1 || (PF && t > lim)) sc[j] = -INFINITY;
+    }
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
+  mx = kg_reduce_max(mx);
+  const float m_max = fmaxf(m_run, mx);
+  // a column with every token masked so far: subtract 0, so that its weights
+  // and alpha come out 0 (not NaN) and its state stays empty
+  const float m_new = (PF && m_max == -INFINITY) ? 0.f : m_max;
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  bf16x8 pop;
+  float psum = 0.f;
+  if constexpr (!PAGE) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 p = (__bf16)__builtin_amdgcn_exp2f(sc[j] - m_new);
+      pop[j] = p;
+      psum += (float)p;   // normalise with the same rounded weights PV uses
+    }
+  } else {
+    const float rvs[2] = {__builtin_amdgcn_rcpf(vs[0]), __builtin_amdgcn_rcpf(vs[1])};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 p = (__bf16)(__builtin_amdgcn_exp2f(sc[j] - m_new) * vs[j >> 2]);
+      pop[j] = p;
+      psum += (float)p * rvs[j >> 2];
+    }
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_max;
+  if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int nb = 0; nb < DPL; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[nb][r] *= alpha;
+  }
+  return pop;
+}
+
 // One chunk: S^T = K Q^T on MFMA, online-softmax update, acc += P V on MFMA.
 // Lane (i = lane % 16, kg = lane / 16): score of q head i for tokens
 // 16*hf + 4*kg + r; PV accumulator for q head 4*kg + r, head dim DPL*i + nb.
@@ -423,14 +518,13 @@ __device__ inline void store_wave_acc(TileSmem<D>& sm, int wave, int i, int kg, 
 // Cross-wave combine of one item from LDS (per column: running max m,
 // weight sum l in units of 2^lse_shift, unnormalised output), then the
 // output row (slot -1) or the partial and its natural-log log-sum-exp.
-// Column c is packed row qrow0 + r0 + c / g, q head h*g + c % g, partial row
-// r0 + c / g of the slot (decode: one row, qrow0 = the request, r0 = 0).  A
-// column with no unmasked token in this item (only possible for multi-token
-// rows) gives o = 0 and lse = -inf, which the merge weighs by zero.
+// Column c is packed row qrow0 + c / g, q head h*g + c % g (decode: one row,
+// qrow0 = the request).  A column with no unmasked token in this item (only
+// possible for multi-token rows) gives o = 0 and lse = -inf, which the merge
+// weighs by zero.
 template <int D>
 __device__ inline void finish_item(const Args& a, const TileSmem<D>& sm, int qrow0, int ncols,
-                                   int h, int slot, float vsc, float lse_shift, int tid,
-                                   int r0 = 0) {
+                                   int h, int slot, float vsc, float lse_shift, int tid) {
   const int g = a.group;
   for (int idx = tid; idx < ncols * D; idx += 64 * kWaves) {
     const int hh = idx / D, d = idx - hh * D;
@@ -450,9 +544,9 @@ __device__ inline void finish_item(const Args& a, const TileSmem<D>& sm, int qro
     const int qr = hh / g;
     const int64_t hq = (int64_t)h * g + (hh - qr * g);
     if (slot < 0) {
-      a.out[((int64_t)(qrow0 + r0 + qr) * a.n_q_heads + hq) * D + d] = o;
+      a.out[((int64_t)(qrow0 + qr) * a.n_q_heads + hq) * D + d] = o;
     } else {
-      const int64_t prow = ((int64_t)slot * a.qb + r0 + qr) * a.n_q_heads + hq;
+      const int64_t prow = ((int64_t)slot * a.qb + qr) * a.n_q_heads + hq;
       a.part_o[prow * D + d] = o;
       if (d == 0)
         a.part_lse[prow] = lsum > 0.f ? (M + log2f(lsum) - lse_shift) * 0.69314718055994531f
@@ -552,22 +646,16 @@ __global__ __launch_bounds__(256) void hda_prologue_kernel(Args a,
 // item's chunks, combine in LDS, and write the output (slot -1) or a partial.
 //
 // Multi-token rows (PF): the item covers nq query rows of request b starting
-// at packed row qrow0 and position pos0.  The rows come in tiles of
-// unit = 16 / g rows (the MFMA's 16 columns); a wave multiplies each chunk it
-// loads by all TPW tiles, so a block of up to TPW * unit rows reads the
-// item's K/V once.  Column i of tile t is row t*unit + i / g, q head
-// h*g + i % g, with causal limit pos0 + t*unit + i / g.  Decode is TPW = 1,
-// nq = 1, qrow0 = b.
-template <int D, bool FP8, bool PAGE, bool PF, int TPW = 1>
+// at packed row qrow0 and position pos0; column i is row i / g, q head
+// h*g + i % g, with causal limit pos0 + i / g.  Decode is nq = 1, qrow0 = b.
+template <int D, bool FP8, bool PAGE, bool PF>
 __device__ inline void process_item(const Args& a, const int32_t* __restrict__ block_table,
                                     TileSmem<D>& sm, int b, int k0, int k1, int slot, int L,
                                     int qrow0, int nq, int pos0, int h, int wave, int lane,
                                     int tid) {
-  static_assert(PF || TPW == 1, "several tiles are for multi-token rows");
   using G = Geo<D, FP8>;
   const int i = lane & 15, kg = lane >> 4;
   const int g = a.group;
-  const int unit = kMaxGroup / g;
   // score and output scales of this kv head (per-page factors are applied
   // per half-chunk instead)
   float qk = a.qk_scale_log2, vsc = a.v_scale;
@@ -575,97 +663,78 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
     qk *= a.k_scales[h];
     vsc *= a.v_scales[h];
   }
-  const int qr = PF ? i / g : 0;
-  const int hh = i - qr * g;
+    const int qr = PF ? i / g : 0;
+    const int hh = i - qr * g;
+    const bool col_live = PF ? qr < nq : i < g;
+    const int lim = col_live ? pos0 + qr : 0x7fffffff;   // causal limit of column i
+    const int64_t qbase = ((int64_t)(qrow0 + qr) * a.n_q_heads + (int64_t)h * g + hh) * D;
 
-  // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
-  const int c_last = (k1 - 1) / kChunk;
-  int c = k0 / kChunk + wave;
-  const bool has_chunks = c <= c_last;   // uniform per wave
-  // (several tiles run at one wave per SIMD: registers for a third set)
-  constexpr int NB = TPW > 1 ? 3 : G::NBUF;
-  Chunk<D, FP8> ring[NB];
-  __amdgpu_buffer_rsrc_t kr[2], vr[2];
+    // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
+    const int c_last = (k1 - 1) / kChunk;
+    int c = k0 / kChunk + wave;
+    const bool has_chunks = c <= c_last;   // uniform per wave
+    Chunk<D, FP8> ring[G::NBUF];
+    __amdgpu_buffer_rsrc_t kr[2], vr[2];
 
-  // q operand (MFMA B) of tile t: lane (i, kg) holds column i, dims
-  // qk_dim(s, kg) + 0..7.
-  bf16x8 qop[TPW][G::STEPS];
-  int lim[TPW];
-  float m_run[TPW], l_run[TPW];
-  f32x4 acc[TPW][G::DPL];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int row = t * unit + qr;
-    const bool col_live = PF ? (qr < unit && row < nq) : i < g;
-    lim[t] = col_live ? pos0 + row : 0x7fffffff;   // causal limit of column i
-    const int64_t qbase = ((int64_t)(qrow0 + row) * a.n_q_heads + (int64_t)h * g + hh) * D;
+    // q operand (MFMA B): lane (i, kg) holds column i, dims qk_dim(s, kg) + 0..7.
+    bf16x8 qop[G::STEPS];
 #pragma unroll
     for (int s2 = 0; s2 < G::STEPS; ++s2) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (col_live) v = *reinterpret_cast<const u32x4*>(a.q + qbase + qk_dim<FP8>(s2, kg));
-      qop[t][s2] = __builtin_bit_cast(bf16x8, v);
+      qop[s2] = __builtin_bit_cast(bf16x8, v);
     }
-    m_run[t] = -INFINITY;
-    l_run[t] = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < G::DPL; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
 
-  if (has_chunks) {
-    // A ring of NB register sets: the loads of the chunk NB-1 steps
-    // ahead are issued before this chunk's math (the scheduling barrier
-    // keeps the compiler from sinking them below it).
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[G::DPL];
 #pragma unroll
-    for (int k = 0; k < NB - 1; ++k) {
-      const int ck = c + k * kWaves;
-      chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, ck, ck <= c_last, kr, vr, ring[k]);
-      issue_chunk<D, FP8>(ring[k], kr, vr, i, kg);
-    }
-    bool done = false;
-    while (!done) {
+    for (int nb = 0; nb < G::DPL; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (has_chunks) {
+      // A ring of G::NBUF register sets: the loads of the chunk NBUF-1 steps
+      // ahead are issued before this chunk's math (the scheduling barrier
+      // keeps the compiler from sinking them below it).
 #pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        const int cn = c + (NB - 1) * kWaves;
-        const int nx = (k + NB - 1) % NB;
-        chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr, ring[nx]);
-        issue_chunk<D, FP8>(ring[nx], kr, vr, i, kg);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_chunk<D, FP8, PAGE, PF>(ring[k], qop[0], c, k0, k1, lim[0], pos0, qk, kg,
-                                        m_run[0], l_run[0], acc[0]);
-        // (tile 0 outside the loop: a one-trip loop here changes the decode
-        // kernel's register allocation)
+      for (int k = 0; k < G::NBUF - 1; ++k) {
+        const int ck = c + k * kWaves;
+        chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, ck, ck <= c_last, kr, vr, ring[k]);
+        issue_chunk<D, FP8>(ring[k], kr, vr, i, kg);
+      }
+      bool done = false;
+      while (!done) {
 #pragma unroll
-        for (int t = 1; t < TPW; ++t)
-          if (t * unit < nq)   // uniform: tiles past the block's rows idle
-            compute_chunk<D, FP8, PAGE, PF>(ring[k], qop[t], c, k0, k1, lim[t], pos0 + t * unit,
-                                            qk, kg, m_run[t], l_run[t], acc[t]);
-        c += kWaves;
-        if (c > c_last) {
-          done = true;
-          break;
+        for (int k = 0; k < G::NBUF; ++k) {
+          const int cn = c + (G::NBUF - 1) * kWaves;
+          const int nx = (k + G::NBUF - 1) % G::NBUF;
+          chunk_rsrc<D, FP8, PAGE>(a, block_table, b, L, h, cn, cn <= c_last, kr, vr, ring[nx]);
+          issue_chunk<D, FP8>(ring[nx], kr, vr, i, kg);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_chunk<D, FP8, PAGE, PF>(ring[k], qop, c, k0, k1, lim, pos0, qk, kg, m_run,
+                                          l_run, acc);
+          c += kWaves;
+          if (c > c_last) {
+            done = true;
+            break;
+          }
         }
       }
     }
-  }
 
-  // Combine the waves of this workgroup, one tile at a time.
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int ncols = PF ? min(unit, nq - t * unit) * g : g;
-    if (t > 0 && ncols <= 0) break;   // uniform across the workgroup
-    float l_tot = l_run[t];
+
+    // Combine the waves of this workgroup.
+    float l_tot = l_run;
     l_tot += __shfl_xor(l_tot, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    // the previous combine (item or tile) has finished reading this LDS
+    // the previous item's combine has finished reading this LDS
     __syncthreads();
     if (kg == 0) {
-      sm.m[wave][i] = m_run[t];
+      sm.m[wave][i] = m_run;
       sm.l[wave][i] = l_tot;
     }
-    store_wave_acc<D>(sm, wave, i, kg, ncols, acc[t]);
+    const int ncols = PF ? nq * g : g;
+    store_wave_acc<D>(sm, wave, i, kg, ncols, acc);
     __syncthreads();
-    finish_item<D>(a, sm, qrow0, ncols, h, slot, vsc, 0.f, tid, t * unit);
-  }
+    finish_item<D>(a, sm, qrow0, ncols, h, slot, vsc, 0.f, tid);
 }
 
 // ---- native-fp8 products: fp8 cache, dim-major V pages, D = 128 ----
@@ -928,79 +997,173 @@ __device__ inline void process_item_fp8n(const Args& a, const int32_t* __restric
 
 // ---- multi-token rows with the K/V chunk shared through LDS ----
 //
-// For blocks of more than 2 * 16/g query rows: the workgroup loads each
-// 32-token K/V chunk of the item once into LDS (256 threads, 16-byte pieces,
-// double-buffered: the next chunk's pieces are in registers while the
-// current one is multiplied), and all four waves use it.  The block's rows
-// come in tiles of unit = 16/g rows (16 columns, the decode kernel's column
-// shape); wave w owns tiles w, w + 4, ... (TPW of them), reads the chunk
-// from LDS into registers once and multiplies it by each of its tiles.  The
-// bytes requested from memory per item drop by the number of busy tiles, the
-// LDS bytes read per MFMA by TPW.  Each wave runs the same per-chunk
-// arithmetic (compute_chunk) and finishes its own columns (no cross-wave
-// combine).  LDS rows are padded by 16 bytes so the fragment reads of 16 rows
-// do not share banks.
-template <int D, bool FP8>
-struct SharedChunk {
-  static constexpr int RB = Geo<D, FP8>::RB;
-  static constexpr int RS = RB + 16;                 // padded row stride
-  uint8_t k[kChunk * RS];
-  uint8_t v[kChunk * RS];
+// For blocks of more than 16/g query rows: the workgroup (NW waves) loads
+// each K/V stage (SUB chunks of 32 tokens) of the item once into LDS and
+// all waves multiply it.  The block's rows come in tiles of unit = 16/g
+// rows (16 columns, the decode kernel's column shape); wave w owns tiles
+// w, w + NW, ... (TPW of them).  The bytes requested from memory per item
+// drop by the number of busy tiles; each wave reads a chunk's operands from
+// LDS once for all its tiles.  Two stages alternate: the next one is loaded
+// into registers while the current one is multiplied (across items too: an
+// item's last stage overlaps the loads of the next item's first).
+//
+// LDS holds each chunk in bf16 (fp8 pages are decoded once, when stored),
+// laid out for the MFMA operands:
+//   k   K rows [token][D], padded by 16 bytes: lane (i, kg) of QK step s
+//       reads dims 32s + 8kg .. +7 of token row 16*hf + i (one 16-byte read;
+//       the 16 rows of a read fall in distinct banks);
+//   vt  V transposed, dim-major: head dim d on row 16 * (d % DPL) + d / DPL
+//       and token t at position 8 * ((t % 16) / 4) + 4 * (t / 16) + t % 4 --
+//       the order of the PV weights' k index -- so that the 8 tokens of dim
+//       DPL*i + nb that lane (i, kg) multiplies in PV block nb are the 16
+//       bytes at row 16*nb + i, position 8*kg.  Rows are 80 bytes apart,
+//       which puts the 16 rows of a read in distinct banks.
+// The transpose happens when a stage is stored: each storing thread holds
+// the same 16-byte column of two adjacent tokens, and writes dword pairs
+// (token t, t+1) of each dim.
+//
+// PV is computed transposed, O^T += V^T P^T (V^T from LDS as MFMA A, the
+// weights as B), which leaves column i of the output in lane (i, kg), the
+// lane that holds column i's scores: the online-softmax rescale is
+// lane-local.
+template <int D, int SUB>
+struct SharedStage {
+  static constexpr int KRS = 2 * D + 16;        // K row stride (bytes)
+  static constexpr int VRS = 2 * kChunk + 16;   // V^T row stride (bytes)
+  uint8_t k[SUB * kChunk * KRS];                // SUB chunks of K rows
+  uint8_t vt[SUB][D * VRS];                     // V^T of each chunk
 };
 
-template <int D, bool FP8, bool PAGE, int NW, int TPW>
-__device__ inline void process_item_shared(const Args& a, const int32_t* __restrict__ block_table,
-                                           SharedChunk<D, FP8> (&buf)[2], int b, int k0,
-                                           int k1, int slot, int L, int qrow0, int nq, int pos0,
-                                           int h, int wave, int lane, int tid) {
-  using G = Geo<D, FP8>;
-  using SC = SharedChunk<D, FP8>;
-  constexpr int PPR = G::RB / 16;                    // 16-byte pieces per row
-  constexpr int PIECES = 2 * kChunk * PPR;           // K and V of one chunk
-  constexpr int PER_T = (PIECES + 64 * NW - 1) / (64 * NW);
-  const int i = lane & 15, kg = lane >> 4;
-  const int g = a.group;
-  const int unit = kMaxGroup / g;                    // rows per tile
-  float qk = a.qk_scale_log2, vsc = a.v_scale;
-  if (!PAGE && a.scale_mode == HDA_SCALE_HEAD) {
-    qk *= a.k_scales[h];
-    vsc *= a.v_scales[h];
-  }
-  const int qr = i / g, hh = i - qr * g;
-  int r0[TPW], nqw[TPW], lim[TPW], lim_min[TPW], lim_max[TPW];
-  bf16x8 qop[TPW][G::STEPS];
-  float m_run[TPW], l_run[TPW];
-  f32x4 acc[TPW][G::DPL];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    r0[t] = (wave + NW * t) * unit;                  // the tile's first row in the block
-    nqw[t] = max(0, min(unit, nq - r0[t]));          // its rows (uniform)
-    const bool col_live = qr < nqw[t];
-    lim[t] = col_live ? pos0 + r0[t] + qr : 0x7fffffff;
-    lim_min[t] = pos0 + r0[t];
-    lim_max[t] = pos0 + r0[t] + nqw[t] - 1;
-    const int64_t qbase = ((int64_t)(qrow0 + r0[t] + qr) * a.n_q_heads + (int64_t)h * g + hh) * D;
-#pragma unroll
-    for (int s2 = 0; s2 < G::STEPS; ++s2) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (col_live) v = *reinterpret_cast<const u32x4*>(a.q + qbase + qk_dim<FP8>(s2, kg));
-      qop[t][s2] = __builtin_bit_cast(bf16x8, v);
-    }
-    m_run[t] = -INFINITY;
-    l_run[t] = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < G::DPL; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+// 32-token chunks per LDS stage of the shared kernel (one stage in flight
+// while the other is multiplied; four chunks per stage measured slower
+// than two).
+constexpr int kSharedSub = 2;
 
-  // cooperative copy of chunk c into registers: piece p = tid + 256 u is
-  // tensor p / (32 PPR), row (p % (32 PPR)) / PPR, 16-byte column p % PPR
-  u32x4 stage[PER_T];
-  float sks[2] = {1.f, 1.f}, svs[2] = {1.f, 1.f};    // page factors of the two halves
-  auto fetch = [&](int c) {
-    const int t0 = c * kChunk;
-    int pg[2];
+// Position of token t (0..31) of a chunk in a V^T row.
+__device__ inline int vt_pos(int t) {
+  return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3);
+}
+
+// S^T = K Q^T for one chunk and one tile from LDS operands kf (K, MFMA A,
+// per 16-token half and QK step), then the online-softmax update; returns
+// the tile's PV weights (MFMA B layout of P^T; lane (i, kg) holds column i).
+// The PV accumulators hold column i in lane (i, kg), so alpha is lane-local.
+//
+// Without per-page factors the score scale is one number: the max is taken
+// over the raw products (the scale is positive) and each weight is
+// exp2(s * scale - m) with one fused multiply-add; the column's weight sum
+// is one more MFMA, a block of 1.0 times the rounded weights (the exact
+// fp32 sum of what PV multiplies), so l_run holds whole-column sums.  With
+// per-page factors the update is softmax_update's, and l_run holds this
+// lane's share of the column sum.
+template <int D, bool PAGE>
+__device__ inline bf16x8 qk_tile(const bf16x8 (&kf)[2][D / 32], const bf16x8 (&qop)[D / 32],
+                                 const float (&ks)[2], const float (&vs)[2], int c, int k0, int k1,
+                                 int lim, int lim_min, float qk_scale_log2, int kg, float& m_run,
+                                 float& l_run, f32x4 (&acc)[D / 16]) {
+  constexpr int DPL = D / 16;
+  f32x4 sacc[2];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+  for (int hf = 0; hf < 2; ++hf) {
+    sacc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+      sacc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[hf][s], qop[s], sacc[hf], 0, 0, 0);
+  }
+  if constexpr (PAGE) {
+    return softmax_update<DPL, true, true>(sacc, ks, vs, c, k0, k1, lim, lim_min, qk_scale_log2,
+                                           kg, m_run, l_run, acc);
+  } else {
+    float sc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sc[j] = sacc[j >> 2][j & 3];
+    const int t0 = c * kChunk;
+    if (t0 < k0 || t0 + kChunk > k1 || t0 + kChunk - 1 > lim_min) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = t0 + 16 * (j >> 2) + 4 * kg + (j & 3);
+        if (t < k0 || t >= k1 || t > lim) sc[j] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    mx = kg_reduce_max(mx) * qk_scale_log2;
+    const float m_max = fmaxf(m_run, mx);
+    // a column with every token masked so far: subtract 0 (weights and
+    // alpha 0, not NaN; its state stays empty)
+    const float m_new = m_max == -INFINITY ? 0.f : m_max;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    bf16x8 pop;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      pop[j] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[j], qk_scale_log2, -m_new));
+    const bf16x8 ones = __builtin_bit_cast(
+        bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+    const f32x4 lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                               0, 0, 0);
+    l_run = l_run * alpha + lsum[0];
+    m_run = m_max;
+    if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < DPL; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nb][r] *= alpha;
+    }
+    return pop;
+  }
+}
+
+// Sixteen-bit halves: (lo of a, lo of b) and (hi of a, hi of b).
+__device__ inline uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ inline uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Register-staged loads of one LDS stage (SUB chunks of K and V) of the
+// shared kernel, by all NW waves.  Loads come in pairs: V pair v = (column
+// v % PPR of tokens 2 (v / PPR) and +1), then K pair k = (16-byte pieces 2k,
+// 2k + 1, piece p being column p % PPR of token p / PPR); task tau =
+// tid + NT u.  The counts are multiples of 64, so a wave's tasks are all of
+// one kind.  Branch-free: a load whose token is past len or has no page
+// reads a valid address (page 0) and is zeroed when stored (ok bit 2u + m),
+// so the wait before a store counts only that stage's loads.
+template <int D, bool FP8, bool PAGE, int NW, int SUB>
+struct StageLoader {
+  using G = Geo<D, FP8>;
+  static constexpr int DPL = D / 16;
+  static constexpr int NT = 64 * NW;
+  static constexpr int STOK = SUB * kChunk;          // tokens per stage
+  static constexpr int PPR = G::RB / 16;             // 16-byte pieces per cached token row
+  static constexpr int VPAIRS = STOK / 2 * PPR;
+  static constexpr int TASKS = VPAIRS + STOK * PPR / 2;
+  static constexpr int TPT = (TASKS + NT - 1) / NT;
+  static constexpr int HALVES = 2 * SUB;             // 16-token groups of a stage
+  static_assert(VPAIRS % 64 == 0 && TASKS % 64 == 0, "wave-uniform task kinds");
+  // When the counts divide by the thread count, slot u holds one kind of
+  // task for every thread; deciding it at compile time keeps every load
+  // outside branches (a conditional load makes the waits before the stores
+  // conservative).
+  static constexpr bool kStaticKinds = VPAIRS % NT == 0 && TASKS % NT == 0;
+  __device__ static bool is_v_task(int u, int tau) {
+    return kStaticKinds ? NT * u < VPAIRS : tau < VPAIRS;
+  }
+  __device__ static bool live_task(int u, int tau) {
+    return kStaticKinds ? NT * u < TASKS : tau < TASKS;
+  }
+  u32x4 st[TPT][2];
+  uint32_t st_ok;
+  float sks[HALVES], svs[HALVES];                    // page factors of the groups
+
+  // the stage from chunk c of request b (length L), kv head h
+  __device__ inline void fetch(const Args& a, const int32_t* __restrict__ block_table, int b,
+                               int L, int h, int c, int tid) {
+    const int t0 = c * kChunk;
+    int pg[HALVES];
+#pragma unroll
+    for (int hf = 0; hf < HALVES; ++hf) {
+      sks[hf] = svs[hf] = 1.f;
       const int t = t0 + 16 * hf;
       const int pidx = t >> a.log2_ps;
       pg[hf] = (t < L && pidx < a.max_pages) ? block_table[(int64_t)b * a.max_pages + pidx] : -1;
@@ -1011,131 +1174,257 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
         }
       }
     }
+    st_ok = 0u;
 #pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      const int pc = tid + 64 * NW * u;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (pc < PIECES) {
-        const int tensor = pc / (kChunk * PPR), rem = pc - tensor * (kChunk * PPR);
-        const int row = rem / PPR, col = rem - row * PPR;
-        const int t = t0 + row, page = pg[row >> 4];
-        if (t < L && page >= 0 && page < a.num_pages) {
-          const uint8_t* base = tensor ? a.v_pages : a.k_pages;
-          const int64_t off = (int64_t)page * a.page_stride + (int64_t)h * a.head_stride +
-                              (int64_t)(t & (a.page_size - 1)) * G::RB + 16 * col;
-          x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+    for (int u = 0; u < TPT; ++u) {
+      const int tau = tid + NT * u;
+      if (!live_task(u, tau)) break;                 // uniform per wave
+      const bool is_v = is_v_task(u, tau);
+      int row[2], col[2];
+      if (is_v) {
+        row[0] = 2 * (tau / PPR);
+        row[1] = row[0] + 1;
+        col[0] = col[1] = tau % PPR;
+      } else {
+        const int p = 2 * (tau - VPAIRS);
+        row[0] = p / PPR;
+        col[0] = p % PPR;
+        row[1] = (p + 1) / PPR;
+        col[1] = (p + 1) % PPR;
+      }
+      const uint8_t* base = is_v ? a.v_pages : a.k_pages;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int t = t0 + row[m], page = pg[row[m] >> 4];
+        const bool ok = t < L && page >= 0 && page < a.num_pages;
+        const int64_t off = (int64_t)(ok ? page : 0) * a.page_stride + (int64_t)h * a.head_stride +
+                            (int64_t)(t & (a.page_size - 1)) * G::RB + 16 * col[m];
+        st[u][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+        st_ok |= (ok ? 1u : 0u) << (2 * u + m);
+      }
+    }
+  }
+  // Store the registers as a stage (bf16, transposed V).
+  __device__ inline void put(SharedStage<D, SUB>& ss, int tid) const {
+    using SS = SharedStage<D, SUB>;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int tau = tid + NT * u;
+      if (!live_task(u, tau)) break;
+      u32x4 x[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        x[m] = ((st_ok >> (2 * u + m)) & 1u) ? st[u][m] : u32x4{0u, 0u, 0u, 0u};
+      if (is_v_task(u, tau)) {
+        const int q = tau / PPR, col = tau % PPR;
+        // tokens 2q, 2q+1 of every row of their chunk's V^T
+        uint8_t* dst = ss.vt[(2 * q) / kChunk] + 2 * vt_pos((2 * q) % kChunk);
+        if constexpr (!FP8) {
+          // dims 8 col + e: dword (token 2q, token 2q + 1)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int d = 8 * col + e;
+            const uint32_t w = (e & 1) ? pair_hi(x[0][e >> 1], x[1][e >> 1])
+                                       : pair_lo(x[0][e >> 1], x[1][e >> 1]);
+            *reinterpret_cast<uint32_t*>(dst + (16 * (d % DPL) + d / DPL) * SS::VRS) = w;
+          }
+        } else {
+          // dims 16 col + e, decoded: bf16 pairs (4k, 4k+1), (4k+2, 4k+3)
+#pragma unroll
+          for (int kq = 0; kq < 4; ++kq) {
+            uint32_t a0, a1, b0, b1;
+            fp8x4_to_bf16x4(x[0][kq], a0, a1);
+            fp8x4_to_bf16x4(x[1][kq], b0, b1);
+            const uint32_t w[4] = {pair_lo(a0, b0), pair_hi(a0, b0), pair_lo(a1, b1),
+                                   pair_hi(a1, b1)};
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const int d = 16 * col + 4 * kq + e2;
+              *reinterpret_cast<uint32_t*>(dst + (16 * (d % DPL) + d / DPL) * SS::VRS) = w[e2];
+            }
+          }
+        }
+      } else {
+        const int p = 2 * (tau - VPAIRS);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int row = (p + m) / PPR, col = (p + m) % PPR;
+          if constexpr (!FP8) {
+            *reinterpret_cast<u32x4*>(ss.k + row * SS::KRS + 16 * col) = x[m];
+          } else {
+            uint32_t w[8];
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) fp8x4_to_bf16x4(x[m][kq], w[2 * kq], w[2 * kq + 1]);
+            *reinterpret_cast<u32x4*>(ss.k + row * SS::KRS + 32 * col) = u32x4{w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<u32x4*>(ss.k + row * SS::KRS + 32 * col + 16) = u32x4{w[4], w[5], w[6], w[7]};
+          }
         }
       }
-      stage[u] = x;
     }
-  };
-  auto put = [&](SC& sc) {
+  }
+};
+
+// Item (b, [k0, k1), slot) of row block (qrow0, nq rows, first position
+// pos0) for kv head h.  On entry the loader holds the item's first stage in
+// registers; during its last stage it fetches the first stage of the next
+// item (next_b, next_L, next_c: request, length, first chunk) when
+// has_next, so that stage's loads overlap this item's arithmetic.
+template <int D, bool FP8, bool PAGE, int NW, int TPW, int SUB>
+__device__ inline void process_item_shared(const Args& a, const int32_t* __restrict__ block_table,
+                                           SharedStage<D, SUB> (&buf)[2],
+                                           StageLoader<D, FP8, PAGE, NW, SUB>& ld, int b, int k0,
+                                           int k1, int slot, int L, int qrow0, int nq, int pos0,
+                                           int h, bool has_next, int next_b, int next_L,
+                                           int next_c, int wave, int lane, int tid) {
+  using SS = SharedStage<D, SUB>;
+  constexpr int DPL = D / 16, STEPS = D / 32;
+  constexpr int HALVES = 2 * SUB;
+  const int i = lane & 15, kg = lane >> 4;
+  const int g = a.group;
+  const int unit = kMaxGroup / g;                    // rows per tile
+  float qk = a.qk_scale_log2, vsc = a.v_scale;
+  if (!PAGE && a.scale_mode == HDA_SCALE_HEAD) {
+    qk *= a.k_scales[h];
+    vsc *= a.v_scales[h];
+  }
+  const int qr = i / g, hh = i - qr * g;
+  int r0[TPW], nqw[TPW], lim[TPW], lim_min[TPW], lim_max[TPW];
+  bf16x8 qop[TPW][STEPS];
+  float m_run[TPW], l_run[TPW];
+  f32x4 acc[TPW][DPL];
 #pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      const int pc = tid + 64 * NW * u;
-      if (pc < PIECES) {
-        const int tensor = pc / (kChunk * PPR), rem = pc - tensor * (kChunk * PPR);
-        const int row = rem / PPR, col = rem - row * PPR;
-        uint8_t* dst = (tensor ? sc.v : sc.k) + row * SC::RS + 16 * col;
-        *reinterpret_cast<u32x4*>(dst) = stage[u];
-      }
+  for (int t = 0; t < TPW; ++t) {
+    r0[t] = (wave + NW * t) * unit;                  // the tile's first row in the block
+    nqw[t] = max(0, min(unit, nq - r0[t]));          // its rows (uniform)
+    const bool col_live = qr < nqw[t];
+    lim[t] = col_live ? pos0 + r0[t] + qr : 0x7fffffff;
+    lim_min[t] = pos0 + r0[t];
+    lim_max[t] = pos0 + r0[t] + nqw[t] - 1;
+    const int64_t qbase = ((int64_t)(qrow0 + r0[t] + qr) * a.n_q_heads + (int64_t)h * g + hh) * D;
+#pragma unroll
+    for (int s2 = 0; s2 < STEPS; ++s2) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (col_live) v = *reinterpret_cast<const u32x4*>(a.q + qbase + 32 * s2 + 8 * kg);
+      qop[t][s2] = __builtin_bit_cast(bf16x8, v);
     }
-  };
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < DPL; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int c_first = k0 / kChunk, c_last = (k1 - 1) / kChunk;
-  float cks[2], cvs[2];
-  fetch(c_first);
-  __syncthreads();                  // the previous item's readers are done with buf
-  put(buf[0]);
-  cks[0] = sks[0]; cks[1] = sks[1]; cvs[0] = svs[0]; cvs[1] = svs[1];
-  __syncthreads();
-  for (int c = c_first; c <= c_last; ++c) {
-    const int cur = (c - c_first) & 1;
-    if (c < c_last) fetch(c + 1);
-    // a tile whose columns see no token of this chunk skips its arithmetic
-    // (and the wave its LDS reads when no tile needs them)
-    bool need[TPW], any = false;
+  const int n_st = (c_last - c_first) / SUB + 1;
+  float cks[HALVES], cvs[HALVES];
+  auto keep_factors = [&]() {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      need[t] = nqw[t] > 0 && c * kChunk <= lim_max[t];
-      any = any || need[t];
+    for (int hf = 0; hf < HALVES; ++hf) {
+      cks[hf] = ld.sks[hf];
+      cvs[hf] = ld.svs[hf];
     }
-    if (any) {
-      const SC& sc = buf[cur];
-      Chunk<D, FP8> ch;
+  };
+  __syncthreads();                  // the previous item's readers are done with buf
+  ld.put(buf[0], tid);
+  keep_factors();
+  __syncthreads();
+  for (int si = 0; si < n_st; ++si) {
+    const int cur = si & 1;
+    {
+      // one call site, always issued (the waits before the stores then
+      // count only its loads); after the last stage of the last item it
+      // reloads this stage, which nothing stores
+      const bool own = si + 1 < n_st;
+      const bool nxt = !own && has_next;
+      ld.fetch(a, block_table, nxt ? next_b : b, nxt ? next_L : L, h,
+               own ? c_first + SUB * (si + 1) : nxt ? next_c : c_first + SUB * si, tid);
+    }
+    const SS& ss = buf[cur];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+    for (int j = 0; j < SUB; ++j) {
+      const int c = c_first + SUB * si + j;
+      if (c > c_last) break;                          // uniform: the item's last stage
+      // a tile whose columns see no token of this chunk skips its arithmetic
+      // (and the wave its LDS reads when no tile needs them)
+      bool need[TPW], any = false;
 #pragma unroll
-        for (int u = 0; u < G::KL; ++u)
-          ch.k[hf][u] = *reinterpret_cast<const u32x4*>(sc.k + (16 * hf + i) * SC::RS + 64 * u + 16 * kg);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint8_t* row = sc.v + (16 * (j >> 2) + 4 * kg + (j & 3)) * SC::RS + i * G::VW * 4;
-        if constexpr (G::VW == 4) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(row);
-          ch.v[j][0] = x[0]; ch.v[j][1] = x[1]; ch.v[j][2] = x[2]; ch.v[j][3] = x[3];
-        } else if constexpr (G::VW == 2) {
-          const u32x2 x = *reinterpret_cast<const u32x2*>(row);
-          ch.v[j][0] = x[0]; ch.v[j][1] = x[1];
-        } else {
-          ch.v[j][0] = *reinterpret_cast<const uint32_t*>(row);
-        }
+      for (int t = 0; t < TPW; ++t) {
+        need[t] = nqw[t] > 0 && c * kChunk <= lim_max[t];
+        any = any || need[t];
       }
-      if constexpr (PAGE) {
-        ch.ks[0] = cks[0]; ch.ks[1] = cks[1]; ch.vs[0] = cvs[0]; ch.vs[1] = cvs[1];
+      if (!any) continue;
+      // QK and softmax of every tile, then PV: the K and V operands are not
+      // held at the same time
+      const float jks[2] = {cks[2 * j], cks[2 * j + 1]}, jvs[2] = {cvs[2 * j], cvs[2 * j + 1]};
+      bf16x8 pop[TPW];
+      {
+        bf16x8 kf[2][STEPS];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int s2 = 0; s2 < STEPS; ++s2)
+            kf[hf][s2] = *reinterpret_cast<const bf16x8*>(
+                ss.k + (kChunk * j + 16 * hf + i) * SS::KRS + 64 * s2 + 16 * kg);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          if (need[t])
+            pop[t] = qk_tile<D, PAGE>(kf, qop[t], jks, jvs, c, k0, k1, lim[t], lim_min[t], qk, kg,
+                                      m_run[t], l_run[t], acc[t]);
       }
+      bf16x8 vf[DPL];
+#pragma unroll
+      for (int nb = 0; nb < DPL; ++nb)
+        vf[nb] = *reinterpret_cast<const bf16x8*>(ss.vt[j] + (16 * nb + i) * SS::VRS + 16 * kg);
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
         if (need[t])
-          compute_chunk<D, FP8, PAGE, true>(ch, qop[t], c, k0, k1, lim[t], lim_min[t], qk, kg,
-                                            m_run[t], l_run[t], acc[t]);
+#pragma unroll
+          for (int nb = 0; nb < DPL; ++nb)   // O^T block nb += V^T P^T
+            acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[nb], pop[t], acc[t][nb], 0, 0, 0);
     }
-    if (c < c_last) {
-      put(buf[cur ^ 1]);
-      cks[0] = sks[0]; cks[1] = sks[1]; cvs[0] = svs[0]; cvs[1] = svs[1];
+    if (si + 1 < n_st) {
+      ld.put(buf[cur ^ 1], tid);
+      keep_factors();
     }
     __syncthreads();
   }
 
-  // finish the wave's own columns: l per column from the score layout
-  // (lane i holds column i), o = acc / l in the accumulator layout
+  // finish the wave's own columns: lane (i, kg) holds column i, head dims
+  // DPL * (4 kg + r) + nb in acc[nb][r] -- 4 DPL consecutive dims from
+  // 4 DPL kg -- and a quarter of the column's weight sum
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    float l_tot = l_run[t];
-    l_tot += __shfl_xor(l_tot, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    // (per-page factors: each lane holds a share of the column's sum)
+    const float l_tot = PAGE ? kg_reduce_sum(l_run[t]) : l_run[t];
     if (nqw[t] == 0) break;
-    const int ncols = nqw[t] * g;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int col = 4 * kg + r;
-      const float lc = __shfl(l_tot, col);
-      if (col >= ncols) continue;
-      const int cq = col / g;
-      const int64_t hq = (int64_t)h * g + (col - cq * g);
-      const float inv = lc > 0.f ? vsc / lc : 0.f;
+    if (i < nqw[t] * g) {
+      const int64_t hq = (int64_t)h * g + hh;
+      const float inv = l_tot > 0.f ? vsc / l_tot : 0.f;
       float* dst;
       if (slot < 0)
-        dst = a.out + ((int64_t)(qrow0 + r0[t] + cq) * a.n_q_heads + hq) * D;
+        dst = a.out + ((int64_t)(qrow0 + r0[t] + qr) * a.n_q_heads + hq) * D;
       else
-        dst = a.part_o + (((int64_t)slot * a.qb + r0[t] + cq) * a.n_q_heads + hq) * D;
+        dst = a.part_o + (((int64_t)slot * a.qb + r0[t] + qr) * a.n_q_heads + hq) * D;
+      dst += 4 * DPL * kg;
 #pragma unroll
-      for (int nb = 0; nb < G::DPL; ++nb) dst[G::DPL * i + nb] = acc[t][nb][r] * inv;
-    }
-    if (slot >= 0 && kg == 0 && i < ncols) {
-      const int cq = i / g;
-      const int64_t prow =
-          ((int64_t)slot * a.qb + r0[t] + cq) * a.n_q_heads + (int64_t)h * g + (i - cq * g);
-      a.part_lse[prow] = l_tot > 0.f ? (m_run[t] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int v4 = 0; v4 < DPL / 4; ++v4)
+          *reinterpret_cast<f32x4*>(dst + DPL * r + 4 * v4) =
+              f32x4{acc[t][4 * v4][r] * inv, acc[t][4 * v4 + 1][r] * inv,
+                    acc[t][4 * v4 + 2][r] * inv, acc[t][4 * v4 + 3][r] * inv};
+      if (slot >= 0 && kg == 0) {
+        const int64_t prow = ((int64_t)slot * a.qb + r0[t] + qr) * a.n_q_heads + hq;
+        a.part_lse[prow] = l_tot > 0.f ? (m_run[t] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+      }
     }
   }
 }
 
 template <int D, bool FP8, bool PAGE, int NW, int TPW>
-__global__ __launch_bounds__(64 * NW, (NW == 4 && TPW == 1) ? 2 : 1) void hda_prefill_shared_kernel(
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void hda_prefill_shared_kernel(
     Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ plan) {
-  __shared__ SharedChunk<D, FP8> buf[2];
+  __shared__ SharedStage<D, kSharedSub> buf[2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x % a.n_kv_heads;
@@ -1144,14 +1433,35 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TPW == 1) ? 2 : 1) void hda_pr
   const int32_t* items = wg_ptr + a.n_wg + 1;
   const int32_t* __restrict__ rows = a.rows;
   const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
-  for (int it = it_begin; it < it_end; ++it) {
+  auto valid = [&](int it) {
     const int rho = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
               slot = items[4 * it + 3];
-    if ((unsigned)rho >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
+    return (unsigned)rho < (unsigned)a.batch && k0 >= 0 && k1 > k0 && slot < a.n_parts;
+  };
+  auto next_valid = [&](int it) {
+    while (it < it_end && !valid(it)) ++it;
+    return it;
+  };
+  StageLoader<D, FP8, PAGE, NW, kSharedSub> ld;
+  int it = next_valid(it_begin);
+  if (it < it_end) {
+    const int b = rows[4 * items[4 * it]];
+    ld.fetch(a, block_table, b, seq_lens[b], h, items[4 * it + 1] / kChunk, tid);
+  }
+  while (it < it_end) {
+    const int rho = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
+              slot = items[4 * it + 3];
     const int b = rows[4 * rho], qrow0 = rows[4 * rho + 1], nq = rows[4 * rho + 2],
               pos0 = rows[4 * rho + 3];
-    process_item_shared<D, FP8, PAGE, NW, TPW>(a, block_table, buf, b, k0, k1, slot, seq_lens[b],
-                                               qrow0, nq, pos0, h, wave, lane, tid);
+    const int nx = next_valid(it + 1);
+    const bool has_next = nx < it_end;
+    const int next_b = has_next ? rows[4 * items[4 * nx]] : 0;
+    const int next_L = has_next ? seq_lens[next_b] : 0;
+    const int next_c = has_next ? items[4 * nx + 1] / kChunk : 0;
+    process_item_shared<D, FP8, PAGE, NW, TPW, kSharedSub>(
+        a, block_table, buf, ld, b, k0, k1, slot, seq_lens[b], qrow0, nq, pos0, h, has_next,
+        next_b, next_L, next_c, wave, lane, tid);
+    it = nx;
   }
 }
 
@@ -1238,8 +1548,8 @@ __device__ inline void run_item(const Args& a, const int32_t* __restrict__ block
 // host plan (DEVPLAN false) or are derived here from the device lengths with
 // the same rule (DEVPLAN true), in the same order.  NATIVE selects the
 // native-fp8 item routine (D = 128).
-template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE, bool PF = false, int TPW = 1>
-__global__ __launch_bounds__(64 * kWaves, TPW == 1 ? 2 : 1) void hda_decode_kernel(
+template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE, bool PF = false>
+__global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
     Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ plan) {
   // The plan, lengths and block table are read-only here and reached by
@@ -1264,8 +1574,8 @@ __global__ __launch_bounds__(64 * kWaves, TPW == 1 ? 2 : 1) void hda_decode_kern
       if ((unsigned)rho >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
       const int b = rows[4 * rho], qrow0 = rows[4 * rho + 1], nq = rows[4 * rho + 2],
                 pos0 = rows[4 * rho + 3];
-      process_item<D, FP8, PAGE, true, TPW>(a, block_table, sm, b, k0, k1, slot, seq_lens[b],
-                                            qrow0, nq, pos0, h, wave, lane, tid);
+      process_item<D, FP8, PAGE, true>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], qrow0,
+                                       nq, pos0, h, wave, lane, tid);
     }
   } else if constexpr (!DEVPLAN) {
     const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
@@ -1529,17 +1839,14 @@ static_assert(HDA_PREFILL_MAX_TILES == 16, "largest block: 8 waves of two tiles"
 
 template <int D, bool FP8, bool PAGE>
 hipError_t launch_prefill(Args a, int grid, int n_rows, hipStream_t stream, void* split_event) {
-  // by the largest block, in tiles of 16/g rows: one or two tiles per wave
-  // on the wave's own chunks, else chunks shared through LDS by four waves
-  // holding one or two tiles each
+  // by the largest block, in tiles of 16/g rows: one tile on the decode
+  // kernel's column shape (the waves split the item's chunks), else chunks
+  // shared through LDS by 4 waves of one tile, 8 waves of one, or 8 of two
   const int unit = kMaxGroup / a.group;
   const dim3 blk(64 * kWaves);
   if (a.qb <= unit)
-    hipLaunchKernelGGL((hda_decode_kernel<D, FP8, false, PAGE, false, true, 1>), dim3(grid), blk,
-                       0, stream, a, a.block_table, a.seq_lens, a.plan);
-  else if (a.qb <= 2 * unit)
-    hipLaunchKernelGGL((hda_decode_kernel<D, FP8, false, PAGE, false, true, 2>), dim3(grid), blk,
-                       0, stream, a, a.block_table, a.seq_lens, a.plan);
+    hipLaunchKernelGGL((hda_decode_kernel<D, FP8, false, PAGE, false, true>), dim3(grid), blk, 0,
+                       stream, a, a.block_table, a.seq_lens, a.plan);
   else if (a.qb <= 4 * unit)
     hipLaunchKernelGGL((hda_prefill_shared_kernel<D, FP8, PAGE, 4, 1>), dim3(grid), blk, 0, stream,
                        a, a.block_table, a.seq_lens, a.plan);

@@ -289,7 +289,7 @@ int32_t hda_prefill_rows_per_block(int32_t n_q_heads, int32_t n_kv_heads) {
 }
 
 // Block size for a batch: tiles of 16/g rows, as many as the mean query run
-// fills, rounded up to a power of two (1, 2, 4 or 8 tiles: the four kernel
+// fills, rounded up to a power of two (1, 2, 4, 8 or 16 tiles; the kernel
 // shapes).  A longer block lets more query rows share each K/V load; one
 // longer than most requests' runs leaves tiles idle.
 int32_t hda_prefill_block_rows(const int32_t* q_lens, int32_t batch, int32_t n_q_heads,

@@ -269,7 +269,7 @@ def hda_prefill_rows_per_block(n_q_heads: int, n_kv_heads: int) -> int:
 
 
 def hda_prefill_block_rows(q_lens, n_q_heads: int, n_kv_heads: int) -> int:
-    """Block size (rows) for a batch: 1, 2, 4 or 8 tiles by the mean query run."""
+    """Block size (rows) for a batch: 1, 2, 4, 8 or 16 tiles by the mean query run."""
     ql = _lens(q_lens)
     return load_library().hda_prefill_block_rows(_i32p(ql), len(ql), int(n_q_heads),
                                                  int(n_kv_heads))

@@ -1,7 +1,10 @@
 """GPU parity of multi-token attention (hda_prefill) against the fp64 oracle.
 
-Row blocks of 1, 2, 4 or 8 tiles of 16 / group query rows (the four kernel
-shapes) go through the decode tile planner; checked element by element at
+Row blocks of 1, 2, 4, 8 or 16 tiles of 16 / group query rows (the column
+kernel and the three LDS-shared shapes) go through the decode tile planner;
+every block of an item loads its next stage while multiplying the current
+one, the last stage of an item the next item's first; checked element by
+element at
 sizes the oracle finishes in seconds (ragged q lengths, partial blocks whose
 last tiles are idle, blocks split over workgroups, plan tiles not aligned to
 chunks, every group size the kernel takes), one query per request bitwise
@@ -47,12 +50,14 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("tiles", [1, 2, 4, 8, 16], ids=["1tile", "2tiles", "4tiles-lds", "8tiles-lds", "16tiles-lds"])
+@pytest.mark.parametrize("tiles", [1, 2, 4, 8, 16],
+                         ids=["1tile-columns", "2tiles-lds4", "4tiles-lds4", "8tiles-lds8",
+                              "16tiles-lds8x2"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_prefill_parity(name, tiles):
-    """Blocks of 1 or 2 tiles of 16/g rows (decode column shape, each wave
-    multiplying its chunks by every tile), or of 4 or 8 tiles with each K/V
-    chunk loaded once into LDS for the 4 waves."""
+    """Blocks of 1 tile of 16/g rows (decode column shape), or of 2 to 16
+    tiles with each K/V chunk loaded once into LDS (4 waves of one tile, 8 of
+    one, 8 of two) and multiplied by every tile."""
     w, lens, qlens = CASES[name]
     inp = make_inputs(w, lengths=lens, q_lens=qlens)
     ref = ref_prefill(inp)
