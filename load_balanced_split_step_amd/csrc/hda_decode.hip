@@ -1640,26 +1640,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
 constexpr int kMergeEarly = 32;    // partial rows loaded before the weights
 constexpr int kMergeStage = 512;   // slot weights staged in LDS per pass
 
-//
-// Multi-token launches (PF): workgroup (row block, row in block, q head);
-// slot s holds qb x Hq partial rows, and the output row is the block's
-// packed row.  A partial with lse = -inf (a column with no token in that
-// item) has weight zero and o = 0.
-template <int D, bool DEVPLAN, bool PF = false>
+template <int D, bool DEVPLAN>
 __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __restrict__ plan,
                                                       const int32_t* __restrict__ seq_lens) {
   __shared__ float sm_w[kMergeStage];
   __shared__ float sm_red[2][D / 64];
   const int d = threadIdx.x, lane = d & 63, wave = d >> 6;
   const int hq = blockIdx.x % a.n_q_heads;
-  const int rb = blockIdx.x / a.n_q_heads;          // request (decode) or block * qb + row
-  const int b = PF ? rb / a.qb : rb, qr = PF ? rb - b * a.qb : 0;
-  int s0, s1, orow = b;
-  if constexpr (PF) {
-    const int32_t* __restrict__ rows = a.rows;
-    if (qr >= rows[4 * b + 2]) return;               // past the block's rows
-    orow = rows[4 * b + 1] + qr;
-  }
+  const int b = blockIdx.x / a.n_q_heads;
+  const int qr = 0, orow = b;
+  int s0, s1;
   if constexpr (!DEVPLAN) {
     const int32_t* rpp = plan + HDA_PLAN_HEADER_INTS + a.n_wg + 1 + 4 * a.n_items;
     s0 = max(0, rpp[b]);
@@ -1726,6 +1716,92 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
     for (; k < cn; ++k) acc += sm_w[k] * po[(int64_t)(c0 + k) * row_stride];
   }
   a.out[((int64_t)orow * a.n_q_heads + hq) * D + d] = acc;
+}
+
+// Merge of multi-token partials: workgroup (row block, row in block, group
+// of 256 / (D/4) q heads), 256 threads, thread t owning float4 column t % Q
+// (Q = D/4) of head t / Q of the group.  Per head, the weights are the
+// decode merge's, computed in the same order (max over slots; the sum of
+// exp(lse - M) as the decode merge's D/64 waves would add it, each wave's
+// lanes taking slots lane + 64w, + D, ... and reducing with the same
+// butterfly; the slots accumulated in order), so a row merges to exactly
+// what hda_merge_kernel gives.  Eight slots' loads are issued before their
+// weights are applied.  (One workgroup of D threads per row and head
+// measured latency-bound on multi-token batches: 2.2x slower.)
+constexpr int kMergeRowsThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMergeRowsThreads) void hda_merge_rows_kernel(
+    Args a, const int32_t* __restrict__ plan) {
+  constexpr int Q = D / 4;                           // float4 columns per head
+  constexpr int HPW = kMergeRowsThreads / Q;         // heads per workgroup
+  constexpr int U = 8;                               // slots in flight
+  __shared__ float sM[HPW], sInv[HPW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Hq = a.n_q_heads;
+  const int groups = (Hq + HPW - 1) / HPW;
+  const int rb = blockIdx.x / groups, hg = blockIdx.x - rb * groups;
+  const int b = rb / a.qb, qr = rb - b * a.qb;
+  const int32_t* __restrict__ rows = a.rows;
+  if (qr >= rows[4 * b + 2]) return;                // past the block's rows
+  const int orow = rows[4 * b + 1] + qr;
+  const int32_t* rpp = plan + HDA_PLAN_HEADER_INTS + a.n_wg + 1 + 4 * a.n_items;
+  const int s0 = max(0, rpp[b]), s1 = min(a.n_parts, rpp[b + 1]);
+  if (s1 <= s0) return;
+  const int n = s1 - s0;
+  const int64_t lstride = (int64_t)a.qb * Hq;       // between slots, in rows
+  const float* lse = a.part_lse + (int64_t)s0 * lstride + (int64_t)qr * Hq;
+  for (int j = wave; j < HPW; j += kMergeRowsThreads / 64) {
+    const int h = hg * HPW + j;
+    if (h >= Hq) break;
+    float m = -INFINITY;
+    for (int k = lane; k < n; k += 64) m = fmaxf(m, lse[(int64_t)k * lstride + h]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float total = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) {
+      const int d = 64 * w + lane;
+      float t = d < n ? expf(lse[(int64_t)d * lstride + h] - m) : 0.f;
+      for (int k = d + D; k < n; k += D) t += expf(lse[(int64_t)k * lstride + h] - m);
+      total += wave_sum(t);
+    }
+    if (lane == 0) {
+      sM[j] = m;
+      sInv[j] = 1.0f / total;
+    }
+  }
+  __syncthreads();
+  const int j = tid / Q, h = hg * HPW + j;
+  if (h >= Hq) return;
+  const float M = sM[j], inv = sInv[j];
+  const int64_t row_stride = lstride * D;            // floats between slots
+  const float* po = a.part_o + ((int64_t)s0 * lstride + (int64_t)qr * Hq + h) * D + 4 * (tid % Q);
+  const float* lh = lse + h;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + U <= n; k += U) {
+    f32x4 v[U];
+    float l[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(k + u) * row_stride);
+      l[u] = lh[(int64_t)(k + u) * lstride];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = expf(l[u] - M) * inv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += w * v[u][e];
+    }
+  }
+  for (; k < n; ++k) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(po + (int64_t)k * row_stride);
+    const float w = expf(lh[(int64_t)k * lstride] - M) * inv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += w * v[e];
+  }
+  *reinterpret_cast<f32x4*>(a.out + ((int64_t)orow * Hq + h) * D + 4 * (tid % Q)) = acc;
 }
 
 // The plan in the host format, built from device lengths by one wave with
@@ -1863,8 +1939,9 @@ hipError_t launch_prefill(Args a, int grid, int n_rows, hipStream_t stream, void
     if (e != hipSuccess) return e;
   }
   if (a.n_parts == 0) return e;
-  hipLaunchKernelGGL((hda_merge_kernel<D, false, true>), dim3(n_rows * a.qb * a.n_q_heads),
-                     dim3(D), 0, stream, a, a.plan, a.seq_lens);
+  const int groups = (a.n_q_heads + kMergeRowsThreads / (D / 4) - 1) / (kMergeRowsThreads / (D / 4));
+  hipLaunchKernelGGL((hda_merge_rows_kernel<D>), dim3(n_rows * a.qb * groups),
+                     dim3(kMergeRowsThreads), 0, stream, a, a.plan);
   return hipGetLastError();
 }
 
