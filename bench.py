@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E spec
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "load_balanced_split_step_amd", "csrc", "hda_decode.hip")
 METRIC = "decode-attn µs/step + KV GB/s (% HBM peak), 1×128K+31×4K mix, 1 GPU"
@@ -61,7 +62,38 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the streaming-read probe (a pure read of the tile kernel's "
+                         "algorithmic bytes: the measured read ceiling)")
     return ap.parse_args()
+
+
+def read_probe(nbytes, reps=10):
+    """The measured read ceiling for a launch that must read `nbytes`:
+    hda_read_probe (each wave streams its own contiguous region, 16-byte
+    non-temporal loads) over that many bytes, best of a few launch sizes,
+    timed with events on the current stream."""
+    import torch
+    import load_balanced_split_step_amd.hda as hda
+    nbytes = (int(nbytes) + 15) // 16 * 16
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    best = None
+    for wgs in (512, 1024, 2048):
+        sink = torch.empty(wgs * 256, dtype=torch.int32, device="cuda:0")
+        hda.hda_read_probe(buf, wgs, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            hda.hda_read_probe(buf, wgs, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"bytes": nbytes, "n_workgroups": wgs, "us": round(us, 2), "gbs": round(gbs, 1),
+                    "kernel": "hda_read_probe_kernel"}
+    del buf
+    return best
 
 
 def algorithmic_bytes(inp, plan_len):
@@ -263,11 +295,29 @@ def bench_prefill(args, w, inp):
     reread_kv = int(np.asarray(row_lens, np.int64).sum()) * per_tok
     algo = reread_kv + n_q * w.n_q_heads * w.head_dim * (2 + 4) + R * 16 + plan_len * 4
     achieved = algo / (kmean * 1e-3) / 1e9
+    # matrix-core work: QK and PV, 2 flops per multiply-add, over each row's
+    # causal extent (position + 1 cached tokens)
+    extents = sum(int(k) - int(q) + r + 1 for k, q in zip(lens, qlens) for r in range(int(q)))
+    flops = 4 * w.head_dim * w.n_q_heads * extents
+    tflops = flops / (kmean * 1e-3) / 1e12
+    # roofline: HBM below the bf16 ridge point (peak flops / peak bytes)
+    mfma_bound = flops / algo > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     log(f"prefill step {ms_per_step * 1e3:.1f} us wall, kernels {dmean * 1e3:.1f} us, "
         f"tile kernel {kmean * 1e3:.1f} us; {R} row blocks of <= {qb} rows "
         f"({tiles} tile{'s' if tiles > 1 else ''} of {unit}"
         f"{', K/V chunks shared through LDS' if tiles > 1 else ''}), "
-        f"KV read {reread_kv / unique_kv:.2f}x the cache")
+        f"KV read {reread_kv / unique_kv:.2f}x the cache; {tflops:.0f} TFLOP/s "
+        f"({flops / algo:.0f} flop/B)")
+    kernel_name = ("hda_prefill_shared_kernel (HIP events on its stream)" if tiles > 1 else
+                   "hda_decode_kernel, multi-token rows (HIP events on its stream)")
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops": flops, "kernel": kernel_name}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes": algo, "kernel": kernel_name}
     res = {
         "metric": "multi-token attention: query rows/s (row blocks through the decode planner), 1 GPU",
         "value": round(n_q / (ms_per_step * 1e-3), 1),
@@ -286,18 +336,23 @@ def bench_prefill(args, w, inp):
         "us_per_step": {"wall": round(ms_per_step * 1e3, 2), "kernels_mean": round(dmean * 1e3, 2),
                         "tile_kernel_mean": round(kmean * 1e3, 2)},
         "kv_gbs_unique": round(unique_kv / (dmean * 1e-3) / 1e9, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes": algo,
-                     "kernel": "hda_decode_kernel, multi-token rows (HIP events on its stream)"},
+        "roofline": roof,
+        "matrix_core": {"algorithmic_flops": flops, "tflops": round(tflops, 2),
+                        "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                        "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "flop_per_byte": round(flops / algo, 1)},
     }
+    if not args.no_read_probe:
+        res["read_probe"] = read_probe(algo)
+        log(f"read probe: {res['read_probe']['gbs']:.0f} GB/s reading the same "
+            f"{algo / 1e9:.2f} GB; the tile kernel moves its bytes at "
+            f"{achieved / res['read_probe']['gbs']:.1%} of that rate")
     if not args.no_cpu:
         log("timing the fp64 prefill oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline_prefill(inp, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 
 
 def bench_router(args):
@@ -597,6 +652,12 @@ def main():
                                 "graph_replay_wall_us": round(graph_ms * 1e3, 2),
                                 "kv_gbs_graph": round(kv / (graph_ms * 1e-3) / 1e9, 2)},
     }
+
+    if not args.no_read_probe:
+        res["read_probe"] = read_probe(algo)
+        log(f"read probe: {res['read_probe']['gbs']:.0f} GB/s reading the same "
+            f"{algo / 1e9:.2f} GB ({res['read_probe']['n_workgroups']} workgroups); the tile "
+            f"kernel reaches {achieved / res['read_probe']['gbs']:.1%} of it")
 
     if args.copy_probe:
         # a plain copy kernel of known size: reads and writes 2^30 bytes per

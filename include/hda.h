@@ -419,6 +419,22 @@ int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo, int32_t t
                     int32_t experts, int32_t hidden, float* out, void* workspace,
                     int64_t workspace_bytes, void* stream);
 
+/*
+ * ---- Measurement ----
+ *
+ * Not part of the attention method: a streaming-read probe that gives the
+ * attention roofline a measured ceiling next to the published 8 TB/s.  One
+ * kernel on `stream` reads buf [device] (16-byte aligned; bytes a multiple
+ * of 16) once with the attention kernels' access pattern -- each wave a
+ * contiguous region, 16-byte non-temporal loads, eight in flight per lane --
+ * over n_workgroups workgroups of 256 threads, and writes to sink [device]
+ * uint32[n_workgroups * 256] the XOR of the words each thread read (their
+ * XOR is the XOR of the whole buffer).  The caller times it.  Asynchronous.
+ * Errors: HDA_ERR_INVALID_ARG, HDA_ERR_HIP.
+ */
+int hda_read_probe(const void* buf, int64_t bytes, int32_t n_workgroups, uint32_t* sink,
+                   void* stream);
+
 /* Static description of a status code. */
 const char* hda_status_string(int status);
 

@@ -45,7 +45,8 @@ EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_plan_static", "hda_plan_validat
            "hda_plan_device", "hda_prefill_rows_per_block", "hda_prefill_block_rows",
            "hda_prefill_rows",
            "hda_prefill_workspace_bytes", "hda_prefill", "hda_router_split_weights",
-           "hda_router_workspace_bytes", "hda_router_gemm", "hda_status_string", "hda_version",
+           "hda_router_workspace_bytes", "hda_router_gemm", "hda_read_probe", "hda_status_string",
+           "hda_version",
            "hda_params_bytes")
 
 
@@ -123,6 +124,7 @@ def load_library(path: Optional[str] = None):
         "hda_router_split_weights": (ctypes.c_int, [vp, i64, vp, vp, vp]),
         "hda_router_workspace_bytes": (i64, [i32, i32, i32]),
         "hda_router_gemm": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
+        "hda_read_probe": (ctypes.c_int, [vp, i64, i32, vp, vp]),
         "hda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "hda_version": (ctypes.c_int, []),
         "hda_params_bytes": (i64, []),
@@ -340,6 +342,19 @@ def hda_router_gemm(x, w_hi, w_lo, tokens: int, experts: int, hidden: int, out, 
                                         int(workspace_bytes), _stream(stream))
     if st != HDA_OK:
         raise HdaError(st, "hda_router_gemm")
+
+
+def hda_read_probe(buf, n_workgroups: int, sink, stream=None) -> None:
+    """Enqueue the streaming-read probe over the device tensor `buf` (see
+    include/hda.h); `sink` is a uint32/int32 device tensor of
+    n_workgroups * 256 elements."""
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() < int(n_workgroups) * 256:
+        raise ValueError("sink smaller than n_workgroups * 256 words")
+    st = load_library().hda_read_probe(_ptr(buf), int(nbytes), int(n_workgroups), _ptr(sink),
+                                       _stream(stream))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_read_probe")
 
 
 class RouterWeights:

@@ -441,3 +441,15 @@ def test_router_argument_errors(lib):
         assert call(ws=FAKE + 0x4000, wsb=need - 4) == E.HDA_ERR_WORKSPACE
     assert lib.hda_router_split_weights(None, 10, vp(FAKE), vp(FAKE), None) == E.HDA_ERR_INVALID_ARG
     assert lib.hda_router_split_weights(vp(FAKE), 0, vp(FAKE), vp(FAKE), None) == E.HDA_ERR_INVALID_ARG
+
+
+def test_read_probe_argument_errors(lib):
+    """The read probe rejects bad arguments on the host, before any launch."""
+    import ctypes
+    vp = ctypes.c_void_p
+    assert lib.hda_read_probe(None, 1024, 4, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
+    assert lib.hda_read_probe(vp(FAKE), 1024, 4, None, None) == hda.HDA_ERR_INVALID_ARG
+    assert lib.hda_read_probe(vp(FAKE), 1000, 4, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
+    assert lib.hda_read_probe(vp(FAKE), 0, 4, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
+    assert lib.hda_read_probe(vp(FAKE), 1024, 0, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
+    assert lib.hda_read_probe(vp(FAKE + 8), 1024, 4, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
