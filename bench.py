@@ -96,6 +96,25 @@ def read_probe(nbytes, reps=10):
     return best
 
 
+def single_stream_gbs(nbytes=64 << 20, reps=5):
+    """Read rate of one 4-wave workgroup alone on the GPU (hda_read_probe with
+    one workgroup): what a static split's longest chunk streams at."""
+    import torch
+    import load_balanced_split_step_amd.hda as hda
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.empty(256, dtype=torch.int32, device="cuda:0")
+    hda.hda_read_probe(buf, 1, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        hda.hda_read_probe(buf, 1, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del buf
+    return nbytes / (us * 1e-6) / 1e9
+
+
 def algorithmic_bytes(inp, plan_len):
     """Bytes one launch must move: every cached K/V row of every kv head,
     q, the output, the block-table entries in use, lengths and plan."""
@@ -539,6 +558,23 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    # a1 and a2 apart, outside the timed region: the host planner (C++) and
+    # the plan's upload (HIP events around the copy on the launch stream)
+    host0 = pinned[0].numpy()
+    t0 = time.perf_counter()
+    for _ in range(200):
+        n_plan = hda.hda_plan_into(lens, tl, W, host0)
+    host_plan_us = (time.perf_counter() - t0) * 1e6 / 200
+    torch.cuda.synchronize()
+    u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    u0.record(stream)
+    for _ in range(50):
+        plan_dev[0][:n_plan].copy_(pinned[0][:n_plan], non_blocking=True)
+    u1.record(stream)
+    torch.cuda.synchronize()
+    upload_us = u0.elapsed_time(u1) * 1e3 / 50
+    log(f"host plan {host_plan_us:.1f} us, plan upload {upload_us:.1f} us ({n_plan} ints)")
+
     # separate pass with HIP events on the launch stream for kernel durations
     n_prof = max(10, min(args.steps, 50))
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(n_prof)]
@@ -647,6 +683,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": algo,
                      "kernel": "hda_decode_kernel (tile kernel; HIP events on its stream)"},
+        "plan": {"host_us": round(host_plan_us, 2), "upload_us": round(upload_us, 2),
+                 "plan_ints": int(n_plan)},
         "max_abs_diff_vs_static4_plan": static_diff,
         "device_planned_step": {"wall_us": round(auto_ms * 1e3, 2),
                                 "graph_replay_wall_us": round(graph_ms * 1e3, 2),
@@ -689,7 +727,17 @@ def main():
         best = min(static, key=static.get)
         S_h = max(1, min(64, math.ceil(256 * 2 / (len(lens) * w.n_kv_heads))))
         S_h = 1 << (S_h - 1).bit_length()
+        # a static split is as slow as its longest chunk: one workgroup
+        # streaming max(len)/S tokens of one kv head (K and V)
+        one_wg = single_stream_gbs()
+        per_tok = 2 * w.head_dim * (1 if w.kv_dtype == "fp8" else 2)
+        predicted = {S: math.ceil(int(lens.max()) / S) * per_tok / (one_wg * 1e9) * 1e6
+                     for S in static}
+        log(f"one workgroup streams {one_wg:.1f} GB/s alone; static S=1 predicted "
+            f"{predicted[1]:.0f} us from its longest chunk")
         res["load_balance"] = {
+            "single_workgroup_gbs": round(one_wg, 2),
+            "static_predicted_us": {str(k): round(v, 1) for k, v in predicted.items()},
             "dynamic_decode_us": round(dmean * 1e3, 2),
             "static_us": {str(k): round(v * 1e3, 2) for k, v in static.items()},
             "static_best_S": best,
