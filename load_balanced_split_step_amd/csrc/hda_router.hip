@@ -144,18 +144,23 @@ __global__ __launch_bounds__(64 * kWaves) void hda_router_gemm_kernel(RouterArgs
   }
 }
 
-// Large batches: 128 tokens x 128 experts per workgroup, K sliced by 32 and
-// staged through LDS (double-buffered: the next slice is loaded into
-// registers while the current one is multiplied).  Wave (wm, wn) owns the
-// 64 x 64 sub-tile at (64 wm, 64 wn): 4 x 4 blocks for each product.  LDS
-// rows are 64 bytes (32 bf16), so the 64 lanes of a fragment read cover one
-// contiguous KiB and do not conflict.
+// Large batches: 128 tokens x 128 experts per workgroup, K sliced by 64 (two
+// MFMA steps per barrier; slices of 32 measured 10% slower) and staged
+// through LDS (double-buffered: the next slice is loaded into registers
+// while the current one is multiplied).  Wave (wm, wn) owns the 64 x 64
+// sub-tile at (64 wm, 64 wn): 4 x 4 blocks for each product.  LDS rows hold
+// 64 bf16 and are padded to 144 bytes: the 16 lanes of a fragment read that
+// share a k offset read 16 rows, whose 16-byte pieces then fall in distinct
+// bank groups (36 i mod 64 dwords; unpadded rows put several rows on the
+// same banks).
 constexpr int kBigM = 128, kBigN = 128;
+constexpr int kBigK = 64;             // K per LDS stage (two MFMA steps)
+constexpr int kBigRow = kBigK + 8;    // padded LDS row, in bf16
 
 struct BigStage {
-  uint16_t a[kBigM][kStepK];
-  uint16_t bh[kBigN][kStepK];
-  uint16_t bl[kBigN][kStepK];
+  uint16_t a[kBigM][kBigRow];
+  uint16_t bh[kBigN][kBigRow];
+  uint16_t bl[kBigN][kBigRow];
 };
 
 __global__ __launch_bounds__(64 * kWaves, 2) void hda_router_gemm_lds_kernel(RouterArgs a) {
@@ -171,22 +176,23 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_router_gemm_lds_kernel(Rou
   const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.w_hi, (int64_t)a.E * a.H * 2);
   const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.w_lo, (int64_t)a.E * a.H * 2);
 
-  // global -> LDS copy: 512 16-byte chunks per tile, two per thread; chunk c
-  // is row c / 4, k offset 8 (c % 4)
-  int64_t ga[2], gb[2];
-  int lrow[2], lcol[2];
+  // global -> LDS copy: 1024 16-byte chunks per tile, four per thread; chunk
+  // c is row c / 8, k offset 8 (c % 8)
+  constexpr int kChunks = kBigM * kBigK / 8 / 256;   // per thread per tile
+  int64_t ga[kChunks], gb[kChunks];
+  int lrow[kChunks], lcol[kChunks];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kChunks; ++u) {
     const int c = tid + 256 * u;
-    lrow[u] = c >> 2;
-    lcol[u] = 8 * (c & 3);
+    lrow[u] = c >> 3;
+    lcol[u] = 8 * (c & 7);
     ga[u] = ((int64_t)(t0 + lrow[u]) * a.H + lcol[u]) * 2;
     gb[u] = ((int64_t)(e0 + lrow[u]) * a.H + lcol[u]) * 2;
   }
-  u32x4 ra[2], rh[2], rl[2];
+  u32x4 ra[kChunks], rh[kChunks], rl[kChunks];
   auto load = [&](int k) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kChunks; ++u) {
       ra[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(ga[u] + 2 * k), 0, 0));
       rh[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hr, (int)(gb[u] + 2 * k), 0, 0));
       rl[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(lr, (int)(gb[u] + 2 * k), 0, 0));
@@ -194,7 +200,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_router_gemm_lds_kernel(Rou
   };
   auto store = [&](BigStage& s) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kChunks; ++u) {
       *reinterpret_cast<u32x4*>(&s.a[lrow[u]][lcol[u]]) = ra[u];
       *reinterpret_cast<u32x4*>(&s.bh[lrow[u]][lcol[u]]) = rh[u];
       *reinterpret_cast<u32x4*>(&s.bl[lrow[u]][lcol[u]]) = rl[u];
@@ -209,29 +215,32 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_router_gemm_lds_kernel(Rou
       acc_hi[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc_lo[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  const int nk = (ke - kb) / kStepK;
+  const int nk = (ke - kb) / kBigK;
   load(kb);
   store(st[0]);
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) load(kb + kStepK * (ks + 1));
+    if (ks + 1 < nk) load(kb + kBigK * (ks + 1));
     const BigStage& s = st[ks & 1];
-    bf16x8 fa[4], fh[4], fl[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      fa[m] = *reinterpret_cast<const bf16x8*>(&s.a[64 * wm + 16 * m + i][8 * kg]);
+    for (int kk = 0; kk < kBigK; kk += kStepK) {
+      bf16x8 fa[4], fh[4], fl[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      fh[n] = *reinterpret_cast<const bf16x8*>(&s.bh[64 * wn + 16 * n + i][8 * kg]);
-      fl[n] = *reinterpret_cast<const bf16x8*>(&s.bl[64 * wn + 16 * n + i][8 * kg]);
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m)
+        fa[m] = *reinterpret_cast<const bf16x8*>(&s.a[64 * wm + 16 * m + i][kk + 8 * kg]);
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        acc_hi[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fh[n], acc_hi[m][n], 0, 0, 0);
-        acc_lo[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fl[n], acc_lo[m][n], 0, 0, 0);
+        fh[n] = *reinterpret_cast<const bf16x8*>(&s.bh[64 * wn + 16 * n + i][kk + 8 * kg]);
+        fl[n] = *reinterpret_cast<const bf16x8*>(&s.bl[64 * wn + 16 * n + i][kk + 8 * kg]);
       }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          acc_hi[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fh[n], acc_hi[m][n], 0, 0, 0);
+          acc_lo[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fl[n], acc_lo[m][n], 0, 0, 0);
+        }
+    }
     if (ks + 1 < nk) store(st[(ks + 1) & 1]);
     __syncthreads();
   }
@@ -295,12 +304,12 @@ struct RouterShape {
 // register kernel (measured: 64 large tiles alone leave three quarters of
 // the compute units idle).
 constexpr int64_t kBigMinGroups = 256;
-constexpr int kBigMinSteps = 16;
+constexpr int kBigMinStages = 8;      // K per workgroup >= 8 stages (512)
 
 RouterShape router_shape(int32_t T, int32_t E, int32_t H) {
   RouterShape r;
   const int64_t big_tiles = (int64_t)((T + kBigM - 1) / kBigM) * ((E + kBigN - 1) / kBigN);
-  const int64_t max_split = H / (kStepK * kBigMinSteps);
+  const int64_t max_split = H % kBigK ? 0 : H / (kBigK * kBigMinStages);
   if (max_split >= 1 && big_tiles * max_split >= kBigMinGroups) {
     r.big = true;
     r.mb = 8;
@@ -308,8 +317,8 @@ RouterShape router_shape(int32_t T, int32_t E, int32_t H) {
     r.tiles_e = (E + kBigN - 1) / kBigN;
     int64_t S = (kBigMinGroups + big_tiles - 1) / big_tiles;
     S = S < 1 ? 1 : (S > max_split ? max_split : S);
-    const int steps = H / kStepK;
-    r.k_per_wg = (int)((steps + S - 1) / S) * kStepK;
+    const int stages = H / kBigK;
+    r.k_per_wg = (int)((stages + S - 1) / S) * kBigK;
     r.S = (H + r.k_per_wg - 1) / r.k_per_wg;
     return r;
   }

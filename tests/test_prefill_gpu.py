@@ -45,6 +45,11 @@ CASES = {
     "full_s": (Workload("full_s", 4, 16, 4, 128, 16, seed=80), [1, 33, 130, 257], [1, 33, 130, 257]),
     "fp8_page_pf": (CONFIGS["fp8_page"].with_(name="fp8_page_pf", batch=6, len_range=(100, 2500),
                                               prologue=False, q_len_range=(1, 40)), None, None),
+    "fp8_d64_tensor": (Workload("fp8_d64_tensor", 4, 16, 4, 64, 16, kv_dtype="fp8", seed=83),
+                       [40, 700, 129, 2000], [7, 33, 1, 64]),
+    "fp8_head_pf": (CONFIGS["fp8_page"].with_(name="fp8_head_pf", batch=5, len_range=(100, 2000),
+                                              prologue=False, kv_scale="head",
+                                              q_len_range=(1, 50)), None, None),
     "g16": (Workload("g16", 3, 32, 2, 128, 64, seed=81), [700, 90, 2000], [20, 3, 33]),
     "g1": (Workload("g1", 3, 4, 4, 64, 32, seed=82), [300, 64, 65], [40, 64, 1]),
 }
