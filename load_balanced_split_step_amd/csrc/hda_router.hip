@@ -257,13 +257,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_router_gemm_lds_kernel(Rou
       }
 }
 
-// Sum of the S partial tiles, in slot order.  The loads of a batch of 16
-// partials are all issued before any is added (one memory round trip per
-// batch instead of one per partial); the additions keep slot order.
+// Sum of the S partial tiles, in slot order.  The loads of a batch of
+// kBatch partials are all issued before any is added (one memory round trip
+// per batch instead of one per partial); the additions keep slot order.
+// Batches of 64 for many splits (small token counts: 56 splits at hidden
+// 7168 take one round trip instead of four), of 16 for few (a 64-wide batch
+// of mostly idle loads slowed the million-output reductions of large token
+// counts by a quarter).
+template <int kBatch>
 __global__ __launch_bounds__(256) void hda_router_reduce_kernel(const float* __restrict__ part,
                                                                 float* __restrict__ out,
                                                                 int64_t n, int S) {
-  constexpr int kBatch = 16;
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (j >= n) return;
   float acc = 0.f;
@@ -391,8 +395,11 @@ extern "C" int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo
   if (hipGetLastError() != hipSuccess) return HDA_ERR_HIP;
   if (r.S > 1) {
     const int64_t n = (int64_t)tokens * experts;
-    hipLaunchKernelGGL(hda_router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                       hs, a.part, out, n, r.S);
+    const dim3 g((unsigned)((n + 255) / 256));
+    if (r.S > 16)
+      hipLaunchKernelGGL(hda_router_reduce_kernel<64>, g, dim3(256), 0, hs, a.part, out, n, r.S);
+    else
+      hipLaunchKernelGGL(hda_router_reduce_kernel<16>, g, dim3(256), 0, hs, a.part, out, n, r.S);
     if (hipGetLastError() != hipSuccess) return HDA_ERR_HIP;
   }
   return HDA_OK;

@@ -39,11 +39,14 @@ def test_split_bit_exact():
     assert np.array_equal(rw.lo.cpu().numpy().view(np.uint16), lo)
 
 
-# the last four take the LDS-staged 128 x 128 kernel (with 13, 4 and 1
-# hidden splits; the last with ragged token and expert edges)
+# 1280, 4096, 16384 and 16300 tokens take the LDS-staged 128 x 128 kernel
+# (with 13, 4, 1 and 1 hidden splits; 16300 x 300 with ragged token and
+# expert edges); 4096 x 2080 has a hidden size the 64-wide K stages do not
+# divide and runs on the register kernel
 SHAPES = [(1, 256, 7168), (5, 24, 96), (16, 256, 7168), (33, 100, 7168), (64, 256, 7168),
           (100, 256, 7168), (257, 72, 1024), (600, 256, 7168), (1280, 256, 7168),
-          (4096, 256, 7168), (16384, 256, 7168), (16300, 300, 1024)]
+          (4096, 256, 7168), (16384, 256, 7168), (16300, 300, 1024),
+          (4096, 256, 2080)]   # hidden % 64 == 32: a large batch on the register kernel
 
 
 @pytest.mark.parametrize("T,E,H", SHAPES)
