@@ -1077,13 +1077,28 @@ __device__ inline bf16x8 qk_tile(const bf16x8 (&kf)[2][D / 32], const bf16x8 (&q
     float sc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) sc[j] = sacc[j >> 2][j & 3];
+    // Masks, in two uniform branches taken only by the chunks that need
+    // them: tokens before k0 (an item starting inside the chunk), and tokens
+    // past the column's last visible one, hi = min(k1 - 1, causal limit);
+    // each element's offset 16 (j / 4) + j % 4 is a constant compared with
+    // a per-lane threshold.  (A single test of both bounds, the same for
+    // every tile, was hoisted by the compiler out of the tiles' branches and
+    // paid on every chunk.)
     const int t0 = c * kChunk;
-    if (t0 < k0 || t0 + kChunk > k1 || t0 + kChunk - 1 > lim_min) {
+    if (t0 < k0) {
+      // (the threshold through readfirstlane, a convergent operation, keeps
+      // these tests inside the branch)
+      const int d = __builtin_amdgcn_readfirstlane(k0 - t0) - 4 * kg;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = t0 + 16 * (j >> 2) + 4 * kg + (j & 3);
-        if (t < k0 || t >= k1 || t > lim) sc[j] = -INFINITY;
-      }
+      for (int j = 0; j < 8; ++j)
+        if (16 * (j >> 2) + (j & 3) < d) sc[j] = -INFINITY;
+    }
+    const int hi_min = min(k1 - 1, lim_min);
+    if (t0 + kChunk - 1 > hi_min) {
+      const int r = min(k1 - 1, lim) - t0 - 4 * kg;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (16 * (j >> 2) + (j & 3) > r) sc[j] = -INFINITY;
     }
     float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                      fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
@@ -1364,6 +1379,10 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
           for (int s2 = 0; s2 < STEPS; ++s2)
             kf[hf][s2] = *reinterpret_cast<const bf16x8*>(
                 ss.k + (kChunk * j + 16 * hf + i) * SS::KRS + 64 * s2 + 16 * kg);
+        // every fragment read in flight before the first product (left to
+        // itself the scheduler can reuse one register set and wait on each
+        // read in turn)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
           if (need[t])
@@ -1374,6 +1393,7 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
 #pragma unroll
       for (int nb = 0; nb < DPL; ++nb)
         vf[nb] = *reinterpret_cast<const bf16x8*>(ss.vt[j] + (16 * nb + i) * SS::VRS + 16 * kg);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
         if (need[t])
