@@ -26,6 +26,8 @@ unless they bring several query rows):
             check of 3 draft tokens plus one), causal over the cache
   chunked   16 requests, cache lengths log-uniform in [2048, 32768], a
             chunk of U{16..128} new query rows each (chunked prefill)
+  chunked_fp8  the same lengths and rows over an fp8 E4M3FN cache with
+            per-tensor scales
 
 Recipe (the pages use no dataset; these stand in for a serving batch):
   * numpy PCG64 streams spawned from SeedSequence(seed), one stream per
@@ -121,6 +123,8 @@ CONFIGS = {
                         q_lens=(4,) * 32, seed=6),
     "chunked": Workload("chunked", 16, 64, 8, 128, 64, len_range=(2048, 32768),
                         q_len_range=(16, 128), seed=7),
+    "chunked_fp8": Workload("chunked_fp8", 16, 64, 8, 128, 64, kv_dtype="fp8",
+                            len_range=(2048, 32768), q_len_range=(16, 128), seed=7),
 }
 
 _CHUNK_SLABS = 256
