@@ -30,6 +30,7 @@
 // HBM-bound (8 flop per KV byte for bf16), so MFMA only does the small dense
 // products.
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -292,6 +293,25 @@ __device__ inline float kg_reduce_sum(float x) {
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Maximum of two scores (numbers or -inf) as v_med3_f32(a, b, +inf), with
+// +inf in a register the compiler does not see through (it would turn the
+// median back into fmaxf, which on matrix-core results costs a NaN-quieting
+// maximum per operand).
+__device__ inline float opaque_inf() {
+  float x = INFINITY;
+  asm("" : "+v"(x));
+  return x;
+}
+__device__ inline float qmax(float a, float b, float inf) {
+  return __builtin_amdgcn_fmed3f(a, b, inf);
+}
+__device__ inline float kg_reduce_qmax(float x, float inf) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = qmax(__uint_as_float(a[0]), __uint_as_float(a[1]), inf);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return qmax(__uint_as_float(b[0]), __uint_as_float(b[1]), inf);
 }
 
 // Online-softmax update for one 32-token chunk of scores sacc (MFMA C
@@ -1008,30 +1028,51 @@ __device__ inline void process_item_fp8n(const Args& a, const int32_t* __restric
 // item's last stage overlaps the loads of the next item's first).
 //
 // LDS holds each chunk in bf16 (fp8 pages are decoded once, when stored),
-// laid out for the MFMA operands:
-//   k   K rows [token][D], padded by 16 bytes: lane (i, kg) of QK step s
-//       reads dims 32s + 8kg .. +7 of token row 16*hf + i (one 16-byte read;
-//       the 16 rows of a read fall in distinct banks);
-//   vt  V transposed, dim-major: head dim d on row 16 * (d % DPL) + d / DPL
-//       and token t at position 8 * ((t % 16) / 4) + 4 * (t / 16) + t % 4 --
-//       the order of the PV weights' k index -- so that the 8 tokens of dim
-//       DPL*i + nb that lane (i, kg) multiplies in PV block nb are the 16
-//       bytes at row 16*nb + i, position 8*kg.  Rows are 80 bytes apart,
-//       which puts the 16 rows of a read in distinct banks.
+// laid out so that every MFMA operand is one 16-byte read per lane and no
+// read has a bank conflict.  (gfx950 serves a 16-byte read 16 lanes at a
+// time, and measured conflict-free only when lanes 0-7 and lanes 8-15 of
+// each group each cover one aligned half of the 64 banks: rows padded by 16
+// bytes, which spread a group over all banks but straddle the halves, took
+// twice the cycles.)
+//   k   K rows [token][D]; 16-byte quad q of token row r sits at
+//       k_off(r, q): for D = 128, rows of 256 bytes with the quad XOR-ed
+//       by r mod 16; for D = 64, rows r and r + 8 of each 16 share 256-byte
+//       lines, quad q of row r in half (q / 4) ^ (r / 8 mod 2) at position
+//       (r ^ q) mod 8.  Lane (i, kg) of QK step s reads quad 4s + kg of
+//       token row 16*hf + i.
+//   vt  V transposed, dim-major: head dim d on row rho = 16 * (d % DPL) +
+//       d / DPL and token t at position 8 * ((t % 16) / 4) + 4 * (t / 16) +
+//       t % 4 -- the order of the PV weights' k index -- stored by blocks of
+//       16 rows, each block as 4 runs (one per 8 positions) of its 16 rows'
+//       16-byte pieces: lane (i, kg) of PV block nb reads the contiguous
+//       piece 16 * i of run kg of block nb.
 // The transpose happens when a stage is stored: each storing thread holds
 // the same 16-byte column of two adjacent tokens, and writes dword pairs
-// (token t, t+1) of each dim.
+// (token t, t+1) of each dim; the four token pairs a wave stores per column
+// fill one 16-byte piece.
 //
 // PV is computed transposed, O^T += V^T P^T (V^T from LDS as MFMA A, the
 // weights as B), which leaves column i of the output in lane (i, kg), the
 // lane that holds column i's scores: the online-softmax rescale is
 // lane-local.
 template <int D, int SUB>
-struct SharedStage {
-  static constexpr int KRS = 2 * D + 16;        // K row stride (bytes)
-  static constexpr int VRS = 2 * kChunk + 16;   // V^T row stride (bytes)
-  uint8_t k[SUB * kChunk * KRS];                // SUB chunks of K rows
-  uint8_t vt[SUB][D * VRS];                     // V^T of each chunk
+struct alignas(16) SharedStage {
+  static_assert(D == 64 || D == 128, "stage layouts for head dims 64 and 128");
+  uint8_t k[SUB * kChunk * 2 * D];              // SUB chunks of K rows
+  uint8_t vt[SUB][D * 2 * kChunk];              // V^T of each chunk
+  // byte offset of 16-byte quad q of token row r
+  __device__ static int k_off(int r, int q) {
+    if constexpr (D == 128) {
+      return r * 256 + 16 * (q ^ (r & 15));
+    } else {
+      return (r >> 4) * 2048 + (r & 7) * 256 +
+             16 * (8 * ((q >> 2) ^ ((r >> 3) & 1)) + ((r ^ q) & 7));
+    }
+  }
+  // byte offset of (V^T row rho, token position pos) within a chunk
+  __device__ static int vt_off(int rho, int pos) {
+    return 1024 * (rho >> 4) + 256 * (pos >> 3) + 16 * (rho & 15) + 2 * (pos & 7);
+  }
 };
 
 // 32-token chunks per LDS stage of the shared kernel (one stage in flight
@@ -1039,30 +1080,41 @@ struct SharedStage {
 // than two).
 constexpr int kSharedSub = 2;
 
+// Weights of the shared kernel's lazily rescaled softmax stay below 2^8.
+constexpr float kLazyLog2 = 8.f;
+
 // Position of token t (0..31) of a chunk in a V^T row.
 __device__ inline int vt_pos(int t) {
   return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3);
 }
 
+// First token (within the stage) of V token pair q: the pairs of chunk
+// q / 16 in the order that puts four consecutive pairs (the ones a wave
+// stores for a column) at the four dwords of one V^T piece: positions
+// 8a + {0, 2, 4, 6} hold tokens 4a + {0, 2, 16, 18}.
+__device__ inline int v_pair_token(int q) {
+  const int qc = q & 15;
+  return kChunk * (q >> 4) + 4 * (qc >> 2) + 16 * ((qc >> 1) & 1) + 2 * (qc & 1);
+}
+
 // S^T = K Q^T for one chunk and one tile from LDS operands kf (K, MFMA A,
-// per 16-token half and QK step), then the online-softmax update; returns
-// the tile's PV weights (MFMA B layout of P^T; lane (i, kg) holds column i).
+// per 16-token half and QK step) -- qk_scores -- and the online-softmax
+// update -- softmax_tile, which returns the tile's PV weights (MFMA B layout
+// of P^T; lane (i, kg) holds column i).
 // The PV accumulators hold column i in lane (i, kg), so alpha is lane-local.
 //
 // Without per-page factors the score scale is one number: the max is taken
 // over the raw products (the scale is positive) and each weight is
-// exp2(s * scale - m) with one fused multiply-add; the column's weight sum
+// exp2(s * scale - m) with one fused multiply-add, m being a lazily raised
+// reference (any reference gives the same quotient acc / l, up to rounding;
+// this one keeps the weights below 2^kLazyLog2); the column's weight sum
 // is one more MFMA, a block of 1.0 times the rounded weights (the exact
-// fp32 sum of what PV multiplies), so l_run holds whole-column sums.  With
-// per-page factors the update is softmax_update's, and l_run holds this
-// lane's share of the column sum.
-template <int D, bool PAGE>
-__device__ inline bf16x8 qk_tile(const bf16x8 (&kf)[2][D / 32], const bf16x8 (&qop)[D / 32],
-                                 const float (&ks)[2], const float (&vs)[2], int c, int k0, int k1,
-                                 int lim, int lim_min, float qk_scale_log2, int kg, float& m_run,
-                                 float& l_run, f32x4 (&acc)[D / 16]) {
-  constexpr int DPL = D / 16;
-  f32x4 sacc[2];
+// fp32 sum of what PV multiplies) accumulated in l_acc, whose element 0
+// holds the whole column's sum.  With per-page factors the update is
+// softmax_update's, and l_run holds this lane's share of the column sum.
+template <int D>
+__device__ inline void qk_scores(const bf16x8 (&kf)[2][D / 32], const bf16x8 (&qop)[D / 32],
+                                 f32x4 (&sacc)[2]) {
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     sacc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1070,6 +1122,14 @@ __device__ inline bf16x8 qk_tile(const bf16x8 (&kf)[2][D / 32], const bf16x8 (&q
     for (int s = 0; s < D / 32; ++s)
       sacc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[hf][s], qop[s], sacc[hf], 0, 0, 0);
   }
+}
+
+template <int D, bool PAGE>
+__device__ inline bf16x8 softmax_tile(f32x4 (&sacc)[2], const float (&ks)[2],
+                                      const float (&vs)[2], int c, int k0, int k1, int lim,
+                                      int lim_min, float qk_scale_log2, int kg, float& m_run,
+                                      float& l_run, f32x4& l_acc, f32x4 (&acc)[D / 16]) {
+  constexpr int DPL = D / 16;
   if constexpr (PAGE) {
     return softmax_update<DPL, true, true>(sacc, ks, vs, c, k0, k1, lim, lim_min, qk_scale_log2,
                                            kg, m_run, l_run, acc);
@@ -1100,30 +1160,32 @@ __device__ inline bf16x8 qk_tile(const bf16x8 (&kf)[2][D / 32], const bf16x8 (&q
       for (int j = 0; j < 8; ++j)
         if (16 * (j >> 2) + (j & 3) > r) sc[j] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mx = kg_reduce_max(mx) * qk_scale_log2;
-    const float m_max = fmaxf(m_run, mx);
-    // a column with every token masked so far: subtract 0 (weights and
-    // alpha 0, not NaN; its state stays empty)
-    const float m_new = m_max == -INFINITY ? 0.f : m_max;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    bf16x8 pop;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      pop[j] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[j], qk_scale_log2, -m_new));
-    const bf16x8 ones = __builtin_bit_cast(
-        bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-    const f32x4 lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, f32x4{0.f, 0.f, 0.f, 0.f},
-                                                               0, 0, 0);
-    l_run = l_run * alpha + lsum[0];
-    m_run = m_max;
-    if (__ballot(alpha != 1.0f) != 0) {
+    const float inf = opaque_inf();
+    float mx = qmax(qmax(qmax(sc[0], sc[1], inf), qmax(sc[2], sc[3], inf), inf),
+                    qmax(qmax(sc[4], sc[5], inf), qmax(sc[6], sc[7], inf), inf), inf);
+    mx = kg_reduce_qmax(mx, inf) * qk_scale_log2;
+    // The reference m_run moves only when a column's maximum passes it by
+    // more than kLazyLog2 (then every column of the tile rescales), so the
+    // weights stay below 2^kLazyLog2 and most chunks skip the rescale.  It
+    // starts at -FLT_MAX: the first visible token moves it, and a column
+    // with every token masked so far gets weights 0, not NaN.
+    if (__ballot(mx > m_run + kLazyLog2) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_acc[0] *= alpha;
+      m_run = m_new;
 #pragma unroll
       for (int nb = 0; nb < DPL; ++nb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[nb][r] *= alpha;
     }
+    bf16x8 pop;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      pop[j] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[j], qk_scale_log2, -m_run));
+    const bf16x8 ones = __builtin_bit_cast(
+        bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+    l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, l_acc, 0, 0, 0);
     return pop;
   }
 }
@@ -1138,9 +1200,8 @@ __device__ inline uint32_t pair_hi(uint32_t a, uint32_t b) {
 
 // Register-staged loads of one LDS stage (SUB chunks of K and V) of the
 // shared kernel, by all NW waves.  Loads come in pairs: V pair v = (column
-// v % PPR of tokens 2 (v / PPR) and +1), then K pair k = (16-byte pieces 2k,
-// 2k + 1, piece p being column p % PPR of token p / PPR); task tau =
-// tid + NT u.  The counts are multiples of 64, so a wave's tasks are all of
+// v % PPR of tokens t and t + 1, t = v_pair_token(v / PPR)), then K pair k
+// (two 16-byte pieces, task_piece); task tau = tid + NT u.  The counts are multiples of 64, so a wave's tasks are all of
 // one kind.  Branch-free: a load whose token is past len or has no page
 // reads a valid address (page 0) and is zeroed when stored (ok bit 2u + m),
 // so the wait before a store counts only that stage's loads.
@@ -1166,6 +1227,21 @@ struct StageLoader {
   }
   __device__ static bool live_task(int u, int tau) {
     return kStaticKinds ? NT * u < TASKS : tau < TASKS;
+  }
+  // Piece m of K task k: token row and 16-byte column of the cache row.
+  // For bf16 rows of 16 pieces (D = 128) the 16 tasks 16a .. 16a + 15 take
+  // rows 2a (m = 0) and 2a + 1 (m = 1), task 16a + x the piece that lands
+  // on quad x of the swizzled row, so that each store fills a row's 256
+  // bytes; otherwise task k takes pieces 2k and 2k + 1 in row order.
+  __device__ static void task_piece(int k, int m, int& row, int& col) {
+    if constexpr (!FP8 && PPR == 16) {
+      row = 2 * (k >> 4) + m;
+      col = (k & 15) ^ (row & 15);
+    } else {
+      const int p = 2 * k + m;
+      row = p / PPR;
+      col = p % PPR;
+    }
   }
   u32x4 st[TPT][2];
   uint32_t st_ok;
@@ -1197,15 +1273,12 @@ struct StageLoader {
       const bool is_v = is_v_task(u, tau);
       int row[2], col[2];
       if (is_v) {
-        row[0] = 2 * (tau / PPR);
+        row[0] = v_pair_token(tau / PPR);
         row[1] = row[0] + 1;
         col[0] = col[1] = tau % PPR;
       } else {
-        const int p = 2 * (tau - VPAIRS);
-        row[0] = p / PPR;
-        col[0] = p % PPR;
-        row[1] = (p + 1) / PPR;
-        col[1] = (p + 1) % PPR;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) task_piece(tau - VPAIRS, m, row[m], col[m]);
       }
       const uint8_t* base = is_v ? a.v_pages : a.k_pages;
 #pragma unroll
@@ -1231,17 +1304,19 @@ struct StageLoader {
       for (int m = 0; m < 2; ++m)
         x[m] = ((st_ok >> (2 * u + m)) & 1u) ? st[u][m] : u32x4{0u, 0u, 0u, 0u};
       if (is_v_task(u, tau)) {
-        const int q = tau / PPR, col = tau % PPR;
-        // tokens 2q, 2q+1 of every row of their chunk's V^T
-        uint8_t* dst = ss.vt[(2 * q) / kChunk] + 2 * vt_pos((2 * q) % kChunk);
+        const int col = tau % PPR;
+        // tokens t, t + 1 (one dword) of every V^T row their column covers
+        const int t = v_pair_token(tau / PPR);
+        uint8_t* dst = ss.vt[t / kChunk];
+        const int pos = vt_pos(t % kChunk);
         if constexpr (!FP8) {
-          // dims 8 col + e: dword (token 2q, token 2q + 1)
+          // dims 8 col + e: dword (token t, token t + 1)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int d = 8 * col + e;
             const uint32_t w = (e & 1) ? pair_hi(x[0][e >> 1], x[1][e >> 1])
                                        : pair_lo(x[0][e >> 1], x[1][e >> 1]);
-            *reinterpret_cast<uint32_t*>(dst + (16 * (d % DPL) + d / DPL) * SS::VRS) = w;
+            *reinterpret_cast<uint32_t*>(dst + SS::vt_off(16 * (d % DPL) + d / DPL, pos)) = w;
           }
         } else {
           // dims 16 col + e, decoded: bf16 pairs (4k, 4k+1), (4k+2, 4k+3)
@@ -1255,23 +1330,23 @@ struct StageLoader {
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
               const int d = 16 * col + 4 * kq + e2;
-              *reinterpret_cast<uint32_t*>(dst + (16 * (d % DPL) + d / DPL) * SS::VRS) = w[e2];
+              *reinterpret_cast<uint32_t*>(dst + SS::vt_off(16 * (d % DPL) + d / DPL, pos)) = w[e2];
             }
           }
         }
       } else {
-        const int p = 2 * (tau - VPAIRS);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const int row = (p + m) / PPR, col = (p + m) % PPR;
+          int row, col;
+          task_piece(tau - VPAIRS, m, row, col);
           if constexpr (!FP8) {
-            *reinterpret_cast<u32x4*>(ss.k + row * SS::KRS + 16 * col) = x[m];
+            *reinterpret_cast<u32x4*>(ss.k + SS::k_off(row, col)) = x[m];
           } else {
             uint32_t w[8];
 #pragma unroll
             for (int kq = 0; kq < 4; ++kq) fp8x4_to_bf16x4(x[m][kq], w[2 * kq], w[2 * kq + 1]);
-            *reinterpret_cast<u32x4*>(ss.k + row * SS::KRS + 32 * col) = u32x4{w[0], w[1], w[2], w[3]};
-            *reinterpret_cast<u32x4*>(ss.k + row * SS::KRS + 32 * col + 16) = u32x4{w[4], w[5], w[6], w[7]};
+            *reinterpret_cast<u32x4*>(ss.k + SS::k_off(row, 2 * col)) = u32x4{w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<u32x4*>(ss.k + SS::k_off(row, 2 * col + 1)) = u32x4{w[4], w[5], w[6], w[7]};
           }
         }
       }
@@ -1306,6 +1381,7 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
   int r0[TPW], nqw[TPW], lim[TPW], lim_min[TPW], lim_max[TPW];
   bf16x8 qop[TPW][STEPS];
   float m_run[TPW], l_run[TPW];
+  f32x4 l_acc[TPW];                                  // column sums in [0] (no page factors)
   f32x4 acc[TPW][DPL];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -1322,8 +1398,9 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
       if (col_live) v = *reinterpret_cast<const u32x4*>(a.q + qbase + 32 * s2 + 8 * kg);
       qop[t][s2] = __builtin_bit_cast(bf16x8, v);
     }
-    m_run[t] = -INFINITY;
+    m_run[t] = PAGE ? -INFINITY : -FLT_MAX;        // (the lazy reference of qk_tile)
     l_run[t] = 0.f;
+    l_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < DPL; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -1367,9 +1444,13 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
         any = any || need[t];
       }
       if (!any) continue;
-      // QK and softmax of every tile, then PV: the K and V operands are not
-      // held at the same time
+      // QK of every tile with rows (all products in flight before the first
+      // softmax), the V operand reads, the softmax of every tile that sees
+      // the chunk, then PV.  (With per-page factors, whose softmax holds more
+      // registers, each tile's softmax follows its QK and the V reads come
+      // after.)
       const float jks[2] = {cks[2 * j], cks[2 * j + 1]}, jvs[2] = {cvs[2 * j], cvs[2 * j + 1]};
+      f32x4 sacc[TPW][2];
       bf16x8 pop[TPW];
       {
         bf16x8 kf[2][STEPS];
@@ -1378,21 +1459,33 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
 #pragma unroll
           for (int s2 = 0; s2 < STEPS; ++s2)
             kf[hf][s2] = *reinterpret_cast<const bf16x8*>(
-                ss.k + (kChunk * j + 16 * hf + i) * SS::KRS + 64 * s2 + 16 * kg);
+                ss.k + SS::k_off(kChunk * j + 16 * hf + i, 4 * s2 + kg));
         // every fragment read in flight before the first product (left to
         // itself the scheduler can reuse one register set and wait on each
         // read in turn)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
-          if (need[t])
-            pop[t] = qk_tile<D, PAGE>(kf, qop[t], jks, jvs, c, k0, k1, lim[t], lim_min[t], qk, kg,
-                                      m_run[t], l_run[t], acc[t]);
+        for (int t = 0; t < TPW; ++t) {
+          if constexpr (!PAGE) {
+            if (nqw[t] > 0) qk_scores<D>(kf, qop[t], sacc[t]);
+          } else if (need[t]) {
+            qk_scores<D>(kf, qop[t], sacc[t]);
+            pop[t] = softmax_tile<D, PAGE>(sacc[t], jks, jvs, c, k0, k1, lim[t], lim_min[t], qk,
+                                           kg, m_run[t], l_run[t], l_acc[t], acc[t]);
+          }
+        }
       }
       bf16x8 vf[DPL];
 #pragma unroll
       for (int nb = 0; nb < DPL; ++nb)
-        vf[nb] = *reinterpret_cast<const bf16x8*>(ss.vt[j] + (16 * nb + i) * SS::VRS + 16 * kg);
+        vf[nb] = *reinterpret_cast<const bf16x8*>(ss.vt[j] + 1024 * nb + 256 * kg + 16 * i);
+      if constexpr (!PAGE) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          if (need[t])
+            pop[t] = softmax_tile<D, PAGE>(sacc[t], jks, jvs, c, k0, k1, lim[t], lim_min[t], qk,
+                                           kg, m_run[t], l_run[t], l_acc[t], acc[t]);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
@@ -1414,7 +1507,7 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     // (per-page factors: each lane holds a share of the column's sum)
-    const float l_tot = PAGE ? kg_reduce_sum(l_run[t]) : l_run[t];
+    const float l_tot = PAGE ? kg_reduce_sum(l_run[t]) : l_acc[t][0];
     if (nqw[t] == 0) break;
     if (i < nqw[t] * g) {
       const int64_t hq = (int64_t)h * g + hh;
