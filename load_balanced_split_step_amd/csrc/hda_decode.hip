@@ -1048,8 +1048,7 @@ __device__ inline void process_item_fp8n(const Args& a, const int32_t* __restric
 //       piece 16 * i of run kg of block nb.
 // The transpose happens when a stage is stored: each storing thread holds
 // the same 16-byte column of two adjacent tokens, and writes dword pairs
-// (token t, t+1) of each dim; the four token pairs a wave stores per column
-// fill one 16-byte piece.
+// (token t, t+1) of each dim.
 //
 // PV is computed transposed, O^T += V^T P^T (V^T from LDS as MFMA A, the
 // weights as B), which leaves column i of the output in lane (i, kg), the
@@ -1086,15 +1085,6 @@ constexpr float kLazyLog2 = 8.f;
 // Position of token t (0..31) of a chunk in a V^T row.
 __device__ inline int vt_pos(int t) {
   return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3);
-}
-
-// First token (within the stage) of V token pair q: the pairs of chunk
-// q / 16 in the order that puts four consecutive pairs (the ones a wave
-// stores for a column) at the four dwords of one V^T piece: positions
-// 8a + {0, 2, 4, 6} hold tokens 4a + {0, 2, 16, 18}.
-__device__ inline int v_pair_token(int q) {
-  const int qc = q & 15;
-  return kChunk * (q >> 4) + 4 * (qc >> 2) + 16 * ((qc >> 1) & 1) + 2 * (qc & 1);
 }
 
 // S^T = K Q^T for one chunk and one tile from LDS operands kf (K, MFMA A,
@@ -1200,8 +1190,8 @@ __device__ inline uint32_t pair_hi(uint32_t a, uint32_t b) {
 
 // Register-staged loads of one LDS stage (SUB chunks of K and V) of the
 // shared kernel, by all NW waves.  Loads come in pairs: V pair v = (column
-// v % PPR of tokens t and t + 1, t = v_pair_token(v / PPR)), then K pair k
-// (two 16-byte pieces, task_piece); task tau = tid + NT u.  The counts are multiples of 64, so a wave's tasks are all of
+// v % PPR of tokens 2 (v / PPR) and +1), then K pair k (two 16-byte pieces,
+// task_piece); task tau = tid + NT u.  The counts are multiples of 64, so a wave's tasks are all of
 // one kind.  Branch-free: a load whose token is past len or has no page
 // reads a valid address (page 0) and is zeroed when stored (ok bit 2u + m),
 // so the wait before a store counts only that stage's loads.
@@ -1222,6 +1212,10 @@ struct StageLoader {
   // outside branches (a conditional load makes the waits before the stores
   // conservative).
   static constexpr bool kStaticKinds = VPAIRS % NT == 0 && TASKS % NT == 0;
+  // Both loads of a task slot fall in one 16-token group in every lane of a
+  // wave when a cache row has at least 8 pieces: V pairs of a wave then span
+  // at most 16 tokens, and a K slot's rows 8 (task_piece).
+  static constexpr bool kUniformGroup = PPR >= 8;
   __device__ static bool is_v_task(int u, int tau) {
     return kStaticKinds ? NT * u < VPAIRS : tau < VPAIRS;
   }
@@ -1251,17 +1245,24 @@ struct StageLoader {
   __device__ inline void fetch(const Args& a, const int32_t* __restrict__ block_table, int b,
                                int L, int h, int c, int tid) {
     const int t0 = c * kChunk;
-    int pg[HALVES];
+    // page of 16-token group hf of the stage (page 0 when the group has no
+    // valid page: its loads are then zeroed when stored)
+    auto group_page = [&](int hf, bool& pok) {
+      const int t = t0 + 16 * hf;
+      const int pidx = t >> a.log2_ps;
+      const int pg = (t < L && pidx < a.max_pages) ? block_table[(int64_t)b * a.max_pages + pidx] : -1;
+      pok = pg >= 0 && pg < a.num_pages;
+      return pok ? pg : 0;
+    };
 #pragma unroll
     for (int hf = 0; hf < HALVES; ++hf) {
       sks[hf] = svs[hf] = 1.f;
-      const int t = t0 + 16 * hf;
-      const int pidx = t >> a.log2_ps;
-      pg[hf] = (t < L && pidx < a.max_pages) ? block_table[(int64_t)b * a.max_pages + pidx] : -1;
       if constexpr (PAGE) {
-        if (pg[hf] >= 0 && pg[hf] < a.num_pages) {
-          sks[hf] = a.k_scales[(int64_t)pg[hf] * a.n_kv_heads + h];
-          svs[hf] = a.v_scales[(int64_t)pg[hf] * a.n_kv_heads + h];
+        bool pok;
+        const int pg = group_page(hf, pok);
+        if (pok) {
+          sks[hf] = a.k_scales[(int64_t)pg * a.n_kv_heads + h];
+          svs[hf] = a.v_scales[(int64_t)pg * a.n_kv_heads + h];
         }
       }
     }
@@ -1273,22 +1274,40 @@ struct StageLoader {
       const bool is_v = is_v_task(u, tau);
       int row[2], col[2];
       if (is_v) {
-        row[0] = v_pair_token(tau / PPR);
+        row[0] = 2 * (tau / PPR);
         row[1] = row[0] + 1;
         col[0] = col[1] = tau % PPR;
       } else {
 #pragma unroll
         for (int m = 0; m < 2; ++m) task_piece(tau - VPAIRS, m, row[m], col[m]);
       }
-      const uint8_t* base = is_v ? a.v_pages : a.k_pages;
+      const uint8_t* pool = is_v ? a.v_pages : a.k_pages;
+      if constexpr (kUniformGroup) {
+        // both loads of the slot, in every lane of the wave, fall in one
+        // 16-token group: one page lookup, a uniform slab address and a
+        // 32-bit offset per lane
+        const int hf = __builtin_amdgcn_readfirstlane(row[0] >> 4);
+        bool pok;
+        const int pg = group_page(hf, pok);
+        const uint8_t* slab = pool + (int64_t)pg * a.page_stride + (int64_t)h * a.head_stride;
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int t = t0 + row[m], page = pg[row[m] >> 4];
-        const bool ok = t < L && page >= 0 && page < a.num_pages;
-        const int64_t off = (int64_t)(ok ? page : 0) * a.page_stride + (int64_t)h * a.head_stride +
-                            (int64_t)(t & (a.page_size - 1)) * G::RB + 16 * col[m];
-        st[u][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
-        st_ok |= (ok ? 1u : 0u) << (2 * u + m);
+        for (int m = 0; m < 2; ++m) {
+          const int t = t0 + row[m];
+          const uint32_t in_page = (uint32_t)((t & (a.page_size - 1)) * G::RB + 16 * col[m]);
+          st[u][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(slab + in_page));
+          st_ok |= (t < L && pok ? 1u : 0u) << (2 * u + m);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int t = t0 + row[m];
+          bool pok;
+          const int pg = group_page(row[m] >> 4, pok);
+          const int64_t off = (int64_t)pg * a.page_stride + (int64_t)h * a.head_stride +
+                              (int64_t)(t & (a.page_size - 1)) * G::RB + 16 * col[m];
+          st[u][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pool + off));
+          st_ok |= (t < L && pok ? 1u : 0u) << (2 * u + m);
+        }
       }
     }
   }
@@ -1306,7 +1325,7 @@ struct StageLoader {
       if (is_v_task(u, tau)) {
         const int col = tau % PPR;
         // tokens t, t + 1 (one dword) of every V^T row their column covers
-        const int t = v_pair_token(tau / PPR);
+        const int t = 2 * (tau / PPR);
         uint8_t* dst = ss.vt[t / kChunk];
         const int pos = vt_pos(t % kChunk);
         if constexpr (!FP8) {
