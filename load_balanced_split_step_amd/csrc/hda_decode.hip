@@ -1266,45 +1266,57 @@ struct StageLoader {
         }
       }
     }
-    st_ok = 0u;
+    // rows and columns of every slot's loads
+    int row[TPT][2], col[TPT][2];
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int tau = tid + NT * u;
-      if (!live_task(u, tau)) break;                 // uniform per wave
-      const bool is_v = is_v_task(u, tau);
-      int row[2], col[2];
-      if (is_v) {
-        row[0] = 2 * (tau / PPR);
-        row[1] = row[0] + 1;
-        col[0] = col[1] = tau % PPR;
+      if (is_v_task(u, tau)) {
+        row[u][0] = 2 * (tau / PPR);
+        row[u][1] = row[u][0] + 1;
+        col[u][0] = col[u][1] = tau % PPR;
       } else {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) task_piece(tau - VPAIRS, m, row[m], col[m]);
+        for (int m = 0; m < 2; ++m) task_piece(tau - VPAIRS, m, row[u][m], col[u][m]);
       }
-      const uint8_t* pool = is_v ? a.v_pages : a.k_pages;
-      if constexpr (kUniformGroup) {
-        // both loads of the slot, in every lane of the wave, fall in one
-        // 16-token group: one page lookup, a uniform slab address and a
-        // 32-bit offset per lane
-        const int hf = __builtin_amdgcn_readfirstlane(row[0] >> 4);
-        bool pok;
-        const int pg = group_page(hf, pok);
-        const uint8_t* slab = pool + (int64_t)pg * a.page_stride + (int64_t)h * a.head_stride;
+    }
+    st_ok = 0u;
+    if constexpr (kUniformGroup) {
+      // both loads of a slot, in every lane of the wave, fall in one 16-token
+      // group: one page lookup per slot (all slots' lookups issued together),
+      // a uniform slab address and a 32-bit offset per lane
+      int pg[TPT];
+      bool pok[TPT];
+#pragma unroll
+      for (int u = 0; u < TPT; ++u)
+        pg[u] = group_page(__builtin_amdgcn_readfirstlane(row[u][0] >> 4), pok[u]);
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int tau = tid + NT * u;
+        if (!live_task(u, tau)) break;               // uniform per wave
+        const uint8_t* slab = (is_v_task(u, tau) ? a.v_pages : a.k_pages) +
+                              (int64_t)pg[u] * a.page_stride + (int64_t)h * a.head_stride;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const int t = t0 + row[m];
-          const uint32_t in_page = (uint32_t)((t & (a.page_size - 1)) * G::RB + 16 * col[m]);
+          const int t = t0 + row[u][m];
+          const uint32_t in_page = (uint32_t)((t & (a.page_size - 1)) * G::RB + 16 * col[u][m]);
           st[u][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(slab + in_page));
-          st_ok |= (t < L && pok ? 1u : 0u) << (2 * u + m);
+          st_ok |= (t < L && pok[u] ? 1u : 0u) << (2 * u + m);
         }
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int tau = tid + NT * u;
+        if (!live_task(u, tau)) break;               // uniform per wave
+        const uint8_t* pool = is_v_task(u, tau) ? a.v_pages : a.k_pages;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const int t = t0 + row[m];
+          const int t = t0 + row[u][m];
           bool pok;
-          const int pg = group_page(row[m] >> 4, pok);
+          const int pg = group_page(row[u][m] >> 4, pok);
           const int64_t off = (int64_t)pg * a.page_stride + (int64_t)h * a.head_stride +
-                              (int64_t)(t & (a.page_size - 1)) * G::RB + 16 * col[m];
+                              (int64_t)(t & (a.page_size - 1)) * G::RB + 16 * col[u][m];
           st[u][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pool + off));
           st_ok |= (t < L && pok ? 1u : 0u) << (2 * u + m);
         }
