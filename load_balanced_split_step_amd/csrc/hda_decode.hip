@@ -1088,19 +1088,10 @@ __device__ inline int vt_pos(int t) {
 }
 
 // S^T = K Q^T for one chunk and one tile from LDS operands kf (K, MFMA A,
-// per 16-token half and QK step) -- qk_scores -- and the online-softmax
-// update -- softmax_tile, which returns the tile's PV weights (MFMA B layout
-// of P^T; lane (i, kg) holds column i).
-// The PV accumulators hold column i in lane (i, kg), so alpha is lane-local.
-//
-// Without per-page factors the score scale is one number: the max is taken
-// over the raw products (the scale is positive) and each weight is
-// exp2(s * scale - m) with one fused multiply-add, m being a lazily raised
-// reference (any reference gives the same quotient acc / l, up to rounding;
-// this one keeps the weights below 2^kLazyLog2); the column's weight sum
-// is one more MFMA, a block of 1.0 times the rounded weights (the exact
-// fp32 sum of what PV multiplies) accumulated in l_acc, whose element 0
-// holds the whole column's sum.  With per-page factors the update is
+// per 16-token half and QK step) -- qk_scores -- then the online-softmax
+// update, which yields the tile's PV weights (MFMA B layout of P^T; lane
+// (i, kg) holds column i).  The PV accumulators hold column i in lane (i, kg),
+// so alpha is lane-local.  With per-page factors the update is
 // softmax_update's, and l_run holds this lane's share of the column sum.
 template <int D>
 __device__ inline void qk_scores(const bf16x8 (&kf)[2][D / 32], const bf16x8 (&qop)[D / 32],
@@ -1114,69 +1105,91 @@ __device__ inline void qk_scores(const bf16x8 (&kf)[2][D / 32], const bf16x8 (&q
   }
 }
 
-template <int D, bool PAGE>
-__device__ inline bf16x8 softmax_tile(f32x4 (&sacc)[2], const float (&ks)[2],
-                                      const float (&vs)[2], int c, int k0, int k1, int lim,
-                                      int lim_min, float qk_scale_log2, int kg, float& m_run,
-                                      float& l_run, f32x4& l_acc, f32x4 (&acc)[D / 16]) {
+// The update without per-page factors, for all TPW tiles of a wave at once
+// (one branch per mask and one for the rescale serve every tile, so that the
+// tiles' dependency chains interleave; tiles that see none of the chunk come
+// out with weights 0 and unchanged state).  The score scale is one number:
+// the max is taken over the raw products (the scale is positive) and each
+// weight is exp2(s * scale - m) with one fused multiply-add, m being a
+// lazily raised reference (any reference gives the same quotient acc / l, up
+// to rounding): it moves only when a column's maximum passes it by more than
+// kLazyLog2, so the weights stay below 2^kLazyLog2 and most chunks skip the
+// rescale.  It starts at -FLT_MAX: the first visible token moves it, and a
+// column with every token masked so far gets weights 0, not NaN.  The
+// column's weight sum is one more MFMA, a block of 1.0 times the rounded
+// weights (the exact fp32 sum of what PV multiplies) accumulated in l_acc,
+// whose element 0 holds the whole column's sum.  Masks come in two uniform
+// branches, taken only by the chunks that need them: tokens before k0 (an
+// item starting inside the chunk), and tokens past a column's last visible
+// one, hi = min(k1 - 1, causal limit); each element's offset 16 (j / 4) +
+// j % 4 is a constant compared with a per-lane threshold (the threshold of
+// the first through readfirstlane, a convergent operation, which keeps the
+// tests inside the branch).
+template <int D, int TPW>
+__device__ inline void softmax_tiles(f32x4 (&sacc)[TPW][2], int c, int k0, int k1,
+                                     const int (&lim)[TPW], const int (&lim_min)[TPW],
+                                     float qk_scale_log2, int kg, float (&m_run)[TPW],
+                                     f32x4 (&l_acc)[TPW], f32x4 (&acc)[TPW][D / 16],
+                                     bf16x8 (&pop)[TPW]) {
   constexpr int DPL = D / 16;
-  if constexpr (PAGE) {
-    return softmax_update<DPL, true, true>(sacc, ks, vs, c, k0, k1, lim, lim_min, qk_scale_log2,
-                                           kg, m_run, l_run, acc);
-  } else {
-    float sc[8];
+  float sc[TPW][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sc[j] = sacc[j >> 2][j & 3];
-    // Masks, in two uniform branches taken only by the chunks that need
-    // them: tokens before k0 (an item starting inside the chunk), and tokens
-    // past the column's last visible one, hi = min(k1 - 1, causal limit);
-    // each element's offset 16 (j / 4) + j % 4 is a constant compared with
-    // a per-lane threshold.  (A single test of both bounds, the same for
-    // every tile, was hoisted by the compiler out of the tiles' branches and
-    // paid on every chunk.)
-    const int t0 = c * kChunk;
-    if (t0 < k0) {
-      // (the threshold through readfirstlane, a convergent operation, keeps
-      // these tests inside the branch)
-      const int d = __builtin_amdgcn_readfirstlane(k0 - t0) - 4 * kg;
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sc[t][j] = sacc[t][j >> 2][j & 3];
+  const int t0 = c * kChunk;
+  if (t0 < k0) {
+    const int d = __builtin_amdgcn_readfirstlane(k0 - t0) - 4 * kg;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (16 * (j >> 2) + (j & 3) < d) sc[j] = -INFINITY;
-    }
-    const int hi_min = min(k1 - 1, lim_min);
-    if (t0 + kChunk - 1 > hi_min) {
-      const int r = min(k1 - 1, lim) - t0 - 4 * kg;
+        if (16 * (j >> 2) + (j & 3) < d) sc[t][j] = -INFINITY;
+  }
+  int hi_min = k1 - 1;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) hi_min = min(hi_min, lim_min[t]);
+  if (t0 + kChunk - 1 > hi_min) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int r = min(k1 - 1, lim[t]) - t0 - 4 * kg;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (16 * (j >> 2) + (j & 3) > r) sc[j] = -INFINITY;
+        if (16 * (j >> 2) + (j & 3) > r) sc[t][j] = -INFINITY;
     }
-    const float inf = opaque_inf();
-    float mx = qmax(qmax(qmax(sc[0], sc[1], inf), qmax(sc[2], sc[3], inf), inf),
-                    qmax(qmax(sc[4], sc[5], inf), qmax(sc[6], sc[7], inf), inf), inf);
-    mx = kg_reduce_qmax(mx, inf) * qk_scale_log2;
-    // The reference m_run moves only when a column's maximum passes it by
-    // more than kLazyLog2 (then every column of the tile rescales), so the
-    // weights stay below 2^kLazyLog2 and most chunks skip the rescale.  It
-    // starts at -FLT_MAX: the first visible token moves it, and a column
-    // with every token masked so far gets weights 0, not NaN.
-    if (__ballot(mx > m_run + kLazyLog2) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_acc[0] *= alpha;
-      m_run = m_new;
+  }
+  const float inf = opaque_inf();
+  float mx[TPW];
+  bool grow = false;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    mx[t] = qmax(qmax(qmax(sc[t][0], sc[t][1], inf), qmax(sc[t][2], sc[t][3], inf), inf),
+                 qmax(qmax(sc[t][4], sc[t][5], inf), qmax(sc[t][6], sc[t][7], inf), inf), inf);
+    mx[t] = kg_reduce_qmax(mx[t], inf) * qk_scale_log2;
+    grow = grow || mx[t] > m_run[t] + kLazyLog2;
+  }
+  // the reference moves for every tile when any column needs it
+  if (__ballot(grow) != 0) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const float m_new = fmaxf(m_run[t], mx[t]);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);
+      l_acc[t][0] *= alpha;
+      m_run[t] = m_new;
 #pragma unroll
       for (int nb = 0; nb < DPL; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[nb][r] *= alpha;
+        for (int r = 0; r < 4; ++r) acc[t][nb][r] *= alpha;
     }
-    bf16x8 pop;
+  }
+  const bf16x8 ones = __builtin_bit_cast(
+      bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      pop[j] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[j], qk_scale_log2, -m_run));
-    const bf16x8 ones = __builtin_bit_cast(
-        bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-    l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, l_acc, 0, 0, 0);
-    return pop;
+      pop[t][j] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][j], qk_scale_log2, -m_run[t]));
+    l_acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop[t], l_acc[t], 0, 0, 0);
   }
 }
 
@@ -1501,8 +1514,9 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
             if (nqw[t] > 0) qk_scores<D>(kf, qop[t], sacc[t]);
           } else if (need[t]) {
             qk_scores<D>(kf, qop[t], sacc[t]);
-            pop[t] = softmax_tile<D, PAGE>(sacc[t], jks, jvs, c, k0, k1, lim[t], lim_min[t], qk,
-                                           kg, m_run[t], l_run[t], l_acc[t], acc[t]);
+            pop[t] = softmax_update<D / 16, true, true>(sacc[t], jks, jvs, c, k0, k1, lim[t],
+                                                        lim_min[t], qk, kg, m_run[t], l_run[t],
+                                                        acc[t]);
           }
         }
       }
@@ -1510,13 +1524,8 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
 #pragma unroll
       for (int nb = 0; nb < DPL; ++nb)
         vf[nb] = *reinterpret_cast<const bf16x8*>(ss.vt[j] + 1024 * nb + 256 * kg + 16 * i);
-      if constexpr (!PAGE) {
-#pragma unroll
-        for (int t = 0; t < TPW; ++t)
-          if (need[t])
-            pop[t] = softmax_tile<D, PAGE>(sacc[t], jks, jvs, c, k0, k1, lim[t], lim_min[t], qk,
-                                           kg, m_run[t], l_run[t], l_acc[t], acc[t]);
-      }
+      if constexpr (!PAGE)
+        softmax_tiles<D, TPW>(sacc, c, k0, k1, lim, lim_min, qk, kg, m_run, l_acc, acc, pop);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
