@@ -1511,7 +1511,8 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
           if constexpr (!PAGE) {
-            if (nqw[t] > 0) qk_scores<D>(kf, qop[t], sacc[t]);
+            // every tile, branch-free (a tile without rows has q = 0)
+            qk_scores<D>(kf, qop[t], sacc[t]);
           } else if (need[t]) {
             qk_scores<D>(kf, qop[t], sacc[t]);
             pop[t] = softmax_update<D / 16, true, true>(sacc[t], jks, jvs, c, k0, k1, lim[t],
@@ -1527,11 +1528,14 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
       if constexpr (!PAGE)
         softmax_tiles<D, TPW>(sacc, c, k0, k1, lim, lim_min, qk, kg, m_run, l_acc, acc, pop);
       __builtin_amdgcn_sched_barrier(0);
+      // O^T block nb += V^T P^T; for bf16 pages without per-page factors for
+      // every tile, branch-free (weights 0 where a tile sees none of the
+      // chunk): measured faster there, slower for fp8 pages
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
-        if (need[t])
+        if ((!PAGE && !FP8) || need[t])
 #pragma unroll
-          for (int nb = 0; nb < DPL; ++nb)   // O^T block nb += V^T P^T
+          for (int nb = 0; nb < DPL; ++nb)
             acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[nb], pop[t], acc[t][nb], 0, 0, 0);
     }
     if (si + 1 < n_st) {
