@@ -1442,7 +1442,7 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
       if (col_live) v = *reinterpret_cast<const u32x4*>(a.q + qbase + 32 * s2 + 8 * kg);
       qop[t][s2] = __builtin_bit_cast(bf16x8, v);
     }
-    m_run[t] = PAGE ? -INFINITY : -FLT_MAX;        // (the lazy reference of qk_tile)
+    m_run[t] = PAGE ? -INFINITY : -FLT_MAX;        // (the lazy reference of softmax_tiles)
     l_run[t] = 0.f;
     l_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
