@@ -8,8 +8,10 @@ element at
 sizes the oracle finishes in seconds (ragged q lengths, partial blocks whose
 last tiles are idle, blocks split over workgroups, plan tiles not aligned to
 chunks, every group size the kernel takes), one query per request bitwise
-equal to the decode path, and the full-size speculative-check and chunked
-workloads on sampled rows.
+equal to the decode path, score patterns that move the softmax's running
+maximum again and again (keys growing along the sequence, a late key that
+dominates), and the full-size speculative-check and chunked workloads on
+sampled rows.
 Bar: 2e-2 (bf16 cache), 6e-2 (fp8 cache) max-abs error.
 """
 
@@ -19,7 +21,7 @@ import torch
 
 import load_balanced_split_step_amd.hda as hda
 import oracle
-from load_balanced_split_step_amd.workloads import CONFIGS, Workload, make_inputs
+from load_balanced_split_step_amd.workloads import CONFIGS, Workload, _bf16_bits, make_inputs
 from tests.gpu_util import TOL, need_gpu, scale_kw, max_err
 
 pytestmark = pytest.mark.gpu
@@ -81,6 +83,50 @@ def test_prefill_parity(name, tiles):
         print(f"{name} {pname} {tiles} tiles: {len(rows)} blocks, "
               f"P={int(plan[6])}, max err {err:.3e}", flush=True)
         assert err <= tol, (name, pname, err)
+
+
+def _reshape_keys(inp, rate, jump):
+    """Scale the cached key of token t of every request by 1 + rate * t, and
+    the key of its last cached token before the new rows by `jump` more
+    (bf16, round to nearest even; the poisoned slots past each length stay
+    as they are): the scores grow along the sequence, so the running maximum
+    keeps moving, and the late key dominates the columns it aligns with."""
+    w = inp["workload"]
+    ps = w.page_size
+    k = inp["k_pages"].copy()
+    for b, L in enumerate(inp["seq_lens"]):
+        L = int(L)
+        t_jump = L - int(inp["q_lens"][b]) - 1
+        for p in range(-(-L // ps)):
+            pg = int(inp["block_table"][b, p])
+            n = min(ps, L - p * ps)
+            t = p * ps + np.arange(n)
+            f = (1.0 + rate * t) * np.where(t == t_jump, jump, 1.0)
+            rows = oracle.bf16_to_f64(k[pg, :, :n, :]) * f[None, :, None]
+            k[pg, :, :n, :] = _bf16_bits(rows.astype(np.float32))
+    return dict(inp, k_pages=k)
+
+
+@pytest.mark.parametrize("tiles", [1, 2, 4, 16], ids=["1tile", "2tiles", "4tiles", "16tiles"])
+@pytest.mark.parametrize("pattern", ["growth", "jump"])
+def test_prefill_moving_maximum(pattern, tiles):
+    """Keys scaled up along the sequence (x 1 + t / 40: the column maxima
+    pass the softmax's reference by more than 2^8 again and again), or in
+    addition one late key x 40; bf16 cache, the default plan and a fine one."""
+    w = CONFIGS["chunked"].with_(name="moving_max", batch=4, len_range=(300, 2500),
+                                 q_len_range=(1, 40), seed=84)
+    inp = _reshape_keys(make_inputs(w), 1.0 / 40, 40.0 if pattern == "jump" else 1.0)
+    ref = ref_prefill(inp)
+    dev = hda.DeviceBatch.from_inputs(inp)
+    qb = hda.hda_prefill_rows_per_block(w.n_q_heads, w.n_kv_heads) * tiles
+    rows, row_lens = hda.hda_prefill_rows(inp["q_lens"], inp["seq_lens"], qb)
+    for pname, plan in [("default", dev.prefill_plan(inp["q_lens"], tiles=tiles)[1]),
+                        ("dyn-64-11", hda.hda_plan(row_lens, 64, 11))]:
+        out = dev.prefill(rows, plan)
+        torch.cuda.synchronize()
+        err = max_err(out, ref)
+        print(f"{pattern} {pname} {tiles} tiles: max err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], (pattern, pname, err)
 
 
 def test_single_query_rows_bitwise_equal_decode():
