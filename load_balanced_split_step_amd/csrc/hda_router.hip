@@ -309,6 +309,11 @@ struct RouterShape {
 // the compute units idle).
 constexpr int64_t kBigMinGroups = 256;
 constexpr int kBigMinStages = 8;      // K per workgroup >= 8 stages (512)
+// The split-K register kernel splits the hidden dimension until its tiles
+// make about this many workgroups (one per compute unit: measured against
+// 128, 192, 384 and 512 over 1 to 16384 tokens, best at 256 and 1024 tokens
+// -- fewer partial tiles to write and add -- and equal elsewhere).
+constexpr int64_t kSmallTargetGroups = 256;
 
 RouterShape router_shape(int32_t T, int32_t E, int32_t H) {
   RouterShape r;
@@ -333,7 +338,7 @@ RouterShape router_shape(int32_t T, int32_t E, int32_t H) {
   const int64_t base = (int64_t)r.tiles_t * r.tiles_e;
   constexpr int kRound = kStepK * kWaves;                 // one K step per wave
   const int rounds_total = (H + kRound - 1) / kRound;     // >= 1 for H >= 1; last may be partial
-  int64_t S = (512 + base - 1) / base;
+  int64_t S = (kSmallTargetGroups + base - 1) / base;
   S = S < 1 ? 1 : (S > rounds_total ? rounds_total : S);
   const int rounds = (int)((rounds_total + S - 1) / S);   // per workgroup, >= 1
   r.k_per_wg = rounds * kRound;
