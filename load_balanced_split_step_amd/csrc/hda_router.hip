@@ -146,13 +146,15 @@ __global__ __launch_bounds__(64 * kWaves) void hda_router_gemm_kernel(RouterArgs
 
 // Large batches: 128 tokens x 128 experts per workgroup, K sliced by 64 (two
 // MFMA steps per barrier; slices of 32 measured 10% slower) and staged
-// through LDS (double-buffered: the next slice is loaded into registers
-// while the current one is multiplied).  Wave (wm, wn) owns the 64 x 64
-// sub-tile at (64 wm, 64 wn): 4 x 4 blocks for each product.  LDS rows hold
-// 64 bf16 and are padded to 144 bytes: the 16 lanes of a fragment read that
-// share a k offset read 16 rows, whose 16-byte pieces then fall in distinct
-// bank groups (36 i mod 64 dwords; unpadded rows put several rows on the
-// same banks).
+// through LDS (two stages) from registers loaded two slices ahead (two
+// register sets; one slice ahead left each step waiting ~3x its MFMA time
+// on memory).  Eight waves: wave (wm, wn) owns the 64 x 32 sub-tile at
+// (64 wm, 32 wn), 4 x 2 blocks for each product, which keeps the
+// accumulators and both register sets within 256 registers (two waves per
+// SIMD).  LDS rows hold 64 bf16 and are padded to 144 bytes: the 16 lanes of
+// a fragment read that share a k offset read 16 rows, whose 16-byte pieces
+// then fall in distinct bank groups (36 i mod 64 dwords; unpadded rows put
+// several rows on the same banks).
 constexpr int kBigM = 128, kBigN = 128;
 constexpr int kBigK = 64;             // K per LDS stage (two MFMA steps)
 constexpr int kBigRow = kBigK + 8;    // padded LDS row, in bf16
@@ -163,12 +165,15 @@ struct BigStage {
   uint16_t bl[kBigN][kBigRow];
 };
 
-__global__ __launch_bounds__(64 * kWaves, 2) void hda_router_gemm_lds_kernel(RouterArgs a) {
+constexpr int kBigWaves = 8;          // 2 x 4 waves of 64 x 32 sub-tiles
+
+__global__ __launch_bounds__(64 * kBigWaves, 1) void hda_router_gemm_lds_kernel(RouterArgs a) {
   __shared__ BigStage st[2];
+  constexpr int NT = 64 * kBigWaves;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, kg = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;         // rows 64 wm.., experts 32 wn..
   const int t0 = blockIdx.x * kBigM, e0 = blockIdx.y * kBigN;
   const int kb = blockIdx.z * a.k_per_wg;
   const int ke = min(a.H, kb + a.k_per_wg);
@@ -176,82 +181,100 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_router_gemm_lds_kernel(Rou
   const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.w_hi, (int64_t)a.E * a.H * 2);
   const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.w_lo, (int64_t)a.E * a.H * 2);
 
-  // global -> LDS copy: 1024 16-byte chunks per tile, four per thread; chunk
+  // global -> LDS copy: 1024 16-byte chunks per tile, two per thread; chunk
   // c is row c / 8, k offset 8 (c % 8)
-  constexpr int kChunks = kBigM * kBigK / 8 / 256;   // per thread per tile
+  constexpr int kChunks = kBigM * kBigK / 8 / NT;    // per thread per tile
   int64_t ga[kChunks], gb[kChunks];
   int lrow[kChunks], lcol[kChunks];
 #pragma unroll
   for (int u = 0; u < kChunks; ++u) {
-    const int c = tid + 256 * u;
+    const int c = tid + NT * u;
     lrow[u] = c >> 3;
     lcol[u] = 8 * (c & 7);
     ga[u] = ((int64_t)(t0 + lrow[u]) * a.H + lcol[u]) * 2;
     gb[u] = ((int64_t)(e0 + lrow[u]) * a.H + lcol[u]) * 2;
   }
-  u32x4 ra[kChunks], rh[kChunks], rl[kChunks];
-  auto load = [&](int k) {
+  // two register sets: the slice two steps ahead is in flight while the
+  // next one waits to be stored
+  struct Regs { u32x4 a[kChunks], h[kChunks], l[kChunks]; } r0, r1;
+  auto load = [&](Regs& r, int k) {
 #pragma unroll
     for (int u = 0; u < kChunks; ++u) {
-      ra[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(ga[u] + 2 * k), 0, 0));
-      rh[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hr, (int)(gb[u] + 2 * k), 0, 0));
-      rl[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(lr, (int)(gb[u] + 2 * k), 0, 0));
+      // (the K offset as the scalar offset: no per-step address arithmetic
+      // in registers the compiler might then have to wait for)
+      r.a[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)ga[u], 2 * k, 0));
+      r.h[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hr, (int)gb[u], 2 * k, 0));
+      r.l[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(lr, (int)gb[u], 2 * k, 0));
     }
   };
-  auto store = [&](BigStage& s) {
+  auto store = [&](const Regs& r, BigStage& s) {
 #pragma unroll
     for (int u = 0; u < kChunks; ++u) {
-      *reinterpret_cast<u32x4*>(&s.a[lrow[u]][lcol[u]]) = ra[u];
-      *reinterpret_cast<u32x4*>(&s.bh[lrow[u]][lcol[u]]) = rh[u];
-      *reinterpret_cast<u32x4*>(&s.bl[lrow[u]][lcol[u]]) = rl[u];
+      *reinterpret_cast<u32x4*>(&s.a[lrow[u]][lcol[u]]) = r.a[u];
+      *reinterpret_cast<u32x4*>(&s.bh[lrow[u]][lcol[u]]) = r.h[u];
+      *reinterpret_cast<u32x4*>(&s.bl[lrow[u]][lcol[u]]) = r.l[u];
     }
   };
 
-  f32x4 acc_hi[4][4], acc_lo[4][4];
+  f32x4 acc_hi[4][2], acc_lo[4][2];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < 2; ++n) {
       acc_hi[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc_lo[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  const int nk = (ke - kb) / kBigK;
-  load(kb);
-  store(st[0]);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) load(kb + kBigK * (ks + 1));
-    const BigStage& s = st[ks & 1];
+  auto compute = [&](const BigStage& s) {
 #pragma unroll
     for (int kk = 0; kk < kBigK; kk += kStepK) {
-      bf16x8 fa[4], fh[4], fl[4];
+      bf16x8 fa[4], fh[2], fl[2];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         fa[m] = *reinterpret_cast<const bf16x8*>(&s.a[64 * wm + 16 * m + i][kk + 8 * kg]);
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        fh[n] = *reinterpret_cast<const bf16x8*>(&s.bh[64 * wn + 16 * n + i][kk + 8 * kg]);
-        fl[n] = *reinterpret_cast<const bf16x8*>(&s.bl[64 * wn + 16 * n + i][kk + 8 * kg]);
+      for (int n = 0; n < 2; ++n) {
+        fh[n] = *reinterpret_cast<const bf16x8*>(&s.bh[32 * wn + 16 * n + i][kk + 8 * kg]);
+        fl[n] = *reinterpret_cast<const bf16x8*>(&s.bl[32 * wn + 16 * n + i][kk + 8 * kg]);
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
+        for (int n = 0; n < 2; ++n) {
           acc_hi[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fh[n], acc_hi[m][n], 0, 0, 0);
           acc_lo[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fl[n], acc_lo[m][n], 0, 0, 0);
         }
     }
-    if (ks + 1 < nk) store(st[(ks + 1) & 1]);
+  };
+  // slices alternate between LDS stages 0 and 1 and register sets r0 and
+  // r1 (the loop is unrolled by two so that both are named statically)
+  const int nk = (ke - kb) / kBigK;
+  load(r0, kb);
+  store(r0, st[0]);
+  __syncthreads();
+  if (nk > 1) load(r1, kb + kBigK);
+  // The loads two slices ahead are always issued (the last slice again
+  // past the end; nothing stores those): with a branch around them the
+  // wait before storing the next slice would count the loads of both paths
+  // and drain the ones in flight.
+  for (int ks = 0; ks < nk; ks += 2) {
+    load(r0, kb + kBigK * min(ks + 2, nk - 1));
+    compute(st[0]);
+    if (ks + 1 < nk) store(r1, st[1]);
+    __syncthreads();
+    if (ks + 1 >= nk) break;
+    load(r1, kb + kBigK * min(ks + 3, nk - 1));
+    compute(st[1]);
+    if (ks + 2 < nk) store(r0, st[0]);
     __syncthreads();
   }
   float* dst = gridDim.z > 1 ? a.part + (int64_t)blockIdx.z * a.T * a.E : a.out;
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 64 * wm + 16 * m + 4 * kg + r, e = e0 + 64 * wn + 16 * n + i;
+        const int t = t0 + 64 * wm + 16 * m + 4 * kg + r, e = e0 + 32 * wn + 16 * n + i;
         if (t < a.T && e < a.E)
           dst[(int64_t)t * a.E + e] = acc_hi[m][n][r] + acc_lo[m][n][r] * kResidualScale;
       }
@@ -392,7 +415,7 @@ extern "C" int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const dim3 grid(r.tiles_t, r.tiles_e, r.S);
   if (r.big)
-    hipLaunchKernelGGL(hda_router_gemm_lds_kernel, grid, dim3(64 * kWaves), 0, hs, a);
+    hipLaunchKernelGGL(hda_router_gemm_lds_kernel, grid, dim3(64 * kBigWaves), 0, hs, a);
   else if (r.mb == 2)
     hipLaunchKernelGGL(hda_router_gemm_kernel<2>, grid, dim3(64 * kWaves), 0, hs, a);
   else
