@@ -151,19 +151,24 @@ __global__ __launch_bounds__(64 * kWaves) void hda_router_gemm_kernel(RouterArgs
 // on memory).  Eight waves: wave (wm, wn) owns the 64 x 32 sub-tile at
 // (64 wm, 32 wn), 4 x 2 blocks for each product, which keeps the
 // accumulators and both register sets within 256 registers (two waves per
-// SIMD).  LDS rows hold 64 bf16 and are padded to 144 bytes: the 16 lanes of
-// a fragment read that share a k offset read 16 rows, whose 16-byte pieces
-// then fall in distinct bank groups (36 i mod 64 dwords; unpadded rows put
-// several rows on the same banks).
+// SIMD).  LDS tiles are swizzled (big_off) so that fragment reads are
+// conflict-free.
 constexpr int kBigM = 128, kBigN = 128;
 constexpr int kBigK = 64;             // K per LDS stage (two MFMA steps)
-constexpr int kBigRow = kBigK + 8;    // padded LDS row, in bf16
 
+// A tile of 128 rows of 64 bf16 (8 16-byte quads): rows r and r + 8 of each
+// 16 share a 256-byte line, quad q of row r in half (q / 4) ^ (r / 8 mod 2)
+// at position (r ^ q) mod 8, so that the 16 rows of a fragment read (one
+// quad each) put lanes 0-7 and lanes 8-15 each on one aligned half of the
+// banks (the rule gfx950's 16-byte reads are conflict-free under).
 struct BigStage {
-  uint16_t a[kBigM][kBigRow];
-  uint16_t bh[kBigN][kBigRow];
-  uint16_t bl[kBigN][kBigRow];
+  uint8_t a[kBigM * 2 * kBigK];
+  uint8_t bh[kBigN * 2 * kBigK];
+  uint8_t bl[kBigN * 2 * kBigK];
 };
+__device__ inline int big_off(int r, int q) {
+  return (r >> 4) * 2048 + (r & 7) * 256 + 16 * (8 * ((q >> 2) ^ ((r >> 3) & 1)) + ((r ^ q) & 7));
+}
 
 constexpr int kBigWaves = 8;          // 2 x 4 waves of 64 x 32 sub-tiles
 
@@ -210,9 +215,10 @@ __global__ __launch_bounds__(64 * kBigWaves, 1) void hda_router_gemm_lds_kernel(
   auto store = [&](const Regs& r, BigStage& s) {
 #pragma unroll
     for (int u = 0; u < kChunks; ++u) {
-      *reinterpret_cast<u32x4*>(&s.a[lrow[u]][lcol[u]]) = r.a[u];
-      *reinterpret_cast<u32x4*>(&s.bh[lrow[u]][lcol[u]]) = r.h[u];
-      *reinterpret_cast<u32x4*>(&s.bl[lrow[u]][lcol[u]]) = r.l[u];
+      const int off = big_off(lrow[u], lcol[u] / 8);
+      *reinterpret_cast<u32x4*>(s.a + off) = r.a[u];
+      *reinterpret_cast<u32x4*>(s.bh + off) = r.h[u];
+      *reinterpret_cast<u32x4*>(s.bl + off) = r.l[u];
     }
   };
 
@@ -230,11 +236,11 @@ __global__ __launch_bounds__(64 * kBigWaves, 1) void hda_router_gemm_lds_kernel(
       bf16x8 fa[4], fh[2], fl[2];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        fa[m] = *reinterpret_cast<const bf16x8*>(&s.a[64 * wm + 16 * m + i][kk + 8 * kg]);
+        fa[m] = *reinterpret_cast<const bf16x8*>(s.a + big_off(64 * wm + 16 * m + i, kk / 8 + kg));
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        fh[n] = *reinterpret_cast<const bf16x8*>(&s.bh[32 * wn + 16 * n + i][kk + 8 * kg]);
-        fl[n] = *reinterpret_cast<const bf16x8*>(&s.bl[32 * wn + 16 * n + i][kk + 8 * kg]);
+        fh[n] = *reinterpret_cast<const bf16x8*>(s.bh + big_off(32 * wn + 16 * n + i, kk / 8 + kg));
+        fl[n] = *reinterpret_cast<const bf16x8*>(s.bl + big_off(32 * wn + 16 * n + i, kk / 8 + kg));
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m)
