@@ -332,12 +332,13 @@ struct RouterShape {
 };
 
 // The LDS-staged 128 x 128 kernel takes a batch when its tiles, split along
-// the hidden dimension into ranges of at least 16 K steps, reach 256
-// workgroups (one per compute unit); smaller batches take the split-K
-// register kernel (measured: 64 large tiles alone leave three quarters of
-// the compute units idle).
+// the hidden dimension into ranges of at least 4 LDS stages (256 of K),
+// reach 256 workgroups (one per compute unit); smaller batches take the
+// split-K register kernel (measured: 64 large tiles alone leave three
+// quarters of the compute units idle; ranges of at least 8 stages kept 1024
+// tokens on the register kernel, 27.6 us against 20.8).
 constexpr int64_t kBigMinGroups = 256;
-constexpr int kBigMinStages = 8;      // K per workgroup >= 8 stages (512)
+constexpr int kBigMinStages = 4;      // K per workgroup >= 4 stages (256)
 // The split-K register kernel splits the hidden dimension until its tiles
 // make about this many workgroups (one per compute unit: measured against
 // 128, 192, 384 and 512 over 1 to 16384 tokens, best at 256 and 1024 tokens
