@@ -54,6 +54,10 @@ CASES = {
                                               q_len_range=(1, 50)), None, None),
     "g16": (Workload("g16", 3, 32, 2, 128, 64, seed=81), [700, 90, 2000], [20, 3, 33]),
     "g1": (Workload("g1", 3, 4, 4, 64, 32, seed=82), [300, 64, 65], [40, 64, 1]),
+    "ps128": (Workload("ps128", 4, 16, 2, 128, 128, seed=85), [1000, 129, 384, 2100],
+              [50, 3, 64, 17]),
+    "ps1024_fp8": (Workload("ps1024_fp8", 3, 16, 2, 128, 1024, kv_dtype="fp8", seed=86),
+                   [1500, 1024, 3000], [20, 64, 5]),
 }
 
 
