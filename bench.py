@@ -3,9 +3,10 @@
 
 A step is one pass of the whole hot path over one batch: the host planner
 (hda_plan) rebuilds the tile plan from the current lengths, the plan goes to
-the device with an async copy from pinned memory, and hda_decode runs the
-attention kernel (tile loads, QK, online softmax, PV, log-sum-exp merge) on
-the torch stream.  Inputs are resident in HBM before timing starts.
+the device inside the tile kernel's launch arguments (plans longer than
+HDA_PLAN_ARG_INTS ints through hda_plan_upload; `--upload copy` for an async
+copy from pinned memory), and hda_decode runs the attention kernel (tile
+loads, QK, online softmax, PV, log-sum-exp merge) on the torch stream.  Inputs are resident in HBM before timing starts.
 
 Default workload: the 1 x 131072 + 31 x 4096 extreme mix (bf16 cache, 64 q /
 8 kv heads, head dim 128, page 64, random page placement).  The KV pools are
@@ -57,6 +58,10 @@ def parse():
     ap.add_argument("--tile-len", type=int, default=None)
     ap.add_argument("--workgroups", type=int, default=None)
     ap.add_argument("--copies", type=int, default=4, help="KV pool copies rotated over")
+    ap.add_argument("--upload", choices=["args", "kernel", "copy"], default="args",
+                    help="plan upload: in the tile kernel's launch arguments (plans up to "
+                         "HDA_PLAN_ARG_INTS ints, else as 'kernel'), in a store kernel's "
+                         "launch arguments (hda_plan_upload), or an async copy from pinned memory")
     ap.add_argument("--no-static", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -529,12 +534,20 @@ def main():
     def step(s, events=None):
         j = s % NB
         if used[j]:
-            done_ev[j].synchronize()           # the upload that last read pinned[j] is done
+            done_ev[j].synchronize()           # the copy that last read pinned[j] is done
         host = pinned[j].numpy()
         n = hda.hda_plan_into(lens, tl, W, host)                  # a1: plan from current lengths
-        plan_dev[j][:n].copy_(pinned[j][:n], non_blocking=True)   # a2: upload (same stream)
-        done_ev[j].record(stream)
-        used[j] = True
+        # a2: upload on the same stream; launch arguments are copied when the
+        # launch is enqueued, so only the async copy holds on to pinned[j]
+        dplan = plan_dev[j]
+        if args.upload == "args" and n <= hda.HDA_PLAN_ARG_INTS:
+            dplan = None                                          # in hda_decode's launch
+        elif args.upload in ("args", "kernel"):
+            hda.hda_plan_upload(host, plan_dev[j], stream, plan_len=n)
+        else:
+            plan_dev[j][:n].copy_(pinned[j][:n], non_blocking=True)
+            done_ev[j].record(stream)
+            used[j] = True
         kp, vp = copies[s % len(copies)]
         if events is not None:
             events[0].record(stream)
@@ -542,7 +555,7 @@ def main():
         else:
             params.split_event = None
         hda.hda_decode(params, dev.t["q"], kp, vp, dev.t["block_table"], dev.t["seq_lens"],
-                       host[:n], plan_dev[j], out, stream)               # a3..a9
+                       host[:n], dplan, out, stream)                     # a3..a9
         if events is not None:
             events[2].record(stream)
         return n
@@ -568,8 +581,13 @@ def main():
     torch.cuda.synchronize()
     u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     u0.record(stream)
-    for _ in range(50):
-        plan_dev[0][:n_plan].copy_(pinned[0][:n_plan], non_blocking=True)
+    upload_mode = ("args" if args.upload == "args" and n_plan <= hda.HDA_PLAN_ARG_INTS
+                   else "kernel" if args.upload != "copy" else "copy")
+    for _ in range(50):         # in "args" mode the plan rides in the tile launch: 0 here
+        if upload_mode == "kernel":
+            hda.hda_plan_upload(host0, plan_dev[0], stream, plan_len=n_plan)
+        elif upload_mode == "copy":
+            plan_dev[0][:n_plan].copy_(pinned[0][:n_plan], non_blocking=True)
     u1.record(stream)
     torch.cuda.synchronize()
     upload_us = u0.elapsed_time(u1) * 1e3 / 50
@@ -684,6 +702,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": algo,
                      "kernel": "hda_decode_kernel (tile kernel; HIP events on its stream)"},
         "plan": {"host_us": round(host_plan_us, 2), "upload_us": round(upload_us, 2),
+                 "upload": upload_mode,
                  "plan_ints": int(n_plan)},
         "max_abs_diff_vs_static4_plan": static_diff,
         "device_planned_step": {"wall_us": round(auto_ms * 1e3, 2),

@@ -213,6 +213,9 @@ typedef struct hda_params {
   int32_t reserved0;          /* must be 0 */
 } hda_params;
 
+/* Longest plan hda_decode accepts in its launch arguments (plan_dev NULL). */
+#define HDA_PLAN_ARG_INTS 896
+
 /*
  * One decode step enqueued on `stream`: the optional new-token prologue
  * kernel (RMSNorm + RoPE of q and k, k/v stored to slot len-1, all fused in
@@ -228,15 +231,19 @@ typedef struct hda_params {
  *                is row t % page_size of page block_table[b][t / page_size]
  *   seq_lens     [device] int32 [B], the same lengths the plan was built for
  *   plan_host    [host] the plan (header read for the launch shape)
- *   plan_dev     [device] an identical copy of the plan, plan_len ints
+ *   plan_dev     [device] an identical copy of the plan, plan_len ints; or
+ *                NULL when plan_len <= HDA_PLAN_ARG_INTS: the plan then
+ *                travels in the tile kernel's launch arguments (no upload
+ *                on the stream; plan_host is free once the call returns)
  *   out          [device] float32 [B][Hq][D]
  *   stream       hipStream_t, or NULL for the default stream
  * q head h reads kv head floor(h * Hkv / Hq).  Rows past len_b are never
  * used, whatever they hold.
  * Errors (all detected on the host before any launch): HDA_ERR_INVALID_ARG,
- * HDA_ERR_UNSUPPORTED, HDA_ERR_PLAN_MISMATCH, HDA_ERR_BAD_PLAN,
- * HDA_ERR_WORKSPACE (workspace missing or too small); HDA_ERR_HIP if a
- * launch fails.  Device faults
+ * HDA_ERR_UNSUPPORTED (also: plan_dev NULL with a longer plan),
+ * HDA_ERR_PLAN_MISMATCH, HDA_ERR_BAD_PLAN (header, length or workgroup item
+ * ranges), HDA_ERR_WORKSPACE (workspace missing or too small); HDA_ERR_HIP if
+ * a launch fails.  Device faults
  * surface at the caller's next synchronisation.
  */
 int hda_decode(const hda_params* p, const void* q, void* k_pages,
@@ -282,6 +289,23 @@ int64_t hda_workspace_bytes_bound(int32_t batch, int32_t n_workgroups,
  */
 int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
                     int32_t n_workgroups, int32_t* plan, int64_t capacity, void* stream);
+
+/* Plan ints carried by one launch of hda_plan_upload. */
+#define HDA_PLAN_UPLOAD_CHUNK 1000
+
+/*
+ * Copies a host plan (plan_len ints, any size) to plan_dev [device, 4-byte
+ * aligned] on `stream` inside the kernel arguments of a small store kernel,
+ * one launch per HDA_PLAN_UPLOAD_CHUNK ints: the per-step upload of the plan
+ * (the arex-research page has the tile allocation redone every decode step)
+ * without a separate copy on the stream.  Launch arguments are copied when
+ * the launch is enqueued, so plan_host may be pageable memory and may be
+ * reused as soon as the call returns.  Asynchronous on the device.  Errors:
+ * HDA_ERR_INVALID_ARG (null pointer, plan_len < 1, misaligned plan_dev),
+ * HDA_ERR_HIP (a launch failed).
+ */
+int hda_plan_upload(const int32_t* plan_host, int64_t plan_len, int32_t* plan_dev,
+                    void* stream);
 
 /* Largest row block of hda_prefill, in units of hda_prefill_rows_per_block(). */
 #define HDA_PREFILL_MAX_TILES 16

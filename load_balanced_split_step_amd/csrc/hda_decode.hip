@@ -33,6 +33,7 @@
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "hda.h"
 
@@ -1785,6 +1786,44 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
   }
 }
 
+// The same tile kernel for a host plan carried in the launch arguments (at
+// most kArgPlanInts ints): no upload precedes it on the stream.  Workgroup 0
+// also turns req_part_ptr into the per-request slot ranges the merge launch
+// reads, as a device-planned launch records them.
+constexpr int kArgPlanInts = HDA_PLAN_ARG_INTS;
+struct ArgPlan {
+  int32_t v[kArgPlanInts];
+};
+
+template <int D, bool FP8, bool PAGE, bool NATIVE>
+__global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_argplan_kernel(
+    Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    ArgPlan pl) {
+  __shared__ TileSmem<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x % a.n_kv_heads;
+  const int w = blockIdx.x / a.n_kv_heads;
+  const int32_t* wg_ptr = pl.v + HDA_PLAN_HEADER_INTS;
+  const int32_t* items = wg_ptr + a.n_wg + 1;
+  if (a.n_parts > 0 && blockIdx.x == 0) {
+    const int32_t* rpp = items + 4 * a.n_items;
+    for (int b = tid; b < a.batch; b += 64 * kWaves) {
+      const int s0 = rpp[b];
+      a.req_slots[2 * b] = s0;
+      a.req_slots[2 * b + 1] = rpp[b + 1] - s0;
+    }
+  }
+  const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
+  for (int it = it_begin; it < it_end; ++it) {
+    const int b = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
+              slot = items[4 * it + 3];
+    if ((unsigned)b >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
+    run_item<D, FP8, PAGE, NATIVE>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], h, wave,
+                                   lane, tid);
+  }
+}
+
 // Log-sum-exp merge of split requests: workgroup (b, q head) combines the
 // partials of request b in slot order,
 //   out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M),  M = max_s lse_s.
@@ -1961,6 +2000,32 @@ __global__ __launch_bounds__(kMergeRowsThreads) void hda_merge_rows_kernel(
   *reinterpret_cast<f32x4*>(a.out + ((int64_t)orow * Hq + h) * D + 4 * (tid % Q)) = acc;
 }
 
+// A host plan carried to device memory inside a launch's kernel arguments:
+// the runtime copies the arguments when the launch is enqueued, so the
+// stream sees one small kernel and no separate copy, and the caller's host
+// buffer is free again as soon as the launch returns.
+constexpr int kUploadInts = HDA_PLAN_UPLOAD_CHUNK;
+struct UploadChunk {
+  int32_t v[kUploadInts];
+};
+
+static_assert(kUploadInts <= 4 * 256, "one load round per thread");
+
+__global__ __launch_bounds__(256) void hda_plan_store_kernel(UploadChunk c,
+                                                             int32_t* __restrict__ dst, int n) {
+  int32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {   // all argument reads in flight before the stores
+    const int i = threadIdx.x + 256 * j;
+    r[j] = i < n ? c.v[i] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    if (i < n) dst[i] = r[j];
+  }
+}
+
 // The plan in the host format, built from device lengths by one wave with
 // the device-side planning arithmetic (the same items the tile kernel derives
 // for itself in a device-planned launch).
@@ -2043,7 +2108,7 @@ __global__ __launch_bounds__(64) void hda_plan_kernel(const int32_t* __restrict_
 
 template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE = false>
 hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_t stream,
-                  void* split_event) {
+                  void* split_event, const ArgPlan* ap) {
   hipError_t e;
   if (prologue) {
     hipLaunchKernelGGL((hda_prologue_kernel<D, FP8>), dim3(a.batch * a.n_kv_heads), dim3(256), 0,
@@ -2052,8 +2117,12 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
     if (e != hipSuccess) return e;
     a.q = q_prime;   // attention reads the normalised, rotated q
   }
-  hipLaunchKernelGGL((hda_decode_kernel<D, FP8, DEVPLAN, PAGE, NATIVE>), dim3(grid),
-                     dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens, a.plan);
+  if (!DEVPLAN && ap)
+    hipLaunchKernelGGL((hda_decode_argplan_kernel<D, FP8, PAGE, NATIVE>), dim3(grid),
+                       dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens, *ap);
+  else
+    hipLaunchKernelGGL((hda_decode_kernel<D, FP8, DEVPLAN, PAGE, NATIVE>), dim3(grid),
+                       dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens, a.plan);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (split_event) {
@@ -2061,8 +2130,13 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
     if (e != hipSuccess) return e;
   }
   if (DEVPLAN || a.n_parts > 0) {
-    hipLaunchKernelGGL((hda_merge_kernel<D, DEVPLAN>), dim3(a.batch * a.n_q_heads), dim3(D), 0,
-                       stream, a, a.plan, a.seq_lens);
+    // slot ranges from the device plan or the argument plan, else from plan_dev
+    if (DEVPLAN || ap)
+      hipLaunchKernelGGL((hda_merge_kernel<D, true>), dim3(a.batch * a.n_q_heads), dim3(D), 0,
+                         stream, a, a.plan, a.seq_lens);
+    else
+      hipLaunchKernelGGL((hda_merge_kernel<D, false>), dim3(a.batch * a.n_q_heads), dim3(D), 0,
+                         stream, a, a.plan, a.seq_lens);
     e = hipGetLastError();
   }
   return e;
@@ -2114,12 +2188,13 @@ hipError_t launch_prefill_d(const Args& a, bool fp8, int grid, int n_rows, hipSt
 // them for bf16).
 template <int D, bool DEVPLAN>
 hipError_t launch_d(const Args& a, bool fp8, bool native, int grid, bool pro, uint16_t* qp,
-                    hipStream_t st, void* ev) {
+                    hipStream_t st, void* ev, const ArgPlan* ap = nullptr) {
   if constexpr (D == 128)
-    if (native) return launch<128, true, DEVPLAN, false, true>(a, grid, pro, qp, st, ev);
-  if (!fp8) return launch<D, false, DEVPLAN, false>(a, grid, pro, qp, st, ev);
-  return a.scale_mode == HDA_SCALE_PAGE ? launch<D, true, DEVPLAN, true>(a, grid, pro, qp, st, ev)
-                                        : launch<D, true, DEVPLAN, false>(a, grid, pro, qp, st, ev);
+    if (native) return launch<128, true, DEVPLAN, false, true>(a, grid, pro, qp, st, ev, ap);
+  if (!fp8) return launch<D, false, DEVPLAN, false>(a, grid, pro, qp, st, ev, ap);
+  return a.scale_mode == HDA_SCALE_PAGE
+             ? launch<D, true, DEVPLAN, true>(a, grid, pro, qp, st, ev, ap)
+             : launch<D, true, DEVPLAN, false>(a, grid, pro, qp, st, ev, ap);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -2226,12 +2301,19 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
                           float* out, void* stream) {
   int st = check_params(p, q, k_pages, v_pages, block_table, seq_lens, out);
   if (st != HDA_OK) return st;
-  if (!plan_host || !plan_dev) return HDA_ERR_INVALID_ARG;
+  if (!plan_host) return HDA_ERR_INVALID_ARG;
   if (plan_len < HDA_PLAN_HEADER_INTS || plan_host[0] != HDA_PLAN_VERSION) return HDA_ERR_BAD_PLAN;
+  if (!plan_dev && plan_len > kArgPlanInts) return HDA_ERR_UNSUPPORTED;
   if (plan_host[1] != p->batch) return HDA_ERR_PLAN_MISMATCH;
   const int64_t W = plan_host[3], N = plan_host[5], P = plan_host[6];
   if (W < 1 || N < 1 || P < 0 || plan_len != HDA_PLAN_HEADER_INTS + (W + 1) + 4 * N + p->batch + 1)
     return HDA_ERR_BAD_PLAN;
+  // workgroup item ranges stay inside the item list (items themselves are
+  // range-checked by the kernel)
+  const int32_t* wg_ptr = plan_host + HDA_PLAN_HEADER_INTS;
+  if (wg_ptr[0] != 0 || wg_ptr[W] != N) return HDA_ERR_BAD_PLAN;
+  for (int64_t w = 0; w < W; ++w)
+    if (wg_ptr[w + 1] < wg_ptr[w]) return HDA_ERR_BAD_PLAN;
   const int64_t grid = W * p->n_kv_heads;
   if (grid > 0x7fffffffLL) return HDA_ERR_UNSUPPORTED;
   const int64_t ws_need = hda_workspace_bytes(plan_host, plan_len, p->n_q_heads, p->n_kv_heads,
@@ -2248,10 +2330,13 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
   const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
   const bool native = p->math == HDA_MATH_FP8;
   const bool pro = p->prologue != 0;
-  hipError_t e =
-      p->head_dim == 64
-          ? launch_d<64, false>(a, fp8, native, (int)grid, pro, a.q_prime, hs, p->split_event)
-          : launch_d<128, false>(a, fp8, native, (int)grid, pro, a.q_prime, hs, p->split_event);
+  ArgPlan ap;   // the plan in the launch arguments when no device copy is given
+  if (!plan_dev) memcpy(ap.v, plan_host, (size_t)plan_len * sizeof(int32_t));
+  const ArgPlan* app = plan_dev ? nullptr : &ap;
+  hipError_t e = p->head_dim == 64 ? launch_d<64, false>(a, fp8, native, (int)grid, pro, a.q_prime,
+                                                        hs, p->split_event, app)
+                                   : launch_d<128, false>(a, fp8, native, (int)grid, pro,
+                                                          a.q_prime, hs, p->split_event, app);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
 }
 
@@ -2346,6 +2431,21 @@ extern "C" int hda_prefill(const hda_params* p, const void* q, const void* k_pag
                      ? launch_prefill_d<64>(a, fp8, (int)grid, (int)R, hs, p->split_event)
                      : launch_prefill_d<128>(a, fp8, (int)grid, (int)R, hs, p->split_event);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
+}
+
+extern "C" int hda_plan_upload(const int32_t* plan_host, int64_t plan_len, int32_t* plan_dev,
+                               void* stream) {
+  if (!plan_host || !plan_dev || plan_len < 1 || ((uintptr_t)plan_dev & 3u))
+    return HDA_ERR_INVALID_ARG;
+  UploadChunk c;
+  for (int64_t off = 0; off < plan_len; off += kUploadInts) {
+    const int n = (int)(plan_len - off < kUploadInts ? plan_len - off : kUploadInts);
+    memcpy(c.v, plan_host + off, (size_t)n * sizeof(int32_t));
+    hipLaunchKernelGGL(hda_plan_store_kernel, dim3(1), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), c, plan_dev + off, n);
+    if (hipGetLastError() != hipSuccess) return HDA_ERR_HIP;
+  }
+  return HDA_OK;
 }
 
 extern "C" int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,

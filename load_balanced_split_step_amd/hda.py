@@ -37,12 +37,14 @@ HDA_MATH_FP8 = 1
 HDA_V_TOKEN_MAJOR = 0
 HDA_V_DIM_MAJOR = 1
 HDA_PREFILL_MAX_TILES = 16
+HDA_PLAN_UPLOAD_CHUNK = 1000   # plan ints per hda_plan_upload launch
+HDA_PLAN_ARG_INTS = 896        # longest plan hda_decode takes in its launch arguments
 PLAN_HEADER_INTS = 8
 
 # every symbol include/hda.h declares
 EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_plan_static", "hda_plan_validate",
            "hda_workspace_bytes", "hda_decode", "hda_decode_auto", "hda_workspace_bytes_bound",
-           "hda_plan_device", "hda_prefill_rows_per_block", "hda_prefill_block_rows",
+           "hda_plan_device", "hda_plan_upload", "hda_prefill_rows_per_block", "hda_prefill_block_rows",
            "hda_prefill_rows",
            "hda_prefill_workspace_bytes", "hda_prefill", "hda_router_split_weights",
            "hda_router_workspace_bytes", "hda_router_gemm", "hda_read_probe", "hda_status_string",
@@ -115,6 +117,7 @@ def load_library(path: Optional[str] = None):
                                            vp, vp]),
         "hda_workspace_bytes_bound": (i64, [i32, i32, i32, i32]),
         "hda_plan_device": (ctypes.c_int, [vp, i32, i32, i32, vp, i64, vp]),
+        "hda_plan_upload": (ctypes.c_int, [pi32, i64, vp, vp]),
         "hda_prefill_rows_per_block": (i32, [i32, i32]),
         "hda_prefill_block_rows": (i32, [pi32, i32, i32, i32]),
         "hda_prefill_rows": (ctypes.c_int, [pi32, pi32, i32, i32, pi32, pi32, i64, pi64]),
@@ -264,6 +267,26 @@ def hda_plan_device(seq_lens, batch: int, tile_len: int, n_workgroups: int, plan
                              _ptr(plan), int(capacity), _stream(stream))
     if st != HDA_OK:
         raise HdaError(st, "hda_plan_device")
+
+
+def hda_plan_upload(plan, plan_dev, stream=None, plan_len=None) -> None:
+    """Enqueue the copy of a host plan (np.int32, first `plan_len` ints) into
+    `plan_dev` through store-kernel launch arguments; `plan` may be reused
+    once this returns."""
+    plan = np.asarray(plan)
+    if plan.dtype != np.int32 or not plan.flags.c_contiguous:
+        raise TypeError("plan must be a C-contiguous int32 array")
+    n = plan.size if plan_len is None else int(plan_len)
+    if n > plan.size:
+        raise ValueError("plan_len exceeds the host plan")
+    if hasattr(plan_dev, "numel") and (plan_dev.element_size() != 4 or plan_dev.numel() < n
+                                       or not plan_dev.is_contiguous()):
+        raise ValueError("plan_dev must be a contiguous 4-byte tensor of at least plan_len elements")
+    lib = load_library()
+    st = lib.hda_plan_upload(plan.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n,
+                             _ptr(plan_dev), _stream(stream))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_plan_upload")
 
 
 def hda_prefill_rows_per_block(n_q_heads: int, n_kv_heads: int) -> int:

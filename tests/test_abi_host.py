@@ -201,6 +201,18 @@ def test_decode_argument_errors(lib):
     assert _decode_status(lib, _params(), plan[:-1]) == E.HDA_ERR_BAD_PLAN
     bad = plan.copy(); bad[0] = 9
     assert _decode_status(lib, _params(), bad) == E.HDA_ERR_BAD_PLAN
+    # workgroup item ranges: start at 0, never decrease, end at N
+    W = int(plan[3])
+    for pos, val in ((8, 1), (8 + W, int(plan[5]) + 1), (8 + W, int(plan[5]) - 1)):
+        bad = plan.copy(); bad[pos] = val
+        assert _decode_status(lib, _params(), bad) == E.HDA_ERR_BAD_PLAN, (pos, val)
+    bad = plan.copy(); bad[9], bad[10] = bad[10], bad[9] - 1
+    assert _decode_status(lib, _params(), bad) == E.HDA_ERR_BAD_PLAN
+    # a plan in the launch arguments (no device copy) is limited in length
+    long_lens = np.full(300, 100, dtype=np.int32)
+    long_plan = hda.hda_plan(long_lens, 64, 64)
+    assert long_plan.size > hda.HDA_PLAN_ARG_INTS
+    assert _decode_status(lib, _params(batch=300), long_plan, pd=None) == E.HDA_ERR_UNSUPPORTED
     assert _decode_status(lib, _params(workspace=None), plan) == E.HDA_ERR_WORKSPACE
     assert _decode_status(lib, _params(workspace_bytes=100), plan) == E.HDA_ERR_WORKSPACE
     # scale granularity
@@ -453,3 +465,18 @@ def test_read_probe_argument_errors(lib):
     assert lib.hda_read_probe(vp(FAKE), 0, 4, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
     assert lib.hda_read_probe(vp(FAKE), 1024, 0, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
     assert lib.hda_read_probe(vp(FAKE + 8), 1024, 4, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
+
+
+def test_plan_upload_argument_errors(lib):
+    """The plan upload rejects bad arguments on the host, before any launch."""
+    import ctypes
+    vp = ctypes.c_void_p
+    plan = np.arange(16, dtype=np.int32)
+    pp = plan.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.hda_plan_upload(None, 16, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
+    assert lib.hda_plan_upload(pp, 16, None, None) == hda.HDA_ERR_INVALID_ARG
+    assert lib.hda_plan_upload(pp, 0, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
+    assert lib.hda_plan_upload(pp, -3, vp(FAKE), None) == hda.HDA_ERR_INVALID_ARG
+    assert lib.hda_plan_upload(pp, 16, vp(FAKE + 2), None) == hda.HDA_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        hda.hda_plan_upload(plan, 0, plan_len=17)
