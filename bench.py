@@ -700,7 +700,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": algo,
-                     "kernel": "hda_decode_kernel (tile kernel; HIP events on its stream)"},
+                     "kernel": ("hda_decode_argplan_kernel (tile kernel, plan in its launch "
+                                "arguments; HIP events on its stream)" if upload_mode == "args" else
+                                "hda_decode_kernel (tile kernel; HIP events on its stream)")},
         "plan": {"host_us": round(host_plan_us, 2), "upload_us": round(upload_us, 2),
                  "upload": upload_mode,
                  "plan_ints": int(n_plan)},

@@ -1832,11 +1832,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_argplan_kernel(
 // owns output dim d.  The first kMergeEarly partial rows are loaded up front,
 // before the weights are known, so that the whole merge costs about one
 // memory round trip for typical slot counts.  (One workgroup per kv head
-// instead was measured 3x slower on a request split 32 ways.)
+// instead was measured 3x slower on a request split 32 ways.)  RECORDED: the
+// slot ranges come from a.req_slots, where the tile kernel recorded them (a
+// device-planned launch, or a plan in the launch arguments), else from the
+// plan's req_part_ptr in device memory.
 constexpr int kMergeEarly = 32;    // partial rows loaded before the weights
 constexpr int kMergeStage = 512;   // slot weights staged in LDS per pass
 
-template <int D, bool DEVPLAN>
+template <int D, bool RECORDED>
 __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __restrict__ plan,
                                                       const int32_t* __restrict__ seq_lens) {
   __shared__ float sm_w[kMergeStage];
@@ -1846,7 +1849,7 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
   const int b = blockIdx.x / a.n_q_heads;
   const int qr = 0, orow = b;
   int s0, s1;
-  if constexpr (!DEVPLAN) {
+  if constexpr (!RECORDED) {
     const int32_t* rpp = plan + HDA_PLAN_HEADER_INTS + a.n_wg + 1 + 4 * a.n_items;
     s0 = max(0, rpp[b]);
     s1 = min(a.n_parts, rpp[b + 1]);
