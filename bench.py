@@ -233,7 +233,9 @@ def cpu_baseline_prefill(inp, budget_s):
 
 def bench_prefill(args, w, inp):
     """Multi-token step: row blocks and plan on the host from the current
-    lengths, async upload of both from pinned memory, hda_prefill."""
+    lengths, both uploaded in one hda_plan_upload call (rows, then the plan,
+    in one device buffer; `--upload copy`: two async copies from pinned
+    memory), hda_prefill."""
     import numpy as np
     import torch
     import load_balanced_split_step_amd.hda as hda
@@ -261,6 +263,9 @@ def bench_prefill(args, w, inp):
     pin_rows = [torch.empty(4 * R, dtype=torch.int32).pin_memory() for _ in range(NB)]
     d_plan = [torch.empty(cap, dtype=torch.int32, device="cuda:0") for _ in range(NB)]
     d_rows = [torch.empty(4 * R, dtype=torch.int32, device="cuda:0") for _ in range(NB)]
+    # one upload of [rows | plan]: 4R ints keep the plan 16-byte aligned
+    host_both = np.empty(4 * R + cap, dtype=np.int32)
+    d_both = [torch.empty(4 * R + cap, dtype=torch.int32, device="cuda:0") for _ in range(NB)]
     n_q = int(qlens.sum())
     out = torch.empty((n_q, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
@@ -273,12 +278,21 @@ def bench_prefill(args, w, inp):
         if used[j]:
             done_ev[j].synchronize()
         r, rl = hda.hda_prefill_rows(qlens, lens, block_rows())          # row blocks
-        pin_rows[j].numpy()[:] = r.reshape(-1)
-        n = hda.hda_plan_into(rl, tl, W, pin_plan[j].numpy())           # the decode planner
-        d_rows[j].copy_(pin_rows[j], non_blocking=True)
-        d_plan[j][:n].copy_(pin_plan[j][:n], non_blocking=True)
-        done_ev[j].record(stream)
-        used[j] = True
+        if args.upload == "copy":
+            pin_rows[j].numpy()[:] = r.reshape(-1)
+            n = hda.hda_plan_into(rl, tl, W, pin_plan[j].numpy())       # the decode planner
+            d_rows[j].copy_(pin_rows[j], non_blocking=True)
+            d_plan[j][:n].copy_(pin_plan[j][:n], non_blocking=True)
+            done_ev[j].record(stream)
+            used[j] = True
+            h_rows, h_plan = pin_rows[j].numpy(), pin_plan[j].numpy()[:n]
+            dr, dp = d_rows[j], d_plan[j]
+        else:
+            host_both[:4 * R] = r.reshape(-1)
+            n = hda.hda_plan_into(rl, tl, W, host_both[4 * R:])         # the decode planner
+            hda.hda_plan_upload(host_both, d_both[j], stream, plan_len=4 * R + n)
+            h_rows, h_plan = host_both[:4 * R], host_both[4 * R:4 * R + n]
+            dr, dp = d_both[j][:4 * R], d_both[j][4 * R:]
         kp, vp = copies[s % len(copies)]
         if events is not None:
             events[0].record(stream)
@@ -286,8 +300,7 @@ def bench_prefill(args, w, inp):
         else:
             params.split_event = None
         hda.hda_prefill(params, dev.t["q"], kp, vp, dev.t["block_table"], dev.t["seq_lens"], n_q,
-                        pin_rows[j].numpy().reshape(R, 4), d_rows[j], pin_plan[j].numpy()[:n],
-                        d_plan[j], out, stream)
+                        h_rows.reshape(R, 4), dr, h_plan, dp, out, stream)
         if events is not None:
             events[2].record(stream)
         return n
@@ -350,6 +363,7 @@ def bench_prefill(args, w, inp):
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8",
         "data": "synthetic",
+        "plan_upload": "copy" if args.upload == "copy" else "kernel (rows and plan, one launch)",
         "config": {"workload": f"{args.workload}: {len(lens)} requests, {n_q} query rows over "
                                f"{int(lens.sum())} cached tokens",
                    "batch": int(len(lens)), "query_rows": n_q, "kv_tokens": int(lens.sum()),
