@@ -104,3 +104,36 @@ def test_decode_plan_in_launch_arguments(name):
         n += 1
     print(f"{name}: {n} plans in launch arguments, bitwise equal", flush=True)
     assert n >= 3
+
+
+def _lengths_for_plan_size(size):
+    """Seeded search for a batch whose plan has exactly `size` ints."""
+    rng = np.random.default_rng(5)
+    while True:
+        B, W, tl = int(rng.integers(30, 140)), int(rng.integers(8, 300)), int(rng.choice([64, 128]))
+        lens = rng.integers(1, 1500, size=B).astype(np.int32)
+        if hda.hda_plan_capacity(B, W) < size:
+            continue
+        plan = hda.hda_plan(lens, tl, W)
+        if plan.size == size:
+            return lens, plan
+
+
+def test_plan_in_launch_arguments_at_the_limit():
+    """The longest plan the launch arguments take (HDA_PLAN_ARG_INTS ints)
+    gives the device-plan outputs bitwise; one int more is refused."""
+    lens, plan = _lengths_for_plan_size(hda.HDA_PLAN_ARG_INTS)
+    w = CONFIGS["tiny"].with_(name="arg_limit", batch=len(lens))
+    inp = make_inputs(w, lengths=lens)
+    dev = hda.DeviceBatch.from_inputs(inp)
+    a = _decode_plan_in_args(dev, plan)
+    b = dev.decode(plan)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    lens2, plan2 = _lengths_for_plan_size(hda.HDA_PLAN_ARG_INTS + 1)
+    inp2 = make_inputs(CONFIGS["tiny"].with_(name="arg_over", batch=len(lens2)), lengths=lens2)
+    dev2 = hda.DeviceBatch.from_inputs(inp2)
+    with pytest.raises(hda.HdaError) as e:
+        _decode_plan_in_args(dev2, plan2)
+    assert e.value.status == hda.HDA_ERR_UNSUPPORTED
+    print(f"{plan.size} ints in the launch arguments; {plan2.size} refused", flush=True)
