@@ -1924,8 +1924,8 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
 // exp(lse - M) as the decode merge's D/64 waves would add it, each wave's
 // lanes taking slots lane + 64w, + D, ... and reducing with the same
 // butterfly; the slots accumulated in order), so a row merges to exactly
-// what hda_merge_kernel gives.  Eight slots' loads are issued before their
-// weights are applied.  (One workgroup of D threads per row and head
+// what hda_merge_kernel gives.  The first 16 slots' outputs are loaded before
+// the weights are known, then eight slots' loads at a time.  (One workgroup of D threads per row and head
 // measured latency-bound on multi-token batches: 2.2x slower.)
 constexpr int kMergeRowsThreads = 256;
 
@@ -1934,7 +1934,10 @@ __global__ __launch_bounds__(kMergeRowsThreads) void hda_merge_rows_kernel(
     Args a, const int32_t* __restrict__ plan) {
   constexpr int Q = D / 4;                           // float4 columns per head
   constexpr int HPW = kMergeRowsThreads / Q;         // heads per workgroup
-  constexpr int U = 8;                               // slots in flight
+  constexpr int NWV = kMergeRowsThreads / 64;        // waves
+  constexpr int HPV = (HPW + NWV - 1) / NWV;         // heads per wave in the weight pass
+  constexpr int U = 8;                               // slots in flight past the first E
+  constexpr int E = 16;                              // slots loaded before the weights
   __shared__ float sM[HPW], sInv[HPW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Hq = a.n_q_heads;
@@ -1950,35 +1953,83 @@ __global__ __launch_bounds__(kMergeRowsThreads) void hda_merge_rows_kernel(
   const int n = s1 - s0;
   const int64_t lstride = (int64_t)a.qb * Hq;       // between slots, in rows
   const float* lse = a.part_lse + (int64_t)s0 * lstride + (int64_t)qr * Hq;
-  for (int j = wave; j < HPW; j += kMergeRowsThreads / 64) {
-    const int h = hg * HPW + j;
-    if (h >= Hq) break;
-    float m = -INFINITY;
-    for (int k = lane; k < n; k += 64) m = fmaxf(m, lse[(int64_t)k * lstride + h]);
+  const int j = tid / Q, h = hg * HPW + j;           // this thread's head in the output pass
+  const int hc = min(h, Hq - 1);                     // loads stay in range past Hq
+  const int64_t row_stride = lstride * D;            // floats between slots
+  const float* po = a.part_o + ((int64_t)s0 * lstride + (int64_t)qr * Hq + hc) * D + 4 * (tid % Q);
+  const float* lh = lse + hc;
+  // Loads in issue order: the weight pass's lse values (slot = lane), then
+  // the first E slots' outputs and lse for the output pass.  Completion
+  // counting is in order, so the weight pass waits for its own loads only.
+  // Indices are clamped rather than branched around, so no wait is merged.
+  float ls[HPV];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float total = 0.f;
+  for (int jj = 0; jj < HPV; ++jj) {
+    const int hw = min(hg * HPW + wave + NWV * jj, Hq - 1);
+    ls[jj] = lse[(int64_t)min(lane, n - 1) * lstride + hw];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 v0[E];
+  float l0[E];
 #pragma unroll
-    for (int w = 0; w < D / 64; ++w) {
-      const int d = 64 * w + lane;
-      float t = d < n ? expf(lse[(int64_t)d * lstride + h] - m) : 0.f;
-      for (int k = d + D; k < n; k += D) t += expf(lse[(int64_t)k * lstride + h] - m);
-      total += wave_sum(t);
-    }
-    if (lane == 0) {
-      sM[j] = m;
-      sInv[j] = 1.0f / total;
+  for (int u = 0; u < E; ++u) {
+    const int64_t k = min(u, n - 1);
+    v0[u] = *reinterpret_cast<const f32x4*>(po + k * row_stride);
+    l0[u] = lh[k * lstride];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // weights per head: max over slots, then the sum of exp(lse - M) as the
+  // decode merge's D/64 waves add it (lanes take slots lane + 64w, + D, ...);
+  // slot `lane` comes from ls, further slots (n > 64) are loaded here
+  float mh[HPV];
+#pragma unroll
+  for (int jj = 0; jj < HPV; ++jj) mh[jj] = lane < n ? fmaxf(-INFINITY, ls[jj]) : -INFINITY;
+  if (n > 64) {
+#pragma unroll
+    for (int jj = 0; jj < HPV; ++jj) {
+      const int hw = min(hg * HPW + wave + NWV * jj, Hq - 1);
+      for (int k = lane + 64; k < n; k += 64) mh[jj] = fmaxf(mh[jj], lse[(int64_t)k * lstride + hw]);
     }
   }
-  __syncthreads();
-  const int j = tid / Q, h = hg * HPW + j;
+#pragma unroll
+  for (int jj = 0; jj < HPV; ++jj) {
+    const int jw = wave + NWV * jj;
+    const int hw = min(hg * HPW + jw, Hq - 1);
+    float m = mh[jj];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float total = wave_sum(lane < n ? expf(ls[jj] - m) : 0.f);
+    if (n > 64) {
+      total = 0.f;
+#pragma unroll
+      for (int w = 0; w < D / 64; ++w) {
+        const int d = 64 * w + lane;
+        float t = d < n ? expf(lse[(int64_t)d * lstride + hw] - m) : 0.f;
+        for (int k = d + D; k < n; k += D) t += expf(lse[(int64_t)k * lstride + hw] - m);
+        total += wave_sum(t);
+      }
+    }
+    if (lane == 0 && jw < HPW && hg * HPW + jw < Hq) {
+      sM[jw] = m;
+      sInv[jw] = 1.0f / total;
+    }
+  }
+  // LDS-only barrier: the output loads above stay in flight across it
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   if (h >= Hq) return;
   const float M = sM[j], inv = sInv[j];
-  const int64_t row_stride = lstride * D;            // floats between slots
-  const float* po = a.part_o + ((int64_t)s0 * lstride + (int64_t)qr * Hq + h) * D + 4 * (tid % Q);
-  const float* lh = lse + h;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int k = 0;
+#pragma unroll
+  for (int u = 0; u < E; ++u) {
+    if (u < n) {
+      const float w = expf(l0[u] - M) * inv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += w * v0[u][e];
+    }
+  }
+  int k = E;
   for (; k + U <= n; k += U) {
     f32x4 v[U];
     float l[U];
