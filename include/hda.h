@@ -234,7 +234,9 @@ typedef struct hda_params {
  *   plan_dev     [device] an identical copy of the plan, plan_len ints; or
  *                NULL when plan_len <= HDA_PLAN_ARG_INTS: the plan then
  *                travels in the tile kernel's launch arguments (no upload
- *                on the stream; plan_host is free once the call returns)
+ *                on the stream; plan_host is free once the call returns),
+ *                and the tile kernel records each request's slot range in
+ *                the workspace for the merge
  *   out          [device] float32 [B][Hq][D]
  *   stream       hipStream_t, or NULL for the default stream
  * q head h reads kv head floor(h * Hkv / Hq).  Rows past len_b are never
@@ -300,9 +302,10 @@ int hda_plan_device(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
  * (the arex-research page has the tile allocation redone every decode step)
  * without a separate copy on the stream.  Launch arguments are copied when
  * the launch is enqueued, so plan_host may be pageable memory and may be
- * reused as soon as the call returns.  Asynchronous on the device.  Errors:
- * HDA_ERR_INVALID_ARG (null pointer, plan_len < 1, misaligned plan_dev),
- * HDA_ERR_HIP (a launch failed).
+ * reused as soon as the call returns.  Asynchronous on the device.  Any
+ * int32 array travels the same way (hda_prefill's row blocks and plan side
+ * by side in one buffer, for one launch).  Errors: HDA_ERR_INVALID_ARG (null
+ * pointer, plan_len < 1, misaligned plan_dev), HDA_ERR_HIP (a launch failed).
  */
 int hda_plan_upload(const int32_t* plan_host, int64_t plan_len, int32_t* plan_dev,
                     void* stream);
