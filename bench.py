@@ -165,18 +165,63 @@ def time_plan_kernel(dev, plan, copies, steps, warmup):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def cpu_baseline(inp, budget_s):
+def host_info():
+    """The host the oracle runs on: cores this process may use, the OS's
+    CPU count, the CPU model, and the BLAS threads numpy's matrix products
+    use (the oracle's parallelism)."""
+    from threadpoolctl import threadpool_info
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"affinity_cores": int(aff), "os_cpu_count": os.cpu_count(), "cpu_model": model,
+            "blas_threads": int(blas)}
+
+
+def cpu_baseline(inp, budget_s, one_thread=False):
     """The fp64 oracle, as it stands, on a bounded sample of the workload:
     whole requests, shortest first, cycling over the batch until the time
-    budget is spent.  Rate = KV bytes of the requests done / seconds."""
+    budget is spent.  Rate = KV bytes of the requests done / seconds.  With
+    one_thread, BLAS is held to one thread."""
+    import contextlib
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
     w = inp["workload"]
     order = np.argsort(inp["seq_lens"], kind="stable")
     q64 = oracle.bf16_to_f64(inp["q"])
-    done, toks, t0 = [], 0, time.perf_counter()
+    done, toks = [], 0
     seq = order.tolist() * 64
+    limit = threadpool_limits(limits=1) if one_thread else contextlib.nullcontext()
+    with limit:
+        info = host_info()
+        t0 = time.perf_counter()
+        toks, done = _oracle_passes(inp, q64, seq, budget_s, t0)
+    secs = time.perf_counter() - t0
+    elem = 1 if w.kv_dtype == "fp8" else 2
+    kvb = toks * w.n_kv_heads * w.head_dim * 2 * elem
+    threads = info["blas_threads"]
+    return {"value": round(kvb / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", **{k: v for k, v in info.items() if k != "blas_threads"},
+            "sample": f"{len(done)} request passes over the {len(inp['seq_lens'])}-request "
+                      f"batch, shortest first ({toks} KV tokens) in {secs:.1f} s; "
+                      f"numpy fp64, BLAS threads {threads} (cores = the BLAS threads used)"}
+
+
+def _oracle_passes(inp, q64, seq, budget_s, t0):
+    import oracle
+    w = inp["workload"]
+    done, toks = [], 0
     for b in seq:
         sub = [b]
         oracle.attention_reference(q64[sub], inp["k_pages"], inp["v_pages"],
@@ -188,15 +233,7 @@ def cpu_baseline(inp, budget_s):
         toks += int(inp["seq_lens"][b])
         if time.perf_counter() - t0 >= budget_s:
             break
-    secs = time.perf_counter() - t0
-    elem = 1 if w.kv_dtype == "fp8" else 2
-    kvb = toks * w.n_kv_heads * w.head_dim * 2 * elem
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(kvb / secs / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(done)} request passes over the {len(inp['seq_lens'])}-request "
-                      f"batch, shortest first ({toks} KV tokens) in {secs:.1f} s; "
-                      f"numpy fp64, BLAS threads {threads}"}
+    return toks, done
 
 
 def cpu_baseline_prefill(inp, budget_s):
@@ -205,7 +242,6 @@ def cpu_baseline_prefill(inp, budget_s):
     KV bytes each query row reads (its causal prefix) per second."""
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_info
     w = inp["workload"]
     order = np.argsort(inp["seq_lens"], kind="stable")
     off = oracle.q_offsets(inp["q_lens"])
@@ -224,11 +260,12 @@ def cpu_baseline_prefill(inp, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     secs = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(kvb / secs / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+    info = host_info()
+    threads = info.pop("blas_threads")
+    return {"value": round(kvb / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", **info,
             "sample": f"{done} request passes (shortest caches first) in {secs:.1f} s; "
-                      f"numpy fp64, BLAS threads {threads}"}
+                      f"numpy fp64, BLAS threads {threads} (cores = the BLAS threads used)"}
 
 
 def bench_prefill(args, w, inp):
@@ -481,7 +518,6 @@ def bench_router(args):
         # the fp64 oracle on a bounded sample: exact split products of
         # 1024-token batches, repeated until the time budget is spent
         import oracle
-        from threadpoolctl import threadpool_info
         log("timing the fp64 router oracle on a bounded sample")
         x = big["x"][:1024]
         hi, lo = oracle.split_router_weights(big["w"])
@@ -490,11 +526,13 @@ def bench_router(args):
             oracle.router_split_reference(x, hi, lo)
             n += 1
         secs = time.perf_counter() - t0
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = host_info()
+        threads = info.pop("blas_threads")
         res["cpu_baseline"] = {"value": round(n * 4.0 * 1024 * H * E / secs / 1e12, 4),
-                               "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                               "unit": "TFLOP/s", "cores": threads, "kind": "oracle", **info,
                                "sample": f"{n} exact split products of 1024 tokens in {secs:.1f} s; "
-                                         f"numpy fp64, BLAS threads {threads}"}
+                                         f"numpy fp64, BLAS threads {threads} (cores = the BLAS "
+                                         f"threads used)"}
     print(json.dumps(res), flush=True)
 
 
@@ -554,9 +592,10 @@ def main():
         # a2: upload on the same stream; launch arguments are copied when the
         # launch is enqueued, so only the async copy holds on to pinned[j]
         dplan = plan_dev[j]
-        if args.upload == "args" and n <= hda.HDA_PLAN_ARG_INTS:
-            dplan = None                                          # in hda_decode's launch
-        elif args.upload in ("args", "kernel"):
+        if args.upload == "args":
+            # in hda_decode's launch arguments, or hda_plan_upload when longer
+            dplan = hda.plan_to_device(host, n, plan_dev[j], stream)
+        elif args.upload == "kernel":
             hda.hda_plan_upload(host, plan_dev[j], stream, plan_len=n)
         else:
             plan_dev[j][:n].copy_(pinned[j][:n], non_blocking=True)
@@ -784,6 +823,14 @@ def main():
     if not args.no_cpu:
         log("timing the fp64 oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        if args.workload == "extreme":
+            # the oracle on one thread, on the two smallest workloads
+            one = {}
+            for name, budget in (("tiny", 2.0), ("uniform", 4.0)):
+                small = make_inputs(CONFIGS[name])
+                one[name] = cpu_baseline(small, budget, one_thread=True)
+                log(f"oracle, 1 thread, {name}: {one[name]['value']} GB/s")
+            res["cpu_baseline"]["one_thread"] = one
 
     print(json.dumps(res), flush=True)
 

@@ -76,11 +76,16 @@ extern "C" {
  *   HDA_MATH_BF16  cache elements widened exactly to bf16, q in bf16,
  *                  softmax weights rounded to bf16; fp32 accumulation
  *   HDA_MATH_FP8   fp8 cache only: QK^T and PV on fp8 matrix-core operands.
- *                  q is quantised per (request, q head) to E4M3 with scale
- *                  amax/448 (codes round-to-nearest-even from q/scale in
- *                  float32) and the softmax weights are rounded to E4M3
- *                  (times 2^8) before PV, the normaliser summing the same
- *                  rounded weights.  Needs v_layout HDA_V_DIM_MAJOR, D 128,
+ *                  q is quantised per (request, q head) with scale
+ *                  s = amax/448 as x = q/s (float32) = hi + lo/16, hi =
+ *                  E4M3(x), lo = E4M3(16 (x - hi)), both round-to-nearest-
+ *                  even (two QK products: the high part and the residual
+ *                  kept at 16x scale, as the pages' Router GEMM keeps its
+ *                  weights: remio.ai page, Router GEMM section); the
+ *                  softmax weights z = p 2^8 enter PV as E4M3(z) plus
+ *                  the E4M3 of its residual (two products into one
+ *                  accumulator), the normaliser summing the same weights.
+ *                  Needs v_layout HDA_V_DIM_MAJOR, D 128,
  *                  page_size >= 64 and tensor or head scales.
  * The pages report FP8 execution and name cache precision as a setting the
  * results depend on (remio.ai page, section "Lo que la afirmación de un
@@ -139,6 +144,21 @@ int hda_plan(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
              int64_t* plan_len);
 
 /*
+ * A launch width for hda_plan: *n_workgroups = W for tiles of tile_len over
+ * seq_lens [host] int32[batch] (each >= 1).  W_max is the width that keeps
+ * wg_per_cu 4-wave workgroups resident on each of n_cu compute units over
+ * all n_kv_heads (at most the tile count); among the widths from W_max down
+ * to W_max / 2 whose busiest workgroup holds no more tiles than at W_max,
+ * the one with the fewest partial slots, the widest on a tie.  (The pages
+ * size the tiles and their assignment to the current workload: remio.ai
+ * page, section "Por qué Tencent HPC importa para el serving de modelos en
+ * línea"; the width rule is this library's.)  Cost O(batch x W_max).
+ * Errors: HDA_ERR_INVALID_ARG.
+ */
+int hda_launch_config(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads, int32_t n_cu,
+                      int32_t wg_per_cu, int32_t tile_len, int32_t* n_workgroups);
+
+/*
  * Static split baseline in the same format: request b is cut into n_splits
  * chunks [floor(c*len_b/S), floor((c+1)*len_b/S)), chunk c handled by
  * workgroup b*S + c (W = B*S); empty chunks leave their workgroup without an
@@ -159,13 +179,19 @@ int hda_plan_validate(const int32_t* plan, int64_t plan_len,
                       const int32_t* seq_lens, int32_t batch);
 
 /*
- * Bytes of workspace hda_decode needs for this plan: partial outputs
- * float32 [P][Hq][D], partial log-sum-exp float32 [P][Hq], the prologue's
- * normalised, rotated q as bf16 [B][Hq][D] (used only when the prologue is
- * on), and per-request slot ranges int32 [B][2] (used only by
- * hda_decode_auto), each region aligned to 256 bytes.  Its contents need no
- * initialisation.  Returns -1 for a malformed plan header or non-positive
- * sizes.
+ * Bytes of workspace hda_decode needs for this plan, in this order, each
+ * region starting on a 256-byte boundary: the device check words int32
+ * [W][Hkv] (one per tile workgroup, rewritten by every call; read by
+ * hda_decode_check), partial outputs float32 [P][Hq][D], partial
+ * log-sum-exp float32 [P][Hq], the prologue's normalised, rotated q as bf16
+ * [B][Hq][D] (used only when the prologue is on), and per-request slot
+ * ranges int32 [B][2] (written by the tile kernel when the plan is built on
+ * the device or travels in the launch arguments, and read by the merge).
+ * Its contents need no initialisation.  Returns -1 for a malformed plan
+ * header or non-positive sizes.  The plan is the one described above
+ * (remio.ai page, section "Por qué Tencent HPC importa para el serving de
+ * modelos en línea": the split requests' partial results are what the
+ * workspace holds).
  */
 int64_t hda_workspace_bytes(const int32_t* plan, int64_t plan_len,
                             int32_t n_q_heads, int32_t n_kv_heads,
@@ -229,7 +255,8 @@ typedef struct hda_params {
  *                or fp8 codes; written only by the prologue (slot len_b-1)
  *   block_table  [device] int32 [B][max_pages_per_req]; token t of request b
  *                is row t % page_size of page block_table[b][t / page_size]
- *   seq_lens     [device] int32 [B], the same lengths the plan was built for
+ *   seq_lens     [device] int32 [B], the lengths the plan was built for (see
+ *                the device check below when they may differ)
  *   plan_host    [host] the plan (header read for the launch shape)
  *   plan_dev     [device] an identical copy of the plan, plan_len ints; or
  *                NULL when plan_len <= HDA_PLAN_ARG_INTS: the plan then
@@ -240,7 +267,19 @@ typedef struct hda_params {
  *   out          [device] float32 [B][Hq][D]
  *   stream       hipStream_t, or NULL for the default stream
  * q head h reads kv head floor(h * Hkv / Hq).  Rows past len_b are never
- * used, whatever they hold.
+ * used, whatever they hold: every item's range is cut at the device length
+ * seq_lens[b] before its tokens are read or scored.
+ * Device check: the plan and the device lengths can disagree (a plan kept
+ * from an earlier step while lengths changed -- the pages require the tiles
+ * to be rebuilt as lengths change: remio.ai page, section "Por qué Tencent
+ * HPC importa para el serving de modelos en línea").  Each tile workgroup
+ * records in its check word whether one of its items ended past its
+ * request's device length (HDA_CHECK_PAST_LEN: those tokens were masked, so
+ * the output is still exact attention over seq_lens[b] as long as every
+ * token below it is covered) or whether a request's last item ended before
+ * it (HDA_CHECK_SHORT: the tokens after the plan's end were not attended).
+ * hda_decode_check reads the words back.  The words live in the workspace;
+ * without a workspace (P = 0, no prologue) nothing is recorded.
  * Errors (all detected on the host before any launch): HDA_ERR_INVALID_ARG,
  * HDA_ERR_UNSUPPORTED (also: plan_dev NULL with a longer plan),
  * HDA_ERR_PLAN_MISMATCH, HDA_ERR_BAD_PLAN (header, length or workgroup item
@@ -253,6 +292,43 @@ int hda_decode(const hda_params* p, const void* q, void* k_pages,
                const int32_t* seq_lens, const int32_t* plan_host,
                const int32_t* plan_dev, int64_t plan_len, float* out,
                void* stream);
+
+/*
+ * Debug form of hda_decode (plan in device memory, plan_dev not NULL) that
+ * also counts coverage: every token a tile wave scores adds one visit to
+ * its cache row for its kv head, in visits [device] int32
+ * [num_pages][page_size][Hkv] (index (page * page_size + row) * Hkv + h),
+ * which the caller zeroes first.  A plan that tiles each [0, len_b) exactly
+ * once leaves 1 on every row below len_b of every request -- a row shared
+ * by several requests' block tables, once per request -- and 0 elsewhere.
+ * The pages' planner hands every tile of every request to exactly one
+ * thread block (remio.ai page, section "Por qué Tencent HPC importa para el
+ * serving de modelos en línea"); this checks the kernels' loops keep that.
+ * Outputs as hda_decode (slower: one atomic add per token and kv head).
+ * Errors as hda_decode; HDA_ERR_INVALID_ARG also for visits or plan_dev NULL.
+ */
+int hda_decode_coverage(const hda_params* p, const void* q, void* k_pages, void* v_pages,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* plan_host, const int32_t* plan_dev, int64_t plan_len,
+                        float* out, int32_t* visits, void* stream);
+
+/* Device check bits (hda_decode_check). */
+#define HDA_CHECK_PAST_LEN 1  /* an item reached past its request's device length (masked) */
+#define HDA_CHECK_SHORT 2     /* a request's last item ended before its device length */
+
+/*
+ * Reads the device check words the last hda_decode, hda_decode_auto or
+ * hda_prefill call with this workspace wrote: n_workgroups (the plan's W)
+ * times p->n_kv_heads int32 words at the start of p->workspace.  Waits for
+ * `stream` (the stream of that call) to finish, then copies the words to the
+ * host; *flags receives their bitwise OR (HDA_CHECK_* bits).  Returns HDA_OK
+ * when no bit is set, HDA_ERR_PLAN_MISMATCH when one is, HDA_ERR_INVALID_ARG
+ * (null pointers, n_workgroups < 1, a workspace too small for the words) or
+ * HDA_ERR_HIP.  A device-planned call always records 0 (its plan is built
+ * from the device lengths).  This is a synchronising debug aid, not part of
+ * the per-step path.
+ */
+int hda_decode_check(const hda_params* p, int32_t n_workgroups, int32_t* flags, void* stream);
 
 /*
  * The same decode step with the plan built on the device: each workgroup
@@ -277,7 +353,8 @@ int hda_decode_auto(const hda_params* p, const void* q, void* k_pages, void* v_p
 /*
  * Workspace bytes that suffice for any plan over `batch` requests and
  * `n_workgroups` workgroups (partial slots <= W + B - 1), in the layout of
- * hda_workspace_bytes.  -1 for non-positive arguments.
+ * hda_workspace_bytes (the check words counted as W x Hq, a bound on
+ * W x Hkv).  -1 for non-positive arguments.
  */
 int64_t hda_workspace_bytes_bound(int32_t batch, int32_t n_workgroups,
                                   int32_t n_q_heads, int32_t head_dim);
@@ -368,11 +445,11 @@ int hda_prefill_rows(const int32_t* q_lens, const int32_t* kv_lens, int32_t batc
 
 /* Workspace bytes for hda_prefill with this plan and blocks of at most
  * rows_per_block rows (1 .. HDA_PREFILL_MAX_TILES x
- * hda_prefill_rows_per_block): partial outputs
- * float32 [P][rows_per_block][Hq][D], then partial log-sum-exps float32
- * [P][rows_per_block][Hq], each region aligned to 256 bytes (hda_prefill
- * lays them out with the largest block's row count).  -1 on a malformed
- * header or sizes. */
+ * hda_prefill_rows_per_block): the device check words int32 [W][Hkv] (as
+ * for hda_decode), partial outputs float32 [P][rows_per_block][Hq][D], then
+ * partial log-sum-exps float32 [P][rows_per_block][Hq], each region aligned
+ * to 256 bytes (hda_prefill lays them out with the largest block's row
+ * count).  -1 on a malformed header or sizes. */
 int64_t hda_prefill_workspace_bytes(const int32_t* plan, int64_t plan_len, int32_t n_q_heads,
                                     int32_t n_kv_heads, int32_t head_dim,
                                     int32_t rows_per_block);
@@ -395,11 +472,14 @@ int64_t hda_prefill_workspace_bytes(const int32_t* plan, int64_t plan_len, int32
  *   plan_host,
  *   plan_dev     hda_plan(row_lens, n_rows, tile_len, W), as for hda_decode
  *   out          [device] float32 [n_q][Hq][D]
+ * Tokens at or past kv_lens[b] are never scored (an item's range is cut at
+ * the device length); an item that reached past it sets HDA_CHECK_PAST_LEN
+ * in its workgroup's check word (hda_decode_check with the plan's W).
  * Errors (host, before any launch): HDA_ERR_INVALID_ARG (incl. a block out
  * of range or with more than HDA_PREFILL_MAX_TILES x
  * hda_prefill_rows_per_block rows),
- * HDA_ERR_UNSUPPORTED, HDA_ERR_BAD_PLAN, HDA_ERR_WORKSPACE; HDA_ERR_HIP if a
- * launch fails.
+ * HDA_ERR_UNSUPPORTED, HDA_ERR_BAD_PLAN (header, length or workgroup item
+ * ranges), HDA_ERR_WORKSPACE; HDA_ERR_HIP if a launch fails.
  */
 int hda_prefill(const hda_params* p, const void* q, const void* k_pages, const void* v_pages,
                 const int32_t* block_table, const int32_t* kv_lens, int32_t n_q,

@@ -31,6 +31,7 @@
 // products.
 #include <hip/hip_runtime.h>
 #include <float.h>
+#include <type_traits>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -62,6 +63,8 @@ struct Args {
   float* part_lse;
   uint16_t* q_prime;     // workspace copy of the prologue's q' (bf16 [B][Hq][D])
   int32_t* req_slots;    // device-planned launches: per request (first slot, slot count)
+  int32_t* check;        // per tile workgroup: HDA_CHECK_* bits of this call (null: none)
+  int32_t* cover;        // coverage launches: visits per (page, row, kv head)
   const int32_t* rows;   // multi-token launches: row blocks [n][4] (request, first packed
                          // row, rows, position of the first row)
   const uint16_t* q_norm_w;
@@ -669,7 +672,42 @@ __global__ __launch_bounds__(256) void hda_prologue_kernel(Args a,
 // Multi-token rows (PF): the item covers nq query rows of request b starting
 // at packed row qrow0 and position pos0; column i is row i / g, q head
 // h*g + i % g, with causal limit pos0 + i / g.  Decode is nq = 1, qrow0 = b.
-template <int D, bool FP8, bool PAGE, bool PF>
+// A plan item's range against its request's length L on the device: cut at
+// L (a plan built for longer lengths then leaves the tokens past L out; an
+// item wholly past L becomes empty) and return the check bits --
+// HDA_CHECK_PAST_LEN when the item reached past L, HDA_CHECK_SHORT when the
+// request's last item ends before L (the plan was built for shorter
+// lengths; those tokens stay unattended).
+__device__ inline int cut_at_len(int& k1, int L, bool last) {
+  if (k1 > L) {
+    k1 = L;
+    return HDA_CHECK_PAST_LEN;
+  }
+  return last && k1 < L ? HDA_CHECK_SHORT : 0;
+}
+
+// The workgroup's check word (one writer per word; every launch rewrites it).
+__device__ inline void write_check(const Args& a, int bits, int tid) {
+  if (a.check && tid == 0) a.check[blockIdx.x] = bits;
+}
+
+// Coverage counting (debug launches only): each token of chunk c inside the
+// item's range [k0, k1) -- the tokens the chunk's softmax keeps -- adds one
+// visit to its cache row (physical page, row in page) for kv head h.
+template <int CH>
+__device__ inline void count_visits(const Args& a, const int32_t* __restrict__ block_table, int b,
+                                    int h, int c, int k0, int k1, int lane) {
+  if (lane >= CH) return;
+  const int t = c * CH + lane;
+  if (t < k0 || t >= k1) return;
+  const int pidx = t >> a.log2_ps;
+  const int page = pidx < a.max_pages ? block_table[(int64_t)b * a.max_pages + pidx] : -1;
+  if (page < 0 || page >= a.num_pages) return;
+  atomicAdd(&a.cover[((int64_t)page * a.page_size + (t & (a.page_size - 1))) * a.n_kv_heads + h],
+            1);
+}
+
+template <int D, bool FP8, bool PAGE, bool PF, bool COVER = false>
 __device__ inline void process_item(const Args& a, const int32_t* __restrict__ block_table,
                                     TileSmem<D>& sm, int b, int k0, int k1, int slot, int L,
                                     int qrow0, int nq, int pos0, int h, int wave, int lane,
@@ -693,7 +731,9 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
     // Chunks c_first + wave, + kWaves, ...; two register sets in flight.
     const int c_last = (k1 - 1) / kChunk;
     int c = k0 / kChunk + wave;
-    const bool has_chunks = c <= c_last;   // uniform per wave
+    // uniform per wave; an item left empty by the cut at the device length
+    // computes nothing and writes an empty partial (o = 0, lse = -inf)
+    const bool has_chunks = k0 < k1 && c <= c_last;
     Chunk<D, FP8> ring[G::NBUF];
     __amdgpu_buffer_rsrc_t kr[2], vr[2];
 
@@ -732,6 +772,7 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
           __builtin_amdgcn_sched_barrier(0);
           compute_chunk<D, FP8, PAGE, PF>(ring[k], qop, c, k0, k1, lim, pos0, qk, kg, m_run,
                                           l_run, acc);
+          if constexpr (COVER) count_visits<kChunk>(a, block_table, b, h, c, k0, k1, lane);
           c += kWaves;
           if (c > c_last) {
             done = true;
@@ -762,16 +803,19 @@ __device__ inline void process_item(const Args& a, const int32_t* __restrict__ b
 //
 // QK^T and PV take the fp8 codes as MFMA operands directly.  A wave takes
 // 64-token chunks (one page of 64, or a 64-token run of a larger page).
-//   QK: four 16-token M blocks, each one v_mfma_scale_f32_16x16x128_f8f6f4
-//       (scales 2^0) of K rows against q quantised to E4M3 per q head
-//       (s_q = amax / 448).  Row m of block mb is token
+//   QK: four 16-token M blocks, each two v_mfma_scale_f32_16x16x128_f8f6f4
+//       of K rows against q quantised per q head (s_q = amax / 448) as an
+//       E4M3 high part (operand scale 2^0) plus an E4M3 residual x 16
+//       (operand scale 2^-4).  Row m of block mb is token
 //       16*(m/4) + 4*mb + m%4, so lane (i, kg) ends up with the scores of
 //       q head i for its 16 consecutive tokens 16*kg .. 16*kg+15.
-//   PV: the softmax weights, shifted by 2^8 and rounded to E4M3, against V
+//   PV: the softmax weights, shifted by 2^8 and kept as an E4M3 value plus
+//       an E4M3 residual (two products into one accumulator), against V
 //       codes read from dim-major pages, where those 16 tokens of one head
 //       dim are 16 consecutive bytes: two v_mfma_f32_16x16x32_fp8_fp8 per
-//       16-dim block (lane i takes dim 16*nb + i), no transposes.  The weight sum comes from the same
-//       rounded weights through one more MFMA against a block of 1.0 codes.
+//       16-dim block and part (lane i takes dim 16*nb + i), no transposes.
+//       The weight sum comes from the same rounded weights through more
+//       MFMAs against a block of 1.0 codes.
 constexpr int kChunkN = 64;
 constexpr uint64_t kFp8Ones = 0x3838383838383838ull;   // eight E4M3 1.0 codes
 
@@ -841,7 +885,8 @@ __device__ inline uint64_t pack64(uint32_t lo, uint32_t hi) {
 // One 64-token chunk: scores, online-softmax update, acc += P8 V8, and the
 // rounded weights' sum into lacc (both in units of 2^8).  qs = score scale of
 // lane i's q head in log2 units (sm_scale * k scale * s_q * log2 e).
-__device__ inline void compute_chunk_n(const ChunkN& ch, const i32x8& qop, int c, int k0, int k1,
+__device__ inline void compute_chunk_n(const ChunkN& ch, const i32x8& qop, const i32x8& qlo,
+                                       int c, int k0, int k1,
                                        int rows, float qs, int kg, float& m_run, f32x4 (&acc)[8],
                                        f32x4& lacc) {
   float sc[16];
@@ -851,8 +896,10 @@ __device__ inline void compute_chunk_n(const ChunkN& ch, const i32x8& qop, int c
                        (int)ch.k[mb][0][3], (int)ch.k[mb][1][0], (int)ch.k[mb][1][1],
                        (int)ch.k[mb][1][2], (int)ch.k[mb][1][3]};
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 sacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qop, z, 0, 0, 0, 127,
-                                                                       0, 127);
+    // K q_hi, then + K q_lo with q_lo's operand scale 2^-4 (E8M0 code 123)
+    f32x4 sacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qop, z, 0, 0, 0, 127, 0,
+                                                                 127);
+    sacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qlo, sacc, 0, 0, 0, 127, 0, 123);
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[4 * mb + r] = sacc[r] * qs;
   }
@@ -871,15 +918,25 @@ __device__ inline void compute_chunk_n(const ChunkN& ch, const i32x8& qop, int c
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(m_run, mx);
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-  uint32_t pw[4];
+  // weights z = p 2^8 as a = E4M3(z) plus b = E4M3(z - a) (the difference
+  // is exact in float32): both go through PV into the same accumulator, so
+  // the product sees a + b, within 2^-8 z + 2^-10 of z where a alone is
+  // within 2^-4 z
+  uint32_t pw[4], pr[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float e0 = __builtin_amdgcn_exp2f(sc[4 * q] - m_new) * 256.f;
-    const float e1 = __builtin_amdgcn_exp2f(sc[4 * q + 1] - m_new) * 256.f;
-    const float e2 = __builtin_amdgcn_exp2f(sc[4 * q + 2] - m_new) * 256.f;
-    const float e3 = __builtin_amdgcn_exp2f(sc[4 * q + 3] - m_new) * 256.f;
-    uint32_t x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-    pw[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, (int)x, true);
+    float e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_exp2f(sc[4 * q + j] - m_new) * 256.f;
+    const int x = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+    const int a = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], x, true);
+    pw[q] = (uint32_t)a;
+    const float r0 = e[0] - __builtin_amdgcn_cvt_f32_fp8(a, 0);
+    const float r1 = e[1] - __builtin_amdgcn_cvt_f32_fp8(a, 1);
+    const float r2 = e[2] - __builtin_amdgcn_cvt_f32_fp8(a, 2);
+    const float r3 = e[3] - __builtin_amdgcn_cvt_f32_fp8(a, 3);
+    const int y = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+    pr[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, y, true);
   }
   m_run = m_new;
   if (__ballot(alpha != 1.0f) != 0) {
@@ -894,8 +951,11 @@ __device__ inline void compute_chunk_n(const ChunkN& ch, const i32x8& qop, int c
     for (int r = 0; r < 4; ++r) lacc[r] *= ar[r];
   }
   // weights of tokens 16*kg + 8*ks + j, j = 0..7, for K steps ks = 0, 1
+  // (p: the E4M3 weights, r: their residuals)
   const long p0 = (long)pack64(pw[0], pw[1]);
   const long p1 = (long)pack64(pw[2], pw[3]);
+  const long r0 = (long)pack64(pr[0], pr[1]);
+  const long r1 = (long)pack64(pr[2], pr[3]);
   // V columns past len hold anything (a NaN code times a zero weight would
   // still poison the sum): zero them in the last chunk of a request
   uint32_t vm[4] = {~0u, ~0u, ~0u, ~0u};
@@ -911,17 +971,22 @@ __device__ inline void compute_chunk_n(const ChunkN& ch, const i32x8& qop, int c
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
     const u32x4 v = ch.v[nb];
-    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-        p0, (long)pack64(v[0] & vm[0], v[1] & vm[1]), acc[nb], 0, 0, 0);
-    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-        p1, (long)pack64(v[2] & vm[2], v[3] & vm[3]), acc[nb], 0, 0, 0);
+    const long v0 = (long)pack64(v[0] & vm[0], v[1] & vm[1]);
+    const long v1 = (long)pack64(v[2] & vm[2], v[3] & vm[3]);
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(p0, v0, acc[nb], 0, 0, 0);
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(p1, v1, acc[nb], 0, 0, 0);
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(r0, v0, acc[nb], 0, 0, 0);
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(r1, v1, acc[nb], 0, 0, 0);
   }
   lacc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(p0, (long)kFp8Ones, lacc, 0, 0, 0);
   lacc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(p1, (long)kFp8Ones, lacc, 0, 0, 0);
+  lacc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(r0, (long)kFp8Ones, lacc, 0, 0, 0);
+  lacc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(r1, (long)kFp8Ones, lacc, 0, 0, 0);
 }
 
 // One plan item in the native-fp8 mode (see process_item for the shape of
 // the loop and the combine).
+template <bool COVER = false>
 __device__ inline void process_item_fp8n(const Args& a, const int32_t* __restrict__ block_table,
                                          TileSmem<128>& sm, int b, int k0, int k1, int slot,
                                          int L, int h, int wave, int lane, int tid) {
@@ -954,20 +1019,34 @@ __device__ inline void process_item_fp8n(const Args& a, const int32_t* __restric
   amax = fmaxf(amax, __shfl_xor(amax, 16));
   amax = fmaxf(amax, __shfl_xor(amax, 32));
   const float s_q = amax > 0.f ? amax / 448.0f : 1.0f;
-  i32x8 qop;
+  // q / s_q as a high part and a residual: hi = E4M3(x), lo = E4M3(16 (x -
+  // hi)) (the difference is exact in float32), so the score uses
+  // s_q (hi + lo / 16) -- relative error about 2^-8 instead of E4M3's 2^-4,
+  // the quantisation that dominated this mode's error.  The split is the
+  // Router GEMM's (a high part plus a residual kept at a larger scale and
+  // scaled back in the product) applied to q; the two products share the K
+  // operand, the second taking the 2^-4 as its operand scale.
+  i32x8 qop, qlo;
 #pragma unroll
   for (int dw = 0; dw < 8; ++dw) {
     float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = fminf(fmaxf(qv[4 * dw + e] / s_q, -448.f), 448.f);
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-    qop[dw] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+    const int h01 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    const int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h01, true);
+    qop[dw] = hi;
+    const float r0 = (x[0] - __builtin_amdgcn_cvt_f32_fp8(hi, 0)) * 16.f;
+    const float r1 = (x[1] - __builtin_amdgcn_cvt_f32_fp8(hi, 1)) * 16.f;
+    const float r2 = (x[2] - __builtin_amdgcn_cvt_f32_fp8(hi, 2)) * 16.f;
+    const float r3 = (x[3] - __builtin_amdgcn_cvt_f32_fp8(hi, 3)) * 16.f;
+    const int l01 = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+    qlo[dw] = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l01, true);
   }
   const float qs = qk * s_q;
 
   const int c_last = (k1 - 1) / kChunkN;
   int c = k0 / kChunkN + wave;
-  const bool has_chunks = c <= c_last;
+  const bool has_chunks = k0 < k1 && c <= c_last;
   ChunkN ring[2];
   int rows_of[2];
   __amdgpu_buffer_rsrc_t kr, vr;
@@ -993,7 +1072,8 @@ __device__ inline void process_item_fp8n(const Args& a, const int32_t* __restric
         rows_of[1 - k] = chunk_rsrc_n(a, block_table, b, L, h, cn, cn <= c_last, kr, vr);
         issue_chunk_n(ring[1 - k], kr, vr, koff, voff, a.page_size);
         __builtin_amdgcn_sched_barrier(0);
-        compute_chunk_n(ring[k], qop, c, k0, k1, rows_of[k], qs, kg, m_run, acc, lacc);
+        compute_chunk_n(ring[k], qop, qlo, c, k0, k1, rows_of[k], qs, kg, m_run, acc, lacc);
+        if constexpr (COVER) count_visits<kChunkN>(a, block_table, b, h, c, k0, k1, lane);
         c += kWaves;
         if (c > c_last) {
           done = true;
@@ -1591,15 +1671,42 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void hda_prefill_shared_k
   const int32_t* items = wg_ptr + a.n_wg + 1;
   const int32_t* __restrict__ rows = a.rows;
   const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
-  auto valid = [&](int it) {
+  auto well_formed = [&](int it) {
     const int rho = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
               slot = items[4 * it + 3];
     return (unsigned)rho < (unsigned)a.batch && k0 >= 0 && k1 > k0 && slot < a.n_parts;
+  };
+  // an item with tokens below its request's device length (the range is cut
+  // there; see cut_at_len)
+  auto valid = [&](int it) {
+    return well_formed(it) &&
+           min(items[4 * it + 2], seq_lens[rows[4 * items[4 * it]]]) > items[4 * it + 1];
   };
   auto next_valid = [&](int it) {
     while (it < it_end && !valid(it)) ++it;
     return it;
   };
+  // Check bits; items left empty by the cut write an empty partial
+  // (o = 0, lse = -inf: weighed zero by the merge) here, the others below.
+  {
+    const int g = a.group;
+    int chk = 0;
+    for (int it = it_begin; it < it_end; ++it) {
+      if (!well_formed(it)) continue;
+      const int rho = items[4 * it], k0 = items[4 * it + 1], slot = items[4 * it + 3];
+      int k1 = items[4 * it + 2];
+      chk |= cut_at_len(k1, seq_lens[rows[4 * rho]], false);
+      if (k1 > k0 || slot < 0) continue;
+      const int nq = rows[4 * rho + 2];
+      for (int idx = tid; idx < nq * g * D; idx += 64 * NW) {
+        const int r = idx / (g * D), rem = idx - r * g * D, hh = rem / D, d = rem - hh * D;
+        const int64_t prow = ((int64_t)slot * a.qb + r) * a.n_q_heads + (int64_t)h * g + hh;
+        a.part_o[prow * D + d] = 0.f;
+        if (d == 0) a.part_lse[prow] = -INFINITY;
+      }
+    }
+    write_check(a, chk, tid);
+  }
   StageLoader<D, FP8, PAGE, NW, kSharedSub> ld;
   int it = next_valid(it_begin);
   if (it < it_end) {
@@ -1616,9 +1723,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void hda_prefill_shared_k
     const int next_b = has_next ? rows[4 * items[4 * nx]] : 0;
     const int next_L = has_next ? seq_lens[next_b] : 0;
     const int next_c = has_next ? items[4 * nx + 1] / kChunk : 0;
+    const int L = seq_lens[b];
     process_item_shared<D, FP8, PAGE, NW, TPW, kSharedSub>(
-        a, block_table, buf, ld, b, k0, k1, slot, seq_lens[b], qrow0, nq, pos0, h, has_next,
-        next_b, next_L, next_c, wave, lane, tid);
+        a, block_table, buf, ld, b, k0, min(k1, L), slot, L, qrow0, nq, pos0, h, has_next, next_b,
+        next_L, next_c, wave, lane, tid);
     it = nx;
   }
 }
@@ -1691,22 +1799,24 @@ __device__ inline uint32_t total_tiles(const int32_t* __restrict__ seq_lens, int
 }
 
 // One item by the kernel variant's item routine.
-template <int D, bool FP8, bool PAGE, bool NATIVE>
+template <int D, bool FP8, bool PAGE, bool NATIVE, bool COVER = false>
 __device__ inline void run_item(const Args& a, const int32_t* __restrict__ block_table,
                                 TileSmem<D>& sm, int b, int k0, int k1, int slot, int L, int h,
                                 int wave, int lane, int tid) {
   if constexpr (NATIVE)
-    process_item_fp8n(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
+    process_item_fp8n<COVER>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
   else
-    process_item<D, FP8, PAGE, false>(a, block_table, sm, b, k0, k1, slot, L, b, 1, L - 1, h,
-                                      wave, lane, tid);
+    process_item<D, FP8, PAGE, false, COVER>(a, block_table, sm, b, k0, k1, slot, L, b, 1, L - 1,
+                                             h, wave, lane, tid);
 }
+
 
 // Workgroup (w, h): W * Hkv workgroups, kv head fastest.  Items come from the
 // host plan (DEVPLAN false) or are derived here from the device lengths with
 // the same rule (DEVPLAN true), in the same order.  NATIVE selects the
 // native-fp8 item routine (D = 128).
-template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE, bool PF = false>
+template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE, bool PF = false,
+          bool COVER = false>
 __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
     Args a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ plan) {
@@ -1726,27 +1836,37 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_kernel(
     const int32_t* items = wg_ptr + a.n_wg + 1;
     const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
     const int32_t* __restrict__ rows = a.rows;
+    int chk = 0;
     for (int it = it_begin; it < it_end; ++it) {
-      const int rho = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
-                slot = items[4 * it + 3];
+      const int rho = items[4 * it], k0 = items[4 * it + 1], slot = items[4 * it + 3];
+      int k1 = items[4 * it + 2];
       if ((unsigned)rho >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
       const int b = rows[4 * rho], qrow0 = rows[4 * rho + 1], nq = rows[4 * rho + 2],
                 pos0 = rows[4 * rho + 3];
-      process_item<D, FP8, PAGE, true>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], qrow0,
-                                       nq, pos0, h, wave, lane, tid);
+      const int L = seq_lens[b];
+      chk |= cut_at_len(k1, L, false);
+      process_item<D, FP8, PAGE, true>(a, block_table, sm, b, k0, k1, slot, L, qrow0, nq, pos0, h,
+                                       wave, lane, tid);
     }
+    write_check(a, chk, tid);
   } else if constexpr (!DEVPLAN) {
     const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
     const int32_t* items = wg_ptr + a.n_wg + 1;
     const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
+    int chk = 0;
     for (int it = it_begin; it < it_end; ++it) {
-      const int b = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
-                slot = items[4 * it + 3];
+      const int b = items[4 * it], k0 = items[4 * it + 1], slot = items[4 * it + 3];
+      int k1 = items[4 * it + 2];
       if ((unsigned)b >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
-      run_item<D, FP8, PAGE, NATIVE>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], h, wave,
-                                     lane, tid);
+      const int L = seq_lens[b];
+      chk |= cut_at_len(k1, L, it + 1 >= a.n_items || items[4 * (it + 1)] != b);
+      run_item<D, FP8, PAGE, NATIVE, COVER>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane,
+                                            tid);
     }
+    write_check(a, chk, tid);
   } else {
+    // the plan comes from the device lengths themselves: nothing to check
+    write_check(a, 0, tid);
     // Every wave derives the same plan facts; they stay wave-uniform.
     const uint32_t T = total_tiles(seq_lens, a.batch, a.tile_len, lane);
     const SplitDev sp{T / (uint32_t)a.n_wg, T % (uint32_t)a.n_wg};
@@ -1806,7 +1926,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_argplan_kernel(
   const int w = blockIdx.x / a.n_kv_heads;
   const int32_t* wg_ptr = pl.v + HDA_PLAN_HEADER_INTS;
   const int32_t* items = wg_ptr + a.n_wg + 1;
-  if (a.n_parts > 0 && blockIdx.x == 0) {
+  if (a.n_parts > 0 && a.req_slots && blockIdx.x == 0) {   // (a merge list needs none)
     const int32_t* rpp = items + 4 * a.n_items;
     for (int b = tid; b < a.batch; b += 64 * kWaves) {
       const int s0 = rpp[b];
@@ -1815,13 +1935,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_argplan_kernel(
     }
   }
   const int it_begin = wg_ptr[w], it_end = wg_ptr[w + 1];
+  int chk = 0;
   for (int it = it_begin; it < it_end; ++it) {
-    const int b = items[4 * it], k0 = items[4 * it + 1], k1 = items[4 * it + 2],
-              slot = items[4 * it + 3];
+    const int b = items[4 * it], k0 = items[4 * it + 1], slot = items[4 * it + 3];
+    int k1 = items[4 * it + 2];
     if ((unsigned)b >= (unsigned)a.batch || k0 < 0 || k1 <= k0 || slot >= a.n_parts) continue;
-    run_item<D, FP8, PAGE, NATIVE>(a, block_table, sm, b, k0, k1, slot, seq_lens[b], h, wave,
-                                   lane, tid);
+    const int L = seq_lens[b];
+    chk |= cut_at_len(k1, L, it + 1 >= a.n_items || items[4 * (it + 1)] != b);
+    run_item<D, FP8, PAGE, NATIVE>(a, block_table, sm, b, k0, k1, slot, L, h, wave, lane, tid);
   }
+  write_check(a, chk, tid);
 }
 
 // Log-sum-exp merge of split requests: workgroup (b, q head) combines the
@@ -1839,25 +1962,49 @@ __global__ __launch_bounds__(64 * kWaves, 2) void hda_decode_argplan_kernel(
 constexpr int kMergeEarly = 32;    // partial rows loaded before the weights
 constexpr int kMergeStage = 512;   // slot weights staged in LDS per pass
 
-template <int D, bool RECORDED>
+// Where the merge finds each request's slot range: the plan's req_part_ptr
+// in device memory, the ranges the tile kernel recorded in the workspace,
+// or a list of the split requests in the merge's own launch arguments (the
+// host knows them from its plan; the grid then covers only those requests).
+// (Plain int constants, not an enum: a kernel's mangled name must come out
+// the same in the host and the device compilation, and an unnamed type's
+// compiler-made name need not.)
+constexpr int kSlotsPlan = 0, kSlotsRecorded = 1, kSlotsList = 2;
+constexpr int kMergeListMax = 256;
+struct MergeList {
+  int32_t v[3 * kMergeListMax];   // (request, first slot, slot count) per split request
+};
+struct NoMergeList {};
+template <int SRC>
+using MergeArg = typename std::conditional<SRC == kSlotsList, MergeList, NoMergeList>::type;
+
+template <int D, int SRC>
 __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __restrict__ plan,
-                                                      const int32_t* __restrict__ seq_lens) {
+                                                      const int32_t* __restrict__ seq_lens,
+                                                      MergeArg<SRC> ml) {
   __shared__ float sm_w[kMergeStage];
   __shared__ float sm_red[2][D / 64];
   const int d = threadIdx.x, lane = d & 63, wave = d >> 6;
   const int hq = blockIdx.x % a.n_q_heads;
-  const int b = blockIdx.x / a.n_q_heads;
-  const int qr = 0, orow = b;
-  int s0, s1;
-  if constexpr (!RECORDED) {
+  const int e = blockIdx.x / a.n_q_heads;
+  const int qr = 0;
+  int b, s0, s1;
+  if constexpr (SRC == kSlotsList) {
+    b = ml.v[3 * e];
+    s0 = max(0, ml.v[3 * e + 1]);
+    s1 = min(a.n_parts, ml.v[3 * e + 1] + ml.v[3 * e + 2]);
+  } else if constexpr (SRC == kSlotsPlan) {
+    b = e;
     const int32_t* rpp = plan + HDA_PLAN_HEADER_INTS + a.n_wg + 1 + 4 * a.n_items;
     s0 = max(0, rpp[b]);
     s1 = min(a.n_parts, rpp[b + 1]);
   } else {
+    b = e;
     if (seq_lens[b] < 1) return;                    // no item, nothing recorded
     s0 = max(0, a.req_slots[2 * b]);
     s1 = min(a.n_parts, s0 + a.req_slots[2 * b + 1]);
   }
+  const int orow = b;
   if (s1 <= s0) return;
   const int n = s1 - s0;
   const int64_t lstride = (int64_t)a.qb * a.n_q_heads;   // between slots, in rows
@@ -2160,9 +2307,10 @@ __global__ __launch_bounds__(64) void hda_plan_kernel(const int32_t* __restrict_
   }
 }
 
-template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE = false>
+template <int D, bool FP8, bool DEVPLAN, bool PAGE, bool NATIVE = false, bool COVER = false>
 hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_t stream,
-                  void* split_event, const ArgPlan* ap) {
+                  void* split_event, const ArgPlan* ap, const MergeList* ml, int n_split) {
+  if (ml) a.req_slots = nullptr;   // the merge's ranges travel in its own arguments
   hipError_t e;
   if (prologue) {
     hipLaunchKernelGGL((hda_prologue_kernel<D, FP8>), dim3(a.batch * a.n_kv_heads), dim3(256), 0,
@@ -2175,8 +2323,9 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
     hipLaunchKernelGGL((hda_decode_argplan_kernel<D, FP8, PAGE, NATIVE>), dim3(grid),
                        dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens, *ap);
   else
-    hipLaunchKernelGGL((hda_decode_kernel<D, FP8, DEVPLAN, PAGE, NATIVE>), dim3(grid),
-                       dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens, a.plan);
+    hipLaunchKernelGGL((hda_decode_kernel<D, FP8, DEVPLAN, PAGE, NATIVE, false, COVER>),
+                       dim3(grid), dim3(64 * kWaves), 0, stream, a, a.block_table, a.seq_lens,
+                       a.plan);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (split_event) {
@@ -2184,13 +2333,17 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
     if (e != hipSuccess) return e;
   }
   if (DEVPLAN || a.n_parts > 0) {
-    // slot ranges from the device plan or the argument plan, else from plan_dev
-    if (DEVPLAN || ap)
-      hipLaunchKernelGGL((hda_merge_kernel<D, true>), dim3(a.batch * a.n_q_heads), dim3(D), 0,
-                         stream, a, a.plan, a.seq_lens);
+    // slot ranges from the host's list of split requests, else recorded by
+    // the tile kernel (device plan, argument plan), else from plan_dev
+    if (!DEVPLAN && ml)
+      hipLaunchKernelGGL((hda_merge_kernel<D, kSlotsList>), dim3(n_split * a.n_q_heads), dim3(D),
+                         0, stream, a, a.plan, a.seq_lens, *ml);
+    else if (DEVPLAN || ap)
+      hipLaunchKernelGGL((hda_merge_kernel<D, kSlotsRecorded>), dim3(a.batch * a.n_q_heads),
+                         dim3(D), 0, stream, a, a.plan, a.seq_lens, NoMergeList{});
     else
-      hipLaunchKernelGGL((hda_merge_kernel<D, false>), dim3(a.batch * a.n_q_heads), dim3(D), 0,
-                         stream, a, a.plan, a.seq_lens);
+      hipLaunchKernelGGL((hda_merge_kernel<D, kSlotsPlan>), dim3(a.batch * a.n_q_heads), dim3(D),
+                         0, stream, a, a.plan, a.seq_lens, NoMergeList{});
     e = hipGetLastError();
   }
   return e;
@@ -2240,15 +2393,18 @@ hipError_t launch_prefill_d(const Args& a, bool fp8, int grid, int n_rows, hipSt
 
 // Per-page scales are built for the fp8 cache only (check_params refuses
 // them for bf16).
-template <int D, bool DEVPLAN>
+template <int D, bool DEVPLAN, bool COVER = false>
 hipError_t launch_d(const Args& a, bool fp8, bool native, int grid, bool pro, uint16_t* qp,
-                    hipStream_t st, void* ev, const ArgPlan* ap = nullptr) {
+                    hipStream_t st, void* ev, const ArgPlan* ap = nullptr,
+                    const MergeList* ml = nullptr, int ns = 0) {
   if constexpr (D == 128)
-    if (native) return launch<128, true, DEVPLAN, false, true>(a, grid, pro, qp, st, ev, ap);
-  if (!fp8) return launch<D, false, DEVPLAN, false>(a, grid, pro, qp, st, ev, ap);
+    if (native)
+      return launch<128, true, DEVPLAN, false, true, COVER>(a, grid, pro, qp, st, ev, ap, ml, ns);
+  if (!fp8)
+    return launch<D, false, DEVPLAN, false, false, COVER>(a, grid, pro, qp, st, ev, ap, ml, ns);
   return a.scale_mode == HDA_SCALE_PAGE
-             ? launch<D, true, DEVPLAN, true>(a, grid, pro, qp, st, ev, ap)
-             : launch<D, true, DEVPLAN, false>(a, grid, pro, qp, st, ev, ap);
+             ? launch<D, true, DEVPLAN, true, false, COVER>(a, grid, pro, qp, st, ev, ap, ml, ns)
+             : launch<D, true, DEVPLAN, false, false, COVER>(a, grid, pro, qp, st, ev, ap, ml, ns);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -2294,6 +2450,20 @@ int check_params(const hda_params* p, const void* q, const void* k_pages, const 
   return HDA_OK;
 }
 
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Workgroup item ranges of a plan (header and length already checked):
+// wg_ptr from 0, non-decreasing, ending at N, so that the kernels' item
+// loops stay inside the item list (the items themselves are range-checked
+// on the device).
+bool wg_ranges_ok(const int32_t* plan, int64_t W, int64_t N) {
+  const int32_t* wg_ptr = plan + HDA_PLAN_HEADER_INTS;
+  if (wg_ptr[0] != 0 || wg_ptr[W] != N) return false;
+  for (int64_t w = 0; w < W; ++w)
+    if (wg_ptr[w + 1] < wg_ptr[w]) return false;
+  return true;
+}
+
 Args make_args(const hda_params* p, const void* q, void* k_pages, void* v_pages,
                const int32_t* block_table, const int32_t* seq_lens, float* out, int64_t W,
                int64_t P) {
@@ -2306,15 +2476,21 @@ Args make_args(const hda_params* p, const void* q, void* k_pages, void* v_pages,
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.out = out;
+  // workspace: check words [W][Hkv], partial o [P][Hq][D], partial lse
+  // [P][Hq], q' of the prologue [B][Hq][D] bf16, per-request slot ranges
+  // [B][2], each from a 256-byte boundary
   uint8_t* ws = static_cast<uint8_t*>(p->workspace);
-  const int64_t o_bytes = (P * p->n_q_heads * D * 4 + 255) / 256 * 256;
-  const int64_t l_bytes = (P * p->n_q_heads * 4 + 255) / 256 * 256;
-  a.part_o = ws ? reinterpret_cast<float*>(ws) : nullptr;
-  a.part_lse = ws ? reinterpret_cast<float*>(ws + o_bytes) : nullptr;
-  // q' of the prologue follows the partials, then the per-request slot ranges
-  a.q_prime = ws ? reinterpret_cast<uint16_t*>(ws + o_bytes + l_bytes) : nullptr;
-  const int64_t qp_bytes = ((int64_t)p->batch * p->n_q_heads * D * 2 + 255) / 256 * 256;
-  a.req_slots = ws ? reinterpret_cast<int32_t*>(ws + o_bytes + l_bytes + qp_bytes) : nullptr;
+  const int64_t c_bytes = round256(W * p->n_kv_heads * 4);
+  const int64_t o_bytes = round256(P * p->n_q_heads * D * 4);
+  const int64_t l_bytes = round256(P * p->n_q_heads * 4);
+  const int64_t qp_bytes = round256((int64_t)p->batch * p->n_q_heads * D * 2);
+  a.check = ws ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  a.part_o = ws ? reinterpret_cast<float*>(ws + c_bytes) : nullptr;
+  a.part_lse = ws ? reinterpret_cast<float*>(ws + c_bytes + o_bytes) : nullptr;
+  a.q_prime = ws ? reinterpret_cast<uint16_t*>(ws + c_bytes + o_bytes + l_bytes) : nullptr;
+  a.req_slots = ws ? reinterpret_cast<int32_t*>(ws + c_bytes + o_bytes + l_bytes + qp_bytes)
+                   : nullptr;
+  a.cover = nullptr;
   a.q_norm_w = static_cast<const uint16_t*>(p->q_norm_w);
   a.k_norm_w = static_cast<const uint16_t*>(p->k_norm_w);
   a.k_new = static_cast<const uint16_t*>(p->k_new);
@@ -2345,14 +2521,16 @@ Args make_args(const hda_params* p, const void* q, void* k_pages, void* v_pages,
   return a;
 }
 
-int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
-
 }  // namespace
 
-extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, void* v_pages,
-                          const int32_t* block_table, const int32_t* seq_lens,
-                          const int32_t* plan_host, const int32_t* plan_dev, int64_t plan_len,
-                          float* out, void* stream) {
+namespace {
+
+// hda_decode, and with `cover` its coverage-counting debug form (plan in
+// device memory only).
+int decode_step(const hda_params* p, const void* q, void* k_pages, void* v_pages,
+                const int32_t* block_table, const int32_t* seq_lens, const int32_t* plan_host,
+                const int32_t* plan_dev, int64_t plan_len, float* out, void* stream,
+                int32_t* cover) {
   int st = check_params(p, q, k_pages, v_pages, block_table, seq_lens, out);
   if (st != HDA_OK) return st;
   if (!plan_host) return HDA_ERR_INVALID_ARG;
@@ -2362,12 +2540,7 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
   const int64_t W = plan_host[3], N = plan_host[5], P = plan_host[6];
   if (W < 1 || N < 1 || P < 0 || plan_len != HDA_PLAN_HEADER_INTS + (W + 1) + 4 * N + p->batch + 1)
     return HDA_ERR_BAD_PLAN;
-  // workgroup item ranges stay inside the item list (items themselves are
-  // range-checked by the kernel)
-  const int32_t* wg_ptr = plan_host + HDA_PLAN_HEADER_INTS;
-  if (wg_ptr[0] != 0 || wg_ptr[W] != N) return HDA_ERR_BAD_PLAN;
-  for (int64_t w = 0; w < W; ++w)
-    if (wg_ptr[w + 1] < wg_ptr[w]) return HDA_ERR_BAD_PLAN;
+  if (!wg_ranges_ok(plan_host, W, N)) return HDA_ERR_BAD_PLAN;
   const int64_t grid = W * p->n_kv_heads;
   if (grid > 0x7fffffffLL) return HDA_ERR_UNSUPPORTED;
   const int64_t ws_need = hda_workspace_bytes(plan_host, plan_len, p->n_q_heads, p->n_kv_heads,
@@ -2377,6 +2550,9 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
     return HDA_ERR_WORKSPACE;
 
   Args a = make_args(p, q, k_pages, v_pages, block_table, seq_lens, out, W, P);
+  // without partial slots or prologue the workspace is optional; the check
+  // words are then recorded only when it is large enough
+  if (!p->workspace || p->workspace_bytes < ws_need) a.check = nullptr;
   a.plan = plan_dev;
   a.n_items = (int32_t)N;
   a.tile_len = plan_host[2];
@@ -2384,22 +2560,96 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
   const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
   const bool native = p->math == HDA_MATH_FP8;
   const bool pro = p->prologue != 0;
+  // the split requests and their slot ranges, for a merge over them alone
+  MergeList ml;
+  int n_split = 0;
+  bool listed = P > 0;
+  {
+    const int32_t* rpp = plan_host + HDA_PLAN_HEADER_INTS + (W + 1) + 4 * N;
+    for (int64_t b = 0; listed && b < p->batch; ++b) {
+      const int32_t cnt = rpp[b + 1] - rpp[b];
+      if (cnt <= 0) continue;
+      if (n_split == kMergeListMax) {
+        listed = false;
+        break;
+      }
+      ml.v[3 * n_split] = (int32_t)b;
+      ml.v[3 * n_split + 1] = rpp[b];
+      ml.v[3 * n_split + 2] = cnt;
+      ++n_split;
+    }
+    if (n_split == 0) listed = false;
+  }
+  const MergeList* mlp = listed ? &ml : nullptr;
+  hipError_t e;
+  if (cover) {
+    if (!plan_dev) return HDA_ERR_INVALID_ARG;
+    a.cover = cover;
+    e = p->head_dim == 64 ? launch_d<64, false, true>(a, fp8, native, (int)grid, pro, a.q_prime,
+                                                      hs, p->split_event, nullptr, mlp, n_split)
+                          : launch_d<128, false, true>(a, fp8, native, (int)grid, pro, a.q_prime,
+                                                       hs, p->split_event, nullptr, mlp, n_split);
+    return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
+  }
   ArgPlan ap;   // the plan in the launch arguments when no device copy is given
   if (!plan_dev) memcpy(ap.v, plan_host, (size_t)plan_len * sizeof(int32_t));
   const ArgPlan* app = plan_dev ? nullptr : &ap;
-  hipError_t e = p->head_dim == 64 ? launch_d<64, false>(a, fp8, native, (int)grid, pro, a.q_prime,
-                                                        hs, p->split_event, app)
-                                   : launch_d<128, false>(a, fp8, native, (int)grid, pro,
-                                                          a.q_prime, hs, p->split_event, app);
+  e = p->head_dim == 64 ? launch_d<64, false>(a, fp8, native, (int)grid, pro, a.q_prime, hs,
+                                              p->split_event, app, mlp, n_split)
+                        : launch_d<128, false>(a, fp8, native, (int)grid, pro, a.q_prime, hs,
+                                               p->split_event, app, mlp, n_split);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, void* v_pages,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          const int32_t* plan_host, const int32_t* plan_dev, int64_t plan_len,
+                          float* out, void* stream) {
+  return decode_step(p, q, k_pages, v_pages, block_table, seq_lens, plan_host, plan_dev,
+                     plan_len, out, stream, nullptr);
+}
+
+extern "C" int hda_decode_coverage(const hda_params* p, const void* q, void* k_pages,
+                                   void* v_pages, const int32_t* block_table,
+                                   const int32_t* seq_lens, const int32_t* plan_host,
+                                   const int32_t* plan_dev, int64_t plan_len, float* out,
+                                   int32_t* visits, void* stream) {
+  if (!visits || !plan_dev) return HDA_ERR_INVALID_ARG;
+  return decode_step(p, q, k_pages, v_pages, block_table, seq_lens, plan_host, plan_dev,
+                     plan_len, out, stream, visits);
+}
+
+extern "C" int hda_decode_check(const hda_params* p, int32_t n_workgroups, int32_t* flags,
+                                void* stream) {
+  if (!p || !flags || n_workgroups < 1 || p->n_kv_heads < 1 || !p->workspace)
+    return HDA_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)n_workgroups * p->n_kv_heads;
+  if (p->workspace_bytes < n * 4) return HDA_ERR_INVALID_ARG;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t buf[1024];
+  int32_t bits = 0;
+  for (int64_t off = 0; off < n; off += 1024) {
+    const int64_t m = n - off < 1024 ? n - off : 1024;
+    if (hipMemcpyAsync(buf, static_cast<const int32_t*>(p->workspace) + off, (size_t)m * 4,
+                       hipMemcpyDeviceToHost, hs) != hipSuccess ||
+        hipStreamSynchronize(hs) != hipSuccess)
+      return HDA_ERR_HIP;
+    for (int64_t i = 0; i < m; ++i) bits |= buf[i];
+  }
+  *flags = bits;
+  return bits ? HDA_ERR_PLAN_MISMATCH : HDA_OK;
 }
 
 extern "C" int64_t hda_workspace_bytes_bound(int32_t batch, int32_t n_workgroups,
                                              int32_t n_q_heads, int32_t head_dim) {
   if (batch < 1 || n_workgroups < 1 || n_q_heads < 1 || head_dim < 1) return -1;
   const int64_t P = (int64_t)n_workgroups + batch - 1;   // partial slots <= items <= W + B - 1
-  return round256(P * n_q_heads * head_dim * 4) + round256(P * n_q_heads * 4) +
-         round256((int64_t)batch * n_q_heads * head_dim * 2) + round256((int64_t)batch * 8);
+  // check words counted as W x Hq (>= W x Hkv, the count a launch writes)
+  return round256((int64_t)n_workgroups * n_q_heads * 4) + round256(P * n_q_heads * head_dim * 4) +
+         round256(P * n_q_heads * 4) + round256((int64_t)batch * n_q_heads * head_dim * 2) +
+         round256((int64_t)batch * 8);
 }
 
 extern "C" int hda_decode_auto(const hda_params* p, const void* q, void* k_pages, void* v_pages,
@@ -2444,6 +2694,7 @@ extern "C" int hda_prefill(const hda_params* p, const void* q, const void* k_pag
   const int64_t R = plan_host[1], W = plan_host[3], N = plan_host[5], P = plan_host[6];
   if (R < 1 || W < 1 || N < 1 || P < 0 || plan_len != HDA_PLAN_HEADER_INTS + (W + 1) + 4 * N + R + 1)
     return HDA_ERR_BAD_PLAN;
+  if (!wg_ranges_ok(plan_host, W, N)) return HDA_ERR_BAD_PLAN;
   const int32_t unit = hda_prefill_rows_per_block(p->n_q_heads, p->n_kv_heads);
   if (unit < 1) return HDA_ERR_UNSUPPORTED;
   // every block inside its request and the packed q (the kernel trusts
@@ -2463,13 +2714,19 @@ extern "C" int hda_prefill(const hda_params* p, const void* q, const void* k_pag
                                                       p->n_kv_heads, p->head_dim, qb);
   if (ws_need < 0) return HDA_ERR_BAD_PLAN;
   if (P > 0 && (!p->workspace || p->workspace_bytes < ws_need)) return HDA_ERR_WORKSPACE;
+  // without partial slots a smaller workspace may still hold the check words
+  const bool ws_ok = p->workspace && p->workspace_bytes >= ws_need;
 
   Args a = make_args(p, q, const_cast<void*>(k_pages), const_cast<void*>(v_pages), block_table,
                      kv_lens, out, W, 0);
-  const int64_t o_bytes = ((int64_t)P * qb * p->n_q_heads * p->head_dim * 4 + 255) / 256 * 256;
-  a.part_o = static_cast<float*>(p->workspace);
-  a.part_lse = p->workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(p->workspace) + o_bytes)
-                            : nullptr;
+  // workspace: check words [W][Hkv], partial o [P][qb][Hq][D], partial lse
+  // [P][qb][Hq], each from a 256-byte boundary
+  uint8_t* ws = ws_ok ? static_cast<uint8_t*>(p->workspace) : nullptr;
+  const int64_t c_bytes = round256(W * p->n_kv_heads * 4);
+  const int64_t o_bytes = round256((int64_t)P * qb * p->n_q_heads * p->head_dim * 4);
+  a.check = ws ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  a.part_o = ws ? reinterpret_cast<float*>(ws + c_bytes) : nullptr;
+  a.part_lse = ws ? reinterpret_cast<float*>(ws + c_bytes + o_bytes) : nullptr;
   a.q_prime = nullptr;
   a.req_slots = nullptr;
   a.n_parts = (int32_t)P;

@@ -270,16 +270,58 @@ int hda_plan_validate(const int32_t* plan, int64_t plan_len,
   return HDA_OK;
 }
 
+// Launch width for a step.  W_max fills wg_per_cu resident workgroups per
+// compute unit over all kv heads (never more workgroups than tiles).  The
+// step takes about as long as its busiest workgroup, ceil(T / W) tiles, and
+// every split request costs partial slots (written by the tile kernel, read
+// by the merge) and an extra item start in each workgroup it touches; so
+// among the widths from W_max down to W_max / 2 whose busiest workgroup
+// holds no more tiles than at W_max, take the one with the fewest partial
+// slots (the widest on a tie).  For 1 x 131072 + 31 x 4096 tokens in tiles
+// of 128 over 8 kv heads this is 63 (32 tiles each: every 4096-token request
+// whole in one workgroup) rather than 64 (every request split).
+int hda_launch_config(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads, int32_t n_cu,
+                      int32_t wg_per_cu, int32_t tile_len, int32_t* n_workgroups) {
+  if (!n_workgroups || n_kv_heads < 1 || n_cu < 1 || wg_per_cu < 1 || tile_len < 1)
+    return HDA_ERR_INVALID_ARG;
+  int st = check_lens(seq_lens, batch);
+  if (st != HDA_OK) return st;
+  int64_t T = 0;
+  for (int32_t b = 0; b < batch; ++b) T += tiles_of(seq_lens[b], tile_len);
+  if (T > kI32Max) return HDA_ERR_INVALID_ARG;
+  const int64_t w_max = std::max<int64_t>(1, std::min<int64_t>(T, (int64_t)n_cu * wg_per_cu / n_kv_heads));
+  const int64_t per = (T + w_max - 1) / w_max;
+  int64_t best_w = w_max, best_p = -1;
+  for (int64_t W = w_max; W >= std::max<int64_t>(1, w_max / 2); --W) {
+    if ((T + W - 1) / W > per) break;
+    const Split sp{T / W, T % W};
+    int64_t P = 0, first = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t n = tiles_of(seq_lens[b], tile_len);
+      const int64_t k = sp.owner(first + n - 1) - sp.owner(first) + 1;
+      if (k > 1) P += k;
+      first += n;
+    }
+    if (best_p < 0 || P < best_p) {
+      best_p = P;
+      best_w = W;
+    }
+  }
+  *n_workgroups = (int32_t)best_w;
+  return HDA_OK;
+}
+
 int64_t hda_workspace_bytes(const int32_t* plan, int64_t plan_len,
                             int32_t n_q_heads, int32_t n_kv_heads,
                             int32_t head_dim) {
   if (!plan || plan_len < HDA_PLAN_HEADER_INTS || n_q_heads < 1 ||
       n_kv_heads < 1 || head_dim < 1)
     return -1;
-  if (plan[0] != HDA_PLAN_VERSION || plan[1] < 1 || plan[6] < 0) return -1;
-  const int64_t B = plan[1], P = plan[6];
-  return round_up(P * n_q_heads * head_dim * 4, 256) + round_up(P * n_q_heads * 4, 256) +
-         round_up(B * n_q_heads * head_dim * 2, 256) + round_up(B * 8, 256);
+  if (plan[0] != HDA_PLAN_VERSION || plan[1] < 1 || plan[3] < 1 || plan[6] < 0) return -1;
+  const int64_t B = plan[1], W = plan[3], P = plan[6];
+  return round_up(W * n_kv_heads * 4, 256) + round_up(P * n_q_heads * head_dim * 4, 256) +
+         round_up(P * n_q_heads * 4, 256) + round_up(B * n_q_heads * head_dim * 2, 256) +
+         round_up(B * 8, 256);
 }
 
 int32_t hda_prefill_rows_per_block(int32_t n_q_heads, int32_t n_kv_heads) {
@@ -351,10 +393,11 @@ int64_t hda_prefill_workspace_bytes(const int32_t* plan, int64_t plan_len, int32
   const int32_t unit = hda_prefill_rows_per_block(n_q_heads, n_kv_heads);
   const int32_t qb = rows_per_block;
   if (unit < 1 || qb < 1 || qb > HDA_PREFILL_MAX_TILES * unit || plan[0] != HDA_PLAN_VERSION || plan[1] < 1 ||
-      plan[6] < 0)
+      plan[3] < 1 || plan[6] < 0)
     return -1;
-  const int64_t P = plan[6];
-  return round_up(P * qb * n_q_heads * head_dim * 4, 256) + round_up(P * qb * n_q_heads * 4, 256);
+  const int64_t W = plan[3], P = plan[6];
+  return round_up(W * n_kv_heads * 4, 256) + round_up(P * qb * n_q_heads * head_dim * 4, 256) +
+         round_up(P * qb * n_q_heads * 4, 256);
 }
 
 const char* hda_status_string(int status) {

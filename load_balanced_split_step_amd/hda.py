@@ -36,14 +36,18 @@ HDA_MATH_BF16 = 0
 HDA_MATH_FP8 = 1
 HDA_V_TOKEN_MAJOR = 0
 HDA_V_DIM_MAJOR = 1
+HDA_CHECK_PAST_LEN = 1         # device check bits (hda_decode_check)
+HDA_CHECK_SHORT = 2
 HDA_PREFILL_MAX_TILES = 16
 HDA_PLAN_UPLOAD_CHUNK = 1000   # plan ints per hda_plan_upload launch
 HDA_PLAN_ARG_INTS = 896        # longest plan hda_decode takes in its launch arguments
 PLAN_HEADER_INTS = 8
 
 # every symbol include/hda.h declares
-EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_plan_static", "hda_plan_validate",
-           "hda_workspace_bytes", "hda_decode", "hda_decode_auto", "hda_workspace_bytes_bound",
+EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_launch_config", "hda_plan_static",
+           "hda_plan_validate",
+           "hda_workspace_bytes", "hda_decode", "hda_decode_coverage", "hda_decode_check",
+           "hda_decode_auto", "hda_workspace_bytes_bound",
            "hda_plan_device", "hda_plan_upload", "hda_prefill_rows_per_block", "hda_prefill_block_rows",
            "hda_prefill_rows",
            "hda_prefill_workspace_bytes", "hda_prefill", "hda_router_split_weights",
@@ -109,10 +113,14 @@ def load_library(path: Optional[str] = None):
         "hda_plan_capacity": (i64, [i32, i32]),
         "hda_plan": (ctypes.c_int, [pi32, i32, i32, i32, pi32, i64, pi64]),
         "hda_plan_static": (ctypes.c_int, [pi32, i32, i32, pi32, i64, pi64]),
+        "hda_launch_config": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, pi32]),
         "hda_plan_validate": (ctypes.c_int, [pi32, i64, pi32, i32]),
         "hda_workspace_bytes": (i64, [pi32, i64, i32, i32, i32]),
         "hda_decode": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp, pi32, vp,
                                       i64, vp, vp]),
+        "hda_decode_coverage": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp,
+                                               pi32, vp, i64, vp, vp, vp]),
+        "hda_decode_check": (ctypes.c_int, [ctypes.POINTER(hda_params), i32, pi32, vp]),
         "hda_decode_auto": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp, i32, i32,
                                            vp, vp]),
         "hda_workspace_bytes_bound": (i64, [i32, i32, i32, i32]),
@@ -232,6 +240,31 @@ def hda_decode(params: hda_params, q, k_pages, v_pages, block_table, seq_lens, p
                         plan_host.size, _ptr(out), _stream(stream))
     if st != HDA_OK:
         raise HdaError(st, "hda_decode")
+
+
+def hda_decode_coverage(params: hda_params, q, k_pages, v_pages, block_table, seq_lens, plan_host,
+                        plan_dev, out, visits, stream=None) -> None:
+    """Enqueue the coverage-counting debug form of one decode step; `visits`
+    is a zeroed device int32 tensor [num_pages * page_size * Hkv]."""
+    lib = load_library()
+    plan_host = np.ascontiguousarray(plan_host, dtype=np.int32)
+    st = lib.hda_decode_coverage(ctypes.byref(params), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                 _ptr(block_table), _ptr(seq_lens), _i32p(plan_host),
+                                 _ptr(plan_dev), plan_host.size, _ptr(out), _ptr(visits),
+                                 _stream(stream))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_decode_coverage")
+
+
+def hda_decode_check(params: hda_params, n_workgroups: int, stream=None) -> int:
+    """Device check bits (HDA_CHECK_*) the last call with this workspace
+    recorded; synchronises the stream."""
+    flags = ctypes.c_int32(0)
+    st = load_library().hda_decode_check(ctypes.byref(params), int(n_workgroups),
+                                         ctypes.byref(flags), _stream(stream))
+    if st not in (HDA_OK, HDA_ERR_PLAN_MISMATCH):
+        raise HdaError(st, "hda_decode_check")
+    return flags.value
 
 
 def hda_workspace_bytes_bound(batch: int, n_workgroups: int, n_q_heads: int, head_dim: int) -> int:
@@ -563,29 +596,74 @@ class DeviceBatch:
         return out
 
     def decode(self, plan, out=None, plan_dev=None, stream=None, k_pages=None, v_pages=None,
-               block_table=None):
+               block_table=None, seq_lens=None, upload="copy"):
+        """One decode step.  upload: "copy" (the plan copied to a device
+        tensor, or the given plan_dev), or "bench" -- the plan in the tile
+        kernel's launch arguments when it fits, else hda_plan_upload into a
+        device buffer: the path bench.py times (plan_to_device)."""
         import torch
         plan = np.ascontiguousarray(plan, dtype=np.int32)
         t = self.t
         if out is None:
             out = torch.empty((self.kw["batch"], self.kw["n_q_heads"], self.kw["head_dim"]),
                               dtype=torch.float32, device=self.device)
-        if plan_dev is None:
+        if upload == "bench":
+            if plan_dev is None:
+                plan_dev = torch.empty(plan.size, dtype=torch.int32, device=self.device)
+            plan_dev = plan_to_device(plan, plan.size, plan_dev, stream)
+        elif plan_dev is None:
             plan_dev = torch.from_numpy(plan).to(self.device)
         p = self.params(plan)
+        self.last_params = p
         hda_decode(p, t["q"], t["k_pages"] if k_pages is None else k_pages,
                    t["v_pages"] if v_pages is None else v_pages,
                    t["block_table"] if block_table is None else block_table,
-                   t["seq_lens"], plan, plan_dev, out, stream)
+                   t["seq_lens"] if seq_lens is None else seq_lens, plan, plan_dev, out, stream)
         return out
+
+    def check(self, plan, stream=None):
+        """HDA_CHECK_* bits the last decode with this batch's workspace recorded."""
+        return hda_decode_check(self.last_params, int(np.asarray(plan)[3]), stream)
+
+    def coverage(self, plan, seq_lens=None, block_table=None):
+        """(out, visits) of the coverage-counting debug step: visits int32
+        [num_pages, page_size, Hkv] on the device."""
+        import torch
+        plan = np.ascontiguousarray(plan, dtype=np.int32)
+        t = self.t
+        kw = self.kw
+        out = torch.empty((kw["batch"], kw["n_q_heads"], kw["head_dim"]), dtype=torch.float32,
+                          device=self.device)
+        visits = torch.zeros((kw["num_pages"], kw["page_size"], kw["n_kv_heads"]),
+                             dtype=torch.int32, device=self.device)
+        p = self.params(plan)
+        hda_decode_coverage(p, t["q"], t["k_pages"], t["v_pages"],
+                            t["block_table"] if block_table is None else block_table,
+                            t["seq_lens"] if seq_lens is None else seq_lens, plan,
+                            torch.from_numpy(plan).to(self.device), out, visits)
+        return out, visits
+
+
+def plan_to_device(plan_host, plan_len: int, plan_dev, stream=None):
+    """The per-step plan upload bench.py times: None when the plan fits the
+    tile kernel's launch arguments (hda_decode then carries it there), else
+    the plan stored into plan_dev by hda_plan_upload, returning plan_dev."""
+    if plan_len <= HDA_PLAN_ARG_INTS:
+        return None
+    hda_plan_upload(plan_host, plan_dev, stream, plan_len=plan_len)
+    return plan_dev
 
 
 def launch_config(seq_lens, n_kv_heads: int, n_cu: int = 256, wg_per_cu: int = 2,
                   tile_len: int = 128):
-    """Default (tile_len, n_workgroups) for a step: enough workgroups for
-    `wg_per_cu` resident 4-wave workgroups per compute unit across all kv
-    heads, never more than there are tiles."""
+    """Default (tile_len, n_workgroups) for a step (hda_launch_config: the
+    width with the fewest partial slots among those whose busiest workgroup
+    is no busier than with `wg_per_cu` resident workgroups per compute
+    unit)."""
     lens = _lens(seq_lens)
-    T = int(((lens.astype(np.int64) + tile_len - 1) // tile_len).sum())
-    W = max(1, min(T, (n_cu * wg_per_cu) // max(1, int(n_kv_heads))))
-    return tile_len, W
+    W = ctypes.c_int32(0)
+    st = load_library().hda_launch_config(_i32p(lens), len(lens), int(n_kv_heads), int(n_cu),
+                                          int(wg_per_cu), int(tile_len), ctypes.byref(W))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_launch_config")
+    return tile_len, W.value

@@ -45,7 +45,7 @@ from .attention import (
 )
 from .prologue import (rms_norm, rope, prologue_step, bf16_encode, write_new_token,
                        slot_scales)
-from .fp8_math import (quantize_q_fp8, dequantized_q, attention_fp8q,
+from .fp8_math import (quantize_q_fp8, quantize_q_residual, dequantized_q, attention_fp8q,
                        weight_rounding_bounds)
 from .prefill import prefill_reference, prefill_rows, q_offsets
 from .router import (split_router_weights, split_value, router_reference,
@@ -57,7 +57,7 @@ __all__ = [
     "gather_request", "attention_reference", "attention_selected",
     "attention_bruteforce", "split_merge_reference", "decode_kv", "row_scales",
     "SCALE_MODES", "rms_norm", "rope", "prologue_step", "bf16_encode", "write_new_token",
-    "slot_scales", "quantize_q_fp8", "dequantized_q", "attention_fp8q",
+    "slot_scales", "quantize_q_fp8", "quantize_q_residual", "dequantized_q", "attention_fp8q",
     "weight_rounding_bounds", "prefill_reference", "prefill_rows", "q_offsets",
     "split_router_weights", "split_value", "router_reference", "router_split_reference",
     "accumulation_bound",

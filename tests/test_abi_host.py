@@ -139,8 +139,11 @@ def test_workspace_bytes(lib):
     plan = hda.hda_plan(lens, 64, 4)          # P = 5
     up = lambda x: (x + 255) // 256 * 256
     q_prime = up(4 * 8 * 64 * 2) + up(4 * 8)  # prologue's q' (B x Hq x D bf16) + slot ranges
-    assert hda.hda_workspace_bytes(plan, 8, 2, 64) == up(5 * 8 * 64 * 4) + up(5 * 8 * 4) + q_prime
-    assert hda.hda_workspace_bytes(hda.hda_plan(lens, 64, 1), 8, 2, 64) == q_prime   # P = 0
+    check = up(4 * 2 * 4)                     # check words, W x Hkv int32
+    assert hda.hda_workspace_bytes(plan, 8, 2, 64) == (check + up(5 * 8 * 64 * 4) + up(5 * 8 * 4)
+                                                       + q_prime)
+    assert hda.hda_workspace_bytes(hda.hda_plan(lens, 64, 1), 8, 2, 64) == up(2 * 4) + q_prime
+    assert hda.hda_workspace_bytes(hda.hda_plan(lens, 64, 100), 8, 2, 64) > up(100 * 2 * 4)
     assert hda.hda_workspace_bytes(plan, 0, 2, 64) == -1
 
 
@@ -254,8 +257,9 @@ def test_header_constants_match_binding():
 
 def test_workspace_bound(lib):
     up = lambda x: (x + 255) // 256 * 256
-    assert hda.hda_workspace_bytes_bound(4, 8, 8, 64) == (up(11 * 8 * 64 * 4) + up(11 * 8 * 4)
-                                                          + up(4 * 8 * 64 * 2) + up(4 * 8))
+    assert hda.hda_workspace_bytes_bound(4, 8, 8, 64) == (up(8 * 8 * 4) + up(11 * 8 * 64 * 4)
+                                                          + up(11 * 8 * 4) + up(4 * 8 * 64 * 2)
+                                                          + up(4 * 8))
     assert hda.hda_workspace_bytes_bound(0, 8, 8, 64) == -1
     # the bound covers every plan over the same batch and workgroup count
     rng = np.random.default_rng(9)
@@ -372,9 +376,10 @@ def test_prefill_workspace_bytes(lib):
     plan = hda.hda_plan(row_lens, 4, 3)
     P = int(plan[6])
     assert P == 2
-    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 2) == up(P * 2 * 64 * 128 * 4) + up(P * 2 * 64 * 4)
-    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 8) == up(P * 8 * 64 * 128 * 4) + up(P * 8 * 64 * 4)
-    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 32) == up(P * 32 * 64 * 128 * 4) + up(P * 32 * 64 * 4)
+    c = up(3 * 8 * 4)                         # check words, W x Hkv int32
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 2) == c + up(P * 2 * 64 * 128 * 4) + up(P * 2 * 64 * 4)
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 8) == c + up(P * 8 * 64 * 128 * 4) + up(P * 8 * 64 * 4)
+    assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 32) == c + up(P * 32 * 64 * 128 * 4) + up(P * 32 * 64 * 4)
     assert hda.hda_prefill_workspace_bytes(plan, 64, 8, 128, 33) == -1     # above 16 x 16/g
     assert hda.hda_prefill_workspace_bytes(plan, 64, 3, 128, 2) == -1
 
@@ -409,8 +414,36 @@ def test_prefill_argument_errors(lib):
     bad = rows.copy(); bad[1, 0] = 3                                     # request out of range
     assert call(_params(**base), rows=bad) == E.HDA_ERR_INVALID_ARG
     assert call(_params(**base), plan=plan[:-1]) == E.HDA_ERR_BAD_PLAN
+    # workgroup item ranges: from 0, non-decreasing, ending at N
+    N = int(plan[5])
+    for k, v in [(8, 1), (9, N + 5), (8 + 3, N - 1)]:
+        bad = plan.copy(); bad[k] = v
+        assert call(_params(**base), plan=bad) == E.HDA_ERR_BAD_PLAN, (k, v)
     assert call(_params(**base, workspace=None)) == E.HDA_ERR_WORKSPACE
     assert call(_params(**base, workspace_bytes=64)) == E.HDA_ERR_WORKSPACE
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers are only used without a GPU")
+def test_check_and_coverage_argument_errors(lib):
+    import ctypes
+    flags = ctypes.c_int32(0)
+    chk = lambda p, W: lib.hda_decode_check(ctypes.byref(p) if p is not None else None, W,
+                                            ctypes.byref(flags), None)
+    assert chk(None, 4) == hda.HDA_ERR_INVALID_ARG
+    assert chk(_params(workspace=None), 4) == hda.HDA_ERR_INVALID_ARG
+    assert chk(_params(), 0) == hda.HDA_ERR_INVALID_ARG
+    assert chk(_params(workspace_bytes=4 * 2 * 4 - 1), 4) == hda.HDA_ERR_INVALID_ARG  # W x Hkv words
+    lens = np.array([17, 64, 200, 513], dtype=np.int32)
+    plan = hda.hda_plan(lens, 64, 4)
+    vp = ctypes.c_void_p
+
+    def cov(visits, plan_dev):
+        return lib.hda_decode_coverage(ctypes.byref(_params()), vp(FAKE), vp(FAKE + 0x1000),
+                                       vp(FAKE + 0x2000), vp(FAKE + 0x3000), vp(FAKE + 0x4000),
+                                       hda._i32p(plan), plan_dev, plan.size, vp(FAKE + 0x5000),
+                                       visits, None)
+    assert cov(None, vp(FAKE + 0x6000)) == hda.HDA_ERR_INVALID_ARG
+    assert cov(vp(FAKE + 0x7000), None) == hda.HDA_ERR_INVALID_ARG
 
 
 def test_router_workspace_bytes_shapes(lib):
@@ -480,3 +513,37 @@ def test_plan_upload_argument_errors(lib):
     assert lib.hda_plan_upload(pp, 16, vp(FAKE + 2), None) == hda.HDA_ERR_INVALID_ARG
     with pytest.raises(ValueError):
         hda.hda_plan_upload(plan, 0, plan_len=17)
+
+
+def test_launch_config(lib):
+    """hda_launch_config: on the extreme mix, 63 workgroups of 32 tiles (each
+    4096-token request whole in one workgroup, only the long request split);
+    in general the width with the fewest partial slots (counted by the
+    oracle planner) among the widths from W_max down to W_max / 2 whose
+    busiest workgroup is no busier than at W_max, the widest on a tie."""
+    import oracle
+    lens = np.array([131072] + [4096] * 31, np.int32)
+    assert hda.launch_config(lens, 8) == (128, 63)
+    assert oracle.plan_dynamic(lens.tolist(), 128, 63).n_partials == 32
+    assert oracle.plan_dynamic(lens.tolist(), 128, 64).n_partials == 94
+    rng = np.random.default_rng(12)
+    for _ in range(200):
+        B = int(rng.integers(1, 70))
+        lens = np.exp(rng.uniform(0, np.log(40000), size=B)).astype(np.int32) + 1
+        hkv = int(rng.choice([1, 2, 4, 8, 16]))
+        tl, W = hda.launch_config(lens, hkv)
+        T = int(sum(-(-int(x) // tl) for x in lens))
+        wmax = max(1, min(T, 512 // hkv))
+        per = -(-T // wmax)
+        cands = [w for w in range(wmax, max(1, wmax // 2) - 1, -1) if -(-T // w) <= per]
+        P = {w: oracle.plan_dynamic(lens.tolist(), tl, w).n_partials for w in cands}
+        best = min(P.values())
+        assert P[W] == best and W == max(w for w in cands if P[w] == best), (lens, hkv, W)
+    f = lambda *a: lib.hda_launch_config(*a)
+    import ctypes
+    out = ctypes.c_int32(0)
+    lens = np.array([5, 6], np.int32)
+    assert f(hda._i32p(lens), 2, 0, 256, 2, 128, ctypes.byref(out)) == hda.HDA_ERR_INVALID_ARG
+    assert f(hda._i32p(lens), 2, 8, 256, 2, 0, ctypes.byref(out)) == hda.HDA_ERR_INVALID_ARG
+    assert f(hda._i32p(lens), 0, 8, 256, 2, 128, ctypes.byref(out)) == hda.HDA_ERR_INVALID_ARG
+    assert f(hda._i32p(lens), 2, 8, 256, 2, 128, None) == hda.HDA_ERR_INVALID_ARG

@@ -3,13 +3,16 @@ MFMA operands, V pages dim-major).
 
 The q quantisation is deterministic and the oracle replays it exactly
 (attention_fp8q); the fp8 rounding of the softmax weights is bounded from
-the exact weights (weight_rounding_bounds).  Bar, per output element:
-|gpu - oracle| <= worst-case bound + 1e-4 (float32 accumulation and the
-matrix cores' fp8 accumulation, measured at about 2^-14 relative); and over
-all elements of a run the squared error stays within 4x the expected
-squared error.  The distance to the exact attention with an unquantised q
-is printed, not bounded here: it is the mode's own q quantisation, which
-the accuracy study measures.  Also: device-planned launches bitwise equal
+the exact weights (weight_rounding_bounds), with the accumulation error of
+the matrix cores' fp8 products (about 2^-14 of the summed magnitudes,
+measured; 2^-12 assumed) in the scores and the token sums.  Bar, per output
+element: |gpu - oracle| <= that worst-case bound + 1e-6 (float32 epilogue
+and merge); and over all elements of a run the squared error stays within
+4x the expected squared error.  The distance to the exact attention with an unquantised q
+(the plain definition over the fp8 cache, fp64) is held to the fp8-cache
+bar, 6e-2 max-abs, like every other mode: at the scaled sizes here and, for
+every output element, at the full size of the fp8 workload through the call
+path bench.py times.  Also: device-planned launches bitwise equal
 to host-planned ones, and the prologue's column write into dim-major V
 pages (attention after it within the fp8 bar of the fp64 oracle with the
 bf16 q', the q quantisation included in that bar's slack).
@@ -58,11 +61,18 @@ def all_pairs(inp):
     return [(b, h) for b in range(len(inp["seq_lens"])) for h in range(inp["workload"].n_q_heads)]
 
 
+# Accumulation error of the fp8 matrix-core products, relative to the sum of
+# the magnitudes they add (a probe measured about 2^-14; 4x margin): the
+# scores' error and the token sums' error in the bound.
+MFMA_EPS = 2.0 ** -12
+
+
 def check_against_bounds(out, inp, q_raw, pairs, label):
     q_eff = oracle.dequantized_q(q_raw)
     kw = scale_kw(inp)
     res = oracle.weight_rounding_bounds(q_eff, inp["k_pages"], inp["v_pages"], inp["block_table"],
-                                        inp["seq_lens"], "fp8", float(inp["sm_scale"]), pairs, **kw)
+                                        inp["seq_lens"], "fp8", float(inp["sm_scale"]), pairs,
+                                        score_eps=MFMA_EPS, sum_eps=MFMA_EPS, **kw)
     o = out.detach().cpu().numpy().astype(np.float64)
     assert np.isfinite(o).all()
     err2 = pred2 = 0.0
@@ -70,8 +80,8 @@ def check_against_bounds(out, inp, q_raw, pairs, label):
     for (b, h) in pairs:
         ref, worst, rms = res[(b, h)]
         e = np.abs(o[b, h] - ref)
-        assert np.all(e <= worst + 1e-4), (label, b, h, float(e.max()), float(worst.min()))
-        worst_ratio = max(worst_ratio, float((e / (worst + 1e-4)).max()))
+        assert np.all(e <= worst + 1e-6), (label, b, h, float(e.max()), float(worst.min()))
+        worst_ratio = max(worst_ratio, float((e / (worst + 1e-6)).max()))
         err2 += float((e * e).sum())
         pred2 += float((rms * rms).sum())
     print(f"{label}: max err/bound {worst_ratio:.3f}, rms err / expected "
@@ -94,6 +104,7 @@ def test_parity_native_fp8(name):
         check_against_bounds(out, inp, inp["q"], pairs, f"{name} {pname}")
         err = max_err(out, exact)
         print(f"{name} {pname}: max |diff| vs unquantised-q attention {err:.3e}", flush=True)
+        assert err <= TOL["fp8"], (name, pname, err)
 
 
 def test_native_device_plan_bitwise_equals_host_plan():
@@ -110,11 +121,12 @@ def test_native_device_plan_bitwise_equals_host_plan():
 
 def _q_prime_from_workspace(dev, plan, B, Hq, D):
     """The prologue's q' (bf16 bits [B, Hq, D]) from the workspace, at the
-    offset the header documents: after the partial outputs float32 [P][Hq][D]
-    and partial log-sum-exps float32 [P][Hq], each region 256-aligned."""
+    offset the header documents: after the check words int32 [W][Hkv], the
+    partial outputs float32 [P][Hq][D] and partial log-sum-exps float32
+    [P][Hq], each region 256-aligned."""
     r256 = lambda x: (x + 255) // 256 * 256
-    P = int(plan[6])
-    off = r256(P * Hq * D * 4) + r256(P * Hq * 4)
+    W, P = int(plan[3]), int(plan[6])
+    off = r256(W * dev.kw["n_kv_heads"] * 4) + r256(P * Hq * D * 4) + r256(P * Hq * 4)
     raw = dev._ws[off:off + B * Hq * D * 2].cpu().numpy()
     return raw.view(np.uint16).reshape(B, Hq, D)
 
@@ -153,14 +165,28 @@ def test_native_prologue_writes_dim_major_column():
     check_against_bounds(out, inp2, qk, all_pairs(inp), "native prologue")
 
 
-def test_native_full_size_sampled():
-    from tests.test_decode_gpu_full import sample_pairs
+def test_native_full_size_every_element():
+    """The fp8 workload at full size (prologue off: the mode's own check of
+    the written token is above), bench.py's launch configuration and plan
+    path: every output within 6e-2 of the plain fp64 oracle, and within the
+    weight-rounding bound on a sample of rows."""
     w = CONFIGS["fp8"].with_(prologue=False)
     inp = make_inputs(w)
     lens = inp["seq_lens"]
     dev = hda.DeviceBatch.from_inputs(inp, math="fp8")
     tl, W = hda.launch_config(lens, w.n_kv_heads)
-    out = dev.decode(hda.hda_plan(lens, tl, W))
+    plan = hda.hda_plan(lens, tl, W)
+    out = dev.decode(plan, upload="bench")
     torch.cuda.synchronize()
-    pairs = sample_pairs(lens, w.n_q_heads, w.group, seed=w.seed)
+    exact = oracle.attention_reference(oracle.bf16_to_f64(inp["q"]), inp["k_pages"], inp["v_pages"],
+                                       inp["block_table"], lens, "fp8", float(inp["sm_scale"]),
+                                       **scale_kw(inp))
+    err = max_err(out, exact)
+    print(f"fp8 full size, native: {out.numel()} outputs, max |gpu - oracle| {err:.3e}",
+          flush=True)
+    assert err <= TOL["fp8"]
+    rng = np.random.default_rng(w.seed)
+    bs = sorted({int(np.argmax(lens)), int(np.argmin(lens))} |
+                set(rng.choice(len(lens), size=6, replace=False).tolist()))
+    pairs = [(b, h) for b in bs for h in range(w.n_q_heads)]
     check_against_bounds(out, inp, inp["q"], pairs, "fp8 full size, native")

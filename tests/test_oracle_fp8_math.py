@@ -4,8 +4,9 @@ q quantisation is checked against the format (the largest element maps to
 448, every code is the nearest-even grid point, the scale is amax / 448 in
 float32) and is the identity on values already on the scaled fp8 grid.  The
 weight-rounding bound is checked against a simulation of the rounding the
-method performs (weights of 64-token chunks rounded to E4M3 against the
-running maximum, online rescaling, normalisation by the rounded weights),
+method performs (weights of 64-token chunks kept as an E4M3 value plus an
+E4M3 residual against the running maximum, online rescaling, normalisation
+by the rounded weights),
 for flat and sharply peaked score distributions; an understated bound is
 planted and must fail.
 """
@@ -39,12 +40,41 @@ def test_quantize_q_format():
     assert np.all(np.abs(dec - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal])
 
 
+def test_quantize_q_residual_format():
+    """The residual codes are the nearest-even E4M3 grid points of
+    16 (x - decode(hi)); the split hi + lo/16 lies within 2^-8 |x| + 2^-14 of
+    x (E4M3's relative rounding 2^-4 taken twice, plus the residual's
+    subnormal floor 2^-10 / 16), eight times closer than hi alone; planted
+    mistakes in the residual's scale (dropped, applied twice) break the
+    bound."""
+    rng = np.random.default_rng(3)
+    q = (rng.standard_normal((6, 5, 128)) * rng.uniform(1e-3, 50, size=(6, 5, 1))).astype(np.float32)
+    q[0, 0, :7] = [0.0, 1e-9, -3e-7, 2.0 ** -20, 5e-5, -1e-4, 3e-3]   # subnormal residuals
+    hi, s_q = fm.quantize_q_fp8(q)
+    lo = fm.quantize_q_residual(q)
+    x = np.clip((q / s_q[..., None]).astype(np.float32), -448, 448).astype(np.float64)
+    r16 = 16.0 * (x - fp8_decode(hi))
+    assert np.abs(r16).max() <= 256.0                        # inside E4M3's range
+    dec = fp8_decode(lo)
+    up = fp8_decode(np.where(lo & 0x7F < 0x7E, lo + 1, lo).astype(np.uint8))
+    dn = fp8_decode(np.where(lo & 0x7F > 0, lo - 1, lo).astype(np.uint8))
+    assert np.all(np.abs(dec - r16) <= np.abs(up - r16)) and np.all(np.abs(dec - r16) <= np.abs(dn - r16))
+    bound = 2.0 ** -8 * np.abs(x) + 2.0 ** -14
+    eff = fp8_decode(hi) + dec / 16.0
+    assert np.all(np.abs(eff - x) <= bound)
+    assert np.abs(eff - x).max() <= np.abs(fp8_decode(hi) - x).max() / 8
+    for bad in (fp8_decode(hi) + dec, fp8_decode(hi) + dec / 256.0):      # planted
+        assert not np.all(np.abs(bad - x) <= bound)
+    np.testing.assert_array_equal(fm.dequantized_q(q), eff * s_q.astype(np.float64)[..., None])
+
+
 def test_quantize_q_zero_row():
     q = np.zeros((1, 2, 64), np.float32)
     q[0, 1, 3] = -2.5
     codes, s_q = fm.quantize_q_fp8(q)
     assert s_q[0, 0] == 1.0 and not codes[0, 0].any()
     assert codes[0, 1, 3] == 0xFE and s_q[0, 1] == np.float32(2.5) / np.float32(448)
+    assert not fm.quantize_q_residual(q).any()
 
 
 def test_quantization_is_identity_on_the_grid():
@@ -60,6 +90,7 @@ def test_quantization_is_identity_on_the_grid():
     q = (fp8_decode(c) * 2.0 ** -3).astype(np.float32)
     codes, s_q = fm.quantize_q_fp8(q)
     assert np.all(s_q == np.float32(0.125)) and np.array_equal(codes, c)
+    assert not fm.quantize_q_residual(q).any()               # nothing left for the residual
     args = (inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"], "fp8",
             float(inp["sm_scale"]))
     kw = dict(k_scale=float(inp["k_scale"]), v_scale=float(inp["v_scale"]))
@@ -69,8 +100,9 @@ def test_quantization_is_identity_on_the_grid():
 
 
 def _simulate(s, v, chunk=64):
-    """Online softmax over chunks with each chunk's weights rounded to E4M3
-    (p * 2^8) against the running maximum; returns o'."""
+    """Online softmax over chunks with each chunk's weights z = p * 2^8,
+    against the running maximum, kept as E4M3(z) plus E4M3 of the residual;
+    returns o'."""
     m = -np.inf
     acc = np.zeros(v.shape[1])
     l = 0.0
@@ -78,7 +110,9 @@ def _simulate(s, v, chunk=64):
         sc = s[c0:c0 + chunk]
         m_new = max(m, sc.max())
         alpha = np.exp(m - m_new) if np.isfinite(m) else 0.0
-        p8 = fp8_decode(fp8_encode(np.exp(sc - m_new) * 256.0)) / 256.0
+        z = np.exp(sc - m_new) * 256.0
+        a = fp8_decode(fp8_encode(z))
+        p8 = (a + fp8_decode(fp8_encode(z - a))) / 256.0
         acc = acc * alpha + p8 @ v[c0:c0 + chunk]
         l = l * alpha + p8.sum()
         m = m_new
@@ -109,7 +143,7 @@ def _bound(s, v, u):
 def test_bound_holds_under_simulated_rounding():
     err2, pred2 = 0.0, 0.0
     for s, v in _cases():
-        o, worst, rms = _bound(s, v, fm.U_E4M3)
+        o, worst, rms = _bound(s, v, fm.U_WEIGHTS)
         e = np.abs(_simulate(s, v) - o)
         assert np.all(e <= worst + 1e-15), float((e / worst).max())
         err2 += float((e * e).sum())
@@ -135,10 +169,23 @@ def test_bound_matches_oracle_function():
         assert np.all(worst > 0) and np.all(rms > 0) and np.all(rms <= worst)
 
 
+def test_weight_split_error():
+    """z = p 2^8 kept as a = E4M3(z) plus b = E4M3(z - a): within 2^-8 z +
+    2^-10 of z over [0, 256] (sixteen times tighter than a alone in the
+    normal range); dropping the residual breaks that bound."""
+    z = np.concatenate([np.linspace(0, 256, 200001), np.exp(np.linspace(-30, np.log(256), 5001))])
+    a = fp8_decode(fp8_encode(z))
+    ab = a + fp8_decode(fp8_encode(z - a))
+    assert np.all(np.abs(ab - z) <= 2.0 ** -8 * z + 2.0 ** -10)
+    assert not np.all(np.abs(a - z) <= 2.0 ** -8 * z + 2.0 ** -10)         # planted: no residual
+    normal = z >= 2.0 ** -6
+    assert np.abs(ab - z)[normal].max() * 16 <= np.abs(a - z)[normal].max()
+
+
 def test_planted_understated_bound_is_caught():
     caught = False
     for s, v in _cases():
-        o, worst, _ = _bound(s, v, 2.0 ** -7)
+        o, worst, _ = _bound(s, v, 2.0 ** -11)
         if np.any(np.abs(_simulate(s, v) - o) > worst):
             caught = True
     assert caught
