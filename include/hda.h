@@ -26,7 +26,8 @@
  *   - Every function that can fail returns an int status (HDA_OK = 0, errors
  *     negative).  No C++ exception crosses this boundary.
  *   - All memory is owned by the caller.  The library allocates no device
- *     memory and never synchronises the stream.
+ *     memory and never synchronises the stream (hda_decode_check, a debug
+ *     aid, does).
  *   - Host pointers are marked [host], device pointers [device].  Device
  *     pointers must stay valid until the work enqueued on the stream ends.
  *   - Functions are reentrant; there is no global mutable state.
@@ -145,15 +146,16 @@ int hda_plan(const int32_t* seq_lens, int32_t batch, int32_t tile_len,
 
 /*
  * A launch width for hda_plan: *n_workgroups = W for tiles of tile_len over
- * seq_lens [host] int32[batch] (each >= 1).  W_max is the width that keeps
- * wg_per_cu 4-wave workgroups resident on each of n_cu compute units over
- * all n_kv_heads (at most the tile count); among the widths from W_max down
- * to W_max / 2 whose busiest workgroup holds no more tiles than at W_max,
- * the one with the fewest partial slots, the widest on a tie.  (The pages
- * size the tiles and their assignment to the current workload: remio.ai
- * page, section "Por qué Tencent HPC importa para el serving de modelos en
- * línea"; the width rule is this library's.)  Cost O(batch x W_max).
- * Errors: HDA_ERR_INVALID_ARG.
+ * seq_lens [host] int32[batch] (each >= 1), at most W_max = the width that
+ * puts wg_per_cu workgroups on each of n_cu compute units over all
+ * n_kv_heads (and at most the tile count).  The step lasts about as long as
+ * its busiest unit, which holds ceil(W Hkv / n_cu) workgroups of
+ * ceil(T / W) tiles; among the widths whose busiest unit holds at most 1/32
+ * more tiles than the least possible, the one with the fewest partial
+ * slots, then the widest.  (The pages size the tiles and their assignment
+ * to the current workload: remio.ai page, section "Por qué Tencent HPC
+ * importa para el serving de modelos en línea"; the width rule is this
+ * library's.)  Cost O(batch x W_max).  Errors: HDA_ERR_INVALID_ARG.
  */
 int hda_launch_config(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads, int32_t n_cu,
                       int32_t wg_per_cu, int32_t tile_len, int32_t* n_workgroups);

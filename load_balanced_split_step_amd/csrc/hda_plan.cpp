@@ -270,16 +270,18 @@ int hda_plan_validate(const int32_t* plan, int64_t plan_len,
   return HDA_OK;
 }
 
-// Launch width for a step.  W_max fills wg_per_cu resident workgroups per
-// compute unit over all kv heads (never more workgroups than tiles).  The
-// step takes about as long as its busiest workgroup, ceil(T / W) tiles, and
-// every split request costs partial slots (written by the tile kernel, read
-// by the merge) and an extra item start in each workgroup it touches; so
-// among the widths from W_max down to W_max / 2 whose busiest workgroup
-// holds no more tiles than at W_max, take the one with the fewest partial
-// slots (the widest on a tie).  For 1 x 131072 + 31 x 4096 tokens in tiles
-// of 128 over 8 kv heads this is 63 (32 tiles each: every 4096-token request
-// whole in one workgroup) rather than 64 (every request split).
+// Launch width for a step.  The tile kernel streams K/V, so a step lasts
+// about as long as its busiest compute unit: with W x Hkv workgroups spread
+// over n_cu units (at most wg_per_cu each), that unit holds
+// ceil(W Hkv / n_cu) workgroups of ceil(T / W) tiles.  A width between one
+// and two workgroups per unit leaves some units with two and the others
+// with one, and the step waits for the doubly loaded ones (measured: 1 x
+// 131072 + 31 x 4096 tokens in tiles of 128 over 8 kv heads takes 161 us at
+// W = 32 or 63, 220 us at W = 40).  So: the widths with the fewest tiles on
+// the busiest unit, within 1/32 of the least; among them the fewest partial
+// slots (each costs a write by the tile kernel and a read by the merge, and
+// P = 0 skips the merge); then the widest.  Extreme mix: 63 (one split
+// request); 32 x 4096 tokens: 32 (one request per workgroup, no merge).
 int hda_launch_config(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads, int32_t n_cu,
                       int32_t wg_per_cu, int32_t tile_len, int32_t* n_workgroups) {
   if (!n_workgroups || n_kv_heads < 1 || n_cu < 1 || wg_per_cu < 1 || tile_len < 1)
@@ -289,11 +291,16 @@ int hda_launch_config(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads
   int64_t T = 0;
   for (int32_t b = 0; b < batch; ++b) T += tiles_of(seq_lens[b], tile_len);
   if (T > kI32Max) return HDA_ERR_INVALID_ARG;
-  const int64_t w_max = std::max<int64_t>(1, std::min<int64_t>(T, (int64_t)n_cu * wg_per_cu / n_kv_heads));
-  const int64_t per = (T + w_max - 1) / w_max;
-  int64_t best_w = w_max, best_p = -1;
-  for (int64_t W = w_max; W >= std::max<int64_t>(1, w_max / 2); --W) {
-    if ((T + W - 1) / W > per) break;
+  const int64_t w_max =
+      std::max<int64_t>(1, std::min<int64_t>(T, (int64_t)n_cu * wg_per_cu / n_kv_heads));
+  auto unit_tiles = [&](int64_t W) {
+    return ((W * n_kv_heads + n_cu - 1) / n_cu) * ((T + W - 1) / W);
+  };
+  int64_t least = unit_tiles(w_max);
+  for (int64_t W = w_max - 1; W >= 1; --W) least = std::min(least, unit_tiles(W));
+  int64_t best_w = -1, best_p = -1;
+  for (int64_t W = w_max; W >= 1; --W) {
+    if (unit_tiles(W) * 32 > least * 33) continue;
     const Split sp{T / W, T % W};
     int64_t P = 0, first = 0;
     for (int32_t b = 0; b < batch; ++b) {

@@ -46,7 +46,8 @@ PLAN_HEADER_INTS = 8
 # every symbol include/hda.h declares
 EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_launch_config", "hda_plan_static",
            "hda_plan_validate",
-           "hda_workspace_bytes", "hda_decode", "hda_decode_coverage", "hda_decode_check",
+           "hda_workspace_bytes", "hda_decode", "hda_decode_coverage",
+           "hda_decode_check",
            "hda_decode_auto", "hda_workspace_bytes_bound",
            "hda_plan_device", "hda_plan_upload", "hda_prefill_rows_per_block", "hda_prefill_block_rows",
            "hda_prefill_rows",
@@ -657,9 +658,8 @@ def plan_to_device(plan_host, plan_len: int, plan_dev, stream=None):
 def launch_config(seq_lens, n_kv_heads: int, n_cu: int = 256, wg_per_cu: int = 2,
                   tile_len: int = 128):
     """Default (tile_len, n_workgroups) for a step (hda_launch_config: the
-    width with the fewest partial slots among those whose busiest workgroup
-    is no busier than with `wg_per_cu` resident workgroups per compute
-    unit)."""
+    fewest tiles on the busiest compute unit, up to `wg_per_cu` workgroups
+    per unit, then the fewest partial slots)."""
     lens = _lens(seq_lens)
     W = ctypes.c_int32(0)
     st = load_library().hda_launch_config(_i32p(lens), len(lens), int(n_kv_heads), int(n_cu),

@@ -516,16 +516,19 @@ def test_plan_upload_argument_errors(lib):
 
 
 def test_launch_config(lib):
-    """hda_launch_config: on the extreme mix, 63 workgroups of 32 tiles (each
-    4096-token request whole in one workgroup, only the long request split);
-    in general the width with the fewest partial slots (counted by the
-    oracle planner) among the widths from W_max down to W_max / 2 whose
-    busiest workgroup is no busier than at W_max, the widest on a tie."""
+    """hda_launch_config: on the extreme mix, 63 workgroups (only the long
+    request split); on the uniform mix 32 (one request per workgroup, no
+    partial slots); in general, by brute force with the oracle planner's
+    partial-slot count: the widest of the widths with the fewest partial
+    slots among those whose busiest compute unit (ceil(W Hkv / 256)
+    workgroups of ceil(T / W) tiles) holds at most 1/32 more tiles than the
+    least possible."""
     import oracle
     lens = np.array([131072] + [4096] * 31, np.int32)
     assert hda.launch_config(lens, 8) == (128, 63)
     assert oracle.plan_dynamic(lens.tolist(), 128, 63).n_partials == 32
-    assert oracle.plan_dynamic(lens.tolist(), 128, 64).n_partials == 94
+    assert hda.launch_config(np.full(32, 4096, np.int32), 8) == (128, 32)
+    assert oracle.plan_dynamic([4096] * 32, 128, 32).n_partials == 0
     rng = np.random.default_rng(12)
     for _ in range(200):
         B = int(rng.integers(1, 70))
@@ -534,8 +537,9 @@ def test_launch_config(lib):
         tl, W = hda.launch_config(lens, hkv)
         T = int(sum(-(-int(x) // tl) for x in lens))
         wmax = max(1, min(T, 512 // hkv))
-        per = -(-T // wmax)
-        cands = [w for w in range(wmax, max(1, wmax // 2) - 1, -1) if -(-T // w) <= per]
+        unit = {w: -(-w * hkv // 256) * -(-T // w) for w in range(1, wmax + 1)}
+        least = min(unit.values())
+        cands = [w for w in unit if unit[w] * 32 <= least * 33]
         P = {w: oracle.plan_dynamic(lens.tolist(), tl, w).n_partials for w in cands}
         best = min(P.values())
         assert P[W] == best and W == max(w for w in cands if P[w] == best), (lens, hkv, W)

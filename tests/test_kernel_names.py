@@ -28,8 +28,9 @@ def _nm(path):
     return [line.split()[-1] for line in out.splitlines() if line.split()]
 
 
-def _device_kernels(fatbin, tmp):
-    names = set()
+def _device_symbols(fatbin, tmp):
+    """(kernel names, all symbol names) of the gfx950 code objects."""
+    names, syms = set(), set()
     for start in range(0, len(fatbin), 8):
         if not fatbin.startswith(MAGIC, start):
             continue
@@ -45,8 +46,10 @@ def _device_kernels(fatbin, tmp):
                 co = os.path.join(tmp, f"co_{start}.o")
                 with open(co, "wb") as f:
                     f.write(fatbin[start + off:start + off + size])
-                names |= {s[:-3] for s in _nm(co) if s.endswith(".kd")}
-    return names
+                all_syms = _nm(co)
+                names |= {s[:-3] for s in all_syms if s.endswith(".kd")}
+                syms |= set(all_syms)
+    return names, syms
 
 
 @pytest.mark.skipif(not (shutil.which("nm") and shutil.which("objcopy")),
@@ -59,8 +62,9 @@ def test_host_kernel_handles_have_device_kernels():
         subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fb}", LIB, os.path.join(tmp, "x")],
                        check=True, capture_output=True)
         with open(fb, "rb") as f:
-            dev = _device_kernels(f.read(), tmp)
-    host = {s for s in _nm(LIB) if s.startswith("_Z") and "_kernel" in s and "__device_stub__" not in s}
+            dev, dev_syms = _device_symbols(f.read(), tmp)
+    host_syms = _nm(LIB)
+    host = {s for s in host_syms if s.startswith("_Z") and "_kernel" in s and "__device_stub__" not in s}
     assert dev, "no gfx950 kernels found in the library"
     assert host, "no kernel handles found in the library"
     missing = sorted(host - dev)
