@@ -25,12 +25,15 @@
  * Conventions
  *   - Every function that can fail returns an int status (HDA_OK = 0, errors
  *     negative).  No C++ exception crosses this boundary.
- *   - All memory is owned by the caller.  The library allocates no device
- *     memory and never synchronises the stream (hda_decode_check, a debug
- *     aid, does).
+ *   - All memory is owned by the caller, except hda_decode_noalloc's
+ *     workspace (a fixed array in the library's device code).  The library
+ *     allocates no device memory and never synchronises the stream
+ *     (hda_decode_check, a debug aid, does).
  *   - Host pointers are marked [host], device pointers [device].  Device
  *     pointers must stay valid until the work enqueued on the stream ends.
- *   - Functions are reentrant; there is no global mutable state.
+ *   - Functions are reentrant; the only global state is the per-device
+ *     address of hda_decode_noalloc's workspace array, set once per device
+ *     under a lock.
  */
 #ifndef HDA_H
 #define HDA_H
@@ -294,6 +297,32 @@ int hda_decode(const hda_params* p, const void* q, void* k_pages,
                const int32_t* seq_lens, const int32_t* plan_host,
                const int32_t* plan_dev, int64_t plan_len, float* out,
                void* stream);
+
+/* Workspace bytes available to hda_decode_noalloc (16 MiB). */
+#define HDA_NOALLOC_WORKSPACE_BYTES 16777216
+
+/*
+ * hda_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels and results, with the workspace taken from an array the
+ * library keeps in device memory -- HDA_NOALLOC_WORKSPACE_BYTES on every GPU
+ * it runs on, held until the process ends -- instead of p->workspace and
+ * p->workspace_bytes, which are ignored.  The caller still passes every
+ * input and output.  A plan whose hda_workspace_bytes exceeds that size
+ * returns HDA_ERR_WORKSPACE before any launch.  Every call on one GPU shares
+ * its array, which keeps the last call's contents (nothing in it needs to
+ * start at zero): calls that overlap on one GPU -- on different streams, or
+ * from threads without ordering -- race; order them on one stream.  The
+ * device check words go to that array and hda_decode_check cannot read
+ * them.  `stream` must belong to the current device (else
+ * HDA_ERR_INVALID_ARG); the first call on each device looks up the array's
+ * address (HDA_ERR_HIP if that fails).  Allocates nothing, on the device or
+ * in any library it calls.  Other arguments and errors as hda_decode.
+ */
+int hda_decode_noalloc(const hda_params* p, const void* q, void* k_pages, void* v_pages,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* plan_host, const int32_t* plan_dev, int64_t plan_len,
+                       float* out, void* stream);
 
 /*
  * Debug form of hda_decode (plan in device memory, plan_dev not NULL) that

@@ -31,6 +31,7 @@
 // products.
 #include <hip/hip_runtime.h>
 #include <float.h>
+#include <mutex>
 #include <type_traits>
 #include <math.h>
 #include <stdint.h>
@@ -2608,6 +2609,62 @@ extern "C" int hda_decode(const hda_params* p, const void* q, void* k_pages, voi
                           const int32_t* plan_host, const int32_t* plan_dev, int64_t plan_len,
                           float* out, void* stream) {
   return decode_step(p, q, k_pages, v_pages, block_table, seq_lens, plan_host, plan_dev,
+                     plan_len, out, stream, nullptr);
+}
+
+// ---- the same step for callers that cannot allocate device memory ----
+//
+// Its workspace is this array: one copy on every GPU the library runs on,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory; its device address on the current GPU comes
+// from hipGetSymbolAddress, looked up on the first call on each device and
+// kept.  Nothing in it needs to start at zero: every region a launch reads
+// is written earlier in the same step (check words by each tile workgroup,
+// partials by the tile kernel before the merge, q' by the prologue).
+namespace {
+
+constexpr int64_t kScratchBytes = HDA_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (stream must run there).
+int scratch_address(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return HDA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return HDA_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return HDA_ERR_HIP;
+    if (sdev != dev) return HDA_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HDA_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return HDA_OK;
+}
+
+}  // namespace
+
+extern "C" int hda_decode_noalloc(const hda_params* p, const void* q, void* k_pages,
+                                  void* v_pages, const int32_t* block_table,
+                                  const int32_t* seq_lens, const int32_t* plan_host,
+                                  const int32_t* plan_dev, int64_t plan_len, float* out,
+                                  void* stream) {
+  if (!p) return HDA_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  const int st = scratch_address(static_cast<hipStream_t>(stream), &ws);
+  if (st != HDA_OK) return st;
+  hda_params local = *p;
+  local.workspace = ws;
+  local.workspace_bytes = kScratchBytes;   // a larger plan: HDA_ERR_WORKSPACE
+  return decode_step(&local, q, k_pages, v_pages, block_table, seq_lens, plan_host, plan_dev,
                      plan_len, out, stream, nullptr);
 }
 

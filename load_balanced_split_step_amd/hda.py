@@ -36,6 +36,7 @@ HDA_MATH_BF16 = 0
 HDA_MATH_FP8 = 1
 HDA_V_TOKEN_MAJOR = 0
 HDA_V_DIM_MAJOR = 1
+HDA_NOALLOC_WORKSPACE_BYTES = 16777216   # hda_decode_noalloc's own workspace
 HDA_CHECK_PAST_LEN = 1         # device check bits (hda_decode_check)
 HDA_CHECK_SHORT = 2
 HDA_PREFILL_MAX_TILES = 16
@@ -46,7 +47,7 @@ PLAN_HEADER_INTS = 8
 # every symbol include/hda.h declares
 EXPORTS = ("hda_plan_capacity", "hda_plan", "hda_launch_config", "hda_plan_static",
            "hda_plan_validate",
-           "hda_workspace_bytes", "hda_decode", "hda_decode_coverage",
+           "hda_workspace_bytes", "hda_decode", "hda_decode_noalloc", "hda_decode_coverage",
            "hda_decode_check",
            "hda_decode_auto", "hda_workspace_bytes_bound",
            "hda_plan_device", "hda_plan_upload", "hda_prefill_rows_per_block", "hda_prefill_block_rows",
@@ -119,6 +120,8 @@ def load_library(path: Optional[str] = None):
         "hda_workspace_bytes": (i64, [pi32, i64, i32, i32, i32]),
         "hda_decode": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp, pi32, vp,
                                       i64, vp, vp]),
+        "hda_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp,
+                                              pi32, vp, i64, vp, vp]),
         "hda_decode_coverage": (ctypes.c_int, [ctypes.POINTER(hda_params), vp, vp, vp, vp, vp,
                                                pi32, vp, i64, vp, vp, vp]),
         "hda_decode_check": (ctypes.c_int, [ctypes.POINTER(hda_params), i32, pi32, vp]),
@@ -241,6 +244,19 @@ def hda_decode(params: hda_params, q, k_pages, v_pages, block_table, seq_lens, p
                         plan_host.size, _ptr(out), _stream(stream))
     if st != HDA_OK:
         raise HdaError(st, "hda_decode")
+
+
+def hda_decode_noalloc(params: hda_params, q, k_pages, v_pages, block_table, seq_lens, plan_host,
+                       plan_dev, out, stream=None) -> None:
+    """Enqueue one decode step with the library's own device workspace
+    (params.workspace is ignored; see include/hda.h)."""
+    lib = load_library()
+    plan_host = np.ascontiguousarray(plan_host, dtype=np.int32)
+    st = lib.hda_decode_noalloc(ctypes.byref(params), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                _ptr(block_table), _ptr(seq_lens), _i32p(plan_host),
+                                _ptr(plan_dev), plan_host.size, _ptr(out), _stream(stream))
+    if st != HDA_OK:
+        raise HdaError(st, "hda_decode_noalloc")
 
 
 def hda_decode_coverage(params: hda_params, q, k_pages, v_pages, block_table, seq_lens, plan_host,

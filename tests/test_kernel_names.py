@@ -7,7 +7,8 @@ gets a compiler-made name that can differ between the two, and the runtime
 then finds no device function for the host's handle and aborts at the first
 launch.  This reads the host's kernel handles from the library's symbol
 table and the device kernels (their .kd descriptors) from the offload
-bundles in its .hip_fatbin section, and compares the two sets.
+bundles in its .hip_fatbin section, and compares the two sets; likewise the
+device array hda_decode_noalloc finds through its host stand-in.
 """
 
 import os
@@ -65,6 +66,9 @@ def test_host_kernel_handles_have_device_kernels():
             dev, dev_syms = _device_symbols(f.read(), tmp)
     host_syms = _nm(LIB)
     host = {s for s in host_syms if s.startswith("_Z") and "_kernel" in s and "__device_stub__" not in s}
+    # the device array hda_decode_noalloc looks up by its host stand-in
+    scratch = [s for s in host_syms if s.endswith("7scratchE")]
+    assert len(scratch) == 1 and scratch[0] in dev_syms, scratch
     assert dev, "no gfx950 kernels found in the library"
     assert host, "no kernel handles found in the library"
     missing = sorted(host - dev)
