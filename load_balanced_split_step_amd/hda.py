@@ -107,6 +107,14 @@ def load_library(path: Optional[str] = None):
     path = path or LIB_PATH
     if not os.path.exists(path):
         raise OSError(f"libhda.so not found at {path}; run __graft_entry__.build()")
+    # torch ships its own HIP runtime; loaded first, it also serves
+    # libhda.so's libamdhip64 dependency.  Loaded after libhda.so, it would be
+    # a second runtime in the process, and launches on torch's streams
+    # would fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     pi32 = ctypes.POINTER(ctypes.c_int32)

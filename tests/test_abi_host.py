@@ -551,3 +551,16 @@ def test_launch_config(lib):
     assert f(hda._i32p(lens), 2, 8, 256, 2, 0, ctypes.byref(out)) == hda.HDA_ERR_INVALID_ARG
     assert f(hda._i32p(lens), 0, 8, 256, 2, 128, ctypes.byref(out)) == hda.HDA_ERR_INVALID_ARG
     assert f(hda._i32p(lens), 2, 8, 256, 2, 128, None) == hda.HDA_ERR_INVALID_ARG
+
+
+def test_one_hip_runtime_in_process():
+    """Loading libhda.so through the binding leaves one HIP runtime mapped
+    (torch's): the binding imports torch before it opens the library."""
+    import subprocess
+    import sys
+    code = ("import load_balanced_split_step_amd.hda as h; h.load_library(); "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'amdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout.strip()
+    libs = eval(out)
+    assert len(libs) == 1, libs
