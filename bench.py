@@ -444,7 +444,7 @@ def bench_router(args):
     from load_balanced_split_step_amd.workloads import ROUTER_CONFIGS, make_router_inputs
     w = ROUTER_CONFIGS["router"]
     E, H = w.experts, w.hidden
-    Ts = [1, 16, 64, 256, 1024, 4096, 16384]
+    Ts = [1, 4, 8, 16, 64, 256, 1024, 4096, 16384]
     big = make_router_inputs(w, tokens=max(Ts))
     rw = hda.RouterWeights(big["w"])
     wf = torch.from_numpy(big["w"]).cuda()

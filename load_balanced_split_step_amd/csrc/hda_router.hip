@@ -10,7 +10,7 @@
 //   out[t][e] = sum_h x[t][h] hi[e][h] + (sum_h x[t][h] lo[e][h]) / 256
 // with fp32 accumulation on v_mfma_f32_16x16x32_bf16.
 //
-// Tiling (small batches).  A workgroup owns TM tokens (32 or 64) x 64 experts and a range of
+// Tiling (9 to a few hundred tokens).  A workgroup owns TM tokens (32 or 64) x 64 experts and a range of
 // the hidden dimension; its 4 waves take interleaved 32-wide K steps of that
 // range, each holding the full TM x 64 tile for both products (2 x TM/16 x 4
 // MFMA blocks), and combine through LDS at the end.  The activation fragment
@@ -286,6 +286,107 @@ __global__ __launch_bounds__(64 * kBigWaves, 1) void hda_router_gemm_lds_kernel(
       }
 }
 
+// Small token counts (T <= 8): one launch, no hidden split and no second
+// kernel.  Workgroup b computes out[t][EPW b + j] for every token t < T and
+// its EPW experts over the whole hidden dimension: thread tid takes the
+// 8-element vectors tid, tid + 256, ..., loading each vector of x (every
+// token) and of both weight parts once, all of a batch's loads issued
+// before its arithmetic; both products accumulate in float32 per thread,
+// then a butterfly within each wave and the four waves in order
+// (deterministic).  Matrix cores would need 16-expert tiles, i.e. 16
+// workgroups streaming 0.46 MB each at hidden 7168; here the weights spread
+// over E / EPW workgroups (256 at EPW 1: 28 KB each) and x comes from L2.
+// Rows past T or E and vectors past H read as zero through the buffer range
+// checks.
+constexpr int kGemvThreads = 256;
+constexpr int kGemvBatch = 4;          // vectors per thread in flight
+
+__device__ inline void bf16x8_to_f32(const bf16x8& v, float (&f)[8]) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __uint_as_float(u[q] << 16);
+    f[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
+  }
+}
+
+template <int TT, int EPW>
+__global__ __launch_bounds__(kGemvThreads) void hda_router_gemv_kernel(RouterArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e0 = blockIdx.x * EPW;
+  const int nv = a.H / 8;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (int64_t)a.T * a.H * 2);
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.w_hi, (int64_t)a.E * a.H * 2);
+  const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.w_lo, (int64_t)a.E * a.H * 2);
+  constexpr int kOut = 0x7ffffff0;     // an offset past every range: reads zero
+  float ah[TT][EPW], al[TT][EPW];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) ah[t][j] = al[t][j] = 0.f;
+  for (int v0 = 0; v0 < nv; v0 += kGemvThreads * kGemvBatch) {
+    bf16x8 xv[kGemvBatch][TT], hv[kGemvBatch][EPW], lv[kGemvBatch][EPW];
+#pragma unroll
+    for (int u = 0; u < kGemvBatch; ++u) {
+      const int v = v0 + tid + kGemvThreads * u;
+      const bool in = v < nv;
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+        xv[u][t] = load8(xr, in ? ((int64_t)t * a.H + 8 * v) * 2 : kOut);
+#pragma unroll
+      for (int j = 0; j < EPW; ++j) {
+        const int64_t off = in ? ((int64_t)(e0 + j) * a.H + 8 * v) * 2 : kOut;
+        hv[u][j] = load8(hr, off);
+        lv[u][j] = load8(lr, off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGemvBatch; ++u) {
+      float wh[EPW][8], wl[EPW][8];
+#pragma unroll
+      for (int j = 0; j < EPW; ++j) {
+        bf16x8_to_f32(hv[u][j], wh[j]);
+        bf16x8_to_f32(lv[u][j], wl[j]);
+      }
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        float xf[8];
+        bf16x8_to_f32(xv[u][t], xf);
+#pragma unroll
+        for (int j = 0; j < EPW; ++j)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            ah[t][j] = __builtin_fmaf(xf[k], wh[j][k], ah[t][j]);
+            al[t][j] = __builtin_fmaf(xf[k], wl[j][k], al[t][j]);
+          }
+      }
+    }
+  }
+  __shared__ float red[4][TT * EPW][2];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
+      float h = ah[t][j], l = al[t][j];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        h += __shfl_xor(h, o);
+        l += __shfl_xor(l, o);
+      }
+      if (lane == 0) {
+        red[wave][t * EPW + j][0] = h;
+        red[wave][t * EPW + j][1] = l;
+      }
+    }
+  __syncthreads();
+  if (tid < TT * EPW) {
+    const int t = tid / EPW, e = e0 + tid % EPW;
+    const float h = (red[0][tid][0] + red[1][tid][0]) + (red[2][tid][0] + red[3][tid][0]);
+    const float l = (red[0][tid][1] + red[1][tid][1]) + (red[2][tid][1] + red[3][tid][1]);
+    if (t < a.T && e < a.E) a.out[(int64_t)t * a.E + e] = h + l * kResidualScale;
+  }
+}
+
 // Sum of the S partial tiles, in slot order.  The loads of a batch of
 // kBatch partials are all issued before any is added (one memory round trip
 // per batch instead of one per partial); the additions keep slot order.
@@ -329,7 +430,11 @@ __global__ __launch_bounds__(256) void hda_router_split_kernel(const float* __re
 struct RouterShape {
   int mb, tiles_t, tiles_e, S, k_per_wg;
   bool big;   // the LDS-staged 128 x 128 kernel
+  int gemv;   // > 0: the one-launch small-batch kernel for up to this many tokens
 };
+
+// Token counts up to this take the one-launch kernel (no hidden split).
+constexpr int kGemvMaxT = 8;
 
 // The LDS-staged 128 x 128 kernel takes a batch when its tiles, split along
 // the hidden dimension into ranges of at least 4 LDS stages (256 of K),
@@ -346,7 +451,12 @@ constexpr int kBigMinStages = 4;      // K per workgroup >= 4 stages (256)
 constexpr int64_t kSmallTargetGroups = 256;
 
 RouterShape router_shape(int32_t T, int32_t E, int32_t H) {
-  RouterShape r;
+  RouterShape r{};
+  if (T <= kGemvMaxT) {
+    r.gemv = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+    r.S = 1;
+    return r;
+  }
   const int64_t big_tiles = (int64_t)((T + kBigM - 1) / kBigM) * ((E + kBigN - 1) / kBigN);
   const int64_t max_split = H % kBigK ? 0 : H / (kBigK * kBigMinStages);
   if (max_split >= 1 && big_tiles * max_split >= kBigMinGroups) {
@@ -420,6 +530,15 @@ extern "C" int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo
   a.H = hidden;
   a.k_per_wg = r.k_per_wg;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (r.gemv) {
+    const dim3 g((unsigned)experts);
+    const dim3 b(kGemvThreads);
+    if (r.gemv == 1) hipLaunchKernelGGL((hda_router_gemv_kernel<1, 1>), g, b, 0, hs, a);
+    else if (r.gemv == 2) hipLaunchKernelGGL((hda_router_gemv_kernel<2, 1>), g, b, 0, hs, a);
+    else if (r.gemv == 4) hipLaunchKernelGGL((hda_router_gemv_kernel<4, 1>), g, b, 0, hs, a);
+    else hipLaunchKernelGGL((hda_router_gemv_kernel<8, 1>), g, b, 0, hs, a);
+    return hipGetLastError() == hipSuccess ? HDA_OK : HDA_ERR_HIP;
+  }
   const dim3 grid(r.tiles_t, r.tiles_e, r.S);
   if (r.big)
     hipLaunchKernelGGL(hda_router_gemm_lds_kernel, grid, dim3(64 * kBigWaves), 0, hs, a);

@@ -43,7 +43,11 @@ def test_split_bit_exact():
 # (with 13, 4, 1 and 1 hidden splits; 16300 x 300 with ragged token and
 # expert edges); 4096 x 2080 has a hidden size the 64-wide K stages do not
 # divide and runs on the register kernel
-SHAPES = [(1, 256, 7168), (5, 24, 96), (16, 256, 7168), (33, 100, 7168), (64, 256, 7168),
+# up to 8 tokens: the one-launch kernel (whole hidden dimension per
+# workgroup, one expert each), also with ragged expert counts and hidden sizes
+# that leave a partial last batch of vectors
+SHAPES = [(1, 256, 7168), (2, 256, 7168), (3, 300, 1024), (5, 24, 96), (7, 5, 7200),
+          (8, 256, 7168), (8, 256, 8192 + 2048), (16, 256, 7168), (33, 100, 7168), (64, 256, 7168),
           (100, 256, 7168), (257, 72, 1024), (600, 256, 7168), (1280, 256, 7168),
           (4096, 256, 7168), (16384, 256, 7168), (16300, 300, 1024),
           (4096, 256, 2080)]   # hidden % 64 == 32: a large batch on the register kernel
