@@ -124,11 +124,18 @@ extern "C" {
  * Upper bound on the plan length for `batch` requests over `n_workgroups`
  * workgroups: 8 + (W+1) + 4(W+B-1) + (B+1).  Also bounds a static plan with
  * n_workgroups = batch * n_splits.  Returns -1 for non-positive arguments.
+ * (The plan is the per-step tile assignment of the remio.ai page, section
+ * "Por qué Tencent HPC importa para el serving de modelos en línea".)
  */
 int64_t hda_plan_capacity(int32_t batch, int32_t n_workgroups);
 
 /*
- * Per-step tile plan.  Tiles of `tile_len` tokens are taken request-major
+ * Per-step tile plan: the planner the remio.ai page describes (section "Por
+ * qué Tencent HPC importa para el serving de modelos en línea": each
+ * request's KV work cut into uniform tiles and assigned to thread blocks by
+ * the current workload, rebuilt as lengths change; arex-research page,
+ * Dynamic Attention paragraphs: tiles allocated every decode step by the
+ * actual KV length).  Tiles of `tile_len` tokens are taken request-major
  * (tile j of request b covers [j*tile_len, min((j+1)*tile_len, len_b)));
  * the T tiles are split contiguously over the W workgroups, the first
  * (T mod W) taking one extra; consecutive tiles of one request within a
@@ -164,7 +171,10 @@ int hda_launch_config(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads
                       int32_t wg_per_cu, int32_t tile_len, int32_t* n_workgroups);
 
 /*
- * Static split baseline in the same format: request b is cut into n_splits
+ * Static split baseline -- the fixed split-KV schedule the pages compare
+ * against (remio.ai page, same section: a static split leaves units idle or
+ * launches empty chunks; "vLLM × HPC-Ops" summary: fixed split-KV
+ * scheduling) -- in the same format: request b is cut into n_splits
  * chunks [floor(c*len_b/S), floor((c+1)*len_b/S)), chunk c handled by
  * workgroup b*S + c (W = B*S); empty chunks leave their workgroup without an
  * item.  This is the fixed split-KV schedule the dynamic plan is compared to.
@@ -174,7 +184,9 @@ int hda_plan_static(const int32_t* seq_lens, int32_t batch, int32_t n_splits,
                     int32_t* plan, int64_t capacity, int64_t* plan_len);
 
 /*
- * Checks a plan against the lengths it will be used with: format and total
+ * Checks a plan (the tile assignment of the remio.ai page's planner, section
+ * "Por qué Tencent HPC importa para el serving de modelos en línea")
+ * against the lengths it will be used with: format and total
  * length, wg_ptr monotone, items in range and covering each [0, len_b)
  * exactly once in token order, slot numbering, and (for a dynamic plan) the
  * tile count.  [host] pointers.  Returns HDA_OK, HDA_ERR_INVALID_ARG,
@@ -202,6 +214,11 @@ int64_t hda_workspace_bytes(const int32_t* plan, int64_t plan_len,
                             int32_t n_q_heads, int32_t n_kv_heads,
                             int32_t head_dim);
 
+/* Shapes, dtypes, scales, prologue inputs and workspace of a step: the
+ * inputs the pages' attention backend takes from the serving framework's KV
+ * cache (remio.ai page, section "Lo que la afirmación de un 48,8 % de TPOT
+ * no demuestra": head dims, cache layout, quantisation scales, RoPE and
+ * normalisation are per-model parameters). */
 typedef struct hda_params {
   int32_t batch;              /* B, must equal the plan's batch */
   int32_t n_q_heads;          /* Hq; Hq / Hkv (the group) in 1..16 */
@@ -248,7 +265,13 @@ typedef struct hda_params {
 #define HDA_PLAN_ARG_INTS 896
 
 /*
- * One decode step enqueued on `stream`: the optional new-token prologue
+ * One decode step -- the pages' "Dynamic Attention": single-token decode
+ * attention over the paged KV cache by the per-step tile plan, per-item
+ * partial softmax results merged by log-sum-exp (remio.ai page, section "Por
+ * qué Tencent HPC importa para el serving de modelos en línea";
+ * arex-research page, Dynamic Attention paragraphs; the fused RoPE +
+ * QK-Norm + KV-write prologue of the "vLLM × HPC-Ops" summary) -- enqueued
+ * on `stream`: the optional new-token prologue
  * kernel (RMSNorm + RoPE of q and k, k/v stored to slot len-1, all fused in
  * one kernel), the tile attention kernel, then the log-sum-exp merge of
  * split requests (only when the plan has partial slots).  Asynchronous; no
@@ -573,7 +596,8 @@ int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo, int32_t t
 int hda_read_probe(const void* buf, int64_t bytes, int32_t n_workgroups, uint32_t* sink,
                    void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code (this library's error convention;
+ * the pages define none). */
 const char* hda_status_string(int status);
 
 /* HDA_VERSION of the built library. */

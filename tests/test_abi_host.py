@@ -64,8 +64,11 @@ def test_static_plan_bit_exact(lib, cfg, S):
 
 
 def test_plan_fuzz_bit_exact(lib):
+    """10^4 random cases: the C++ planners and the oracle planners agree int
+    for int (dynamic plans over random tile lengths and widths, static plans
+    over random split counts), and every C++ plan validates."""
     rng = np.random.default_rng(1234)
-    for _ in range(3000):
+    for _ in range(10000):
         B = int(rng.integers(1, 48))
         hi = int(rng.choice([3, 40, 700, 9000]))
         lens = rng.integers(1, hi + 1, size=B).astype(np.int32)
@@ -78,6 +81,7 @@ def test_plan_fuzz_bit_exact(lib):
             got = hda.hda_plan_static(lens, S)
             want = plan_static(lens.tolist(), S).to_list()
         assert got.tolist() == want
+        assert hda.hda_plan_validate(got, lens) == hda.HDA_OK
         assert hda.hda_plan_validate(got, lens) == hda.HDA_OK
 
 

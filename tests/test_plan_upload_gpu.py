@@ -50,7 +50,7 @@ def test_upload_host_buffer_reusable():
 
 
 @pytest.mark.parametrize("cfg,tile_len,W", [("tiny", 64, 8), ("uniform", 128, 64),
-                                            ("extreme", 128, 64)])
+                                            ("extreme", 128, 64), ("extreme", 128, 63)])
 def test_decode_with_uploaded_plan_bitwise(cfg, tile_len, W):
     inp = make_inputs(CONFIGS[cfg])
     dev = hda.DeviceBatch.from_inputs(inp, device="cuda:0")
@@ -63,6 +63,11 @@ def test_decode_with_uploaded_plan_bitwise(cfg, tile_len, W):
     torch.cuda.synchronize()
     assert np.array_equal(uploaded.cpu().numpy(), plan)
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    if plan.size <= hda.HDA_PLAN_ARG_INTS:
+        # the plan in the tile kernel's launch arguments (the bench's path)
+        c = _decode_plan_in_args(dev, plan)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int32), c.view(torch.int32))
     print(f"{cfg}: {plan.size} plan ints, outputs bitwise equal", flush=True)
 
 
