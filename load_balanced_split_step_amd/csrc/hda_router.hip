@@ -298,8 +298,7 @@ __global__ __launch_bounds__(64 * kBigWaves, 1) void hda_router_gemm_lds_kernel(
 // over E / EPW workgroups (256 at EPW 1: 28 KB each) and x comes from L2.
 // Rows past T or E and vectors past H read as zero through the buffer range
 // checks.
-constexpr int kGemvThreads = 256;
-constexpr int kGemvBatch = 4;          // vectors per thread in flight
+constexpr int kGemvThreadsDefault = 256;
 
 __device__ inline void bf16x8_to_f32(const bf16x8& v, float (&f)[8]) {
   const u32x4 u = __builtin_bit_cast(u32x4, v);
@@ -310,8 +309,10 @@ __device__ inline void bf16x8_to_f32(const bf16x8& v, float (&f)[8]) {
   }
 }
 
-template <int TT, int EPW>
+template <int TT, int EPW, int kGemvThreads = kGemvThreadsDefault>
 __global__ __launch_bounds__(kGemvThreads) void hda_router_gemv_kernel(RouterArgs a) {
+  constexpr int kGemvBatch = 1024 / kGemvThreads;   // vectors per thread in flight
+  constexpr int kWv = kGemvThreads / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e0 = blockIdx.x * EPW;
   const int nv = a.H / 8;
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(kGemvThreads) void hda_router_gemv_kernel(RouterArg
       }
     }
   }
-  __shared__ float red[4][TT * EPW][2];
+  __shared__ float red[kWv][TT * EPW][2];
 #pragma unroll
   for (int t = 0; t < TT; ++t)
 #pragma unroll
@@ -381,8 +382,12 @@ __global__ __launch_bounds__(kGemvThreads) void hda_router_gemv_kernel(RouterArg
   __syncthreads();
   if (tid < TT * EPW) {
     const int t = tid / EPW, e = e0 + tid % EPW;
-    const float h = (red[0][tid][0] + red[1][tid][0]) + (red[2][tid][0] + red[3][tid][0]);
-    const float l = (red[0][tid][1] + red[1][tid][1]) + (red[2][tid][1] + red[3][tid][1]);
+    float h = red[0][tid][0], l = red[0][tid][1];
+#pragma unroll
+    for (int ww = 1; ww < kWv; ++ww) {
+      h += red[ww][tid][0];
+      l += red[ww][tid][1];
+    }
     if (t < a.T && e < a.E) a.out[(int64_t)t * a.E + e] = h + l * kResidualScale;
   }
 }
@@ -532,7 +537,7 @@ extern "C" int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (r.gemv) {
     const dim3 g((unsigned)experts);
-    const dim3 b(kGemvThreads);
+    const dim3 b(kGemvThreadsDefault);
     if (r.gemv == 1) hipLaunchKernelGGL((hda_router_gemv_kernel<1, 1>), g, b, 0, hs, a);
     else if (r.gemv == 2) hipLaunchKernelGGL((hda_router_gemv_kernel<2, 1>), g, b, 0, hs, a);
     else if (r.gemv == 4) hipLaunchKernelGGL((hda_router_gemv_kernel<4, 1>), g, b, 0, hs, a);
