@@ -246,3 +246,23 @@ def test_continuous_batching_membership_changes():
             print(f"step {s} members {members} ({upload}): max err {err:.3e}", flush=True)
             assert err <= TOL["bf16"]
             assert hda.hda_decode_check(p, int(plan[3])) == 0
+
+
+def test_prefill_stale_lengths_report_past_len():
+    """hda_prefill with device cache lengths shorter than the ones its row
+    blocks were planned for: no token at or past a device length is scored
+    (outputs stay finite: the rows past each length hold NaN), and the check
+    words report HDA_CHECK_PAST_LEN; at the planned lengths they are clear."""
+    w = Workload("pf_stale", 4, 16, 2, 128, 32, seed=87)
+    inp = make_inputs(w, lengths=[700, 1500, 96, 3000], q_lens=[5, 40, 17, 64])
+    dev = hda.DeviceBatch.from_inputs(inp)
+    rows, plan = dev.prefill_plan(inp["q_lens"])
+    dev.prefill(rows, plan)
+    p = dev.prefill_params(plan)
+    assert hda.hda_decode_check(p, int(plan[3])) == 0
+    shorter = (inp["seq_lens"] - np.array([3, 0, 20, 1], np.int32)).astype(np.int32)
+    dev.t["seq_lens"].copy_(torch.from_numpy(shorter))
+    out = dev.prefill(rows, plan)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert hda.hda_decode_check(p, int(plan[3])) == hda.HDA_CHECK_PAST_LEN
