@@ -1495,6 +1495,8 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
   using SS = SharedStage<D, SUB>;
   constexpr int DPL = D / 16, STEPS = D / 32;
   constexpr int HALVES = 2 * SUB;
+  // sixteen waves of one tile: K and V fragments read half at a time
+  constexpr bool kHalves = NW == 16 && !PAGE;
   const int i = lane & 15, kg = lane >> 4;
   const int g = a.group;
   const int unit = kMaxGroup / g;                    // rows per tile
@@ -1578,7 +1580,25 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
       const float jks[2] = {cks[2 * j], cks[2 * j + 1]}, jvs[2] = {cvs[2 * j], cvs[2 * j + 1]};
       f32x4 sacc[TPW][2];
       bf16x8 pop[TPW];
-      {
+      if constexpr (kHalves) {
+        // fragments half by half (the register budget of four waves per
+        // SIMD): K for 16 tokens, then their products
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          bf16x8 kh[STEPS];
+#pragma unroll
+          for (int s2 = 0; s2 < STEPS; ++s2)
+            kh[s2] = *reinterpret_cast<const bf16x8*>(
+                ss.k + SS::k_off(kChunk * j + 16 * hf + i, 4 * s2 + kg));
+#pragma unroll
+          for (int t = 0; t < TPW; ++t) {
+            sacc[t][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < STEPS; ++s2)
+              sacc[t][hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[s2], qop[t][s2], sacc[t][hf], 0, 0, 0);
+          }
+        }
+      } else {
         bf16x8 kf[2][STEPS];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -1602,6 +1622,26 @@ __device__ inline void process_item_shared(const Args& a, const int32_t* __restr
                                                         acc[t]);
           }
         }
+      }
+      if constexpr (kHalves) {
+        // the softmax, then V and its products half by half (dims blocks
+        // 0..DPL/2-1, then the rest)
+        softmax_tiles<D, TPW>(sacc, c, k0, k1, lim, lim_min, qk, kg, m_run, l_acc, acc, pop);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          bf16x8 vh[DPL / 2];
+#pragma unroll
+          for (int nb = 0; nb < DPL / 2; ++nb)
+            vh[nb] = *reinterpret_cast<const bf16x8*>(ss.vt[j] + 1024 * (nb + DPL / 2 * h2) +
+                                                       256 * kg + 16 * i);
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int nb = 0; nb < DPL / 2; ++nb)
+              acc[t][nb + DPL / 2 * h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  vh[nb], pop[t], acc[t][nb + DPL / 2 * h2], 0, 0, 0);
+        }
+        continue;
       }
       bf16x8 vf[DPL];
 #pragma unroll
@@ -2356,7 +2396,11 @@ template <int D, bool FP8, bool PAGE>
 hipError_t launch_prefill(Args a, int grid, int n_rows, hipStream_t stream, void* split_event) {
   // by the largest block, in tiles of 16/g rows: one tile on the decode
   // kernel's column shape (the waves split the item's chunks), else chunks
-  // shared through LDS by 4 waves of one tile, 8 waves of one, or 8 of two
+  // shared through LDS by 4 waves of one tile, 8 waves of one, or for the
+  // largest blocks 8 waves of two -- 16 waves of one for an fp8 cache
+  // without per-page factors, whose stage stores decode the codes (the
+  // extra waves hide that work: 641 -> 607 us on the chunked fp8 mix; 602 ->
+  // 631 us for bf16, which keeps 8 x 2)
   const int unit = kMaxGroup / a.group;
   const dim3 blk(64 * kWaves);
   if (a.qb <= unit)
@@ -2368,6 +2412,9 @@ hipError_t launch_prefill(Args a, int grid, int n_rows, hipStream_t stream, void
   else if (a.qb <= 8 * unit)
     hipLaunchKernelGGL((hda_prefill_shared_kernel<D, FP8, PAGE, 8, 1>), dim3(grid), dim3(512), 0,
                        stream, a, a.block_table, a.seq_lens, a.plan);
+  else if constexpr (FP8 && !PAGE)
+    hipLaunchKernelGGL((hda_prefill_shared_kernel<D, FP8, PAGE, 16, 1>), dim3(grid), dim3(1024),
+                       0, stream, a, a.block_table, a.seq_lens, a.plan);
   else
     hipLaunchKernelGGL((hda_prefill_shared_kernel<D, FP8, PAGE, 8, 2>), dim3(grid), dim3(512), 0,
                        stream, a, a.block_table, a.seq_lens, a.plan);
