@@ -1,7 +1,9 @@
 """GPU parity of multi-token attention (hda_prefill) against the fp64 oracle.
 
 Row blocks of 1, 2, 4, 8 or 16 tiles of 16 / group query rows (the column
-kernel and the three LDS-shared shapes) go through the decode tile planner;
+kernel and the LDS-shared shapes: 4 waves of one tile, 8 of one, 8 of two,
+and 16 of one over an fp8 cache without per-page factors) go through the
+decode tile planner;
 every block of an item loads its next stage while multiplying the current
 one, the last stage of an item the next item's first; checked element by
 element at
@@ -63,7 +65,7 @@ CASES = {
 
 @pytest.mark.parametrize("tiles", [1, 2, 4, 8, 16],
                          ids=["1tile-columns", "2tiles-lds4", "4tiles-lds4", "8tiles-lds8",
-                              "16tiles-lds8x2"])
+                              "16tiles-lds8x2-fp8-16x1"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_prefill_parity(name, tiles):
     """Blocks of 1 tile of 16/g rows (decode column shape), or of 2 to 16
