@@ -587,7 +587,7 @@ int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo, int32_t t
  * attention roofline a measured ceiling next to the published 8 TB/s.  One
  * kernel on `stream` reads buf [device] (16-byte aligned; bytes a multiple
  * of 16) once with the attention kernels' access pattern -- each wave a
- * contiguous region, 16-byte non-temporal loads, eight in flight per lane --
+ * contiguous region, 16-byte non-temporal loads, sixteen in flight per lane --
  * over n_workgroups workgroups of 256 threads, and writes to sink [device]
  * uint32[n_workgroups * 256] the XOR of the words each thread read (their
  * XOR is the XOR of the whole buffer).  The caller times it.  Asynchronous.
