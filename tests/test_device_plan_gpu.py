@@ -134,3 +134,53 @@ def test_graph_replay_of_device_planned_step():
         torch.cuda.synchronize()
         assert torch.equal(out_g, eager), step
         print(f"graph replay {step} (lengths +{grow}): equal to eager", flush=True)
+
+
+@pytest.mark.parametrize("cfg", ["uniform", "fp8"])
+def test_decode_auto_empty_slots(cfg):
+    """Batch slots left empty between steps (device length 0) get no item:
+    their output rows are not written (they keep what the buffer held), the
+    prologue writes no new token for them (their pages keep every byte), and
+    the other requests equal the oracle over the requests that have tokens."""
+    import oracle
+    from oracle.prologue import prologue_step, write_new_token
+    lens_full = np.array([700, 300, 1500, 90, 2100, 40], dtype=np.int32)
+    empty = np.array([False, True, False, True, False, False])
+    w = CONFIGS[cfg].with_(name=f"empty_{cfg}", batch=6, lengths=None, len_range=None)
+    inp = make_inputs(w, lengths=lens_full)
+    dev = hda.DeviceBatch.from_inputs(inp)
+    lens = np.where(empty, 0, lens_full).astype(np.int32)
+    dev.t["seq_lens"].copy_(torch.from_numpy(lens))
+    ps = int(inp["k_pages"].shape[2])
+    k_before = dev.t["k_pages"].clone()
+    v_before = dev.t["v_pages"].clone()
+    sentinel = 12345.0
+    out = torch.full((6, w.n_q_heads, w.head_dim), sentinel, dtype=torch.float32, device="cuda:0")
+    dev.decode_auto(64, 9, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[empty] == sentinel)
+    sel = ~empty
+    bt = inp["block_table"][sel]
+    kp, vp = inp["k_pages"], inp["v_pages"]
+    if w.prologue:
+        q_p, _, _, kc, vc = prologue_step(inp["q"][sel], inp["k_new"][sel], inp["v_new"][sel],
+                                          inp["q_norm_w"], inp["k_norm_w"], lens[sel],
+                                          float(inp["rms_eps"]), float(inp["rope_theta"]),
+                                          w.kv_dtype, float(inp["k_scale"]), float(inp["v_scale"]))
+        kp, vp = write_new_token(kp, vp, bt, lens[sel], kc, vc)
+    else:
+        q_p = oracle.bf16_to_f64(inp["q"][sel])
+    ref = oracle.attention_reference(q_p, kp, vp, bt, lens[sel], w.kv_dtype,
+                                     float(inp["sm_scale"]), float(inp["k_scale"]),
+                                     float(inp["v_scale"]))
+    err = float(np.abs(got[sel] - ref).max())
+    print(f"{cfg}: empty slots untouched, others max err {err:.3e}", flush=True)
+    assert err <= TOL[w.kv_dtype]
+    # the empty requests' pages hold the bytes they held before the step
+    page_bytes = k_before.numel() // int(inp["k_pages"].shape[0])
+    for b in np.flatnonzero(empty):
+        for pg in inp["block_table"][b][:(int(lens_full[b]) + ps - 1) // ps]:
+            s = slice(int(pg) * page_bytes, (int(pg) + 1) * page_bytes)
+            assert torch.equal(dev.t["k_pages"][s], k_before[s]), (b, int(pg))
+            assert torch.equal(dev.t["v_pages"][s], v_before[s]), (b, int(pg))
