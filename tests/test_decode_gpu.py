@@ -222,3 +222,28 @@ def test_growth_over_steps():
         err = max_err(out, ref)
         print(f"growth step {s}: max err {err:.3e}", flush=True)
         assert err <= TOL["fp8"]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_merge_of_more_split_requests_than_the_launch_list(kv):
+    """More than 256 split requests: the host's per-request slot list (the
+    merge's launch arguments hold at most 256) gives way to the merge over
+    every request with the plan's slot ranges; outputs at the oracle's values
+    and bitwise equal from one run to the next."""
+    rng = np.random.default_rng(91)
+    lens = rng.integers(65, 400, size=320).astype(np.int32)
+    w = Workload("many_split", 320, 16, 2, 128, 16, kv_dtype=kv, seed=91)
+    inp = make_inputs(w, lengths=lens)
+    plan = hda.hda_plan(lens, 32, 800)
+    rpp = plan[hda.PLAN_HEADER_INTS + 801 + 4 * int(plan[5]):]
+    n_split = int(np.count_nonzero(np.diff(rpp) > 0))
+    assert n_split > 256, n_split
+    ref = oracle_out(inp)
+    dev = hda.DeviceBatch.from_inputs(inp)
+    a = dev.decode(plan)
+    b = dev.decode(plan)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    err = max_err(a, ref)
+    print(f"{kv}: {n_split} split requests, max err {err:.3e}", flush=True)
+    assert err <= TOL[kv]
