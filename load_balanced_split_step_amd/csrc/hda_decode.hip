@@ -31,6 +31,7 @@
 // products.
 #include <hip/hip_runtime.h>
 #include <float.h>
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 #include <math.h>
@@ -2117,7 +2118,7 @@ __global__ __launch_bounds__(D) void hda_merge_kernel(Args a, const int32_t* __r
 // measured latency-bound on multi-token batches: 2.2x slower.)
 constexpr int kMergeRowsThreads = 256;
 
-template <int D>
+template <int D, int E>
 __global__ __launch_bounds__(kMergeRowsThreads) void hda_merge_rows_kernel(
     Args a, const int32_t* __restrict__ plan) {
   constexpr int Q = D / 4;                           // float4 columns per head
@@ -2125,7 +2126,9 @@ __global__ __launch_bounds__(kMergeRowsThreads) void hda_merge_rows_kernel(
   constexpr int NWV = kMergeRowsThreads / 64;        // waves
   constexpr int HPV = (HPW + NWV - 1) / NWV;         // heads per wave in the weight pass
   constexpr int U = 8;                               // slots in flight past the first E
-  constexpr int E = 16;                              // slots loaded before the weights
+  // E: slots loaded before the weights (the launch picks the smallest of 2,
+  // 4, 8, 16 that holds the plan's largest slot count, up to 16: the loads
+  // are clamped, not branched, so every early load is issued)
   __shared__ float sM[HPW], sInv[HPW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Hq = a.n_q_heads;
@@ -2393,7 +2396,8 @@ hipError_t launch(Args a, int grid, bool prologue, uint16_t* q_prime, hipStream_
 static_assert(HDA_PREFILL_MAX_TILES == 16, "largest block: 8 waves of two tiles");
 
 template <int D, bool FP8, bool PAGE>
-hipError_t launch_prefill(Args a, int grid, int n_rows, hipStream_t stream, void* split_event) {
+hipError_t launch_prefill(Args a, int grid, int n_rows, int max_slots, hipStream_t stream,
+                          void* split_event) {
   // by the largest block, in tiles of 16/g rows: one tile on the decode
   // kernel's column shape (the waves split the item's chunks), else chunks
   // shared through LDS by 4 waves of one tile, 8 waves of one, or for the
@@ -2426,17 +2430,25 @@ hipError_t launch_prefill(Args a, int grid, int n_rows, hipStream_t stream, void
   }
   if (a.n_parts == 0) return e;
   const int groups = (a.n_q_heads + kMergeRowsThreads / (D / 4) - 1) / (kMergeRowsThreads / (D / 4));
-  hipLaunchKernelGGL((hda_merge_rows_kernel<D>), dim3(n_rows * a.qb * groups),
-                     dim3(kMergeRowsThreads), 0, stream, a, a.plan);
+  const dim3 mgrid(n_rows * a.qb * groups), mblk(kMergeRowsThreads);
+  if (max_slots <= 2)
+    hipLaunchKernelGGL((hda_merge_rows_kernel<D, 2>), mgrid, mblk, 0, stream, a, a.plan);
+  else if (max_slots <= 4)
+    hipLaunchKernelGGL((hda_merge_rows_kernel<D, 4>), mgrid, mblk, 0, stream, a, a.plan);
+  else if (max_slots <= 8)
+    hipLaunchKernelGGL((hda_merge_rows_kernel<D, 8>), mgrid, mblk, 0, stream, a, a.plan);
+  else
+    hipLaunchKernelGGL((hda_merge_rows_kernel<D, 16>), mgrid, mblk, 0, stream, a, a.plan);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_prefill_d(const Args& a, bool fp8, int grid, int n_rows, hipStream_t st,
-                            void* ev) {
-  if (!fp8) return launch_prefill<D, false, false>(a, grid, n_rows, st, ev);
-  return a.scale_mode == HDA_SCALE_PAGE ? launch_prefill<D, true, true>(a, grid, n_rows, st, ev)
-                                        : launch_prefill<D, true, false>(a, grid, n_rows, st, ev);
+hipError_t launch_prefill_d(const Args& a, bool fp8, int grid, int n_rows, int max_slots,
+                            hipStream_t st, void* ev) {
+  if (!fp8) return launch_prefill<D, false, false>(a, grid, n_rows, max_slots, st, ev);
+  return a.scale_mode == HDA_SCALE_PAGE
+             ? launch_prefill<D, true, true>(a, grid, n_rows, max_slots, st, ev)
+             : launch_prefill<D, true, false>(a, grid, n_rows, max_slots, st, ev);
 }
 
 // Per-page scales are built for the fp8 cache only (check_params refuses
@@ -2842,9 +2854,17 @@ extern "C" int hda_prefill(const hda_params* p, const void* q, const void* k_pag
   a.tile_len = plan_host[2];
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool fp8 = p->kv_dtype == HDA_KV_FP8_E4M3;
+  // the largest slot count of a block (the merge's early loads)
+  int max_slots = 0;
+  {
+    const int32_t* rpp = plan_host + HDA_PLAN_HEADER_INTS + (W + 1) + 4 * N;
+    for (int64_t r = 0; r < R; ++r) max_slots = std::max(max_slots, rpp[r + 1] - rpp[r]);
+  }
   hipError_t e = p->head_dim == 64
-                     ? launch_prefill_d<64>(a, fp8, (int)grid, (int)R, hs, p->split_event)
-                     : launch_prefill_d<128>(a, fp8, (int)grid, (int)R, hs, p->split_event);
+                     ? launch_prefill_d<64>(a, fp8, (int)grid, (int)R, max_slots, hs,
+                                            p->split_event)
+                     : launch_prefill_d<128>(a, fp8, (int)grid, (int)R, max_slots, hs,
+                                             p->split_event);
   return e == hipSuccess ? HDA_OK : HDA_ERR_HIP;
 }
 
