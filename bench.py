@@ -541,7 +541,7 @@ def bench_router(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "bench.py times one GPU: --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

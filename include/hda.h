@@ -52,7 +52,7 @@ extern "C" {
 #define HDA_OK 0
 #define HDA_ERR_INVALID_ARG (-1)   /* null pointer, non-positive size, bad length */
 #define HDA_ERR_CAPACITY (-2)      /* plan buffer too small; *plan_len = ints needed */
-#define HDA_ERR_UNSUPPORTED (-3)   /* shape or dtype this build has no kernel for */
+#define HDA_ERR_UNSUPPORTED (-3)   /* shape or dtype the library has no kernel for */
 #define HDA_ERR_PLAN_MISMATCH (-4) /* plan built for another batch / other lengths */
 #define HDA_ERR_HIP (-5)           /* a HIP launch or runtime call failed */
 #define HDA_ERR_WORKSPACE (-6)     /* workspace missing or smaller than required */
@@ -603,7 +603,7 @@ const char* hda_status_string(int status);
 /* HDA_VERSION of the built library. */
 int hda_version(void);
 
-/* sizeof(hda_params) in this build, for bindings that lay the struct out
+/* sizeof(hda_params) as the library was compiled, for bindings that lay the struct out
  * themselves. */
 int64_t hda_params_bytes(void);
 
