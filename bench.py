@@ -498,7 +498,7 @@ def bench_router(args):
                "speedup_vs_fp32": round(res["torch_fp32"] / res["ours"], 2),
                "tflops": round(flops / (res["ours"] * 1e-6) / 1e12, 1), "bound": bound,
                "achieved": round(ach, 1), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
-               "hidden_splits": ws // (4 * T * E) if ws else 1}
+               "workspace_bytes": ws}
         sweep.append(row)
         log(f"router T={T}: {res['ours']:.1f} us ({row['tflops']} TFLOP/s, {bound} {row['frac']:.3f}), "
             f"torch fp32 {res['torch_fp32']:.1f} us")

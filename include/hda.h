@@ -570,11 +570,15 @@ int64_t hda_router_workspace_bytes(int32_t tokens, int32_t experts, int32_t hidd
  *   w_hi,
  *   w_lo   [device] bf16 [experts][hidden] from hda_router_split_weights
  * hidden must be a multiple of 32; tokens x hidden and experts x hidden
- * below 2^30.  The workspace (hda_router_workspace_bytes) holds partial
- * tiles when the hidden dimension is split across workgroups; partials are
- * added in a fixed order, so results do not vary between runs.
- * Asynchronous on `stream`.  Errors: HDA_ERR_INVALID_ARG,
- * HDA_ERR_UNSUPPORTED, HDA_ERR_WORKSPACE, HDA_ERR_HIP.
+ * below 2^30.  The workspace (hda_router_workspace_bytes; [device],
+ * 16-byte aligned, any content -- nothing needs clearing) holds partial
+ * tiles when the hidden dimension is split across workgroups, and for 9 to
+ * 64 tokens one arrival counter per output tile as well: the last
+ * workgroup of a tile to finish adds its partials, so the call is one
+ * launch.  Partials are added in a fixed (slot) order, so results do not
+ * vary between runs.  Calls that overlap in time on one workspace race.
+ * Asynchronous on `stream`.  Errors: HDA_ERR_INVALID_ARG (also a workspace
+ * not 16-byte aligned), HDA_ERR_UNSUPPORTED, HDA_ERR_WORKSPACE, HDA_ERR_HIP.
  */
 int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo, int32_t tokens,
                     int32_t experts, int32_t hidden, float* out, void* workspace,

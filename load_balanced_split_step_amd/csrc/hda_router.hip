@@ -10,8 +10,10 @@
 //   out[t][e] = sum_h x[t][h] hi[e][h] + (sum_h x[t][h] lo[e][h]) / 256
 // with fp32 accumulation on v_mfma_f32_16x16x32_bf16.
 //
-// Tiling (9 to a few hundred tokens).  A workgroup owns TM tokens (32 or 64) x 64 experts and a range of
-// the hidden dimension; its 4 waves take interleaved 32-wide K steps of that
+// Tiling (65 to a few hundred tokens; 9 to 64 take the one-launch split
+// kernel further down, fewer the one-workgroup-per-expert kernel, more the
+// LDS-staged kernel).  A workgroup owns TM tokens (32 or 64) x 64 experts
+// and a range of the hidden dimension; its 4 waves take interleaved 32-wide K steps of that
 // range, each holding the full TM x 64 tile for both products (2 x TM/16 x 4
 // MFMA blocks), and combine through LDS at the end.  The activation fragment
 // of a K step is loaded once and feeds both products.  When the token and
@@ -22,6 +24,7 @@
 // buffer range checks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
 
 #include "hda.h"
 
@@ -392,6 +395,159 @@ __global__ __launch_bounds__(kGemvThreads) void hda_router_gemv_kernel(RouterArg
   }
 }
 
+// Decode-sized batches (9 to 64 tokens) in one launch.  A workgroup owns
+// TM = 16 MB tokens x 16 experts (one MFMA block wide) and a range of the
+// hidden dimension: with 16-expert tiles, 16 ranges give 256 workgroups at
+// 256 experts, each streaming 28 KB of weights.  Its 4 waves take
+// interleaved 32-wide K steps of the range, every load of a group of NS
+// steps issued before the group's first MFMA (steps past the range read
+// zeros through the range checks), and combine through LDS.  With S > 1
+// ranges the workgroup stores its partial tile in the workspace and arrives
+// at the tile's counter; the last of the S workgroups to arrive adds the S
+// partials in slot order and writes the logits, so the result does not
+// depend on which workgroup came last.
+//
+// Counter word of a tile: a fixed signature in the high 32 bits and the
+// arrivals of the current call in the low 32; at rest (between calls) the
+// count is zero.  An arrival adds one (a single atomic, no retries: the S
+// workgroups of a tile arrive nearly together, and an exchange loop cost
+// one memory round trip per lost race).  A word not at rest -- memory never
+// used by this kernel, whatever it holds -- is detected by its high half
+// and counted by exchange instead: the first exchange writes the signature
+// with one arrival, so the workspace needs no clearing.  The last arriver
+// sets the count back to zero.
+constexpr uint32_t kCounterSig = 0x52544731u;
+
+__device__ inline bool arrive_last(unsigned long long* cnt, int S) {
+  const unsigned long long rest = (unsigned long long)kCounterSig << 32;
+  const unsigned long long old = atomicAdd(cnt, 1ull);
+  if ((old >> 32) == kCounterSig && (uint32_t)old < (uint32_t)S)
+    return (uint32_t)old == (uint32_t)(S - 1);
+  // Each failed exchange returns the word as another arrival left it (at
+  // most S - 1 counted arrivals and S - 1 additions to the stale word), or
+  // once a stale guess, so 2 S attempts always suffice.
+  unsigned long long cur = old + 1;
+  for (int it = 0; it < 2 * S; ++it) {
+    const unsigned long long next =
+        ((cur >> 32) == kCounterSig && (uint32_t)cur < (uint32_t)S) ? cur + 1 : rest + 1;
+    const unsigned long long seen = atomicCAS(cnt, cur, next);
+    if (seen == cur) return (uint32_t)next == (uint32_t)S;
+    cur = seen;
+  }
+  return false;
+}
+
+constexpr int kFusedTN = 16;          // experts per fused tile
+constexpr int kFusedNS = 4;           // K steps per wave per load group
+
+template <int MB>
+__global__ __launch_bounds__(64 * kWaves) void hda_router_fused_kernel(RouterArgs a, float* part,
+                                                                      unsigned long long* cnt) {
+  constexpr int TM = 16 * MB, TN = kFusedTN, NT = TM * TN, NS = kFusedNS;
+  __shared__ float red[kWaves][NT];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, kg = lane >> 4;
+  const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TN, s = blockIdx.z, S = gridDim.z;
+  const int kb = s * a.k_per_wg;
+  const int ke = min(a.H, kb + a.k_per_wg);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (int64_t)a.T * a.H * 2);
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.w_hi, (int64_t)a.E * a.H * 2);
+  const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.w_lo, (int64_t)a.E * a.H * 2);
+  constexpr int kOut = 0x7ffffff0;     // an offset past every range: reads zero
+
+  f32x4 acc_hi[MB], acc_lo[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc_hi[m] = acc_lo[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int64_t xoff[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) xoff[m] = ((int64_t)(t0 + 16 * m + i) * a.H + 8 * kg) * 2;
+  const int64_t woff = ((int64_t)(e0 + i) * a.H + 8 * kg) * 2;
+  for (int g = kb + kStepK * wave; g < ke; g += kStepK * kWaves * NS) {
+    bf16x8 xa[NS][MB], wh[NS], wl[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int k = g + kStepK * kWaves * j;
+      const bool in = k < ke;
+#pragma unroll
+      for (int m = 0; m < MB; ++m) xa[j][m] = load8(xr, in ? xoff[m] + 2 * k : kOut);
+      wh[j] = load8(hr, in ? woff + 2 * k : kOut);
+      wl[j] = load8(lr, in ? woff + 2 * k : kOut);
+    }
+    // keep the scheduler from interleaving the loads with the products
+    // (it would reuse a few registers and serialise the round trips)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        acc_hi[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j][m], wh[j], acc_hi[m], 0, 0, 0);
+        acc_lo[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j][m], wl[j], acc_lo[m], 0, 0, 0);
+      }
+  }
+  // combine the two products, then the four waves; element (tt, ee) of the
+  // tile at tt * TN + ee
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      red[wave][(16 * m + 4 * kg + r) * TN + i] = acc_hi[m][r] + acc_lo[m][r] * kResidualScale;
+  __syncthreads();
+  // thread q < NT / 4 owns elements 4q .. 4q + 3: token 4q / TN, four experts
+  const int q = tid;
+  const bool owner = q < NT / 4;
+  const int tt = 4 * q / TN, ee = 4 * q % TN;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (owner) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = 4 * q + c;
+      v[c] = (red[0][idx] + red[1][idx]) + (red[2][idx] + red[3][idx]);
+    }
+  }
+  const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+  if (S > 1) {
+    if (owner) reinterpret_cast<f32x4*>(part + ((int64_t)tile * S + s) * NT)[q] = v;
+    // Every wave waits for its own stores to reach the L2; after the barrier
+    // one wave releases the partial tile (an L2 write-back) and arrives.  A
+    // release in every wave, or a full fence (which also invalidates the
+    // L2), multiplied that cost.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (wave == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (lane == 0) s_last = arrive_last(cnt + tile, S);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other workgroups' partials
+    if (owner) {
+      // every load of a batch issued (indices clamped, no branches) before
+      // the first addition; the additions keep slot order
+      constexpr int kB = 16;           // partials in flight per thread
+      const f32x4* src = reinterpret_cast<const f32x4*>(part + (int64_t)tile * S * NT) + q;
+      for (int s0 = 0; s0 < S; s0 += kB) {
+        f32x4 pv[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) pv[u] = src[(int64_t)min(s0 + u, S - 1) * (NT / 4)];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+          if (s0 + u < S) v = (s0 + u == 0) ? pv[u] : v + pv[u];
+      }
+    }
+    if (tid == 0) atomicExch(cnt + tile, (unsigned long long)kCounterSig << 32);
+  }
+  const int t = t0 + tt;
+  if (owner && t < a.T) {
+    float* o = a.out + (int64_t)t * a.E + e0 + ee;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (e0 + ee + c < a.E) o[c] = v[c];
+  }
+}
+
 // Sum of the S partial tiles, in slot order.  The loads of a batch of
 // kBatch partials are all issued before any is added (one memory round trip
 // per batch instead of one per partial); the additions keep slot order.
@@ -434,12 +590,17 @@ __global__ __launch_bounds__(256) void hda_router_split_kernel(const float* __re
 // Launch shape: token tile, expert tiles, and the hidden split S.
 struct RouterShape {
   int mb, tiles_t, tiles_e, S, k_per_wg;
-  bool big;   // the LDS-staged 128 x 128 kernel
-  int gemv;   // > 0: the one-launch small-batch kernel for up to this many tokens
+  bool big;    // the LDS-staged 128 x 128 kernel
+  bool fused;  // the one-launch split kernel (16-expert tiles, last arriver adds)
+  int gemv;    // > 0: the one-launch small-batch kernel for up to this many tokens
 };
 
 // Token counts up to this take the one-launch kernel (no hidden split).
 constexpr int kGemvMaxT = 8;
+// Token counts up to this take the one-launch split kernel.
+constexpr int kFusedMaxT = 64;
+// Its hidden split: tiles x ranges about one workgroup per compute unit.
+constexpr int64_t kFusedTargetGroups = 256;
 
 // The LDS-staged 128 x 128 kernel takes a batch when its tiles, split along
 // the hidden dimension into ranges of at least 4 LDS stages (256 of K),
@@ -460,6 +621,18 @@ RouterShape router_shape(int32_t T, int32_t E, int32_t H) {
   if (T <= kGemvMaxT) {
     r.gemv = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
     r.S = 1;
+    return r;
+  }
+  if (T <= kFusedMaxT) {
+    r.fused = true;
+    r.mb = T <= 16 ? 1 : T <= 32 ? 2 : 4;
+    r.tiles_t = 1;
+    r.tiles_e = (E + kFusedTN - 1) / kFusedTN;
+    const int steps_total = H / kStepK;                    // H is a multiple of 32
+    int64_t S = (kFusedTargetGroups + r.tiles_e - 1) / r.tiles_e;
+    S = S < 1 ? 1 : (S > steps_total ? steps_total : S);
+    r.k_per_wg = (int)((steps_total + S - 1) / S) * kStepK;
+    r.S = (H + r.k_per_wg - 1) / r.k_per_wg;
     return r;
   }
   const int64_t big_tiles = (int64_t)((T + kBigM - 1) / kBigM) * ((E + kBigN - 1) / kBigN);
@@ -493,12 +666,25 @@ RouterShape router_shape(int32_t T, int32_t E, int32_t H) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Fused kernel's workspace: one 8-byte counter per tile (rounded up to 256
+// bytes), then S partial tiles of 16 MB x 16 floats per tile.
+int64_t fused_counter_bytes(const RouterShape& r) {
+  return ((int64_t)r.tiles_t * r.tiles_e * 8 + 255) / 256 * 256;
+}
+
+int64_t ws_bytes(const RouterShape& r, int32_t tokens, int32_t experts) {
+  if (r.S <= 1) return 0;
+  if (r.fused)
+    return fused_counter_bytes(r) +
+           (int64_t)r.tiles_t * r.tiles_e * r.S * (16 * r.mb) * kFusedTN * 4;
+  return (int64_t)r.S * tokens * experts * 4;
+}
+
 }  // namespace
 
 extern "C" int64_t hda_router_workspace_bytes(int32_t tokens, int32_t experts, int32_t hidden) {
   if (tokens < 1 || experts < 1 || hidden < kStepK || hidden % kStepK) return -1;
-  const RouterShape r = router_shape(tokens, experts, hidden);
-  return r.S > 1 ? (int64_t)r.S * tokens * experts * 4 : 0;
+  return ws_bytes(router_shape(tokens, experts, hidden), tokens, experts);
 }
 
 extern "C" int hda_router_split_weights(const float* w, int64_t n, void* w_hi, void* w_lo,
@@ -524,6 +710,7 @@ extern "C" int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo
   const RouterShape r = router_shape(tokens, experts, hidden);
   const int64_t need = hda_router_workspace_bytes(tokens, experts, hidden);
   if (need > 0 && (!workspace || workspace_bytes < need)) return HDA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return HDA_ERR_INVALID_ARG;
   RouterArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.w_hi = static_cast<const uint16_t*>(w_hi);
@@ -545,6 +732,18 @@ extern "C" int hda_router_gemm(const void* x, const void* w_hi, const void* w_lo
     return hipGetLastError() == hipSuccess ? HDA_OK : HDA_ERR_HIP;
   }
   const dim3 grid(r.tiles_t, r.tiles_e, r.S);
+  if (r.fused) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    unsigned long long* cnt = reinterpret_cast<unsigned long long*>(ws);
+    float* part = r.S > 1 ? reinterpret_cast<float*>(ws + fused_counter_bytes(r)) : nullptr;
+    if (r.mb == 1)
+      hipLaunchKernelGGL(hda_router_fused_kernel<1>, grid, dim3(64 * kWaves), 0, hs, a, part, cnt);
+    else if (r.mb == 2)
+      hipLaunchKernelGGL(hda_router_fused_kernel<2>, grid, dim3(64 * kWaves), 0, hs, a, part, cnt);
+    else
+      hipLaunchKernelGGL(hda_router_fused_kernel<4>, grid, dim3(64 * kWaves), 0, hs, a, part, cnt);
+    return hipGetLastError() == hipSuccess ? HDA_OK : HDA_ERR_HIP;
+  }
   if (r.big)
     hipLaunchKernelGGL(hda_router_gemm_lds_kernel, grid, dim3(64 * kBigWaves), 0, hs, a);
   else if (r.mb == 2)

@@ -452,15 +452,34 @@ def test_check_and_coverage_argument_errors(lib):
 
 def test_router_workspace_bytes_shapes(lib):
     """The launch-shape arithmetic on the host: every accepted shape gives a
-    whole number of partial tiles (S x T x E x 4 bytes, or none), small and
-    odd hidden sizes included; rejected shapes give -1."""
-    for T in (1, 5, 16, 33, 64, 100, 1000, 20000):
+    whole number of partial tiles, small and odd hidden sizes included --
+    none up to 8 tokens (one workgroup per expert over the whole hidden
+    dimension); from 9 to 64 tokens 8-byte counters for the ceil(E/16)
+    expert tiles (rounded up to 256 bytes) plus S tiles of 16 MB x 16 floats
+    each, MB = 1, 2 or 4 for up to 16, 32 or 64 tokens, S at most H/32;
+    beyond, S x T x E x 4 bytes with S at most ceil(H/128) -- and rejected
+    shapes give -1."""
+    for T in (1, 5, 8, 9, 16, 17, 33, 64, 65, 100, 1000, 20000):
         for E in (1, 24, 64, 256):
             for H in (32, 64, 96, 128, 160, 1024, 7168):
                 n = hda.hda_router_workspace_bytes(T, E, H)
-                assert n >= 0 and n % (4 * T * E) == 0
-                S = n // (4 * T * E)
-                assert S == 0 or 2 <= S <= -(-H // 128)
+                assert n >= 0
+                if T <= 8:
+                    assert n == 0
+                elif T <= 64:
+                    tiles = -(-E // 16)
+                    tm = 16 if T <= 16 else 32 if T <= 32 else 64
+                    if n:
+                        c = -(-tiles * 8 // 256) * 256
+                        assert (n - c) % (tiles * tm * 16 * 4) == 0
+                        S = (n - c) // (tiles * tm * 16 * 4)
+                        assert 2 <= S <= H // 32
+                    else:
+                        assert tiles >= 256 or H == 32
+                else:
+                    assert n % (4 * T * E) == 0
+                    S = n // (4 * T * E)
+                    assert S == 0 or 2 <= S <= -(-H // 128)
     assert hda.hda_router_workspace_bytes(4, 8, 48) == -1
     assert hda.hda_router_workspace_bytes(0, 8, 64) == -1
     assert hda.hda_router_workspace_bytes(4, 8, 0) == -1

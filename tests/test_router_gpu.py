@@ -46,8 +46,13 @@ def test_split_bit_exact():
 # up to 8 tokens: the one-launch kernel (whole hidden dimension per
 # workgroup, one expert each), also with ragged expert counts and hidden sizes
 # that leave a partial last batch of vectors
+# 9 to 64 tokens: one launch, 16-expert tiles, the last workgroup of a tile
+# adds the hidden-split partials (ragged expert counts, hidden sizes of 1 to
+# 225 K steps; 4097 experts and hidden 32 give one range, no partials)
 SHAPES = [(1, 256, 7168), (2, 256, 7168), (3, 300, 1024), (5, 24, 96), (7, 5, 7200),
-          (8, 256, 7168), (8, 256, 8192 + 2048), (16, 256, 7168), (33, 100, 7168), (64, 256, 7168),
+          (8, 256, 7168), (8, 256, 8192 + 2048), (9, 256, 7168), (16, 256, 7168), (20, 17, 96),
+          (12, 40, 32), (24, 4097, 64), (33, 100, 7168), (48, 256, 1024), (64, 256, 7168),
+          (64, 300, 7200),
           (100, 256, 7168), (257, 72, 1024), (600, 256, 7168), (1280, 256, 7168),
           (4096, 256, 7168), (16384, 256, 7168), (16300, 300, 1024),
           (4096, 256, 2080)]   # hidden % 64 == 32: a large batch on the register kernel
@@ -68,7 +73,7 @@ def test_logits_parity(T, E, H):
     o = out.cpu().numpy().astype(np.float64)
     assert torch.equal(out, out2)
     e = np.abs(o - ref)
-    print(f"T={T} E={E} H={H} S={hda.hda_router_workspace_bytes(T, E, H) // max(1, 4 * T * E)}: "
+    print(f"T={T} E={E} H={H} workspace {hda.hda_router_workspace_bytes(T, E, H)} B: "
           f"max |gpu - split ref| {e.max():.3e}, max err/bound {(e / bound).max():.3e}", flush=True)
     assert np.all(e <= bound)
     exact = oracle.router_reference(x, inp["w"])
@@ -78,3 +83,79 @@ def test_logits_parity(T, E, H):
     print(f"   vs exact fp32-weight logits: split kernel {np.abs(o - exact).max():.3e}, "
           f"torch fp32 GEMM {np.abs(f32 - exact).max():.3e}, bf16 weight only (exact sum) "
           f"{np.abs(b16 - exact).max():.3e}", flush=True)
+
+
+def _gemm(rw, x, T, ws, out=None):
+    if out is None:
+        out = torch.empty((T, rw.E), dtype=torch.float32, device="cuda:0")
+    hda.hda_router_gemm(x, rw.hi, rw.lo, T, rw.E, rw.H, out, ws, ws.numel(),
+                        torch.cuda.current_stream())
+    return out
+
+
+def test_one_launch_split_any_workspace_content():
+    """The one-launch split path (9 to 64 tokens) needs no cleared workspace:
+    a counter word without the kernel's signature is counted by exchange on
+    first use, and every call leaves the counters it used at rest.
+    Workspaces filled with random bytes, with 0xff and with zeros give
+    bitwise the same logits, over token counts that alternate on one
+    workspace -- 100 tokens take the two-launch path, whose partial tiles
+    overwrite the counters, so the next one-launch call starts from
+    arbitrary words again."""
+    w = RouterWorkload("r100", 100, 7168, 256, seed=77)
+    inp = make_router_inputs(w)
+    rw = hda.RouterWeights(inp["w"])
+    x = dev_x(inp["x"])
+    need = max(hda.hda_router_workspace_bytes(T, 256, 7168) for T in (16, 32, 64, 100))
+    assert need > 0
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(5)
+    fills = [torch.zeros(need, dtype=torch.uint8, device="cuda:0"),
+             torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0"),
+             torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda:0", generator=g)]
+    ref = {}
+    for T in (16, 32, 64, 100):
+        xt = x[:T].contiguous()
+        hi, lo = oracle.split_router_weights(inp["w"])
+        r = oracle.router_split_reference(inp["x"][:T], hi, lo)
+        bound = oracle.accumulation_bound(inp["x"][:T], hi, lo)
+        ref[T] = _gemm(rw, xt, T, torch.zeros(need, dtype=torch.uint8, device="cuda:0"))
+        torch.cuda.synchronize()
+        assert np.all(np.abs(ref[T].cpu().numpy().astype(np.float64) - r) <= bound)
+    for ws in fills:
+        for T in (16, 64, 100, 32, 64, 100, 16):
+            got = _gemm(rw, x[:T].contiguous(), T, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got, ref[T]), (T, int(ws[0]))
+
+
+def test_one_launch_split_graph_replays():
+    """The last arriver of each tile sets its counter back to rest, so every
+    replay of a captured graph of three calls -- with eager calls on the
+    same workspace in between -- gives the eager logits bit for bit."""
+    T = 48
+    w = RouterWorkload("r48", T, 7168, 256, seed=78)
+    inp = make_router_inputs(w)
+    rw = hda.RouterWeights(inp["w"])
+    x = dev_x(inp["x"])
+    ws = torch.empty(hda.hda_router_workspace_bytes(T, 256, 7168), dtype=torch.uint8,
+                     device="cuda:0")
+    eager = _gemm(rw, x, T, ws).clone()
+    out = torch.zeros_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _gemm(rw, x, T, ws, out)            # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(3):
+            _gemm(rw, x, T, ws, out)
+    for _ in range(4):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        assert torch.equal(_gemm(rw, x, T, ws), eager)
+        torch.cuda.synchronize()
