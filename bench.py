@@ -83,7 +83,7 @@ def read_probe(nbytes, reps=10):
     nbytes = (int(nbytes) + 15) // 16 * 16
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
     best = None
-    for wgs in (512, 1024, 2048):
+    for wgs in (256, 512, 1024, 2048):
         sink = torch.empty(wgs * 256, dtype=torch.int32, device="cuda:0")
         hda.hda_read_probe(buf, wgs, sink)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
