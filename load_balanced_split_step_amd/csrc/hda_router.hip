@@ -27,6 +27,7 @@
 
 
 #include "hda.h"
+#include "hda_arrive.h"
 
 namespace {
 
@@ -407,35 +408,9 @@ __global__ __launch_bounds__(kGemvThreads) void hda_router_gemv_kernel(RouterArg
 // partials in slot order and writes the logits, so the result does not
 // depend on which workgroup came last.
 //
-// Counter word of a tile: a fixed signature in the high 32 bits and the
-// arrivals of the current call in the low 32; at rest (between calls) the
-// count is zero.  An arrival adds one (a single atomic, no retries: the S
-// workgroups of a tile arrive nearly together, and an exchange loop cost
-// one memory round trip per lost race).  A word not at rest -- memory never
-// used by this kernel, whatever it holds -- is detected by its high half
-// and counted by exchange instead: the first exchange writes the signature
-// with one arrival, so the workspace needs no clearing.  The last arriver
-// sets the count back to zero.
+// Counter words of the output tiles: the last-arriver protocol of
+// hda_arrive.h with this kernel's signature.
 constexpr uint32_t kCounterSig = 0x52544731u;
-
-__device__ inline bool arrive_last(unsigned long long* cnt, int S) {
-  const unsigned long long rest = (unsigned long long)kCounterSig << 32;
-  const unsigned long long old = atomicAdd(cnt, 1ull);
-  if ((old >> 32) == kCounterSig && (uint32_t)old < (uint32_t)S)
-    return (uint32_t)old == (uint32_t)(S - 1);
-  // Each failed exchange returns the word as another arrival left it (at
-  // most S - 1 counted arrivals and S - 1 additions to the stale word), or
-  // once a stale guess, so 2 S attempts always suffice.
-  unsigned long long cur = old + 1;
-  for (int it = 0; it < 2 * S; ++it) {
-    const unsigned long long next =
-        ((cur >> 32) == kCounterSig && (uint32_t)cur < (uint32_t)S) ? cur + 1 : rest + 1;
-    const unsigned long long seen = atomicCAS(cnt, cur, next);
-    if (seen == cur) return (uint32_t)next == (uint32_t)S;
-    cur = seen;
-  }
-  return false;
-}
 
 constexpr int kFusedTN = 16;          // experts per fused tile
 constexpr int kFusedNS = 4;           // K steps per wave per load group
@@ -517,7 +492,7 @@ __global__ __launch_bounds__(64 * kWaves) void hda_router_fused_kernel(RouterArg
     __syncthreads();
     if (wave == 0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      if (lane == 0) s_last = arrive_last(cnt + tile, S);
+      if (lane == 0) s_last = hda_arrive_last<kCounterSig>(cnt + tile, S);
     }
     __syncthreads();
     if (!s_last) return;
@@ -537,7 +512,7 @@ __global__ __launch_bounds__(64 * kWaves) void hda_router_fused_kernel(RouterArg
           if (s0 + u < S) v = (s0 + u == 0) ? pv[u] : v + pv[u];
       }
     }
-    if (tid == 0) atomicExch(cnt + tile, (unsigned long long)kCounterSig << 32);
+    if (tid == 0) hda_counter_rest<kCounterSig>(cnt + tile);
   }
   const int t = t0 + tt;
   if (owner && t < a.T) {
