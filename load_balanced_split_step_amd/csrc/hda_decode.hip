@@ -513,7 +513,6 @@ struct TileSmem {
   float acc[kWaves][kMaxGroup][D];
   float m[kWaves][kMaxGroup];
   float l[kWaves][kMaxGroup];
-  __attribute__((aligned(16))) uint16_t q[kMaxGroup][D];
 };
 
 // One wave's PV accumulators into LDS: lane (i, kg) holds column 4*kg + r
