@@ -507,6 +507,13 @@ def test_router_argument_errors(lib):
     if need > 0:
         assert call() == E.HDA_ERR_WORKSPACE
         assert call(ws=FAKE + 0x4000, wsb=need - 4) == E.HDA_ERR_WORKSPACE
+    # 16 tokens take the one-launch split path: its counters and partial
+    # tiles need a workspace, 16-byte aligned
+    need16 = hda.hda_router_workspace_bytes(16, 16, 64)
+    assert need16 > 0
+    assert call(T=16) == E.HDA_ERR_WORKSPACE
+    assert call(T=16, ws=FAKE + 0x4000, wsb=need16 - 1) == E.HDA_ERR_WORKSPACE
+    assert call(T=16, ws=FAKE + 0x4008, wsb=need16) == E.HDA_ERR_INVALID_ARG
     assert lib.hda_router_split_weights(None, 10, vp(FAKE), vp(FAKE), None) == E.HDA_ERR_INVALID_ARG
     assert lib.hda_router_split_weights(vp(FAKE), 0, vp(FAKE), vp(FAKE), None) == E.HDA_ERR_INVALID_ARG
 
